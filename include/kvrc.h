@@ -1,0 +1,186 @@
+/*
+ * kvrc.h - C ABI of the MI355X (gfx950) library for latent-attention KV
+ * preprocessing: the fused RMSNorm + interleaved RoPE + cache scatter of the
+ * per-token key row, and QSAPrepare block-key compression.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is caller-owned DEVICE memory of the current HIP
+ *   device. The library allocates nothing, keeps no state between calls and
+ *   needs no workspace; it is safe to call from several host threads.
+ * - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *   Buffers must stay valid until that work has completed. Caches are
+ *   updated in place.
+ * - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t). All tensors
+ *   are dense row-major with the shapes given below, and every base pointer
+ *   must be 16-byte aligned.
+ * - Problems the host can see are reported synchronously, before anything is
+ *   launched, by the returned status (kvrc_status); nothing is written then.
+ *   Problems only the device can see (an index out of range, a key_length
+ *   smaller than L, a block beyond the capacity) skip the offending token,
+ *   sequence or block, never write out of bounds, and add 1 per skipped unit
+ *   to *err_count when err_count is not NULL (an int32 in device memory that
+ *   the caller clears).
+ * - Duplicate destination indices (where the operation requires them to be
+ *   unique) are not detected; the cache contents are then undefined.
+ * - Arithmetic is IEEE float32: bf16 inputs are widened exactly, each
+ *   operation rounds to nearest even, and outputs are rounded to bf16
+ *   (nearest even) once, at the store.
+ */
+#ifndef KVRC_H
+#define KVRC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The same opaque type HIP uses for its streams. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum kvrc_status {
+    KVRC_OK = 0,
+    KVRC_ERR_NULL = 1,   /* a required pointer is NULL                           */
+    KVRC_ERR_SHAPE = 2,  /* a size is negative or violates a shape rule          */
+    KVRC_ERR_DTYPE = 3,  /* cache dtype unknown, or scale pointer does not match */
+    KVRC_ERR_ALIGN = 4,  /* a base pointer is not 16-byte aligned                */
+    KVRC_ERR_ALIAS = 5,  /* an output overlaps an input it must not overlap      */
+    KVRC_ERR_HIP = 6     /* the HIP runtime refused the launch (e.g. no device)  */
+} kvrc_status;
+
+/* Element type of the ckv cache. */
+typedef enum kvrc_cache_dtype {
+    KVRC_CACHE_BF16 = 0, /* bf16 rows, no scale                                  */
+    KVRC_CACHE_INT8 = 1  /* int8 codes + one float32 scale per row               */
+} kvrc_cache_dtype;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *kvrc_status_string(int32_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t kvrc_version(void);
+
+/*
+ * kvrc_paged_norm_rope_cache - fused key preprocessing into PAGED caches.
+ *
+ * Source: aclnnKvRmsNormRopeCache (Description; Formulas (1) interleaveRope and
+ * (2) rmsNorm; restrictions on index for the PA / PA_BNSD cache modes;
+ * quantisation scenario 1 for an int8 ckv cache) with the per-row scale rule
+ * RowMax(abs)/127 and round of aclnnMlaPrologV3WeightNz (Dequant Scale Query
+ * Nope formula).
+ *
+ * For every token t = b*S + s of kv[B, 1, S, Dv+Dk]:
+ *   v = slot_mapping[t]; v == -1 skips the token (nothing is read or written
+ *   for it);
+ *   y  = rmsnorm(kv[t, 0:Dv]) = (x / sqrt(mean(x*x) + eps)) * gamma
+ *   kr = interleaved RoPE of kv[t, Dv:Dv+Dk] with cos[t], sin[t]:
+ *        x1 = x[0::2], x2 = x[1::2], kr = cat(x1,x2)*cos + cat(-x2,x1)*sin
+ *   ckv_cache[v / block_size, v % block_size, 0, :] = bf16(y)      (BF16), or
+ *        int8 codes rint(y / scale) with scale = max|y| / 127 stored to
+ *        ckv_scale[v / block_size, v % block_size, 0]             (INT8;
+ *        an all-zero row stores scale 0 and codes 0)
+ *   k_cache[v / block_size, v % block_size, 0, :] = bf16(kr)
+ * The sum of squares uses a fixed order (pairwise sum of 64 partials, each
+ * accumulating 8-element chunks c = l, l+64, ...), so results are
+ * deterministic and independent of the launch.
+ *
+ * Arguments (shapes as in the source; N = 1 head):
+ *   kv            bf16  [B, 1, S, Dv+Dk]
+ *   gamma         bf16  [Dv]
+ *   cos, sin      bf16  [B, 1, S, Dk]        one full-width row per token
+ *   slot_mapping  int64 [B*S]                -1 or unique in [0, num_blocks*block_size)
+ *   k_cache       bf16  [num_blocks, block_size, 1, Dk]
+ *   ckv_cache     bf16 or int8 [num_blocks, block_size, 1, Dv]
+ *   ckv_scale     float32 [num_blocks, block_size, 1]; must be NULL for BF16
+ *                 and non-NULL for INT8
+ *   Dv, Dk        multiples of 8, >= 8 (Dk even is the source's rule; 8 is
+ *                 this library's vector width)
+ *   eps           added to the mean square
+ *   err_count     optional device int32, see above
+ * Returns KVRC_OK (also when B*S == 0: nothing is launched and the caches are
+ * untouched), or an error status with nothing written. The outputs must not
+ * overlap the inputs (KVRC_ERR_ALIAS).
+ */
+int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                                   const void *sin, const int64_t *slot_mapping, void *k_cache,
+                                   void *ckv_cache, float *ckv_scale, int64_t B, int64_t S,
+                                   int64_t Dv, int64_t Dk, int64_t num_blocks,
+                                   int64_t block_size, int32_t ckv_dtype, float eps,
+                                   int32_t *err_count, hipStream_t stream);
+
+/*
+ * kvrc_norm_rope_cache - the same computation into CONTIGUOUS (Norm mode)
+ * caches.
+ *
+ * Source: aclnnKvRmsNormRopeCache, restrictions on index for the Norm cache
+ * mode: index is [B, S] with values in [-1, Sc); a value may repeat only
+ * across different batches. Batch b of kv writes batch b of the caches, so
+ * Bc >= B is required.
+ *
+ *   index      int64 [B, S]                 -1 skips; unique within a batch row
+ *   k_cache    bf16  [Bc, 1, Sc, Dk]
+ *   ckv_cache  bf16 or int8 [Bc, 1, Sc, Dv]
+ *   ckv_scale  float32 [Bc, 1, Sc] (INT8 only, else NULL)
+ * Token (b, s) with v = index[b, s] >= 0 writes row [b, 0, v] of each cache.
+ * Other arguments, the returned status and err_count are as for
+ * kvrc_paged_norm_rope_cache.
+ */
+int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                             const void *sin, const int64_t *index, void *k_cache,
+                             void *ckv_cache, float *ckv_scale, int64_t B, int64_t S, int64_t Dv,
+                             int64_t Dk, int64_t Bc, int64_t Sc, int32_t ckv_dtype, float eps,
+                             int32_t *err_count, hipStream_t stream);
+
+/*
+ * qsa_prepare - one index key per complete key block, for sparse attention.
+ *
+ * Source: openvino.opset17.qsa_prepare (description and Parameters list).
+ * For every sequence n:
+ *   K = key_length[n] (key_length[0] for all when key_length_count == 1),
+ *   P = K - L past tokens (all L new tokens are valid), r = P % kbs.
+ *   History token tau is past_incomplete_raw_keys[n, tau - (P - r)] when
+ *   tau < P, else raw_index_keys[n, tau - P].
+ *   For every block b in [P / kbs, K / kbs) (the blocks the new tokens
+ *   complete):
+ *     m = (float32 sum of the block's kbs rows in token order) / kbs
+ *     z = (m / sqrt(mean(m*m) + eps)) * k_norm_weight   (skipped if NULL)
+ *     z[Di-Dr:Di] = interleaved RoPE (as in kvrc_paged_norm_rope_cache)
+ *         with the cos/sin of token b*kbs: past_incomplete_rope[n] when
+ *         b*kbs < P, else rope_cos/rope_sin[n, b*kbs - P]  (skipped if NULL)
+ *     block_keys[n, b, :] = bf16(z)
+ *   Carry state for the next call: r' = K % kbs, t1 = K - r';
+ *     next_incomplete_raw_keys[n, i] = history token t1 + i for i < r';
+ *     next_incomplete_rope[n] = cos || sin of token t1 when r' > 0.
+ *   Rows of block_keys below P / kbs (the past block keys) and rows >= r' of
+ *   the next state are not written.
+ *
+ * Arguments:
+ *   raw_index_keys            bf16 [N, L, Di]
+ *   block_keys                bf16 [N, Bcap, Di]   in/out (past keys in place)
+ *   key_length                int64 [key_length_count], count 1 or N; read on
+ *                             the device only
+ *   rope_cos, rope_sin        float32 [N, L, Dr]; both NULL disables rotation
+ *   k_norm_weight             bf16 [Di]; NULL disables normalisation
+ *   past_incomplete_raw_keys  bf16 [N, kbs-1, Di]; rows >= P % kbs unused
+ *   past_incomplete_rope      float32 [N, 2*Dr] (cos || sin); NULL iff rope off
+ *   next_incomplete_raw_keys  bf16 [N, kbs-1, Di] out; must not overlap any input
+ *   next_incomplete_rope      float32 [N, 2*Dr] out; NULL iff rope off
+ *   Di multiple of 8; Dr even, 2 <= Dr <= Di when rope is on; kbs >= 2.
+ * Returns KVRC_OK (also when N*L == 0: nothing is written, including the next
+ * state), or an error status with nothing written. On the device a sequence
+ * with K < L, or whose blocks reach past Bcap, is skipped (err_count).
+ */
+int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t *key_length,
+                    int64_t key_length_count, const float *rope_cos, const float *rope_sin,
+                    const void *k_norm_weight, const void *past_incomplete_raw_keys,
+                    const float *past_incomplete_rope, void *next_incomplete_raw_keys,
+                    float *next_incomplete_rope, int64_t N, int64_t L, int64_t Di, int64_t Dr,
+                    int64_t Bcap, int64_t key_block_size, float eps, int32_t *err_count,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVRC_H */

@@ -85,8 +85,8 @@ uint16_t orc_f32_to_bf16(float f)
  *   - partial p[l] (l = 0..63) starts at +0 and adds, in increasing c over
  *     the chunks with c mod 64 == l, each element's square x*x (rounded
  *     product, then rounded sum), elements in increasing order;
- *   - the 64 partials are then added pairwise level by level,
- *     p[k] <- p[2k] + p[2k+1], until one value is left.
+ *   - the 64 partials are then folded in halves, level by level:
+ *     p[k] <- p[k] + p[k + w/2] for k < w/2, with w = 64, 32, ..., 2.
  */
 float orc_sumsq_canonical(const float *v, int64_t n)
 {
@@ -101,9 +101,9 @@ float orc_sumsq_canonical(const float *v, int64_t n)
             p[l] = p[l] + sq;
         }
     }
-    for (int width = 64; width > 1; width /= 2)
-        for (int k = 0; k < width / 2; ++k)
-            p[k] = p[2 * k] + p[2 * k + 1];
+    for (int w = 64; w > 1; w /= 2)
+        for (int k = 0; k < w / 2; ++k)
+            p[k] = p[k] + p[k + w / 2];
     return p[0];
 }
 
