@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the fused norm-rope-cache hot path on one MI355X.
+
+One step = one call of the entry point over one batch of the workload
+(default: the paged prefill batch B=8, S=4096, D=576 into PA_BNSD caches
+[8192, 128, 1, 512/64] bf16). Inputs are synthetic and seeded (gen/), already
+resident in HBM when the timed region starts.
+
+Measurement:
+  * R independent buffer sets (inputs and caches) are rotated so that the
+    touched bytes of R consecutive steps exceed the 256 MB Infinity Cache;
+    every step therefore reads its inputs from HBM;
+  * the launches are captured once into a HIP graph (one launch per buffer
+    set) and replayed, so host launch overhead does not enter the timing;
+  * HIP events on the launch stream bracket the K timed steps (after W
+    warm-up steps); ms_per_step and the kernel's average duration are
+    elapsed / K;
+  * roofline: algorithmic bytes per launch (bytes the method must move:
+    kv + cos/sin + index + cache rows written) / average duration, against
+    the MI355X HBM3E peak of 8 TB/s;
+  * traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    scaled by the same counters' reading on a plain copy of known size, read
+    from profiles/traffic_<workload>.json and reported only if the kernel
+    sources are unchanged since the counters were taken (else null);
+  * cpu_baseline: the CPU oracle on the host cores, on the same batch,
+    repeated for about 10 s (rank 0, one GPU only).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s and achieved HBM GB/s (% of MI355X peak), fused norm-rope-cache"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["latent_attention_kv_amd/csrc/norm_rope_cache.hip",
+                  "latent_attention_kv_amd/csrc/qsa_prepare.hip",
+                  "latent_attention_kv_amd/csrc/device_common.hpp",
+                  "latent_attention_kv_amd/csrc/kvrc_launch.hpp"]
+
+WORKLOAD_TEXT = {
+    "prefill_paged": "paged prefill: B=8, S=4096 (32768 tokens), kv [8,1,4096,576] bf16 "
+                     "(Dv=512 RMSNorm, Dk=64 interleaved RoPE), PA_BNSD caches "
+                     "[8192,128,1,512] + [8192,128,1,64] bf16, 32 blocks per sequence",
+    "decode_paged": "paged decode: B=256, S=1, D=576 bf16, caches [4096,128,1,512/64] bf16, "
+                    "unique random slots, 5% skipped (-1)",
+    "quant_paged": "paged int8 ckv cache: B=64, S=1024, D=576 bf16 (sigma 2), ckv int8 "
+                   "[4096,128,1,512] + fp32 scale [4096,128,1], k bf16 [4096,128,1,64]",
+    "norm_tiny": "Norm cache mode: B=2, S=16, D=576, caches [2,1,32,d] bf16",
+    "qsa": "QSAPrepare block keys: N=32, L=2048, Di=128, Dr=64, key_block_size=64",
+}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case) -> tuple[int, int]:
+    """(bytes per launch, tokens per launch) the method must move."""
+    import gen
+    if "raw_index_keys" in case:
+        N, L, Di, Dr, kbs = case["N"], case["L"], case["Di"], case["Dr"], case["kbs"]
+        total = 0
+        for n in range(N):
+            K = int(case["key_length"][n % len(case["key_length"])])
+            P = K - L
+            r, r2 = P % kbs, K % kbs
+            nb = K // kbs - P // kbs
+            total += L * Di * 2 + (r if nb else 0) * Di * 2      # new rows + carried rows read
+            total += nb * (2 * Dr * 4 + Di * 2)                   # first-token rope row + key out
+            total += r2 * Di * 2 * 2 + (2 * Dr * 4 * 2 if r2 else 0)  # carry copy in/out
+            total += 8                                            # key_length
+        return total + Di * 2, N * L
+    T = case["B"] * case["S"]
+    idx = case["slot_mapping"] if case["mode"] == "paged" else case["index"].reshape(-1)
+    written = int((idx >= 0).sum())
+    per = gen.kvrc_bytes_per_written_token(case["Dv"], case["Dk"], case["ckv_dtype"])
+    return written * per + (T - written) * 8 + 2 * case["Dv"], T
+
+
+def touched_bytes(case) -> int:
+    return algorithmic_bytes(case)[0]
+
+
+def build_sets(case, R, dev):
+    """R independent device copies of the inputs and caches."""
+    import numpy as np
+    import torch
+
+    def dbf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def dt(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    sets = []
+    if "raw_index_keys" in case:
+        base = dict(raw=dbf(case["raw_index_keys"]), kl=dt(case["key_length"]),
+                    rc=dt(case["rope_cos"]), rs=dt(case["rope_sin"]), w=dbf(case["k_norm_weight"]),
+                    praw=dbf(case["past_incomplete_raw_keys"]),
+                    prope=dt(case["past_incomplete_rope"]))
+        for _ in range(R):
+            s = {k: v.clone() for k, v in base.items()}
+            s["bk"] = dbf(case["caches"]["block_keys"].numpy())
+            s["nraw"] = torch.empty_like(s["praw"])
+            s["nrope"] = torch.empty_like(s["prope"])
+            sets.append(s)
+        return sets
+    idx_name = "slot_mapping" if case["mode"] == "paged" else "index"
+    base = dict(kv=dbf(case["kv"]), gamma=dbf(case["gamma"]), cos=dbf(case["cos"]),
+                sin=dbf(case["sin"]), idx=dt(case[idx_name]))
+    for _ in range(R):
+        s = {k: v.clone() for k, v in base.items()}
+        for name, spec in case["caches"].items():
+            if spec.dtype == np.uint16:
+                fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
+                s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
+                                     device=dev).view(torch.bfloat16)
+            else:
+                tdt = torch.int8 if spec.dtype == np.int8 else torch.float32
+                s[name] = torch.full(spec.shape, spec.fill, dtype=tdt, device=dev)
+        sets.append(s)
+    return sets
+
+
+def launch(case, s):
+    import latent_attention_kv_amd as k
+    if "raw_index_keys" in case:
+        k.qsa_prepare(s["raw"], s["bk"], s["kl"], s["rc"], s["rs"], s["w"], s["praw"], s["prope"],
+                      s["nraw"], s["nrope"], key_block_size=case["kbs"], eps=case["eps"])
+    elif case["mode"] == "paged":
+        k.kvrc_paged_norm_rope_cache(s["kv"], s["gamma"], s["cos"], s["sin"], s["idx"],
+                                     s["k_cache"], s["ckv_cache"], s.get("ckv_scale"),
+                                     eps=case["eps"])
+    else:
+        k.kvrc_norm_rope_cache(s["kv"], s["gamma"], s["cos"], s["sin"], s["idx"], s["k_cache"],
+                               s["ckv_cache"], s.get("ckv_scale"), eps=case["eps"])
+
+
+def cpu_baseline(case, seconds=10.0):
+    """The oracle, as it is, on the host cores; the full batch repeated."""
+    import oracle
+    import numpy as np
+    threads = oracle.max_threads()
+    n, t0 = 0, time.perf_counter()
+    busy = 0.0
+    while True:
+        if "raw_index_keys" in case:
+            caches = None
+            s0 = time.perf_counter()
+            oracle.run_qsa_case(case, nthreads=threads)
+        else:
+            caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+            args = (case["kv"], case["gamma"], case["cos"], case["sin"])
+            s0 = time.perf_counter()
+            if case["mode"] == "paged":
+                oracle.paged_norm_rope_cache(*args, case["slot_mapping"], caches["k_cache"],
+                                             caches["ckv_cache"], caches.get("ckv_scale"),
+                                             eps=case["eps"], nthreads=threads)
+            else:
+                oracle.norm_rope_cache(*args, case["index"], caches["k_cache"], caches["ckv_cache"],
+                                       caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
+        busy += time.perf_counter() - s0
+        n += 1
+        del caches
+        if time.perf_counter() - t0 >= seconds and n >= 1:
+            break
+    _, tokens = algorithmic_bytes(case)
+    return {"value": round(tokens * n / busy, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full batch ({tokens} tokens) repeated {n} times "
+                      f"({busy:.1f} s of oracle time, input generation and cache "
+                      f"allocation excluded), OpenMP over tokens"}
+
+
+def read_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="prefill_paged", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--sets", type=int, default=0,
+                    help="buffer sets rotated (0: enough to exceed 512 MB touched)")
+    ap.add_argument("--no-graph", action="store_true", help="launch from Python each step")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size 5 times "
+                         "(counter calibration under rocprofv3)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange; no multi-GPU run exists)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gen
+    import latent_attention_kv_amd as k
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    k.lib()
+    dev = torch.device("cuda:0")
+    case = gen.make_config(args.workload)
+    bytes_per_launch, tokens = algorithmic_bytes(case)
+    R = args.sets or max(2, min(64, -(-512 * 2 ** 20 // max(1, touched_bytes(case)))))
+    sets = build_sets(case, R, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    if args.no_graph:
+        def replay():
+            with torch.cuda.stream(stream):
+                for s in sets:
+                    launch(case, s)
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for s in sets:              # one eager pass first (library loaded, args checked)
+                launch(case, s)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for s in sets:
+                launch(case, s)
+
+        def replay():
+            with torch.cuda.stream(stream):
+                g.replay()
+
+    warm_replays = max(1, -(-args.warmup // R))
+    timed_replays = max(1, -(-args.steps // R))
+    for _ in range(warm_replays):
+        replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(timed_replays):
+        replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    steps = timed_replays * R
+    ms = e0.elapsed_time(e1) / steps
+    secs = ms / 1e3
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    achieved = bytes_per_launch / secs / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / secs, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm_replays * R,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "tokens_per_step": tokens, "io_dtype": "bf16",
+                   "buffer_sets_rotated": R, "graph": not args.no_graph},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic(args.workload),
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "kernel_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

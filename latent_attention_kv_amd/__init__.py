@@ -1,0 +1,242 @@
+"""Python binding of libkvrc.so: MI355X (gfx950) latent-attention KV preprocessing.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of ``libkvrc.so``; PyTorch supplies device memory and the stream.
+There is no CPU or PyTorch fallback: if the library is missing, or a tensor
+is not on the GPU, the call raises.
+
+Entry points (same names as the C ABI in ``include/kvrc.h``):
+  * kvrc_paged_norm_rope_cache - RMSNorm + interleaved RoPE + scatter into
+    paged caches [num_blocks, block_size, 1, d] (aclnnKvRmsNormRopeCache,
+    PA_BNSD cache mode)
+  * kvrc_norm_rope_cache       - the same into contiguous caches
+    [Bc, 1, Sc, d] (Norm cache mode)
+  * qsa_prepare                - block keys (openvino.opset17.qsa_prepare)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["kvrc_paged_norm_rope_cache", "kvrc_norm_rope_cache", "qsa_prepare", "KvrcError",
+           "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "prepare_paged_norm_rope_cache",
+           "EXPORTED_SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so")
+CACHE_BF16 = 0
+CACHE_INT8 = 1
+EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
+                    "kvrc_norm_rope_cache", "qsa_prepare")
+
+_lib = None
+
+
+class KvrcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({_status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvrc.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.kvrc_status_string.argtypes = [I32]
+    L.kvrc_status_string.restype = ctypes.c_char_p
+    L.kvrc_version.restype = I32
+    L.kvrc_paged_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
+                                             I32, F, P, P]
+    L.kvrc_paged_norm_rope_cache.restype = I32
+    L.kvrc_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32,
+                                       F, P, P]
+    L.kvrc_norm_rope_cache.restype = I32
+    L.qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F,
+                              P, P]
+    L.qsa_prepare.restype = I32
+    _lib = L
+    return L
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().kvrc_status_string(status).decode()
+    except Exception:  # pragma: no cover - only when the library is missing
+        return "?"
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t, name, dtypes, ndim=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+_BF16 = (torch.bfloat16,)
+
+
+def _kv_shapes(kv, gamma, cos, sin):
+    _need(kv, "kv", _BF16, 4)
+    _need(cos, "cos", _BF16, 4)
+    _need(sin, "sin", _BF16, 4)
+    _need(gamma, "gamma", _BF16, 1)
+    B, n, S, D = kv.shape
+    Dk = cos.shape[-1]
+    Dv = D - Dk
+    if n != 1 or tuple(cos.shape) != (B, 1, S, Dk) or tuple(sin.shape) != (B, 1, S, Dk):
+        raise ValueError("kv must be [B,1,S,Dv+Dk] and cos/sin [B,1,S,Dk]")
+    if tuple(gamma.shape) != (Dv,):
+        raise ValueError("gamma must be [Dv]")
+    return B, S, Dv, Dk
+
+
+def _cache_dtype(ckv_cache, ckv_scale):
+    if ckv_cache.dtype == torch.int8:
+        _need(ckv_scale, "ckv_scale", (torch.float32,))
+        return CACHE_INT8
+    if ckv_scale is not None:
+        raise ValueError("ckv_scale is only used with an int8 ckv cache")
+    return CACHE_BF16
+
+
+def _err_ptr(err_count):
+    if err_count is None:
+        return None
+    _need(err_count, "err_count", (torch.int32,))
+    return err_count.data_ptr()
+
+
+def _check(status, what):
+    if status != 0:
+        raise KvrcError(status, what)
+
+
+def _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale, eps,
+                err_count, stream):
+    B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if slot_mapping.numel() != B * S:
+        raise ValueError("slot_mapping must have B*S entries")
+    if tuple(k_cache.shape) != (NB, BS, 1, Dk) or tuple(ckv_cache.shape) != (NB, BS, 1, Dv):
+        raise ValueError("caches must be [num_blocks, block_size, 1, Dk] and [.., Dv]")
+    dt = _cache_dtype(ckv_cache, ckv_scale)
+    if ckv_scale is not None and tuple(ckv_scale.shape) != (NB, BS, 1):
+        raise ValueError("ckv_scale must be [num_blocks, block_size, 1]")
+    return (_ptr(kv), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(slot_mapping), _ptr(k_cache),
+            _ptr(ckv_cache), _ptr(ckv_scale), B, S, Dv, Dk, NB, BS, dt, float(eps),
+            _err_ptr(err_count), _stream(stream))
+
+
+def kvrc_paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
+                               ckv_scale=None, *, eps=1e-6, err_count=None, stream=None):
+    """Paged (PA_BNSD) fused norm-rope-cache; updates the caches in place."""
+    args = _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale, eps,
+                       err_count, stream)
+    _check(lib().kvrc_paged_norm_rope_cache(*args), "kvrc_paged_norm_rope_cache")
+
+
+def prepare_paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
+                                  ckv_scale=None, *, eps=1e-6, err_count=None, stream=None):
+    """Marshal the arguments once and return a no-argument callable that
+    launches the paged entry point (for repeated launches on fixed buffers)."""
+    args = _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale, eps,
+                       err_count, stream)
+    fn = lib().kvrc_paged_norm_rope_cache
+    cargs = [ctypes.c_void_p(a) if i in (0, 1, 2, 3, 4, 5, 6, 7, 16, 17) else a
+             for i, a in enumerate(args)]
+
+    def launch():
+        st = fn(*cargs)
+        if st != 0:
+            raise KvrcError(st, "kvrc_paged_norm_rope_cache")
+    return launch
+
+
+def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale=None, *,
+                         eps=1e-6, err_count=None, stream=None):
+    """Norm (contiguous) cache mode; index [B, S]; caches [Bc, 1, Sc, d]."""
+    B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
+    _need(index, "index", (torch.int64,), 2)
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    Bc, Sc = k_cache.shape[0], k_cache.shape[2]
+    if tuple(index.shape) != (B, S):
+        raise ValueError("index must be [B, S]")
+    if tuple(k_cache.shape) != (Bc, 1, Sc, Dk) or tuple(ckv_cache.shape) != (Bc, 1, Sc, Dv):
+        raise ValueError("caches must be [Bc, 1, Sc, Dk] and [Bc, 1, Sc, Dv]")
+    dt = _cache_dtype(ckv_cache, ckv_scale)
+    if ckv_scale is not None and tuple(ckv_scale.shape) != (Bc, 1, Sc):
+        raise ValueError("ckv_scale must be [Bc, 1, Sc]")
+    st = lib().kvrc_norm_rope_cache(_ptr(kv), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(index),
+                                    _ptr(k_cache), _ptr(ckv_cache), _ptr(ckv_scale), B, S, Dv, Dk,
+                                    Bc, Sc, dt, float(eps), _err_ptr(err_count), _stream(stream))
+    _check(st, "kvrc_norm_rope_cache")
+
+
+def qsa_prepare(raw_index_keys, block_keys, key_length, rope_cos, rope_sin, k_norm_weight,
+                past_incomplete_raw_keys, past_incomplete_rope, next_incomplete_raw_keys,
+                next_incomplete_rope, *, key_block_size, eps=1e-6, err_count=None, stream=None):
+    """QSAPrepare block keys; writes block_keys rows of the completed blocks and
+    the next carry state. rope_cos/rope_sin/past/next rope None disables the
+    rotation; k_norm_weight None disables the normalisation."""
+    _need(raw_index_keys, "raw_index_keys", _BF16, 3)
+    N, L, Di = raw_index_keys.shape
+    _need(block_keys, "block_keys", _BF16, 3)
+    _need(key_length, "key_length", (torch.int64,), 1)
+    _need(past_incomplete_raw_keys, "past_incomplete_raw_keys", _BF16, 3)
+    _need(next_incomplete_raw_keys, "next_incomplete_raw_keys", _BF16, 3)
+    kbs = int(key_block_size)
+    Bcap = block_keys.shape[1]
+    if tuple(block_keys.shape) != (N, Bcap, Di):
+        raise ValueError("block_keys must be [N, Bcap, Di]")
+    for name, t in (("past_incomplete_raw_keys", past_incomplete_raw_keys),
+                    ("next_incomplete_raw_keys", next_incomplete_raw_keys)):
+        if tuple(t.shape) != (N, kbs - 1, Di):
+            raise ValueError(f"{name} must be [N, key_block_size-1, Di]")
+    Dr = 0
+    if rope_cos is not None:
+        _need(rope_cos, "rope_cos", (torch.float32,), 3)
+        _need(rope_sin, "rope_sin", (torch.float32,), 3)
+        Dr = rope_cos.shape[-1]
+        if tuple(rope_cos.shape) != (N, L, Dr) or tuple(rope_sin.shape) != (N, L, Dr):
+            raise ValueError("rope_cos/rope_sin must be [N, L, Dr]")
+        for name, t in (("past_incomplete_rope", past_incomplete_rope),
+                        ("next_incomplete_rope", next_incomplete_rope)):
+            _need(t, name, (torch.float32,), 2)
+            if tuple(t.shape) != (N, 2 * Dr):
+                raise ValueError(f"{name} must be [N, 2*Dr]")
+    if k_norm_weight is not None:
+        _need(k_norm_weight, "k_norm_weight", _BF16, 1)
+    st = lib().qsa_prepare(_ptr(raw_index_keys), _ptr(block_keys), _ptr(key_length),
+                           key_length.numel(), _ptr(rope_cos), _ptr(rope_sin), _ptr(k_norm_weight),
+                           _ptr(past_incomplete_raw_keys), _ptr(past_incomplete_rope),
+                           _ptr(next_incomplete_raw_keys), _ptr(next_incomplete_rope), N, L, Di,
+                           Dr, Bcap, kbs, float(eps), _err_ptr(err_count), _stream(stream))
+    _check(st, "qsa_prepare")

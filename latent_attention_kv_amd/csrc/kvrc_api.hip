@@ -1,0 +1,251 @@
+// C-ABI entry points (include/kvrc.h): host-side validation, then one launch.
+//
+// Every check happens on the host before any HIP call, in this order:
+// sizes and dtype -> empty input (OK, no launch) -> NULL -> alignment ->
+// aliasing. Only then is the kernel launched on the caller's stream.
+#include "kvrc.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kvrc_launch.hpp"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range span(const void *p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b)
+{
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// a*b with overflow / negative guard (sizes here fit easily in int64).
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0)
+        return false;
+    if (a != 0 && b > INT64_MAX / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? KVRC_OK : KVRC_ERR_HIP; }
+
+// Shared body of the two norm-rope-cache entry points. `rows` is the number
+// of cache rows; rows_per_batch is 0 for paged caches.
+int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *cos, const void *sin,
+                               const int64_t *index, void *k_cache, void *ckv_cache,
+                               float *ckv_scale, int64_t B, int64_t S, int64_t Dv, int64_t Dk,
+                               int64_t rows, int64_t rows_per_batch, int64_t limit,
+                               int32_t ckv_dtype, float eps, int32_t *err_count,
+                               hipStream_t stream)
+{
+    if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8)
+        return KVRC_ERR_DTYPE;
+    if (B < 0 || S < 0 || rows < 0 || limit < 0)
+        return KVRC_ERR_SHAPE;
+    if (Dv < 8 || Dk < 8 || Dv % 8 || Dk % 8)
+        return KVRC_ERR_SHAPE;
+    int64_t T, D = Dv + Dk;
+    if (!mul_ok(B, S, &T) || T > (int64_t)INT32_MAX)
+        return KVRC_ERR_SHAPE;
+    if (T == 0)
+        return KVRC_OK;                       // empty input: caches untouched
+
+    if (!kv || !gamma || !cos || !sin || !index || !k_cache || !ckv_cache)
+        return KVRC_ERR_NULL;
+    const bool int8 = ckv_dtype == KVRC_CACHE_INT8;
+    if (int8 != (ckv_scale != nullptr))
+        return KVRC_ERR_DTYPE;
+    if (!aligned(kv, 16) || !aligned(gamma, 16) || !aligned(cos, 16) || !aligned(sin, 16) ||
+        !aligned(index, 8) || !aligned(k_cache, 16) || !aligned(ckv_cache, 16) ||
+        !aligned(ckv_scale, 4) || !aligned(err_count, 4))
+        return KVRC_ERR_ALIGN;
+
+    int64_t kbytes, cbytes, sbytes = 0;
+    if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (int8 ? 1 : 2), &cbytes) ||
+        (int8 && !mul_ok(rows, 4, &sbytes)))
+        return KVRC_ERR_SHAPE;
+    const Range in[] = {span(kv, T * D * 2), span(gamma, Dv * 2), span(cos, T * Dk * 2),
+                        span(sin, T * Dk * 2), span(index, T * 8)};
+    const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
+                         span(err_count, err_count ? 4 : 0)};
+    for (const Range &o : out) {
+        for (const Range &i : in)
+            if (overlap(o, i))
+                return KVRC_ERR_ALIAS;
+        for (const Range &o2 : out)
+            if (&o2 != &o && overlap(o, o2))
+                return KVRC_ERR_ALIAS;
+    }
+
+    kvrc::NormRopeCacheArgs a;
+    a.kv = static_cast<const uint16_t *>(kv);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.cos = static_cast<const uint16_t *>(cos);
+    a.sin = static_cast<const uint16_t *>(sin);
+    a.index = index;
+    a.k_cache = static_cast<uint16_t *>(k_cache);
+    a.ckv_cache = ckv_cache;
+    a.ckv_scale = ckv_scale;
+    a.T = T;
+    a.S = S;
+    a.Dv = Dv;
+    a.Dk = Dk;
+    a.rows_per_batch = rows_per_batch;
+    a.limit = limit;
+    a.int8 = int8;
+    a.eps = eps;
+    a.err = err_count;
+    (void)hipGetLastError();                  // start from a clean error state
+    return launch_status(kvrc::launch_norm_rope_cache(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvrc_status_string(int32_t status)
+{
+    switch (status) {
+    case KVRC_OK: return "ok";
+    case KVRC_ERR_NULL: return "required pointer is NULL";
+    case KVRC_ERR_SHAPE: return "invalid size or shape";
+    case KVRC_ERR_DTYPE: return "invalid cache dtype or scale pointer";
+    case KVRC_ERR_ALIGN: return "pointer not aligned";
+    case KVRC_ERR_ALIAS: return "output overlaps another buffer";
+    case KVRC_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t kvrc_version(void) { return 100; }
+
+int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                                   const void *sin, const int64_t *slot_mapping, void *k_cache,
+                                   void *ckv_cache, float *ckv_scale, int64_t B, int64_t S,
+                                   int64_t Dv, int64_t Dk, int64_t num_blocks,
+                                   int64_t block_size, int32_t ckv_dtype, float eps,
+                                   int32_t *err_count, hipStream_t stream)
+{
+    int64_t rows;
+    if (num_blocks < 0 || block_size < 1 || !mul_ok(num_blocks, block_size, &rows))
+        return KVRC_ERR_SHAPE;
+    return norm_rope_cache_common(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
+                                  ckv_scale, B, S, Dv, Dk, rows, 0, rows, ckv_dtype, eps,
+                                  err_count, stream);
+}
+
+int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                             const void *sin, const int64_t *index, void *k_cache,
+                             void *ckv_cache, float *ckv_scale, int64_t B, int64_t S, int64_t Dv,
+                             int64_t Dk, int64_t Bc, int64_t Sc, int32_t ckv_dtype, float eps,
+                             int32_t *err_count, hipStream_t stream)
+{
+    int64_t rows;
+    if (Bc < B || Sc < 0 || !mul_ok(Bc, Sc, &rows))
+        return KVRC_ERR_SHAPE;
+    // Sc == 0 with B*S > 0: every index must be -1; rows_per_batch stays > 0
+    // only when there are rows to address.
+    return norm_rope_cache_common(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale, B,
+                                  S, Dv, Dk, rows, Sc > 0 ? Sc : 1, Sc, ckv_dtype, eps,
+                                  err_count, stream);
+}
+
+int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t *key_length,
+                    int64_t key_length_count, const float *rope_cos, const float *rope_sin,
+                    const void *k_norm_weight, const void *past_incomplete_raw_keys,
+                    const float *past_incomplete_rope, void *next_incomplete_raw_keys,
+                    float *next_incomplete_rope, int64_t N, int64_t L, int64_t Di, int64_t Dr,
+                    int64_t Bcap, int64_t key_block_size, float eps, int32_t *err_count,
+                    hipStream_t stream)
+{
+    const int64_t kbs = key_block_size;
+    if (N < 0 || L < 0 || Bcap < 0 || kbs < 2)
+        return KVRC_ERR_SHAPE;
+    if (Di < 8 || Di % 8 || Di > kvrc::kQsaMaxDi)
+        return KVRC_ERR_SHAPE;
+    const bool rope = rope_cos != nullptr;
+    if ((rope_sin != nullptr) != rope || (past_incomplete_rope != nullptr) != rope ||
+        (next_incomplete_rope != nullptr) != rope)
+        return KVRC_ERR_NULL;
+    if (rope && (Dr < 2 || Dr % 2 || Dr > Di))
+        return KVRC_ERR_SHAPE;
+    if (N > 0 && key_length_count != 1 && key_length_count != N)
+        return KVRC_ERR_SHAPE;
+    int64_t NL, rowsN, capN;
+    if (!mul_ok(N, L, &NL) || !mul_ok(N, kbs - 1, &rowsN) || !mul_ok(N, Bcap, &capN))
+        return KVRC_ERR_SHAPE;
+    const int64_t nb_max = (kbs - 1 + L) / kbs;
+    int64_t grid;
+    if (!mul_ok(N, nb_max + 1, &grid) || grid > (int64_t)INT32_MAX)
+        return KVRC_ERR_SHAPE;
+    if (NL == 0)
+        return KVRC_OK;                       // nothing written, next state included
+
+    if (!raw_index_keys || !block_keys || !key_length || !past_incomplete_raw_keys ||
+        !next_incomplete_raw_keys)
+        return KVRC_ERR_NULL;
+    if (!aligned(raw_index_keys, 16) || !aligned(block_keys, 16) || !aligned(key_length, 8) ||
+        !aligned(k_norm_weight, 16) || !aligned(past_incomplete_raw_keys, 16) ||
+        !aligned(next_incomplete_raw_keys, 16) || !aligned(rope_cos, 4) ||
+        !aligned(rope_sin, 4) || !aligned(past_incomplete_rope, 4) ||
+        !aligned(next_incomplete_rope, 4) || !aligned(err_count, 4))
+        return KVRC_ERR_ALIGN;
+
+    const int64_t Drr = rope ? Dr : 0;
+    const Range in[] = {span(raw_index_keys, NL * Di * 2),
+                        span(key_length, key_length_count * 8),
+                        span(rope_cos, NL * Drr * 4),
+                        span(rope_sin, NL * Drr * 4),
+                        span(k_norm_weight, k_norm_weight ? Di * 2 : 0),
+                        span(past_incomplete_raw_keys, rowsN * Di * 2),
+                        span(past_incomplete_rope, N * 2 * Drr * 4)};
+    const Range out[] = {span(block_keys, capN * Di * 2),
+                         span(next_incomplete_raw_keys, rowsN * Di * 2),
+                         span(next_incomplete_rope, N * 2 * Drr * 4),
+                         span(err_count, err_count ? 4 : 0)};
+    for (const Range &o : out) {
+        for (const Range &i : in)
+            if (overlap(o, i))
+                return KVRC_ERR_ALIAS;
+        for (const Range &o2 : out)
+            if (&o2 != &o && overlap(o, o2))
+                return KVRC_ERR_ALIAS;
+    }
+
+    kvrc::QsaArgs a;
+    a.raw = static_cast<const uint16_t *>(raw_index_keys);
+    a.block_keys = static_cast<uint16_t *>(block_keys);
+    a.key_length = key_length;
+    a.klc = key_length_count;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.weight = static_cast<const uint16_t *>(k_norm_weight);
+    a.past_raw = static_cast<const uint16_t *>(past_incomplete_raw_keys);
+    a.past_rope = past_incomplete_rope;
+    a.next_raw = static_cast<uint16_t *>(next_incomplete_raw_keys);
+    a.next_rope = next_incomplete_rope;
+    a.N = N;
+    a.L = L;
+    a.Di = Di;
+    a.Dr = Drr;
+    a.Bcap = Bcap;
+    a.kbs = kbs;
+    a.eps = eps;
+    a.err = err_count;
+    (void)hipGetLastError();
+    return launch_status(kvrc::launch_qsa_prepare(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI entry points (kvrc_api.hip,
+// which validates every argument on the host) and the kernels. Nothing here
+// re-validates: callers pass checked arguments only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvrc {
+
+// One fused norm-rope-cache launch. A token t in [0, T) with index value v
+// writes cache row
+//   rows_per_batch == 0 : v                              (paged mode)
+//   rows_per_batch  > 0 : (t / S) * rows_per_batch + v   (Norm mode)
+// when 0 <= v < limit; v == -1 skips it; any other v is counted in err.
+struct NormRopeCacheArgs {
+    const uint16_t *kv;       // [T, Dv + Dk] bf16
+    const uint16_t *gamma;    // [Dv] bf16
+    const uint16_t *cos;      // [T, Dk] bf16
+    const uint16_t *sin;      // [T, Dk] bf16
+    const int64_t *index;     // [T]
+    uint16_t *k_cache;        // [rows, Dk] bf16
+    void *ckv_cache;          // [rows, Dv] bf16 or int8
+    float *ckv_scale;         // [rows] (int8 only)
+    int64_t T, S, Dv, Dk;
+    int64_t rows_per_batch;   // 0 = paged
+    int64_t limit;            // exclusive bound of a valid index value
+    bool int8;
+    float eps;
+    int32_t *err;             // nullable
+};
+
+hipError_t launch_norm_rope_cache(const NormRopeCacheArgs &a, hipStream_t stream);
+
+// One QSAPrepare launch (see qsa_prepare in kvrc.h for the semantics).
+struct QsaArgs {
+    const uint16_t *raw;          // [N, L, Di]
+    uint16_t *block_keys;         // [N, Bcap, Di]
+    const int64_t *key_length;    // [klc]
+    int64_t klc;
+    const float *rope_cos;        // [N, L, Dr] or null
+    const float *rope_sin;
+    const uint16_t *weight;       // [Di] or null
+    const uint16_t *past_raw;     // [N, kbs-1, Di]
+    const float *past_rope;       // [N, 2 Dr] or null
+    uint16_t *next_raw;           // [N, kbs-1, Di]
+    float *next_rope;             // [N, 2 Dr] or null
+    int64_t N, L, Di, Dr, Bcap, kbs;
+    float eps;
+    int32_t *err;
+};
+
+hipError_t launch_qsa_prepare(const QsaArgs &a, hipStream_t stream);
+
+// Largest Di qsa_prepare accepts (bounded by the per-lane accumulators).
+constexpr int64_t kQsaMaxDi = 4096;
+
+}  // namespace kvrc

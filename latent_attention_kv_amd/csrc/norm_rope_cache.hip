@@ -1,0 +1,307 @@
+// Fused RMSNorm + interleaved RoPE + cache scatter for gfx950 (MI355X).
+//
+// Computes, per token (aclnnKvRmsNormRopeCache, Description and Formulas (1)
+// interleaveRope, (2) rmsNorm; int8 rows use the RowMax(abs)/127 + round rule
+// of aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula):
+//   y  = (x / sqrt(sum(x*x)/Dv + eps)) * gamma          on kv[t, 0:Dv]
+//   kr = cat(x1, x2) * cos + cat(-x2, x1) * sin          on kv[t, Dv:Dv+Dk]
+//   ckv_cache[row] = bf16(y)  or  int8 rint(y / (max|y| / 127)) + scale
+//   k_cache[row]   = bf16(kr)
+//
+// Design (HBM-bound; nothing here is a dense contraction, so no MFMA):
+//   * one wavefront owns TPW whole token rows; the 64 lanes split into TPW
+//     groups of 64/TPW lanes, one group per row;
+//   * a group reads its kv row with coalesced 16-byte loads: lane l holds the
+//     8-element chunks l, l + 64/TPW, ... so every load instruction covers a
+//     contiguous stretch of the row, and writes the ckv row back the same way;
+//   * the square sum runs in a fixed order (per-chunk partials folded in
+//     halves: in-lane first, then xor shuffles), so the result is the same for
+//     every TPW (the order stated in include/kvrc.h);
+//   * the RoPE half is spread so that each lane produces 64/(64/TPW)
+//     consecutive outputs: one contiguous store per lane;
+//   * x/rms, amax/127 and y/scale are IEEE divisions and sqrt is correctly
+//     rounded, so the int8 codes are bit-identical to the float32 definition.
+//
+// The specialised kernel handles Dv = 512, Dk = 64 (the DeepSeek-V3 latent
+// key row); every other multiple-of-8 shape takes the generic kernel (one
+// token per wavefront, loops over chunks).
+#include "device_common.hpp"
+#include "kvrc_launch.hpp"
+
+namespace kvrc {
+namespace {
+
+constexpr int kThreads = 256;             // 4 wavefronts per workgroup
+constexpr int kWaves = kThreads / 64;
+
+// Destination row of token t, or -1 (skip). Counts invalid index values.
+__device__ __forceinline__ int64_t dest_row(const NormRopeCacheArgs &a, int64_t t, bool leader)
+{
+    const int64_t v = a.index[t];
+    if (v >= 0 && v < a.limit)
+        return a.rows_per_batch ? (t / a.S) * a.rows_per_batch + v : v;
+    if (v != -1 && leader && a.err)
+        atomicAdd(a.err, 1);
+    return -1;
+}
+
+// RoPE output o of a row (0 <= o < dk): pair i = o mod dk/2.
+__device__ __forceinline__ float rope_out(float xe, float xo, float c, float s, bool upper)
+{
+    // lower half: x[2i]*c - x[2i+1]*s ; upper half: x[2i+1]*c + x[2i]*s
+    const float p1 = (upper ? xo : xe) * c;
+    const float p2 = (upper ? xe : xo) * s;
+    return upper ? p1 + p2 : p1 - p2;
+}
+
+// ---------------------------------------------------------------------------
+// Dv = 512, Dk = 64: TPW token rows per wavefront.
+// ---------------------------------------------------------------------------
+template <int TPW, bool INT8>
+__global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheArgs a)
+{
+    constexpr int DV = 512, DK = 64, D = DV + DK;
+    constexpr int LPT = 64 / TPW;         // lanes per token row
+    constexpr int NCH = DV / 8 / LPT;     // 16-byte chunks of the norm half per lane
+    constexpr int ROUT = DK / LPT;        // RoPE outputs per lane
+
+    const int lane = threadIdx.x & 63;
+    const int l = lane % LPT;
+    const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t t = wave * TPW + lane / LPT;
+    if (t >= a.T)
+        return;
+    const int64_t row = dest_row(a, t, l == 0);
+    if (row < 0)
+        return;
+
+    // ---- loads: norm half, gamma, RoPE half, cos/sin -----------------------
+    const uint16_t *xr = a.kv + t * D;
+    uint4 xq[NCH], gq[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = l + LPT * j;
+        xq[j] = *reinterpret_cast<const uint4 *>(xr + 8 * c);
+        gq[j] = *reinterpret_cast<const uint4 *>(a.gamma + 8 * c);
+    }
+    const int o0 = l * ROUT;              // first RoPE output of this lane
+    const bool upper = o0 >= DK / 2;
+    const int i0 = o0 & (DK / 2 - 1);     // first pair index
+    float xe[ROUT], xo[ROUT], cv[ROUT], sv[ROUT];
+    {
+        const uint16_t *pr = xr + DV + 2 * i0;
+        const uint16_t *cr = a.cos + t * DK + o0;
+        const uint16_t *sr = a.sin + t * DK + o0;
+        if constexpr (ROUT == 1) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(pr);
+            xe[0] = bf16_lo(w); xo[0] = bf16_hi(w);
+            cv[0] = __uint_as_float((uint32_t)*cr << 16);
+            sv[0] = __uint_as_float((uint32_t)*sr << 16);
+        } else if constexpr (ROUT == 2) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(pr);
+            const uint32_t cw = *reinterpret_cast<const uint32_t *>(cr);
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(sr);
+            xe[0] = bf16_lo(w.x); xo[0] = bf16_hi(w.x);
+            xe[1] = bf16_lo(w.y); xo[1] = bf16_hi(w.y);
+            cv[0] = bf16_lo(cw); cv[1] = bf16_hi(cw);
+            sv[0] = bf16_lo(sw); sv[1] = bf16_hi(sw);
+        } else {
+            static_assert(ROUT == 4, "TPW must be 1, 2 or 4");
+            const uint4 w = *reinterpret_cast<const uint4 *>(pr);
+            const uint2 cw = *reinterpret_cast<const uint2 *>(cr);
+            const uint2 sw = *reinterpret_cast<const uint2 *>(sr);
+            xe[0] = bf16_lo(w.x); xo[0] = bf16_hi(w.x);
+            xe[1] = bf16_lo(w.y); xo[1] = bf16_hi(w.y);
+            xe[2] = bf16_lo(w.z); xo[2] = bf16_hi(w.z);
+            xe[3] = bf16_lo(w.w); xo[3] = bf16_hi(w.w);
+            cv[0] = bf16_lo(cw.x); cv[1] = bf16_hi(cw.x);
+            cv[2] = bf16_lo(cw.y); cv[3] = bf16_hi(cw.y);
+            sv[0] = bf16_lo(sw.x); sv[1] = bf16_hi(sw.x);
+            sv[2] = bf16_lo(sw.y); sv[3] = bf16_hi(sw.y);
+        }
+    }
+
+    // ---- RMSNorm: canonical square sum -----------------------------------
+    float x[NCH][8];
+    float part[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        unpack8(xq[j], x[j]);
+        part[j] = chunk_sumsq(x[j], 0.0f);
+    }
+    // chunk l + LPT*j is partial (l + LPT*j) of 64; fold in halves in-lane
+    // (w = 64 .. LPT) and then across the LPT lanes of the row.
+#pragma unroll
+    for (int w = NCH; w > 1; w /= 2)
+#pragma unroll
+        for (int k = 0; k < w / 2; ++k)
+            part[k] = part[k] + part[k + w / 2];
+    const float ss = fold_sum<LPT>(part[0]);
+    const float ms = ss / (float)DV;
+    const float rms = sqrtf(ms + a.eps);
+
+    float y[NCH][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        float g[8];
+        unpack8(gq[j], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = x[j][e] / rms;
+            y[j][e] = q * g[e];
+        }
+    }
+
+    if constexpr (INT8) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fabsf(y[j][e]));
+        amax = fold_max<LPT>(amax);
+        const float scale = amax / 127.0f;
+        int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * DV;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            float c[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                c[e] = scale == 0.0f ? 0.0f : rintf(y[j][e] / scale);
+            *reinterpret_cast<uint2 *>(dst + 8 * (l + LPT * j)) = pack_codes8(c);
+        }
+        if (l == 0)
+            a.ckv_scale[row] = scale;
+    } else {
+        uint16_t *dst = static_cast<uint16_t *>(a.ckv_cache) + row * DV;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+            *reinterpret_cast<uint4 *>(dst + 8 * (l + LPT * j)) = pack8(y[j]);
+    }
+
+    // ---- RoPE ---------------------------------------------------------------
+    float kr[ROUT];
+#pragma unroll
+    for (int r = 0; r < ROUT; ++r)
+        kr[r] = rope_out(xe[r], xo[r], cv[r], sv[r], upper);
+    uint16_t *kd = a.k_cache + row * DK + o0;
+    if constexpr (ROUT == 1) {
+        *kd = (uint16_t)(pack_bf16x2(kr[0], 0.0f) & 0xffffu);
+    } else if constexpr (ROUT == 2) {
+        *reinterpret_cast<uint32_t *>(kd) = pack_bf16x2(kr[0], kr[1]);
+    } else {
+        uint2 q;
+        q.x = pack_bf16x2(kr[0], kr[1]);
+        q.y = pack_bf16x2(kr[2], kr[3]);
+        *reinterpret_cast<uint2 *>(kd) = q;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Any Dv, Dk that are multiples of 8: one token per wavefront.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCacheArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (t >= a.T)
+        return;
+    const int64_t row = dest_row(a, t, lane == 0);
+    if (row < 0)
+        return;
+    const int64_t Dv = a.Dv, Dk = a.Dk, D = Dv + Dk;
+    const uint16_t *xr = a.kv + t * D;
+    const int64_t nch = Dv / 8;
+
+    // partial `lane` accumulates chunks lane, lane + 64, ... in order
+    float part = 0.0f;
+    for (int64_t c = lane; c < nch; c += 64) {
+        float x[8];
+        unpack8(*reinterpret_cast<const uint4 *>(xr + 8 * c), x);
+        part = chunk_sumsq(x, part);
+    }
+    const float ss = fold_sum<64>(part);
+    const float ms = ss / (float)Dv;
+    const float rms = sqrtf(ms + a.eps);
+
+    if (a.int8) {
+        float amax = 0.0f;
+        for (int64_t c = lane; c < nch; c += 64) {
+            float x[8], g[8];
+            unpack8(*reinterpret_cast<const uint4 *>(xr + 8 * c), x);
+            unpack8(*reinterpret_cast<const uint4 *>(a.gamma + 8 * c), g);
+            for (int e = 0; e < 8; ++e) {
+                const float q = x[e] / rms;
+                amax = fmaxf(amax, fabsf(q * g[e]));
+            }
+        }
+        amax = fold_max<64>(amax);
+        const float scale = amax / 127.0f;
+        int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * Dv;
+        for (int64_t c = lane; c < nch; c += 64) {
+            float x[8], g[8], code[8];
+            unpack8(*reinterpret_cast<const uint4 *>(xr + 8 * c), x);
+            unpack8(*reinterpret_cast<const uint4 *>(a.gamma + 8 * c), g);
+            for (int e = 0; e < 8; ++e) {
+                const float q = x[e] / rms;
+                const float yv = q * g[e];
+                code[e] = scale == 0.0f ? 0.0f : rintf(yv / scale);
+            }
+            *reinterpret_cast<uint2 *>(dst + 8 * c) = pack_codes8(code);
+        }
+        if (lane == 0)
+            a.ckv_scale[row] = scale;
+    } else {
+        uint16_t *dst = static_cast<uint16_t *>(a.ckv_cache) + row * Dv;
+        for (int64_t c = lane; c < nch; c += 64) {
+            float x[8], g[8], yv[8];
+            unpack8(*reinterpret_cast<const uint4 *>(xr + 8 * c), x);
+            unpack8(*reinterpret_cast<const uint4 *>(a.gamma + 8 * c), g);
+            for (int e = 0; e < 8; ++e) {
+                const float q = x[e] / rms;
+                yv[e] = q * g[e];
+            }
+            *reinterpret_cast<uint4 *>(dst + 8 * c) = pack8(yv);
+        }
+    }
+
+    const int64_t h = Dk / 2;
+    for (int64_t o = lane; o < Dk; o += 64) {
+        const bool upper = o >= h;
+        const int64_t i = upper ? o - h : o;
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(xr + Dv + 2 * i);
+        const float c = __uint_as_float((uint32_t)a.cos[t * Dk + o] << 16);
+        const float s = __uint_as_float((uint32_t)a.sin[t * Dk + o] << 16);
+        const float v = rope_out(bf16_lo(w), bf16_hi(w), c, s, upper);
+        a.k_cache[row * Dk + o] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    }
+}
+
+template <int TPW, bool INT8>
+hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
+{
+    const int64_t tokens_per_wg = (int64_t)kWaves * TPW;
+    const int64_t grid = (a.T + tokens_per_wg - 1) / tokens_per_wg;
+    hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows per wavefront for the Dv = 512 / Dk = 64 kernel.
+#ifndef KVRC_TPW
+#define KVRC_TPW 2
+#endif
+
+hipError_t launch_norm_rope_cache(const NormRopeCacheArgs &a, hipStream_t stream)
+{
+    if (a.Dv == 512 && a.Dk == 64)
+        return a.int8 ? launch_d576<KVRC_TPW, true>(a, stream)
+                      : launch_d576<KVRC_TPW, false>(a, stream);
+    const int64_t grid = (a.T + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(norm_rope_cache_generic, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvrc

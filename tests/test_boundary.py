@@ -1,0 +1,162 @@
+"""C-ABI boundary tests that run without a GPU.
+
+* The library loads and exports exactly the functions include/kvrc.h declares.
+* Host-side validation returns the documented status before any HIP call.
+  Every call below is INVALID on purpose (or empty), so nothing is launched and
+  the fake device addresses are never dereferenced.
+* The Python binding refuses CPU tensors and a missing library (no fallback).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import latent_attention_kv_amd as k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvrc.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP = range(7)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+
+
+def test_exports_match_header():
+    names = header_functions()
+    assert names == sorted(k.EXPORTED_SYMBOLS)
+    L = k.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", k.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    assert k.lib().kvrc_version() == 100
+
+
+def test_status_strings():
+    L = k.lib()
+    for s in range(7):
+        assert L.kvrc_status_string(s)
+    assert L.kvrc_status_string(99) == b"unknown status"
+
+
+# fake, 256-byte aligned, non-overlapping "device" addresses (never touched)
+A = {name: (i + 1) << 32 for i, name in enumerate(
+    ["kv", "gamma", "cos", "sin", "idx", "kc", "ckv", "scale", "err"])}
+
+
+def paged(**over):
+    a = dict(kv=A["kv"], gamma=A["gamma"], cos=A["cos"], sin=A["sin"], idx=A["idx"], kc=A["kc"],
+             ckv=A["ckv"], scale=None, B=2, S=3, Dv=512, Dk=64, NB=4, BS=16, dt=0, eps=1e-6,
+             err=None, stream=None)
+    a.update(over)
+    return k.lib().kvrc_paged_norm_rope_cache(a["kv"], a["gamma"], a["cos"], a["sin"], a["idx"],
+                                              a["kc"], a["ckv"], a["scale"], a["B"], a["S"],
+                                              a["Dv"], a["Dk"], a["NB"], a["BS"], a["dt"],
+                                              a["eps"], a["err"], a["stream"])
+
+
+def norm(**over):
+    a = dict(kv=A["kv"], gamma=A["gamma"], cos=A["cos"], sin=A["sin"], idx=A["idx"], kc=A["kc"],
+             ckv=A["ckv"], scale=None, B=2, S=3, Dv=512, Dk=64, Bc=2, Sc=16, dt=0, eps=1e-6,
+             err=None, stream=None)
+    a.update(over)
+    return k.lib().kvrc_norm_rope_cache(a["kv"], a["gamma"], a["cos"], a["sin"], a["idx"],
+                                        a["kc"], a["ckv"], a["scale"], a["B"], a["S"], a["Dv"],
+                                        a["Dk"], a["Bc"], a["Sc"], a["dt"], a["eps"], a["err"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(kv=None), NULL), (dict(gamma=None), NULL), (dict(idx=None), NULL),
+    (dict(kc=None), NULL), (dict(ckv=None), NULL),
+    (dict(Dv=510), SHAPE), (dict(Dk=4), SHAPE), (dict(Dk=60), SHAPE), (dict(Dv=0), SHAPE),
+    (dict(B=-1), SHAPE), (dict(S=-2), SHAPE), (dict(NB=-1), SHAPE), (dict(BS=0), SHAPE),
+    (dict(B=1 << 20, S=1 << 20), SHAPE),
+    (dict(dt=2), DTYPE), (dict(dt=1), DTYPE), (dict(scale=A["scale"]), DTYPE),
+    (dict(kv=A["kv"] + 8), ALIGN), (dict(cos=A["cos"] + 2), ALIGN), (dict(idx=A["idx"] + 4), ALIGN),
+    (dict(kc=A["kc"] + 8), ALIGN), (dict(dt=1, scale=A["scale"] + 2), ALIGN),
+    (dict(err=A["err"] + 2), ALIGN),
+    (dict(kc=A["kv"]), ALIAS), (dict(ckv=A["kc"] + 4096), ALIAS), (dict(ckv=A["sin"]), ALIAS),
+    (dict(dt=1, scale=A["ckv"] + 16), ALIAS), (dict(err=A["kc"]), ALIAS),
+    (dict(B=0), OK), (dict(S=0), OK), (dict(B=0, kv=None, kc=None), OK),
+])
+def test_paged_validation(over, want):
+    assert paged(**over) == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(Bc=1), SHAPE), (dict(Sc=-1), SHAPE), (dict(sin=None), NULL), (dict(Dv=12), SHAPE),
+    (dict(dt=1), DTYPE), (dict(ckv=A["ckv"] + 8), ALIGN), (dict(ckv=A["kc"]), ALIAS),
+    (dict(B=0), OK),
+])
+def test_norm_validation(over, want):
+    assert norm(**over) == want
+
+
+Q = {name: (i + 20) << 32 for i, name in enumerate(
+    ["raw", "bk", "kl", "rc", "rs", "w", "praw", "prope", "nraw", "nrope", "err"])}
+
+
+def qsa(**over):
+    a = dict(raw=Q["raw"], bk=Q["bk"], kl=Q["kl"], klc=3, rc=Q["rc"], rs=Q["rs"], w=Q["w"],
+             praw=Q["praw"], prope=Q["prope"], nraw=Q["nraw"], nrope=Q["nrope"], N=3, L=100,
+             Di=128, Dr=64, Bcap=10, kbs=64, eps=1e-6, err=None, stream=None)
+    a.update(over)
+    return k.lib().qsa_prepare(a["raw"], a["bk"], a["kl"], a["klc"], a["rc"], a["rs"], a["w"],
+                               a["praw"], a["prope"], a["nraw"], a["nrope"], a["N"], a["L"],
+                               a["Di"], a["Dr"], a["Bcap"], a["kbs"], a["eps"], a["err"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(raw=None), NULL), (dict(bk=None), NULL), (dict(kl=None), NULL), (dict(praw=None), NULL),
+    (dict(nraw=None), NULL), (dict(rs=None), NULL), (dict(prope=None), NULL),
+    (dict(nrope=None), NULL), (dict(rc=None, rs=None, prope=None), NULL),
+    (dict(Di=12), SHAPE), (dict(Di=0), SHAPE), (dict(Di=8192), SHAPE), (dict(kbs=1), SHAPE),
+    (dict(Dr=63), SHAPE), (dict(Dr=0), SHAPE), (dict(Dr=256), SHAPE), (dict(klc=2), SHAPE),
+    (dict(N=-1), SHAPE), (dict(L=-1), SHAPE), (dict(Bcap=-1), SHAPE),
+    (dict(raw=Q["raw"] + 8), ALIGN), (dict(kl=Q["kl"] + 4), ALIGN), (dict(rc=Q["rc"] + 2), ALIGN),
+    (dict(nraw=Q["praw"]), ALIAS), (dict(bk=Q["raw"] + 64), ALIAS), (dict(nrope=Q["prope"]), ALIAS),
+    (dict(nraw=Q["bk"] + 1024), ALIAS), (dict(err=Q["bk"]), ALIAS),
+    (dict(N=0), OK), (dict(L=0), OK), (dict(L=0, raw=None), OK),
+])
+def test_qsa_validation(over, want):
+    assert qsa(**over) == want
+
+
+def test_binding_refuses_cpu_tensors():
+    bf = torch.bfloat16
+    kv = torch.zeros(1, 1, 2, 576, dtype=bf)
+    with pytest.raises(ValueError, match="GPU"):
+        k.kvrc_paged_norm_rope_cache(kv, torch.zeros(512, dtype=bf), torch.zeros(1, 1, 2, 64, dtype=bf),
+                                     torch.zeros(1, 1, 2, 64, dtype=bf),
+                                     torch.zeros(2, dtype=torch.int64),
+                                     torch.zeros(4, 4, 1, 64, dtype=bf),
+                                     torch.zeros(4, 4, 1, 512, dtype=bf))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(k, "_lib", None)
+    monkeypatch.setattr(k, "LIB_PATH", "/nonexistent/libkvrc.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        k.lib()
+
+
+def test_product_does_not_import_oracle():
+    """The library package never reaches the oracle (no CPU fallback)."""
+    pkg = os.path.join(ROOT, "latent_attention_kv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "liboracle" not in src and "kvrc_oracle" not in src, f

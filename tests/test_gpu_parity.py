@@ -1,0 +1,393 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bar (per output):
+  * placement of every written row, and every byte no token addresses:
+    bit-exact;
+  * int8 codes: bit-exact; float32 scales and carried rope rows: within
+    1e-5 relative;
+  * bf16 outputs: within 1 bf16 ulp of bf16(oracle float32).
+The five named workloads run at full size in the launch configuration the
+bench times; the edge cases cover ragged tails, skipped and invalid indices,
+other shapes (generic kernel), extreme magnitudes and QSA state chaining.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import latent_attention_kv_amd as k
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _native_library_loaded():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    L = k.lib()
+    assert L._name == k.LIB_PATH
+    yield
+
+
+def dbf(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dt(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def ordered(t):
+    """bf16 (as int16 bits) -> int32 ordered like the values; +-0 -> 0."""
+    x = t.view(torch.int16).to(torch.int32)
+    mag = x & 0x7FFF
+    return torch.where(x < 0, -mag, mag)
+
+
+# ---------------------------------------------------------------------------
+# norm-rope-cache helpers
+# ---------------------------------------------------------------------------
+
+def run_kvrc_gpu(case, err=None, index_override=None):
+    caches = {}
+    for name, spec in case["caches"].items():
+        a = spec.numpy()
+        caches[name] = dbf(a) if spec.dtype == np.uint16 else dt(a)
+    args = (dbf(case["kv"]), dbf(case["gamma"]), dbf(case["cos"]), dbf(case["sin"]))
+    if case["mode"] == "paged":
+        idx = case["slot_mapping"] if index_override is None else index_override
+        k.kvrc_paged_norm_rope_cache(*args, dt(idx), caches["k_cache"], caches["ckv_cache"],
+                                     caches.get("ckv_scale"), eps=case["eps"], err_count=err)
+    else:
+        idx = case["index"] if index_override is None else index_override
+        k.kvrc_norm_rope_cache(*args, dt(idx), caches["k_cache"], caches["ckv_cache"],
+                               caches.get("ckv_scale"), eps=case["eps"], err_count=err)
+    torch.cuda.synchronize()
+    return caches
+
+
+def written_rows(case):
+    if case["mode"] == "paged":
+        v = case["slot_mapping"]
+        return np.unique(v[v >= 0])
+    idx = case["index"]
+    rows = np.arange(case["B"])[:, None] * case["Sc"] + idx
+    return np.unique(rows[idx >= 0])
+
+
+def compare_kvrc(case, got, want, *, exact_bf16=False):
+    """Returns (max bf16 ulp, number of bf16 elements off by one)."""
+    rows = torch.from_numpy(written_rows(case)).to(DEV)
+    max_ulp, off = 0, 0
+    for name, g in got.items():
+        w = want[name]
+        if g.dtype == torch.bfloat16:
+            wd = dbf(w)
+            d = (ordered(g) - ordered(wd)).abs()
+            n_rows = d.shape[0] * (d.shape[1] if case["mode"] == "paged" else d.shape[2])
+            per_row = d.reshape(n_rows, -1).amax(dim=1)
+            untouched = torch.ones(n_rows, dtype=torch.bool, device=DEV)
+            untouched[rows] = False
+            assert int(per_row[untouched].max().item() if untouched.any() else 0) == 0, \
+                f"{name}: bytes outside the written rows changed"
+            m = int(d.max().item())
+            assert m <= (0 if exact_bf16 else 1), f"{name}: {m} bf16 ulps from the oracle"
+            max_ulp = max(max_ulp, m)
+            off += int((d > 0).sum().item())
+            del d, wd
+        elif g.dtype == torch.int8:
+            assert torch.equal(g, dt(w)), f"{name}: int8 codes differ"
+        else:
+            wd = dt(w)
+            assert torch.equal(torch.isnan(g), torch.isnan(wd))
+            rel = ((g - wd).abs() / wd.abs().clamp_min(1e-30)).nan_to_num(0.0)
+            assert float(rel.max().item()) <= 1e-5, f"{name}: relative error above 1e-5"
+    return max_ulp, off
+
+
+NAMED_KVRC = ["norm_tiny", "decode_paged", "prefill_paged", "quant_paged"]
+
+
+@pytest.mark.parametrize("name", NAMED_KVRC)
+def test_named_workload_full_size(name):
+    say(f"[parity] workload {name}")
+    case = gen.make_config(name)
+    want = oracle.run_kvrc_case(case)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_kvrc_gpu(case, err=err)
+    max_ulp, off = compare_kvrc(case, got, want)
+    assert int(err.item()) == 0
+    say(f"[parity] {name}: max bf16 ulp {max_ulp}, elements off by one ulp {off}")
+
+
+@pytest.mark.parametrize("name", NAMED_KVRC)
+def test_named_workload_bit_exact(name):
+    """Stronger than the bar: this implementation uses IEEE division and
+    square root in the oracle's order, so every output is bit-identical."""
+    say(f"[exact] workload {name}")
+    case = gen.make_config(name)
+    want = oracle.run_kvrc_case(case)
+    got = run_kvrc_gpu(case)
+    compare_kvrc(case, got, want, exact_bf16=True)
+
+
+GENERIC_SHAPES = [(8, 8), (64, 16), (128, 32), (520, 72), (1024, 128), (512, 128), (256, 64)]
+
+
+@pytest.mark.parametrize("dv,dk", GENERIC_SHAPES)
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_other_shapes_paged(dv, dk, ckv):
+    say(f"[parity] paged Dv={dv} Dk={dk} {ckv}")
+    case = gen.kvrc_paged_case(100 + dv + dk, B=3, S=37, Dv=dv, Dk=dk, num_blocks=16,
+                               block_size=16, slot_kind="random", skip_frac=0.15, ckv_dtype=ckv,
+                               max_pos=4096)
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+@pytest.mark.parametrize("B,S", [(1, 1), (1, 5), (3, 7), (2, 333), (7, 129)])
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_ragged_token_counts_d576(B, S, ckv):
+    say(f"[parity] d576 ragged B={B} S={S} {ckv}")
+    case = gen.kvrc_paged_case(200 + B * S, B=B, S=S, Dv=512, Dk=64, num_blocks=64,
+                               block_size=32, slot_kind="random", skip_frac=0.2, ckv_dtype=ckv)
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("dv,dk", [(512, 64), (64, 16)])
+def test_norm_mode(ckv, dv, dk):
+    say(f"[parity] norm mode Dv={dv} Dk={dk} {ckv}")
+    case = gen.kvrc_norm_case(300 + dv, B=5, S=21, Dv=dv, Dk=dk, Bc=6, Sc=40, n_skip=9,
+                              ckv_dtype=ckv)
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+@pytest.mark.parametrize("sigma", [1e15, 1e-20, 1e-25, 3e-3])
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_extreme_magnitudes(sigma, ckv):
+    """Large rows, rows whose squares are float32 denormals, small rows."""
+    say(f"[parity] sigma={sigma} {ckv}")
+    case = gen.kvrc_paged_case(400, B=4, S=50, Dv=512, Dk=64, num_blocks=16, block_size=16,
+                               slot_kind="random", sigma=sigma, ckv_dtype=ckv)
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_zero_rows_and_zero_eps(ckv):
+    case = gen.kvrc_paged_case(401, B=2, S=40, Dv=512, Dk=64, num_blocks=8, block_size=16,
+                               slot_kind="random", ckv_dtype=ckv)
+    case["kv"][0, 0, :7] = 0                      # all-zero rows: amax 0 -> scale 0
+    case["kv"][1, 0, 3, :100] = 0x8000            # negative zeros
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+    case["eps"] = 0.0
+    case["kv"][0, 0, :7] = gen.bf16_bits(np.ones((7, 576), np.float32))
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+def test_all_skipped_and_empty():
+    case = gen.kvrc_paged_case(402, B=2, S=9, Dv=512, Dk=64, num_blocks=4, block_size=16,
+                               slot_kind="random")
+    case["slot_mapping"][:] = -1
+    got = run_kvrc_gpu(case)
+    for name, g in got.items():
+        assert torch.equal(g.view(torch.int16) if g.dtype == torch.bfloat16 else g,
+                           dbf(case["caches"][name].numpy()).view(torch.int16))
+    empty = gen.kvrc_paged_case(403, B=0, S=9, Dv=512, Dk=64, num_blocks=4, block_size=16,
+                                slot_kind="random")
+    got = run_kvrc_gpu(empty)
+    assert torch.all(got["k_cache"].view(torch.int16) == gen.BF16_SENTINEL)
+
+
+@pytest.mark.parametrize("mode", ["paged", "norm"])
+def test_invalid_indices_are_skipped_and_counted(mode):
+    if mode == "paged":
+        case = gen.kvrc_paged_case(404, B=3, S=20, Dv=512, Dk=64, num_blocks=8, block_size=16,
+                                   slot_kind="random", skip_frac=0.1)
+        idx = case["slot_mapping"].copy()
+        limit = 8 * 16
+        flat = idx
+    else:
+        case = gen.kvrc_norm_case(405, B=3, S=20, Dv=512, Dk=64, Bc=3, Sc=32, n_skip=5)
+        idx = case["index"].copy()
+        limit = 32
+        flat = idx.reshape(-1)
+    bad_pos = [1, 7, 30]
+    flat[bad_pos[0]] = limit
+    flat[bad_pos[1]] = -2
+    flat[bad_pos[2]] = 1 << 40
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_kvrc_gpu(case, err=err, index_override=idx)
+    assert int(err.item()) == 3
+    clean = dict(case)
+    fixed = idx.copy()
+    fixed.reshape(-1)[bad_pos] = -1
+    clean["slot_mapping" if mode == "paged" else "index"] = fixed
+    compare_kvrc(clean, got, oracle.run_kvrc_case(clean), exact_bf16=True)
+
+
+def test_async_on_caller_stream():
+    """The launch goes to the given stream, ordered with the caller's work."""
+    case = gen.kvrc_paged_case(406, B=4, S=64, Dv=512, Dk=64, num_blocks=16, block_size=32,
+                               slot_kind="random")
+    want = oracle.run_kvrc_case(case)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        kc = dbf(case["caches"]["k_cache"].numpy())
+        ck = dbf(case["caches"]["ckv_cache"].numpy())
+        kv = dbf(case["kv"])
+        k.kvrc_paged_norm_rope_cache(kv, dbf(case["gamma"]), dbf(case["cos"]), dbf(case["sin"]),
+                                     dt(case["slot_mapping"]), kc, ck, eps=case["eps"], stream=s)
+    s.synchronize()
+    compare_kvrc(case, {"k_cache": kc, "ckv_cache": ck}, want, exact_bf16=True)
+
+
+# ---------------------------------------------------------------------------
+# QSA
+# ---------------------------------------------------------------------------
+
+def run_qsa_gpu(case, err=None):
+    N, Di, kbs, Dr = case["N"], case["Di"], case["kbs"], case["Dr"]
+    rope = case["rope_cos"] is not None
+    bk = dbf(case["caches"]["block_keys"].numpy())
+    nraw = dbf(np.full((N, kbs - 1, Di), 0x7FC0, dtype=np.uint16))
+    nrope = torch.full((N, 2 * Dr), float("nan"), device=DEV) if rope else None
+    w = case["k_norm_weight"]
+    k.qsa_prepare(dbf(case["raw_index_keys"]), bk, dt(case["key_length"]),
+                  dt(case["rope_cos"]) if rope else None, dt(case["rope_sin"]) if rope else None,
+                  dbf(w) if w is not None else None, dbf(case["past_incomplete_raw_keys"]),
+                  dt(case["past_incomplete_rope"]) if rope else None, nraw, nrope,
+                  key_block_size=kbs, eps=case["eps"], err_count=err)
+    torch.cuda.synchronize()
+    return bk, nraw, nrope
+
+
+def compare_qsa(got, want, *, exact=False):
+    bk, nraw, nrope = got
+    wbk, wraw, wrope = want
+    d = (ordered(bk) - ordered(dbf(wbk))).abs()
+    m = int(d.max().item())
+    assert m <= (0 if exact else 1), f"block keys: {m} bf16 ulps"
+    # rows never written keep the sentinel exactly
+    written = torch.from_numpy(wbk != gen.BF16_SENTINEL).to(DEV)
+    assert torch.equal(bk.view(torch.int16)[~written],
+                       torch.full_like(bk.view(torch.int16)[~written], gen.BF16_SENTINEL))
+    assert torch.equal(nraw.view(torch.int16), dbf(wraw).view(torch.int16)), "carried rows"
+    if wrope is not None:
+        assert torch.equal(nrope.view(torch.int32), dt(wrope).view(torch.int32)), "carried rope"
+    return m
+
+
+def test_qsa_named_workload_full_size():
+    say("[parity] workload qsa")
+    case = gen.make_config("qsa")
+    want = oracle.run_qsa_case(case)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m = compare_qsa(run_qsa_gpu(case, err=err), want)
+    assert int(err.item()) == 0
+    say(f"[parity] qsa: max bf16 ulp {m}")
+
+
+def test_qsa_named_workload_bit_exact():
+    case = gen.make_config("qsa")
+    compare_qsa(run_qsa_gpu(case), oracle.run_qsa_case(case), exact=True)
+
+
+@pytest.mark.parametrize("N,L,Di,Dr,kbs", [
+    (4, 100, 128, 64, 16), (3, 7, 64, 16, 16), (5, 1, 32, 8, 4), (2, 300, 1024, 128, 24),
+    (6, 65, 8, 2, 3), (1, 2048, 256, 256, 64), (3, 50, 136, 40, 2),
+])
+@pytest.mark.parametrize("variant", ["full", "no_norm", "no_rope", "plain", "broadcast"])
+def test_qsa_shapes_and_features(N, L, Di, Dr, kbs, variant):
+    say(f"[parity] qsa N={N} L={L} Di={Di} Dr={Dr} kbs={kbs} {variant}")
+    case = gen.qsa_case(500 + N + L + Di, N=N, L=L, Di=Di, Dr=Dr, kbs=kbs, past_max=3 * kbs + 5,
+                        key_length_count=1 if variant == "broadcast" else None)
+    if variant in ("no_norm", "plain"):
+        case["k_norm_weight"] = None
+    if variant in ("no_rope", "plain"):
+        case["rope_cos"] = case["rope_sin"] = case["past_incomplete_rope"] = None
+    compare_qsa(run_qsa_gpu(case), oracle.run_qsa_case(case), exact=True)
+
+
+def test_qsa_invalid_lengths_counted():
+    case = gen.qsa_case(600, N=4, L=40, Di=64, Dr=16, kbs=8, past_max=30)
+    kl = case["key_length"].copy()
+    kl[1] = 10                                   # K < L
+    kl[3] = 10_000                               # blocks past Bcap
+    case["key_length"] = kl
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bk, _, _ = run_qsa_gpu(case, err=err)
+    assert int(err.item()) == 2
+    assert torch.all(bk[1].view(torch.int16) == gen.BF16_SENTINEL)
+    assert torch.all(bk[3].view(torch.int16) == gen.BF16_SENTINEL)
+
+
+@pytest.mark.parametrize("seed", [700, 701])
+def test_qsa_chained_calls_match_whole_history(seed):
+    """Random chunking of each sequence's token stream across calls, with the
+    state carried by the library itself, equals (bit for bit) the oracle's
+    single call over the whole stream."""
+    rng = gen.rng_for(seed)
+    N, T, Di, Dr, kbs = 3, 400, 128, 64, 16
+    Bcap = T // kbs + 1
+    raw = gen.bf16_bits(rng.standard_normal((N, T, Di)).astype(np.float32))
+    pos = np.broadcast_to(np.arange(T), (N, T))
+    rc, rs = gen.rope_table_f32(pos, Dr)
+    w = gen.bf16_bits(rng.uniform(0.5, 1.5, Di).astype(np.float32))
+    full = dict(raw_index_keys=raw, key_length=np.full(N, T, np.int64), rope_cos=rc, rope_sin=rs,
+                k_norm_weight=w,
+                past_incomplete_raw_keys=np.full((N, kbs - 1, Di), gen.BF16_NAN, np.uint16),
+                past_incomplete_rope=np.full((N, 2 * Dr), np.nan, np.float32),
+                caches={"block_keys": gen.CacheSpec((N, Bcap, Di), np.uint16, gen.BF16_SENTINEL)},
+                N=N, L=T, Di=Di, Dr=Dr, kbs=kbs, Bcap=Bcap, eps=1e-6)
+    want_bk, _, _ = oracle.run_qsa_case(full)
+    bk = dbf(full["caches"]["block_keys"].numpy())
+    st_raw = dbf(full["past_incomplete_raw_keys"])
+    st_rope = dt(full["past_incomplete_rope"])
+    done = 0
+    while done < T:
+        L = min(int(rng.choice([1, 3, kbs - 1, kbs, kbs + 1, 5 * kbs + 3])), T - done)
+        nraw = dbf(np.full((N, kbs - 1, Di), gen.BF16_NAN, np.uint16))
+        nrope = torch.full((N, 2 * Dr), float("nan"), device=DEV)
+        k.qsa_prepare(dbf(raw[:, done:done + L]), bk, dt(np.full(N, done + L, np.int64)),
+                      dt(rc[:, done:done + L]), dt(rs[:, done:done + L]), dbf(w), st_raw, st_rope,
+                      nraw, nrope, key_block_size=kbs, eps=1e-6)
+        st_raw, st_rope = nraw, nrope
+        done += L
+    torch.cuda.synchronize()
+    assert torch.equal(bk.view(torch.int16), dbf(want_bk).view(torch.int16))
+
+
+def test_graph_replays_match_eager():
+    """The bench replays captured launches: every replay, with eager work and
+    synchronisation in between, must give the eager (oracle-equal) result."""
+    case = gen.kvrc_paged_case(800, B=2, S=300, Dv=512, Dk=64, num_blocks=16, block_size=64,
+                               slot_kind="random", skip_frac=0.05, ckv_dtype="int8")
+    want = oracle.run_kvrc_case(case)
+    ins = (dbf(case["kv"]), dbf(case["gamma"]), dbf(case["cos"]), dbf(case["sin"]),
+           dt(case["slot_mapping"]))
+    kc = dbf(case["caches"]["k_cache"].numpy())
+    ck = dt(case["caches"]["ckv_cache"].numpy())
+    sc = dt(case["caches"]["ckv_scale"].numpy())
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        k.kvrc_paged_norm_rope_cache(*ins, kc, ck, sc, eps=case["eps"])
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        k.kvrc_paged_norm_rope_cache(*ins, kc, ck, sc, eps=case["eps"])
+    for rep in range(4):
+        kc.view(torch.int16).fill_(gen.BF16_SENTINEL)      # eager reset between replays
+        ck.fill_(gen.INT8_SENTINEL)
+        sc.fill_(gen.SCALE_SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare_kvrc(case, {"k_cache": kc, "ckv_cache": ck, "ckv_scale": sc}, want,
+                     exact_bf16=True)
