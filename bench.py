@@ -13,11 +13,13 @@ Measurement:
   * the launches are captured once into a HIP graph (one launch per buffer
     set) and replayed, so host launch overhead does not enter the timing;
   * HIP events on the launch stream bracket the K timed steps (after W
-    warm-up steps); ms_per_step and the kernel's average duration are
-    elapsed / K;
+    warm-up steps): ms_per_step = elapsed / K, value = tokens / step time,
+    and the kernel's average launch duration is the same elapsed / K (one
+    launch per step; the small gaps between graph launches are included, so
+    it is slightly above rocprofv3's per-dispatch duration);
   * roofline: algorithmic bytes per launch (bytes the method must move:
-    kv + cos/sin + index + cache rows written) / average duration, against
-    the MI355X HBM3E peak of 8 TB/s;
+    kv + cos/sin + index + cache rows written) / average launch duration,
+    against the MI355X HBM3E peak of 8 TB/s;
   * traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
     scaled by the same counters' reading on a plain copy of known size, read
     from profiles/traffic_<workload>.json and reported only if the kernel
@@ -42,10 +44,14 @@ if ROOT not in sys.path:
 
 METRIC = "tokens/s and achieved HBM GB/s (% of MI355X peak), fused norm-rope-cache"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["latent_attention_kv_amd/csrc/norm_rope_cache.hip",
-                  "latent_attention_kv_amd/csrc/qsa_prepare.hip",
-                  "latent_attention_kv_amd/csrc/device_common.hpp",
-                  "latent_attention_kv_amd/csrc/kvrc_launch.hpp"]
+_COMMON_SOURCES = ["latent_attention_kv_amd/csrc/device_common.hpp",
+                   "latent_attention_kv_amd/csrc/kvrc_launch.hpp",
+                   "latent_attention_kv_amd/_build.py"]
+KERNEL_SOURCES = {
+    "kvrc": ["latent_attention_kv_amd/csrc/norm_rope_cache.hip"] + _COMMON_SOURCES,
+    "qsa": ["latent_attention_kv_amd/csrc/qsa_prepare.hip"] + _COMMON_SOURCES,
+}
+KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel"}
 
 WORKLOAD_TEXT = {
     "prefill_paged": "paged prefill: B=8, S=4096 (32768 tokens), kv [8,1,4096,576] bf16 "
@@ -60,9 +66,15 @@ WORKLOAD_TEXT = {
 }
 
 
-def source_hash() -> str:
+def kernel_family(workload: str) -> str:
+    return "qsa" if workload == "qsa" else "kvrc"
+
+
+def source_hash(workload: str) -> str:
+    """Hash of the sources that build the workload's kernel (counters taken
+    on another version of them are not reported)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel_family(workload)]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -151,20 +163,22 @@ def launch(case, s):
 
 
 def cpu_baseline(case, seconds=10.0):
-    """The oracle, as it is, on the host cores; the full batch repeated."""
+    """The oracle, as it is, on the host cores: the full batch, repeated until
+    about `seconds` of oracle time have run (caches allocated once, outside
+    the timing; each repeat rewrites the same rows with the same values)."""
     import oracle
-    import numpy as np
     threads = oracle.max_threads()
-    n, t0 = 0, time.perf_counter()
-    busy = 0.0
-    while True:
-        if "raw_index_keys" in case:
-            caches = None
+    n, busy = 0, 0.0
+    if "raw_index_keys" in case:
+        while busy < seconds or n == 0:
             s0 = time.perf_counter()
             oracle.run_qsa_case(case, nthreads=threads)
-        else:
-            caches = {k: spec.numpy() for k, spec in case["caches"].items()}
-            args = (case["kv"], case["gamma"], case["cos"], case["sin"])
+            busy += time.perf_counter() - s0
+            n += 1
+    else:
+        caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+        args = (case["kv"], case["gamma"], case["cos"], case["sin"])
+        while busy < seconds or n == 0:
             s0 = time.perf_counter()
             if case["mode"] == "paged":
                 oracle.paged_norm_rope_cache(*args, case["slot_mapping"], caches["k_cache"],
@@ -173,17 +187,15 @@ def cpu_baseline(case, seconds=10.0):
             else:
                 oracle.norm_rope_cache(*args, case["index"], caches["k_cache"], caches["ckv_cache"],
                                        caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
-        busy += time.perf_counter() - s0
-        n += 1
+            busy += time.perf_counter() - s0
+            n += 1
         del caches
-        if time.perf_counter() - t0 >= seconds and n >= 1:
-            break
     _, tokens = algorithmic_bytes(case)
     return {"value": round(tokens * n / busy, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the full batch ({tokens} tokens) repeated {n} times "
-                      f"({busy:.1f} s of oracle time, input generation and cache "
-                      f"allocation excluded), OpenMP over tokens"}
+            "sample": f"the full batch ({tokens} tokens) run {n} times by the oracle "
+                      f"({busy:.1f} s; input generation and cache allocation excluded), "
+                      f"OpenMP over tokens"}
 
 
 def read_traffic(workload):
@@ -192,9 +204,97 @@ def read_traffic(workload):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(workload):
         return None
     return t.get("bytes_per_launch")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def ingest_profile(args) -> int:
+    """Summarise rocprofv3 output of this bench into profiles/:
+    <kernel>_<workload>.md (kernel-trace stats, counters, commands) and
+    traffic_<workload>.json (HBM bytes per launch, read back by the bench).
+
+    Counters: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two --pmc runs
+    of `bench.py --calib-copy-mib 1024`; each is scaled by copy_bytes / value
+    read on the 1 GiB device copy (the last 5 copyBuffer dispatches of the
+    run), which turns the counter into bytes."""
+    w = args.workload
+    kname = KERNEL_NAME[kernel_family(w)]
+    stats = [r for r in _csv_rows(_find_csv(args.trace_dir, "kernel_stats.csv"))
+             if kname in r["Name"]]
+    if not stats:
+        raise SystemExit(f"{kname} not in the kernel-trace stats")
+    st = stats[0]
+    out = {"workload": w, "kernel": st["Name"], "source_hash": source_hash(w),
+           "trace": {"calls": int(st["Calls"]), "avg_ns": float(st["AverageNs"]),
+                     "min_ns": float(st["MinNs"]), "max_ns": float(st["MaxNs"])},
+           "commands": args.command}
+    copy_bytes = 1024 * 2 ** 20
+    for counter, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
+        rows = _csv_rows(_find_csv(d, "counter_collection.csv"))
+        mine = [float(r["Counter_Value"]) for r in rows
+                if kname in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        copies.sort(key=lambda r: int(r["Dispatch_Id"]))
+        calib = [float(r["Counter_Value"]) for r in copies[-5:]]
+        kib = sum(mine) / len(mine)
+        cal = sum(calib) / len(calib)
+        factor = copy_bytes / (cal * 1024)
+        out[counter] = {"kib_per_dispatch": round(kib, 3), "dispatches": len(mine),
+                        "copy_kib": round(cal, 3), "scale": round(factor, 5),
+                        "bytes_per_dispatch": round(kib * 1024 * factor)}
+    out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_dispatch"] + \
+        out["WRITE_SIZE"]["bytes_per_dispatch"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{w}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    import gen
+    alg, tokens = algorithmic_bytes(gen.make_config(w))
+    avg_s = out["trace"]["avg_ns"] * 1e-9
+    bench_line = open(args.bench_json).read().strip() if args.bench_json else None
+    md = [f"# {kname} - {w}", "",
+          f"Workload: {WORKLOAD_TEXT[w]}.", "",
+          "Commands (from the repository root, on one MI355X):", ""]
+    md += [f"    {c}" for c in args.command] + [""]
+    md += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+           "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|",
+           f"| `{st['Name']}` | {st['Calls']} | {float(st['AverageNs']):.1f} | {st['MinNs']} | "
+           f"{st['MaxNs']} |", "",
+           f"Algorithmic bytes per launch: {alg} ({tokens} tokens) -> "
+           f"{alg / avg_s / 1e9:.1f} GB/s at the average duration "
+           f"({alg / avg_s / 8e12 * 100:.1f} % of 8 TB/s).", "",
+           "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
+           "| counter | KiB per dispatch | on the 1 GiB copy | scale | bytes per dispatch |",
+           "|---|---|---|---|---|"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        c = out[counter]
+        md.append(f"| {counter} | {c['kib_per_dispatch']} | {c['copy_kib']} | {c['scale']} | "
+                  f"{c['bytes_per_dispatch']} |")
+    md += ["", f"Measured traffic per launch: {out['bytes_per_launch']} bytes "
+               f"({out['bytes_per_launch'] / alg * 100:.1f} % of the algorithmic bytes); "
+               f"{out['bytes_per_launch'] / avg_s / 1e9:.1f} GB/s at the average duration.",
+           "", f"Kernel sources hash: {out['source_hash']}."]
+    if bench_line:
+        md += ["", "## bench.py line of the same run", "", "    " + bench_line]
+    name = kname + ("_d576" if kname == "norm_rope_cache" else "")
+    with open(os.path.join(ROOT, "profiles", f"{name}_{w}.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+    return 0
 
 
 def main(argv=None):
@@ -211,8 +311,17 @@ def main(argv=None):
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size 5 times "
                          "(counter calibration under rocprofv3)")
+    ap.add_argument("--ingest-profile", action="store_true",
+                    help="summarise rocprofv3 output into profiles/ (no GPU needed)")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--bench-json")
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args(argv)
 
+    if args.ingest_profile:
+        return ingest_profile(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence with no exchange; no multi-GPU run exists)",
@@ -269,7 +378,7 @@ def main(argv=None):
     steps = timed_replays * R
     ms = e0.elapsed_time(e1) / steps
     secs = ms / 1e3
-
+    kernel_us = ms * 1e3
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -278,7 +387,7 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    achieved = bytes_per_launch / secs / 1e9
+    achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(tokens / secs, 1),
@@ -299,7 +408,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": read_traffic(args.workload),
                      "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "kernel_us": round(ms * 1e3, 3)},
+                     "kernel_us": round(kernel_us, 3)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

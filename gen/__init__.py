@@ -60,8 +60,8 @@ def rope_table_f64(pos, d: int):
     h = d // 2
     i = np.arange(d) % h
     inv = np.power(10000.0, -2.0 * i / d)
-    ang = pos[..., None] * inv
-    return np.cos(ang), np.sin(ang)
+    ang = np.ascontiguousarray(pos[..., None] * inv)
+    return np.ascontiguousarray(np.cos(ang)), np.ascontiguousarray(np.sin(ang))
 
 
 def rope_table_bf16(pos, d: int):
@@ -71,7 +71,7 @@ def rope_table_bf16(pos, d: int):
 
 def rope_table_f32(pos, d: int):
     c, s = rope_table_f64(pos, d)
-    return c.astype(np.float32), s.astype(np.float32)
+    return (np.ascontiguousarray(c, dtype=np.float32), np.ascontiguousarray(s, dtype=np.float32))
 
 
 class CacheSpec:

@@ -1,0 +1,40 @@
+/*
+ * kvrc_selftest.h - numerics self-test of libkvrc's device arithmetic.
+ *
+ * Not part of the method. The kernels of libkvrc reach results bit-identical
+ * to the float32 definition only if their building blocks round exactly as
+ * IEEE float32 does; this entry point runs those building blocks on the GPU
+ * for caller-chosen operands so that a test can compare them with the host's
+ * IEEE results.
+ */
+#ifndef KVRC_SELFTEST_H
+#define KVRC_SELFTEST_H
+
+#include <stdint.h>
+
+#include "kvrc.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * For i in [0, n), with all arrays float32 device memory of n elements
+ * (16-byte aligned, outputs not overlapping inputs):
+ *   q_shared[i] = the shared-divisor correctly rounded quotient a[i] / b[i]
+ *                 used by the kernels (reciprocal RN(1/b[i]) plus two
+ *                 corrections); meaningful on 2^-60 <= b <= 2^60,
+ *                 2^-64 <= |a| <= 2^66
+ *   q_ieee[i]   = a[i] / b[i] with the device's IEEE division
+ *   root[i]     = sqrtf(a[i]) with the device's correctly rounded square root
+ * Returns KVRC_OK, KVRC_ERR_NULL, KVRC_ERR_SHAPE (n < 0), KVRC_ERR_ALIGN,
+ * KVRC_ERR_ALIAS or KVRC_ERR_HIP. Asynchronous on `stream`.
+ */
+int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_shared, float *q_ieee,
+                            float *root, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVRC_SELFTEST_H */

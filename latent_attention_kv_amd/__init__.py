@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so"
 CACHE_BF16 = 0
 CACHE_INT8 = 1
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
-                    "kvrc_norm_rope_cache", "qsa_prepare")
+                    "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F,
                               P, P]
     L.qsa_prepare.restype = I32
+    L.kvrc_selftest_arith.argtypes = [P, P, P, P, P, I64, P]
+    L.kvrc_selftest_arith.restype = I32
     _lib = L
     return L
 
@@ -198,6 +200,18 @@ def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_sca
                                     _ptr(k_cache), _ptr(ckv_cache), _ptr(ckv_scale), B, S, Dv, Dk,
                                     Bc, Sc, dt, float(eps), _err_ptr(err_count), _stream(stream))
     _check(st, "kvrc_norm_rope_cache")
+
+
+def kvrc_selftest_arith(a, b, q_shared, q_ieee, root, *, stream=None):
+    """Device arithmetic self-test (include/kvrc_selftest.h); float32 tensors."""
+    for name, t in (("a", a), ("b", b), ("q_shared", q_shared), ("q_ieee", q_ieee),
+                    ("root", root)):
+        _need(t, name, (torch.float32,), 1)
+        if t.numel() != a.numel():
+            raise ValueError("all self-test arrays must have the same length")
+    st = lib().kvrc_selftest_arith(_ptr(a), _ptr(b), _ptr(q_shared), _ptr(q_ieee), _ptr(root),
+                                   a.numel(), _stream(stream))
+    _check(st, "kvrc_selftest_arith")
 
 
 def qsa_prepare(raw_index_keys, block_keys, key_length, rope_cos, rope_sin, k_norm_weight,

@@ -12,10 +12,48 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Streaming inputs (kv rows, cos/sin rows, read exactly once) are loaded with
+// the non-temporal hint, which keeps them from displacing the shared gamma
+// row and the indices in the caches. Stores use the default policy: on
+// MI355X the non-temporal hint made the cache-row writes slower.
+#ifndef KVRC_NT_LOADS
+#define KVRC_NT_LOADS 1
+#endif
+#ifndef KVRC_NT_STORES
+#define KVRC_NT_STORES 0
+#endif
+
 namespace kvrc {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const void *p)
+{
+#if KVRC_NT_LOADS
+    return __builtin_nontemporal_load(static_cast<const T *>(p));
+#else
+    return *static_cast<const T *>(p);
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void stream_store(void *p, T v)
+{
+#if KVRC_NT_STORES
+    __builtin_nontemporal_store(v, static_cast<T *>(p));
+#else
+    *static_cast<T *>(p) = v;
+#endif
+}
+
+__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ u32x4 to_u32x4(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ uint2 to_uint2(u32x2 v) { return make_uint2(v.x, v.y); }
+__device__ __forceinline__ u32x2 to_u32x2(uint2 v) { return u32x2{v.x, v.y}; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -81,6 +119,42 @@ __device__ __forceinline__ float fold_max(float v)
     for (int m = G / 2; m >= 1; m >>= 1)
         v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
+}
+
+// ---------------------------------------------------------------------------
+// Correctly rounded division with a shared divisor.
+//
+// q = RN(a / b) for many a and one b > 0: with rb = RN(1/b) from one IEEE
+// division, two Newton-Raphson corrections of the quotient
+//   q0 = RN(a * rb)
+//   q1 = RN(q0 + RN(a - q0*b) * rb)      (q1 is within one ulp of a/b)
+//   q2 = RN(q1 + (a - q1*b) * rb)        (a - q1*b is exact in an fma)
+// give q2 = RN(a / b) (Markstein's theorem: a faithful quotient corrected with
+// the correctly rounded reciprocal and the exact remainder rounds correctly),
+// provided no intermediate leaves the normal range. That holds on the domain
+//   2^-60 <= b <= 2^60  and  2^-64 <= |a| <= 2^66:
+// the quotient lies in [2^-124, 2^126], and the remainder a - q*b is zero or a
+// multiple of ulp(q)*ulp(b) > 2^-48 |a| >= 2^-112, hence normal.
+// Callers test the domain and use IEEE division outside it.
+// Five VALU operations per quotient instead of eleven.
+// ---------------------------------------------------------------------------
+constexpr float kFastDivLo = 0x1p-60f;
+constexpr float kFastDivHi = 0x1p60f;
+// Bit pattern of 2^-120: a square x*x at or above it means |x| >= 2^-60.
+constexpr uint32_t kMinSquareBits = 0x03800000u;
+
+__device__ __forceinline__ bool fast_div_divisor_ok(float b)
+{
+    return b >= kFastDivLo && b <= kFastDivHi;    // false for NaN
+}
+
+__device__ __forceinline__ float div_rn_shared(float a, float b, float rb)
+{
+    float q = a * rb;
+    float r = __builtin_fmaf(-q, b, a);
+    q = __builtin_fmaf(r, rb, q);
+    r = __builtin_fmaf(-q, b, a);
+    return __builtin_fmaf(r, rb, q);
 }
 
 // Pack eight int8 codes (given as float integral values in [-127, 127]).

@@ -19,8 +19,10 @@
 //     every TPW (the order stated in include/kvrc.h);
 //   * the RoPE half is spread so that each lane produces 64/(64/TPW)
 //     consecutive outputs: one contiguous store per lane;
-//   * x/rms, amax/127 and y/scale are IEEE divisions and sqrt is correctly
-//     rounded, so the int8 codes are bit-identical to the float32 definition.
+//   * sqrt is correctly rounded and x/rms, amax/127, y/scale are correctly
+//     rounded divisions (IEEE, or the shared-divisor form of
+//     device_common.hpp on its domain), so the outputs and the int8 codes are
+//     bit-identical to the float32 definition.
 //
 // The specialised kernel handles Dv = 512, Dk = 64 (the DeepSeek-V3 latent
 // key row); every other multiple-of-8 shape takes the generic kernel (one
@@ -31,13 +33,17 @@
 namespace kvrc {
 namespace {
 
-constexpr int kThreads = 256;             // 4 wavefronts per workgroup
+#ifndef KVRC_WG_THREADS
+#define KVRC_WG_THREADS 256                // 4 wavefronts per workgroup
+#endif
+constexpr int kThreads = KVRC_WG_THREADS;
 constexpr int kWaves = kThreads / 64;
 
-// Destination row of token t, or -1 (skip). Counts invalid index values.
-__device__ __forceinline__ int64_t dest_row(const NormRopeCacheArgs &a, int64_t t, bool leader)
+// Destination row of token t with index value v, or -1 (skip). Counts
+// invalid index values.
+__device__ __forceinline__ int64_t dest_row(const NormRopeCacheArgs &a, int64_t v, int64_t t,
+                                            bool leader)
 {
-    const int64_t v = a.index[t];
     if (v >= 0 && v < a.limit)
         return a.rows_per_batch ? (t / a.S) * a.rows_per_batch + v : v;
     if (v != -1 && leader && a.err)
@@ -71,9 +77,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
     const int64_t t = wave * TPW + lane / LPT;
     if (t >= a.T)
         return;
-    const int64_t row = dest_row(a, t, l == 0);
-    if (row < 0)
-        return;
+    // The token's inputs do not depend on its index value, so every load is
+    // issued before the index is examined and their latencies overlap; the
+    // stores alone are conditional (a skipped token's reads are wasted).
+    const int64_t v = a.index[t];
 
     // ---- loads: norm half, gamma, RoPE half, cos/sin -----------------------
     const uint16_t *xr = a.kv + t * D;
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int c = l + LPT * j;
-        xq[j] = *reinterpret_cast<const uint4 *>(xr + 8 * c);
+        xq[j] = to_uint4(stream_load<u32x4>(xr + 8 * c));
         gq[j] = *reinterpret_cast<const uint4 *>(a.gamma + 8 * c);
     }
     const int o0 = l * ROUT;              // first RoPE output of this lane
@@ -93,23 +100,23 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
         const uint16_t *cr = a.cos + t * DK + o0;
         const uint16_t *sr = a.sin + t * DK + o0;
         if constexpr (ROUT == 1) {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(pr);
+            const uint32_t w = stream_load<uint32_t>(pr);
             xe[0] = bf16_lo(w); xo[0] = bf16_hi(w);
-            cv[0] = __uint_as_float((uint32_t)*cr << 16);
-            sv[0] = __uint_as_float((uint32_t)*sr << 16);
+            cv[0] = __uint_as_float((uint32_t)stream_load<uint16_t>(cr) << 16);
+            sv[0] = __uint_as_float((uint32_t)stream_load<uint16_t>(sr) << 16);
         } else if constexpr (ROUT == 2) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(pr);
-            const uint32_t cw = *reinterpret_cast<const uint32_t *>(cr);
-            const uint32_t sw = *reinterpret_cast<const uint32_t *>(sr);
+            const uint2 w = to_uint2(stream_load<u32x2>(pr));
+            const uint32_t cw = stream_load<uint32_t>(cr);
+            const uint32_t sw = stream_load<uint32_t>(sr);
             xe[0] = bf16_lo(w.x); xo[0] = bf16_hi(w.x);
             xe[1] = bf16_lo(w.y); xo[1] = bf16_hi(w.y);
             cv[0] = bf16_lo(cw); cv[1] = bf16_hi(cw);
             sv[0] = bf16_lo(sw); sv[1] = bf16_hi(sw);
         } else {
             static_assert(ROUT == 4, "TPW must be 1, 2 or 4");
-            const uint4 w = *reinterpret_cast<const uint4 *>(pr);
-            const uint2 cw = *reinterpret_cast<const uint2 *>(cr);
-            const uint2 sw = *reinterpret_cast<const uint2 *>(sr);
+            const uint4 w = to_uint4(stream_load<u32x4>(pr));
+            const uint2 cw = to_uint2(stream_load<u32x2>(cr));
+            const uint2 sw = to_uint2(stream_load<u32x2>(sr));
             xe[0] = bf16_lo(w.x); xo[0] = bf16_hi(w.x);
             xe[1] = bf16_lo(w.y); xo[1] = bf16_hi(w.y);
             xe[2] = bf16_lo(w.z); xo[2] = bf16_hi(w.z);
@@ -121,13 +128,23 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
         }
     }
 
+    const int64_t row = dest_row(a, v, t, l == 0);
+    const bool write = row >= 0;
+
     // ---- RMSNorm: canonical square sum -----------------------------------
     float x[NCH][8];
     float part[NCH];
+    uint32_t min_sq = 0xffffffffu;        // smallest square (bits) seen by this lane
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         unpack8(xq[j], x[j]);
-        part[j] = chunk_sumsq(x[j], 0.0f);
+        part[j] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sq = x[j][e] * x[j][e];
+            part[j] = part[j] + sq;
+            min_sq = min(min_sq, __float_as_uint(sq));
+        }
     }
     // chunk l + LPT*j is partial (l + LPT*j) of 64; fold in halves in-lane
     // (w = 64 .. LPT) and then across the LPT lanes of the row.
@@ -140,15 +157,29 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
     const float ms = ss / (float)DV;
     const float rms = sqrtf(ms + a.eps);
 
+    // q = x / rms: shared-divisor division when rms and every |x| of this lane
+    // are inside its domain (|x| >= 2^-60 and |x| <= sqrt(Dv)*rms), else IEEE.
     float y[NCH][8];
+    if (fast_div_divisor_ok(rms) && min_sq >= kMinSquareBits) {
+        const float rr = 1.0f / rms;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        float g[8];
-        unpack8(gq[j], g);
+        for (int j = 0; j < NCH; ++j) {
+            float g[8];
+            unpack8(gq[j], g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float q = x[j][e] / rms;
-            y[j][e] = q * g[e];
+            for (int e = 0; e < 8; ++e)
+                y[j][e] = div_rn_shared(x[j][e], rms, rr) * g[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            float g[8];
+            unpack8(gq[j], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float q = x[j][e] / rms;
+                y[j][e] = q * g[e];
+            }
         }
     }
 
@@ -161,22 +192,38 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
                 amax = fmaxf(amax, fabsf(y[j][e]));
         amax = fold_max<LPT>(amax);
         const float scale = amax / 127.0f;
-        int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * DV;
+        // rint(y / scale) with scale in the shared-divisor domain: every y
+        // with |y| >= 2^-64 is inside it (|y| <= amax = 127 scale); a smaller
+        // |y| has |y / scale| < 2^-4, and the (finite, tiny) shared-divisor
+        // quotient then rounds to code 0 exactly as the true one does.
+        float c[NCH][8];
+        if (fast_div_divisor_ok(scale)) {
+            const float rs = 1.0f / scale;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            float c[8];
+            for (int j = 0; j < NCH; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                c[e] = scale == 0.0f ? 0.0f : rintf(y[j][e] / scale);
-            *reinterpret_cast<uint2 *>(dst + 8 * (l + LPT * j)) = pack_codes8(c);
+                for (int e = 0; e < 8; ++e)
+                    c[j][e] = rintf(div_rn_shared(y[j][e], scale, rs));
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    c[j][e] = scale == 0.0f ? 0.0f : rintf(y[j][e] / scale);
         }
-        if (l == 0)
-            a.ckv_scale[row] = scale;
-    } else {
+        if (write) {
+            int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * DV;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                stream_store(dst + 8 * (l + LPT * j), to_u32x2(pack_codes8(c[j])));
+            if (l == 0)
+                a.ckv_scale[row] = scale;
+        }
+    } else if (write) {
         uint16_t *dst = static_cast<uint16_t *>(a.ckv_cache) + row * DV;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
-            *reinterpret_cast<uint4 *>(dst + 8 * (l + LPT * j)) = pack8(y[j]);
+            stream_store(dst + 8 * (l + LPT * j), to_u32x4(pack8(y[j])));
     }
 
     // ---- RoPE ---------------------------------------------------------------
@@ -184,16 +231,15 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
 #pragma unroll
     for (int r = 0; r < ROUT; ++r)
         kr[r] = rope_out(xe[r], xo[r], cv[r], sv[r], upper);
+    if (!write)
+        return;
     uint16_t *kd = a.k_cache + row * DK + o0;
     if constexpr (ROUT == 1) {
-        *kd = (uint16_t)(pack_bf16x2(kr[0], 0.0f) & 0xffffu);
+        stream_store(kd, (uint16_t)(pack_bf16x2(kr[0], 0.0f) & 0xffffu));
     } else if constexpr (ROUT == 2) {
-        *reinterpret_cast<uint32_t *>(kd) = pack_bf16x2(kr[0], kr[1]);
+        stream_store(kd, pack_bf16x2(kr[0], kr[1]));
     } else {
-        uint2 q;
-        q.x = pack_bf16x2(kr[0], kr[1]);
-        q.y = pack_bf16x2(kr[2], kr[3]);
-        *reinterpret_cast<uint2 *>(kd) = q;
+        stream_store(kd, u32x2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])});
     }
 }
 
@@ -206,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
     const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (t >= a.T)
         return;
-    const int64_t row = dest_row(a, t, lane == 0);
+    const int64_t row = dest_row(a, a.index[t], t, lane == 0);
     if (row < 0)
         return;
     const int64_t Dv = a.Dv, Dk = a.Dk, D = Dv + Dk;
@@ -289,16 +335,21 @@ hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
 
 }  // namespace
 
-// Rows per wavefront for the Dv = 512 / Dk = 64 kernel.
-#ifndef KVRC_TPW
-#define KVRC_TPW 2
+// Rows per wavefront for the Dv = 512 / Dk = 64 kernel (measured best on
+// MI355X: 2 for bf16 rows, 4 for int8 rows, whose longer arithmetic gains
+// from the shared per-row work of more rows per wavefront).
+#ifndef KVRC_TPW_BF16
+#define KVRC_TPW_BF16 2
+#endif
+#ifndef KVRC_TPW_INT8
+#define KVRC_TPW_INT8 4
 #endif
 
 hipError_t launch_norm_rope_cache(const NormRopeCacheArgs &a, hipStream_t stream)
 {
     if (a.Dv == 512 && a.Dk == 64)
-        return a.int8 ? launch_d576<KVRC_TPW, true>(a, stream)
-                      : launch_d576<KVRC_TPW, false>(a, stream);
+        return a.int8 ? launch_d576<KVRC_TPW_INT8, true>(a, stream)
+                      : launch_d576<KVRC_TPW_BF16, false>(a, stream);
     const int64_t grid = (a.T + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(norm_rope_cache_generic, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();

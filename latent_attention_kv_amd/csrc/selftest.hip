@@ -1,0 +1,61 @@
+// Device arithmetic self-test (include/kvrc_selftest.h): runs the division
+// and square-root building blocks of the kernels on caller-chosen operands.
+#include "kvrc_selftest.h"
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace {
+
+__global__ __launch_bounds__(256) void arith_kernel(const float *__restrict__ a,
+                                                    const float *__restrict__ b,
+                                                    float *__restrict__ qs,
+                                                    float *__restrict__ qi,
+                                                    float *__restrict__ root, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = a[i], y = b[i];
+        const float ry = 1.0f / y;
+        qs[i] = kvrc::div_rn_shared(x, y, ry);
+        qi[i] = x / y;
+        root[i] = sqrtf(x);
+    }
+}
+
+bool overlaps(const void *p, const void *q, int64_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes;
+}
+
+}  // namespace
+
+extern "C" int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_shared,
+                                       float *q_ieee, float *root, int64_t n,
+                                       hipStream_t stream)
+{
+    if (n < 0)
+        return KVRC_ERR_SHAPE;
+    if (n == 0)
+        return KVRC_OK;
+    if (!a || !b || !q_shared || !q_ieee || !root)
+        return KVRC_ERR_NULL;
+    const void *all[] = {a, b, q_shared, q_ieee, root};
+    for (const void *p : all)
+        if (reinterpret_cast<uintptr_t>(p) % 16)
+            return KVRC_ERR_ALIGN;
+    const int64_t bytes = n * 4;
+    const void *outs[] = {q_shared, q_ieee, root};
+    for (const void *o : outs)
+        for (const void *p : all)
+            if (o != p && overlaps(o, p, bytes))
+                return KVRC_ERR_ALIAS;
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(arith_kernel, dim3(grid), dim3(256), 0, stream, a, b, q_shared, q_ieee,
+                       root, n);
+    return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
+}

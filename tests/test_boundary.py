@@ -17,13 +17,14 @@ import torch
 import latent_attention_kv_amd as k
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvrc.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP = range(7)
 
 
 def header_functions():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t)\s*\*?\s*(\w+)\s*\(", src, re.M)))
 
