@@ -104,6 +104,7 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     a.Dk = Dk;
     a.rows_per_batch = rows_per_batch;
     a.limit = limit;
+    a.cache_rows = rows;
     a.int8 = int8;
     a.eps = eps;
     a.err = err_count;

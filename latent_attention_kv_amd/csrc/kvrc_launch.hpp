@@ -25,6 +25,7 @@ struct NormRopeCacheArgs {
     int64_t T, S, Dv, Dk;
     int64_t rows_per_batch;   // 0 = paged
     int64_t limit;            // exclusive bound of a valid index value
+    int64_t cache_rows;       // rows of each cache (paged: limit; Norm: Bc * Sc)
     bool int8;
     float eps;
     int32_t *err;             // nullable

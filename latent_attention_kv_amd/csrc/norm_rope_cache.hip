@@ -60,10 +60,62 @@ __device__ __forceinline__ float rope_out(float xe, float xo, float c, float s, 
     return upper ? p1 + p2 : p1 - p2;
 }
 
+// Cache rows are written with sc1 (device scope) stores when the cache fits
+// a buffer descriptor (BUF: each cache smaller than 4 GiB): the rows are
+// written through the XCD's L2 instead of being left dirty there, which on
+// MI355X spares the write-back of up to the L2's capacity of dirty lines at
+// the end of the kernel (measured faster than the default policy and than
+// non-temporal stores). The descriptor covers exactly the cache, so the
+// hardware also drops any store outside it. Larger caches use plain global
+// stores.
+#ifndef KVRC_STORE_AUX
+#define KVRC_STORE_AUX 16
+#endif
+
+template <bool BUF>
+class CacheWriter {
+  public:
+    __device__ CacheWriter(void *cache, int64_t bytes) : base_(static_cast<unsigned char *>(cache))
+    {
+        if constexpr (BUF)
+            rsrc_ = __builtin_amdgcn_make_buffer_rsrc(cache, 0, (int)(uint32_t)bytes, kWord3);
+    }
+    template <typename T>
+    __device__ void store(int64_t off, T v) const
+    {
+        if constexpr (BUF)
+            buffer_store(rsrc_, (int)(uint32_t)off, v);
+        else
+            *reinterpret_cast<T *>(base_ + off) = v;
+    }
+
+  private:
+    // Word 3 of a raw (untyped) gfx9 buffer descriptor: 32-bit data format.
+    static constexpr int kWord3 = 0x00020000;
+    static __device__ void buffer_store(__amdgpu_buffer_rsrc_t r, int off, u32x4 v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, KVRC_STORE_AUX);
+    }
+    static __device__ void buffer_store(__amdgpu_buffer_rsrc_t r, int off, u32x2 v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, KVRC_STORE_AUX);
+    }
+    static __device__ void buffer_store(__amdgpu_buffer_rsrc_t r, int off, uint32_t v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, KVRC_STORE_AUX);
+    }
+    static __device__ void buffer_store(__amdgpu_buffer_rsrc_t r, int off, uint16_t v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, KVRC_STORE_AUX);
+    }
+    unsigned char *base_;
+    __amdgpu_buffer_rsrc_t rsrc_;
+};
+
 // ---------------------------------------------------------------------------
 // Dv = 512, Dk = 64: TPW token rows per wavefront.
 // ---------------------------------------------------------------------------
-template <int TPW, bool INT8>
+template <int TPW, bool INT8, bool BUF>
 __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheArgs a)
 {
     constexpr int DV = 512, DK = 64, D = DV + DK;
@@ -212,18 +264,18 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
                     c[j][e] = scale == 0.0f ? 0.0f : rintf(y[j][e] / scale);
         }
         if (write) {
-            int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * DV;
+            const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV);
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
-                stream_store(dst + 8 * (l + LPT * j), to_u32x2(pack_codes8(c[j])));
+                dst.store(row * DV + 8 * (l + LPT * j), to_u32x2(pack_codes8(c[j])));
             if (l == 0)
                 a.ckv_scale[row] = scale;
         }
     } else if (write) {
-        uint16_t *dst = static_cast<uint16_t *>(a.ckv_cache) + row * DV;
+        const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV * 2);
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
-            stream_store(dst + 8 * (l + LPT * j), to_u32x4(pack8(y[j])));
+            dst.store((row * DV + 8 * (l + LPT * j)) * 2, to_u32x4(pack8(y[j])));
     }
 
     // ---- RoPE ---------------------------------------------------------------
@@ -233,14 +285,14 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
         kr[r] = rope_out(xe[r], xo[r], cv[r], sv[r], upper);
     if (!write)
         return;
-    uint16_t *kd = a.k_cache + row * DK + o0;
-    if constexpr (ROUT == 1) {
-        stream_store(kd, (uint16_t)(pack_bf16x2(kr[0], 0.0f) & 0xffffu));
-    } else if constexpr (ROUT == 2) {
-        stream_store(kd, pack_bf16x2(kr[0], kr[1]));
-    } else {
-        stream_store(kd, u32x2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])});
-    }
+    const CacheWriter<BUF> kdst(a.k_cache, a.cache_rows * DK * 2);
+    const int64_t koff = (row * DK + o0) * 2;
+    if constexpr (ROUT == 1)
+        kdst.store(koff, (uint16_t)(pack_bf16x2(kr[0], 0.0f) & 0xffffu));
+    else if constexpr (ROUT == 2)
+        kdst.store(koff, pack_bf16x2(kr[0], kr[1]));
+    else
+        kdst.store(koff, u32x2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])});
 }
 
 // ---------------------------------------------------------------------------
@@ -328,8 +380,17 @@ hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
 {
     const int64_t tokens_per_wg = (int64_t)kWaves * TPW;
     const int64_t grid = (a.T + tokens_per_wg - 1) / tokens_per_wg;
-    hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8>), dim3((uint32_t)grid), dim3(kThreads), 0,
-                       stream, a);
+    // Buffer descriptors hold 32-bit sizes and offsets: each cache must be
+    // smaller than 4 GiB for the sc1 buffer stores.
+    const int64_t rows = a.cache_rows;
+    const bool buf = rows * 512 * (INT8 ? 1 : 2) <= (int64_t)UINT32_MAX &&
+                     rows * 64 * 2 <= (int64_t)UINT32_MAX;
+    if (buf)
+        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8, true>), dim3((uint32_t)grid),
+                           dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8, false>), dim3((uint32_t)grid),
+                           dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

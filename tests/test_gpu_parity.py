@@ -391,3 +391,57 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         compare_kvrc(case, {"k_cache": kc, "ckv_cache": ck, "ckv_scale": sc}, want,
                      exact_bf16=True)
+
+
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_cache_larger_than_4gib(ckv):
+    """Caches of 4 GiB or more take the plain-global-store path: rows beyond the
+    32-bit byte offset must land exactly, and nothing else may change."""
+    Dv, Dk, BS = 512, 64, 128
+    row_bytes = Dv * (2 if ckv == "bf16" else 1)
+    NB = (2 ** 32 // row_bytes) // BS + 64                    # just over 4 GiB of ckv rows
+    say(f"[parity] cache over 4 GiB: {ckv}, {NB} blocks")
+    small = gen.kvrc_paged_case(900, B=2, S=48, Dv=Dv, Dk=Dk, num_blocks=1, block_size=96,
+                                slot_kind="random", ckv_dtype=ckv)
+    T = 96
+    # real slots: half below the 4 GiB offset, half above it
+    rng = gen.rng_for(901)
+    lo = rng.choice(2 ** 32 // row_bytes - 1, size=T // 2, replace=False)
+    hi = 2 ** 32 // row_bytes + rng.choice(NB * BS - 2 ** 32 // row_bytes, size=T // 2,
+                                           replace=False)
+    slots = np.concatenate([lo, hi]).astype(np.int64)
+    rng.shuffle(slots)
+    want = oracle.run_kvrc_case(small)                        # slot t -> compact row small[t]
+    compact = small["slot_mapping"]
+    caches = {"k_cache": torch.full((NB, BS, 1, Dk), gen.BF16_SENTINEL, dtype=torch.int16,
+                                    device=DEV).view(torch.bfloat16)}
+    if ckv == "bf16":
+        caches["ckv_cache"] = torch.full((NB, BS, 1, Dv), gen.BF16_SENTINEL, dtype=torch.int16,
+                                         device=DEV).view(torch.bfloat16)
+        scale = None
+    else:
+        caches["ckv_cache"] = torch.full((NB, BS, 1, Dv), gen.INT8_SENTINEL, dtype=torch.int8,
+                                         device=DEV)
+        scale = torch.full((NB, BS, 1), gen.SCALE_SENTINEL, dtype=torch.float32, device=DEV)
+    k.kvrc_paged_norm_rope_cache(dbf(small["kv"]), dbf(small["gamma"]), dbf(small["cos"]),
+                                 dbf(small["sin"]), dt(slots), caches["k_cache"],
+                                 caches["ckv_cache"], scale, eps=small["eps"])
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(slots).to(DEV)
+    for name, d in (("k_cache", Dk), ("ckv_cache", Dv)):
+        g = caches[name].view(NB * BS, d)
+        w = want[name].reshape(-1, d)[compact]
+        if g.dtype == torch.bfloat16:
+            assert torch.equal(g[idx].view(torch.int16), dbf(w).view(torch.int16)), name
+            sentinel = gen.BF16_SENTINEL
+            changed = int((g.view(torch.int16) != sentinel).sum().item())
+            in_rows = int((g[idx].view(torch.int16) != sentinel).sum().item())
+        else:
+            assert torch.equal(g[idx], dt(w)), name
+            changed = int((g != gen.INT8_SENTINEL).sum().item())
+            in_rows = int((g[idx] != gen.INT8_SENTINEL).sum().item())
+        assert changed == in_rows, f"{name}: bytes outside the written rows changed"
+    if scale is not None:
+        sv = scale.view(-1)
+        assert torch.equal(sv[idx], dt(want["ckv_scale"].reshape(-1)[compact]))
+        assert int((sv != gen.SCALE_SENTINEL).sum().item()) == int((sv[idx] != gen.SCALE_SENTINEL).sum().item())
