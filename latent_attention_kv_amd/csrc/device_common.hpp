@@ -157,6 +157,22 @@ __device__ __forceinline__ float div_rn_shared(float a, float b, float rb)
     return __builtin_fmaf(r, rb, q);
 }
 
+// 1.5 * 2^23: for |q| < 2^22, RN(q + kRoundMagic) = kRoundMagic + rint(q)
+// (ties to even), so the low byte of its bits is rint(q) as an int8.
+constexpr float kRoundMagic = 12582912.0f;
+
+// Low bytes of eight words -> eight consecutive bytes (v_perm_b32).
+__device__ __forceinline__ u32x2 pack_low_bytes8(const uint32_t (&w)[8])
+{
+    // perm(hi, lo, sel): selector byte k picks byte k of lo (0-3) or of hi (4-7);
+    // 0x0c yields a zero byte.
+    const uint32_t a = __builtin_amdgcn_perm(w[1], w[0], 0x0c0c0400u);   // b0 b1 0 0
+    const uint32_t b = __builtin_amdgcn_perm(w[3], w[2], 0x04000c0cu);   // 0 0 b2 b3
+    const uint32_t c = __builtin_amdgcn_perm(w[5], w[4], 0x0c0c0400u);
+    const uint32_t d = __builtin_amdgcn_perm(w[7], w[6], 0x04000c0cu);
+    return u32x2{a | b, c | d};
+}
+
 // Pack eight int8 codes (given as float integral values in [-127, 127]).
 __device__ __forceinline__ uint2 pack_codes8(const float (&c)[8])
 {

@@ -244,30 +244,41 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_d576(NormRopeCacheAr
                 amax = fmaxf(amax, fabsf(y[j][e]));
         amax = fold_max<LPT>(amax);
         const float scale = amax / 127.0f;
-        // rint(y / scale) with scale in the shared-divisor domain: every y
-        // with |y| >= 2^-64 is inside it (|y| <= amax = 127 scale); a smaller
-        // |y| has |y / scale| < 2^-4, and the (finite, tiny) shared-divisor
-        // quotient then rounds to code 0 exactly as the true one does.
-        float c[NCH][8];
+        // code = rint(RN(y / scale)), half to even, as the low byte of
+        // bits(q + 1.5*2^23) (adding that constant rounds |q| < 2^22 to an
+        // integer in the low mantissa bits, ties to even). In the
+        // shared-divisor domain of scale the quotient is first approximated
+        // as t = RN(y * RN(1/scale)), within 3*2^-24*127 < 2^-15 of RN(y/scale)
+        // (|y / scale| <= 127 + 2^-16); wherever t lies farther than 2^-15
+        // from a half-integer both round to the same integer, and the few
+        // elements within 2^-15 of one take the exact quotient.
+        uint32_t cb[NCH][8];
         if (fast_div_divisor_ok(scale)) {
             const float rs = 1.0f / scale;
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    c[j][e] = rintf(div_rn_shared(y[j][e], scale, rs));
+                for (int e = 0; e < 8; ++e) {
+                    const float t = y[j][e] * rs;
+                    const float w = t + kRoundMagic;
+                    if (fabsf(t - (w - kRoundMagic)) > 0.5f - 0x1p-15f)
+                        cb[j][e] = __float_as_uint(div_rn_shared(y[j][e], scale, rs) + kRoundMagic);
+                    else
+                        cb[j][e] = __float_as_uint(w);
+                }
         } else {
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    c[j][e] = scale == 0.0f ? 0.0f : rintf(y[j][e] / scale);
+                    cb[j][e] = __float_as_uint(
+                        (scale == 0.0f ? 0.0f : y[j][e] / scale) + kRoundMagic);
         }
         if (write) {
             const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV);
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
-                dst.store(row * DV + 8 * (l + LPT * j), to_u32x2(pack_codes8(c[j])));
+                dst.store(row * DV + 8 * (l + LPT * j), pack_low_bytes8(cb[j]));
             if (l == 0)
                 a.ckv_scale[row] = scale;
         }
@@ -397,13 +408,13 @@ hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
 }  // namespace
 
 // Rows per wavefront for the Dv = 512 / Dk = 64 kernel (measured best on
-// MI355X: 2 for bf16 rows, 4 for int8 rows, whose longer arithmetic gains
-// from the shared per-row work of more rows per wavefront).
+// MI355X: 2 for both; 4 rows per wavefront shares more per-row work but needs
+// twice the registers, and 1 row halves the work per load instruction).
 #ifndef KVRC_TPW_BF16
 #define KVRC_TPW_BF16 2
 #endif
 #ifndef KVRC_TPW_INT8
-#define KVRC_TPW_INT8 4
+#define KVRC_TPW_INT8 2
 #endif
 
 hipError_t launch_norm_rope_cache(const NormRopeCacheArgs &a, hipStream_t stream)

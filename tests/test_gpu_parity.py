@@ -445,3 +445,36 @@ def test_cache_larger_than_4gib(ckv):
         sv = scale.view(-1)
         assert torch.equal(sv[idx], dt(want["ckv_scale"].reshape(-1)[compact]))
         assert int((sv != gen.SCALE_SENTINEL).sum().item()) == int((sv[idx] != gen.SCALE_SENTINEL).sum().item())
+
+
+def test_int8_exact_ties():
+    """Rows whose quotients y/scale are exact half-integers: eps is chosen so
+    that mean(x^2) + eps = 64^2 (rms = 64 exactly), gamma = 1, max|x| = 127,
+    hence y = x/64, scale = 1/64 and y/scale = x; codes must be
+    rint half-to-even(x). (All squares are multiples of 1/4 and the sums stay
+    below 2^21, so every partial sum is exact in float32.)"""
+    rng = gen.rng_for(950)
+    Dv, Dk, T = 512, 64, 64
+    base = np.zeros(Dv, np.float32)
+    base[0] = 127.0
+    halves = np.arange(-126.5, 127.0, 1.0, dtype=np.float32)       # -126.5 .. 126.5
+    base[1:1 + 180] = rng.choice(halves, 180, replace=False)
+    ss = float(np.sum(base.astype(np.float64) ** 2))
+    ms = np.float32(ss / Dv)
+    assert float(ms) * Dv == ss and ms < 4096
+    eps = float(np.float32(4096.0) - ms)
+    assert np.float32(ms + np.float32(eps)) == 4096.0
+    rows = np.stack([rng.permutation(base) for _ in range(T)])
+    kv = np.concatenate([rows, rng.standard_normal((T, Dk)).astype(np.float32)], axis=1)
+    case = gen.kvrc_paged_case(951, B=1, S=T, Dv=Dv, Dk=Dk, num_blocks=4, block_size=32,
+                               slot_kind="random", ckv_dtype="int8")
+    case["kv"] = gen.bf16_bits(kv).reshape(1, 1, T, Dv + Dk)
+    case["gamma"] = gen.bf16_bits(np.ones(Dv, np.float32))
+    case["eps"] = eps
+    want = oracle.run_kvrc_case(case)
+    got = run_kvrc_gpu(case)
+    compare_kvrc(case, got, want, exact_bf16=True)
+    slots = case["slot_mapping"]
+    codes = got["ckv_cache"].cpu().numpy().reshape(-1, Dv)[slots]
+    np.testing.assert_array_equal(codes, np.rint(rows).astype(np.int8))     # rint: half to even
+    assert np.all(got["ckv_scale"].cpu().numpy().reshape(-1)[slots] == np.float32(1 / 64))

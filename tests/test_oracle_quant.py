@@ -63,3 +63,28 @@ def test_quant_end_to_end_token_int8_row():
     np.testing.assert_array_equal(kc[0, 3, 0], oracle.f32_to_bf16(yr))
     # rows not addressed keep their bytes
     assert np.all(ck.reshape(8, Dv)[[0, 1, 2, 4, 5, 6, 7]] == 0)
+
+
+def test_quant_end_to_end_exact_ties():
+    """Rows built so that rms = 64 exactly (eps = 4096 - mean(x^2)), gamma = 1
+    and max|x| = 127: then y = x/64, scale = 1/64 and y/scale = x, so the
+    stored codes are rint(x) with ties to even (thousands of exact ties)."""
+    rng = rng_for(950)
+    Dv, Dk, T = 512, 64, 16
+    base = np.zeros(Dv, np.float32)
+    base[0] = 127.0
+    base[1:181] = rng.choice(np.arange(-126.5, 127.0, 1.0, dtype=np.float32), 180, replace=False)
+    ms = np.float32(float(np.sum(base.astype(np.float64) ** 2)) / Dv)
+    eps = float(np.float32(4096.0) - ms)
+    rows = np.stack([rng.permutation(base) for _ in range(T)])
+    kv = np.concatenate([rows, np.zeros((T, Dk), np.float32)], axis=1)
+    kvb = bf16_bits(kv).reshape(1, 1, T, Dv + Dk)
+    gamma = bf16_bits(np.ones(Dv, np.float32))
+    cs = np.zeros((1, 1, T, Dk), np.uint16)
+    slots = np.arange(T, dtype=np.int64)
+    kc = np.zeros((1, T, 1, Dk), np.uint16)
+    ck = np.zeros((1, T, 1, Dv), np.int8)
+    sc = np.zeros((1, T, 1), np.float32)
+    oracle.paged_norm_rope_cache(kvb, gamma, cs, cs, slots, kc, ck, sc, eps=eps)
+    np.testing.assert_array_equal(ck.reshape(T, Dv), np.rint(rows).astype(np.int8))
+    assert np.all(sc == np.float32(1 / 64))
