@@ -394,16 +394,17 @@ def test_graph_replays_match_eager():
 
 
 @pytest.mark.parametrize("ckv", ["bf16", "int8"])
-def test_cache_larger_than_4gib(ckv):
-    """Caches of 4 GiB or more take the plain-global-store path: rows beyond the
-    32-bit byte offset must land exactly, and nothing else may change."""
+@pytest.mark.parametrize("T", [96, 4096])
+def test_cache_larger_than_4gib(ckv, T):
+    """Caches of 4 GiB or more take the plain-global-store path (with both the
+    small-batch and the large-batch launch shapes): rows beyond the 32-bit
+    byte offset must land exactly, and nothing else may change."""
     Dv, Dk, BS = 512, 64, 128
     row_bytes = Dv * (2 if ckv == "bf16" else 1)
     NB = (2 ** 32 // row_bytes) // BS + 64                    # just over 4 GiB of ckv rows
-    say(f"[parity] cache over 4 GiB: {ckv}, {NB} blocks")
-    small = gen.kvrc_paged_case(900, B=2, S=48, Dv=Dv, Dk=Dk, num_blocks=1, block_size=96,
+    say(f"[parity] cache over 4 GiB: {ckv}, {NB} blocks, {T} tokens")
+    small = gen.kvrc_paged_case(900, B=2, S=T // 2, Dv=Dv, Dk=Dk, num_blocks=1, block_size=T,
                                 slot_kind="random", ckv_dtype=ckv)
-    T = 96
     # real slots: half below the 4 GiB offset, half above it
     rng = gen.rng_for(901)
     lo = rng.choice(2 ** 32 // row_bytes - 1, size=T // 2, replace=False)
