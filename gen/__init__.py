@@ -32,6 +32,7 @@ INT8_SENTINEL = -128
 SCALE_SENTINEL = -1.0
 
 CONFIG_NAMES = ("norm_tiny", "decode_paged", "prefill_paged", "quant_paged", "qsa")
+EXTRA_NAMES = ("prefill_paged_blk",)
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -171,6 +172,38 @@ def kvrc_paged_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6, sig
                 block_table=blocks)
 
 
+def kvrc_paged_blk_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6, sigma=1.0,
+                        ckv_dtype="bf16", n_skip=0, entry_offsets=False):
+    """Block-indexed paged mode (PA_BLK_BNSD): one index entry per chunk of
+    block_size tokens of a sequence, B * ceil(S/block_size) entries naming
+    distinct random blocks (entry = block*block_size, plus a random offset in
+    [0, block_size) when entry_offsets), n_skip entries set to -1;
+    positions 0..S-1 per sequence."""
+    g = rng_for(seed)
+    kv, gamma = _kv_common(g, B, S, Dv, Dk, sigma)
+    chunks = -(-S // block_size)
+    blocks = g.choice(num_blocks, size=B * chunks, replace=False)
+    entries = (blocks * block_size).astype(np.int64)
+    if entry_offsets:
+        entries += g.integers(0, block_size, size=entries.shape)
+    if n_skip:
+        entries[g.choice(B * chunks, size=n_skip, replace=False)] = -1
+    positions = np.broadcast_to(np.arange(S), (B, S))
+    cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
+    caches = {
+        "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
+        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv),
+                               np.uint16 if ckv_dtype == "bf16" else np.int8,
+                               BF16_SENTINEL if ckv_dtype == "bf16" else INT8_SENTINEL),
+    }
+    if ckv_dtype == "int8":
+        caches["ckv_scale"] = CacheSpec((num_blocks, block_size, 1), np.float32, SCALE_SENTINEL)
+    return dict(mode="paged_blk", kv=kv, gamma=gamma, cos=cos, sin=sin,
+                block_index=np.ascontiguousarray(entries), caches=caches, B=B, S=S, Dv=Dv,
+                Dk=Dk, num_blocks=num_blocks, block_size=block_size, eps=float(eps),
+                ckv_dtype=ckv_dtype)
+
+
 # ---------------------------------------------------------------------------
 # QSA block-key cases
 # ---------------------------------------------------------------------------
@@ -241,6 +274,10 @@ def make_config(name: str, seed: int | None = None):
     if name == "qsa":
         return qsa_case(5 if seed is None else seed, N=32, L=2048, Di=128, Dr=64, kbs=64,
                         past_max=8192, Bcap=160)
+    if name == "prefill_paged_blk":
+        # the prefill batch in block-indexed form: one entry per 128-token chunk
+        return kvrc_paged_blk_case(6 if seed is None else seed, B=8, S=4096, Dv=512, Dk=64,
+                                   num_blocks=8192, block_size=128)
     raise KeyError(name)
 
 

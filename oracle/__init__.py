@@ -61,6 +61,8 @@ def _load():
                                               I64, I64, I, F, I]
     lib.orc_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64,
                                         I64, I, F, I]
+    lib.orc_paged_blk_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64,
+                                                  I64, I64, I, F, I]
     lib.orc_qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64,
                                     I64, I64, F, I]
     lib.orc_qsa_block_key.argtypes = [P, I64, I64, P, P, P, I64, F, P, P]
@@ -185,6 +187,20 @@ def paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
     _check(rc)
 
 
+def paged_blk_norm_rope_cache(kv, gamma, cos, sin, block_index, k_cache, ckv_cache,
+                              ckv_scale=None, *, eps=1e-6, nthreads=None):
+    """Block-indexed paged mode: block_index [B * ceil(S / block_size)]."""
+    B, _, S, D = kv.shape
+    Dk = cos.shape[-1]
+    Dv = D - Dk
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    int8 = ckv_cache.dtype == np.int8
+    rc = _load().orc_paged_blk_norm_rope_cache(
+        _p(kv), _p(gamma), _p(cos), _p(sin), _p(block_index), _p(k_cache), _p(ckv_cache),
+        _p(ckv_scale), B, S, Dv, Dk, NB, BS, int(int8), eps, nthreads or max_threads())
+    _check(rc)
+
+
 def norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale=None, *,
                     eps=1e-6, nthreads=None):
     """Norm mode: index [B,S]; caches [Bc,1,Sc,d]; ckv_scale [Bc,1,Sc]."""
@@ -225,6 +241,10 @@ def run_kvrc_case(case, nthreads=None):
         paged_norm_rope_cache(*args, case["slot_mapping"], caches["k_cache"],
                               caches["ckv_cache"], caches.get("ckv_scale"), eps=case["eps"],
                               nthreads=nthreads)
+    elif case["mode"] == "paged_blk":
+        paged_blk_norm_rope_cache(*args, case["block_index"], caches["k_cache"],
+                                  caches["ckv_cache"], caches.get("ckv_scale"),
+                                  eps=case["eps"], nthreads=nthreads)
     else:
         norm_rope_cache(*args, case["index"], caches["k_cache"], caches["ckv_cache"],
                         caches.get("ckv_scale"), eps=case["eps"], nthreads=nthreads)

@@ -356,6 +356,56 @@ int orc_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const uint16_
     return rc;
 }
 
+/*
+ * Block-indexed paged mode (PA_BLK_BNSD), aclnnKvRmsNormRopeCache, restrictions
+ * on index: block_index holds B * ceil(S / block_size) entries, each -1 or a
+ * value in [0, num_blocks*block_size) whose quotient value / block_size must
+ * not repeat. READING: entry b*ceil(S/BS) + c covers the chunk of tokens
+ * s in [c*BS, (c+1)*BS) of batch b; it names the destination block
+ * value / BS (the quantity the page requires to be unique), and token (b, s)
+ * goes to offset s mod BS of that block; -1 skips the whole chunk.
+ */
+int orc_paged_blk_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const uint16_t *cs,
+                                  const uint16_t *sn, const int64_t *block_index,
+                                  uint16_t *k_cache, void *ckv_cache, float *ckv_scale,
+                                  int64_t B, int64_t S, int64_t Dv, int64_t Dk,
+                                  int64_t num_blocks, int64_t block_size, int ckv_int8,
+                                  float eps, int nthreads)
+{
+    if (B < 0 || S < 0 || Dv < 1 || Dk < 2 || (Dk & 1) || num_blocks < 0 || block_size < 1)
+        return ORC_BAD_ARG;
+    if (ckv_int8 && !ckv_scale)
+        return ORC_BAD_ARG;
+    int64_t T = B * S;
+    if (T == 0)
+        return ORC_OK;
+    int64_t chunks = (S + block_size - 1) / block_size;
+    int64_t n = B * chunks;
+    int64_t *blocks = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t v = block_index[i];
+        if (v < -1 || v >= num_blocks * block_size) {
+            free(blocks);
+            return ORC_BAD_INDEX;
+        }
+        blocks[i] = v < 0 ? -1 : v / block_size;
+    }
+    int rc = check_indices(blocks, n, num_blocks);          /* blocks must not repeat */
+    free(blocks);
+    if (rc)
+        return rc;
+    int64_t *dest = (int64_t *)malloc(sizeof(int64_t) * (size_t)T);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t s = 0; s < S; ++s) {
+            int64_t v = block_index[b * chunks + s / block_size];
+            dest[b * S + s] = v < 0 ? -1 : (v / block_size) * block_size + s % block_size;
+        }
+    rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_int8, k_cache, ckv_cache,
+                    ckv_scale, nthreads);
+    free(dest);
+    return rc;
+}
+
 /* Building blocks exposed for the tests: one token, no cache. */
 void orc_token_outputs(const uint16_t *kv, const uint16_t *gamma, const uint16_t *cs,
                        const uint16_t *sn, int64_t Dv, int64_t Dk, float eps, float *y_norm,

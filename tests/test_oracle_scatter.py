@@ -29,6 +29,13 @@ def _expected_rows(case):
                 continue
             bs = case["block_size"]
             flat = (v // bs) * bs + v % bs
+        elif case["mode"] == "paged_blk":
+            bs = case["block_size"]
+            b, s = divmod(t, S)
+            v = int(case["block_index"][b * (-(-S // bs)) + s // bs])
+            if v == -1:
+                continue
+            flat = (v // bs) * bs + s % bs
         else:
             b, s = divmod(t, S)
             v = int(case["index"][b, s])
@@ -147,3 +154,42 @@ def test_threads_do_not_change_result():
     a = oracle.run_kvrc_case(case, nthreads=1)
     b = oracle.run_kvrc_case(case, nthreads=4)
     _assert_same(a, b)
+
+
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("S,offsets", [(64, False), (40, False), (37, True)])
+def test_paged_blk_scatter_brute_force(ckv, S, offsets):
+    """Block-indexed mode (PA_BLK_BNSD): ragged last chunk, skipped chunks and
+    entries that are not multiples of the block size (only value / BS names
+    the block)."""
+    case = gen.kvrc_paged_blk_case(49, B=3, S=S, Dv=64, Dk=16, num_blocks=24, block_size=16,
+                                   ckv_dtype=ckv, n_skip=2, entry_offsets=offsets)
+    _assert_same(oracle.run_kvrc_case(case), _brute(case))
+
+
+def test_paged_blk_equals_per_token_slots():
+    """A block-indexed call equals a per-token paged call whose slot for token
+    (b, s) is block*BS + s mod BS (block = entry / BS; -1 chunks -> -1)."""
+    case = gen.kvrc_paged_blk_case(50, B=2, S=50, Dv=32, Dk=8, num_blocks=12, block_size=16,
+                                   n_skip=1, entry_offsets=True)
+    blk = oracle.run_kvrc_case(case)
+    BS, S = 16, 50
+    slots = []
+    for b in range(2):
+        for s in range(S):
+            v = int(case["block_index"][b * 4 + s // BS])
+            slots.append(-1 if v < 0 else (v // BS) * BS + s % BS)
+    per_token = dict(case, mode="paged", slot_mapping=np.array(slots, dtype=np.int64))
+    _assert_same(blk, oracle.run_kvrc_case(per_token))
+
+
+def test_paged_blk_invalid_rejected():
+    case = gen.kvrc_paged_blk_case(51, B=2, S=32, Dv=32, Dk=8, num_blocks=8, block_size=16)
+    bad = dict(case, block_index=case["block_index"].copy())
+    bad["block_index"][1] = bad["block_index"][0] + 3           # same block, other offset
+    with pytest.raises(oracle.OracleError, match="duplicate"):
+        oracle.run_kvrc_case(bad)
+    bad["block_index"] = case["block_index"].copy()
+    bad["block_index"][2] = 8 * 16
+    with pytest.raises(oracle.OracleError, match="range"):
+        oracle.run_kvrc_case(bad)
