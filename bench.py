@@ -62,6 +62,9 @@ WORKLOAD_TEXT = {
     "quant_paged": "paged int8 ckv cache: B=64, S=1024, D=576 bf16 (sigma 2), ckv int8 "
                    "[4096,128,1,512] + fp32 scale [4096,128,1], k bf16 [4096,128,1,64]",
     "norm_tiny": "Norm cache mode: B=2, S=16, D=576, caches [2,1,32,d] bf16",
+    "prefill_paged_blk": "paged prefill, block-indexed (PA_BLK_BNSD): B=8, S=4096 (32768 "
+                         "tokens), D=576 bf16, one index entry per 128-token chunk, caches "
+                         "[8192,128,1,512] + [8192,128,1,64] bf16",
     "qsa": "QSAPrepare block keys: N=32, L=2048, Di=128, Dr=64, key_block_size=64",
 }
 
@@ -97,9 +100,17 @@ def algorithmic_bytes(case) -> tuple[int, int]:
             total += 8                                            # key_length
         return total + Di * 2, N * L
     T = case["B"] * case["S"]
+    per = gen.kvrc_bytes_per_written_token(case["Dv"], case["Dk"], case["ckv_dtype"])
+    if case["mode"] == "paged_blk":
+        # one 8-byte entry per chunk instead of one per token
+        S, bs = case["S"], case["block_size"]
+        chunks = -(-S // bs)
+        entries = case["block_index"].reshape(case["B"], chunks)
+        written = sum(min(bs, S - c * bs) for b in range(case["B"]) for c in range(chunks)
+                      if entries[b, c] >= 0)
+        return written * (per - 8) + entries.size * 8 + 2 * case["Dv"], T
     idx = case["slot_mapping"] if case["mode"] == "paged" else case["index"].reshape(-1)
     written = int((idx >= 0).sum())
-    per = gen.kvrc_bytes_per_written_token(case["Dv"], case["Dk"], case["ckv_dtype"])
     return written * per + (T - written) * 8 + 2 * case["Dv"], T
 
 
@@ -131,7 +142,7 @@ def build_sets(case, R, dev):
             s["nrope"] = torch.empty_like(s["prope"])
             sets.append(s)
         return sets
-    idx_name = "slot_mapping" if case["mode"] == "paged" else "index"
+    idx_name = {"paged": "slot_mapping", "paged_blk": "block_index"}.get(case["mode"], "index")
     base = dict(kv=dbf(case["kv"]), gamma=dbf(case["gamma"]), cos=dbf(case["cos"]),
                 sin=dbf(case["sin"]), idx=dt(case[idx_name]))
     for _ in range(R):
@@ -157,6 +168,10 @@ def launch(case, s):
         k.kvrc_paged_norm_rope_cache(s["kv"], s["gamma"], s["cos"], s["sin"], s["idx"],
                                      s["k_cache"], s["ckv_cache"], s.get("ckv_scale"),
                                      eps=case["eps"])
+    elif case["mode"] == "paged_blk":
+        k.kvrc_paged_blk_norm_rope_cache(s["kv"], s["gamma"], s["cos"], s["sin"], s["idx"],
+                                         s["k_cache"], s["ckv_cache"], s.get("ckv_scale"),
+                                         eps=case["eps"])
     else:
         k.kvrc_norm_rope_cache(s["kv"], s["gamma"], s["cos"], s["sin"], s["idx"], s["k_cache"],
                                s["ckv_cache"], s.get("ckv_scale"), eps=case["eps"])
@@ -184,6 +199,10 @@ def cpu_baseline(case, seconds=10.0):
                 oracle.paged_norm_rope_cache(*args, case["slot_mapping"], caches["k_cache"],
                                              caches["ckv_cache"], caches.get("ckv_scale"),
                                              eps=case["eps"], nthreads=threads)
+            elif case["mode"] == "paged_blk":
+                oracle.paged_blk_norm_rope_cache(*args, case["block_index"], caches["k_cache"],
+                                                 caches["ckv_cache"], caches.get("ckv_scale"),
+                                                 eps=case["eps"], nthreads=threads)
             else:
                 oracle.norm_rope_cache(*args, case["index"], caches["k_cache"], caches["ckv_cache"],
                                        caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)

@@ -71,8 +71,8 @@ int32_t kvrc_version(void);
  * Nope formula).
  *
  * For every token t = b*S + s of kv[B, 1, S, Dv+Dk]:
- *   v = slot_mapping[t]; v == -1 skips the token (nothing is read or written
- *   for it);
+ *   v = slot_mapping[t]; v == -1 skips the token (nothing is written for it;
+ *   its inputs may still be read);
  *   y  = rmsnorm(kv[t, 0:Dv]) = (x / sqrt(mean(x*x) + eps)) * gamma
  *   kr = interleaved RoPE of kv[t, Dv:Dv+Dk] with cos[t], sin[t]:
  *        x1 = x[0::2], x2 = x[1::2], kr = cat(x1,x2)*cos + cat(-x2,x1)*sin
@@ -81,9 +81,10 @@ int32_t kvrc_version(void);
  *        ckv_scale[v / block_size, v % block_size, 0]             (INT8;
  *        an all-zero row stores scale 0 and codes 0)
  *   k_cache[v / block_size, v % block_size, 0, :] = bf16(kr)
- * The sum of squares uses a fixed order (pairwise sum of 64 partials, each
- * accumulating 8-element chunks c = l, l+64, ...), so results are
- * deterministic and independent of the launch.
+ * The sum of squares uses a fixed order: 64 partial sums, partial l adding
+ * the squares of the 8-element chunks c = l, l+64, ... in order, folded in
+ * halves (p[k] += p[k + w/2], w = 64 .. 2); results are deterministic,
+ * independent of the launch, and bit-identical to the float32 definition.
  *
  * Arguments (shapes as in the source; N = 1 head):
  *   kv            bf16  [B, 1, S, Dv+Dk]
@@ -108,6 +109,32 @@ int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void
                                    int64_t Dv, int64_t Dk, int64_t num_blocks,
                                    int64_t block_size, int32_t ckv_dtype, float eps,
                                    int32_t *err_count, hipStream_t stream);
+
+/*
+ * kvrc_paged_blk_norm_rope_cache - the same computation into paged caches
+ * addressed by one index entry per block of tokens (block-indexed mode).
+ *
+ * Source: aclnnKvRmsNormRopeCache, restrictions on index for the PA_BLK_BNSD
+ * cache mode: the index has B * ceil(S / block_size) entries, each -1 or a
+ * value in [0, num_blocks * block_size) whose quotient by block_size does not
+ * repeat. Entry b * ceil(S/block_size) + c covers tokens
+ * s in [c * block_size, (c + 1) * block_size) of batch b and names the
+ * destination block entry / block_size; token (b, s) writes offset
+ * s % block_size of that block; -1 skips the whole chunk (the last chunk of a
+ * sequence may be partial).
+ *
+ *   block_index  int64 [B * ceil(S / block_size)]
+ * Caches, other arguments, status and err_count are as for
+ * kvrc_paged_norm_rope_cache (an out-of-range entry skips its chunk and
+ * counts once per token of the chunk).
+ */
+int32_t kvrc_paged_blk_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                                       const void *sin, const int64_t *block_index,
+                                       void *k_cache, void *ckv_cache, float *ckv_scale,
+                                       int64_t B, int64_t S, int64_t Dv, int64_t Dk,
+                                       int64_t num_blocks, int64_t block_size,
+                                       int32_t ckv_dtype, float eps, int32_t *err_count,
+                                       hipStream_t stream);
 
 /*
  * kvrc_norm_rope_cache - the same computation into CONTIGUOUS (Norm mode)

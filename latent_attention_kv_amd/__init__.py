@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in ``include/kvrc.h``):
   * kvrc_paged_norm_rope_cache - RMSNorm + interleaved RoPE + scatter into
     paged caches [num_blocks, block_size, 1, d] (aclnnKvRmsNormRopeCache,
     PA_BNSD cache mode)
+  * kvrc_paged_blk_norm_rope_cache - the same with one index entry per block
+    of tokens (PA_BLK_BNSD cache mode)
   * kvrc_norm_rope_cache       - the same into contiguous caches
     [Bc, 1, Sc, d] (Norm cache mode)
   * qsa_prepare                - block keys (openvino.opset17.qsa_prepare)
@@ -20,15 +22,16 @@ import os
 
 import torch
 
-__all__ = ["kvrc_paged_norm_rope_cache", "kvrc_norm_rope_cache", "qsa_prepare", "KvrcError",
-           "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "prepare_paged_norm_rope_cache",
-           "EXPORTED_SYMBOLS"]
+__all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
+           "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith", "KvrcError", "lib",
+           "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so")
 CACHE_BF16 = 0
 CACHE_INT8 = 1
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
-                    "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith")
+                    "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache", "qsa_prepare",
+                    "kvrc_selftest_arith")
 
 _lib = None
 
@@ -54,6 +57,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_paged_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
                                              I32, F, P, P]
     L.kvrc_paged_norm_rope_cache.restype = I32
+    L.kvrc_paged_blk_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64,
+                                                 I64, I64, I32, F, P, P]
+    L.kvrc_paged_blk_norm_rope_cache.restype = I32
     L.kvrc_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32,
                                        F, P, P]
     L.kvrc_norm_rope_cache.restype = I32
@@ -139,6 +145,7 @@ def _check(status, what):
 
 def _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale, eps,
                 err_count, stream):
+    """Checked C-ABI argument tuple of kvrc_paged_norm_rope_cache."""
     B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
     _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
     _need(k_cache, "k_cache", _BF16, 4)
@@ -164,21 +171,26 @@ def kvrc_paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_c
     _check(lib().kvrc_paged_norm_rope_cache(*args), "kvrc_paged_norm_rope_cache")
 
 
-def prepare_paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
-                                  ckv_scale=None, *, eps=1e-6, err_count=None, stream=None):
-    """Marshal the arguments once and return a no-argument callable that
-    launches the paged entry point (for repeated launches on fixed buffers)."""
-    args = _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale, eps,
-                       err_count, stream)
-    fn = lib().kvrc_paged_norm_rope_cache
-    cargs = [ctypes.c_void_p(a) if i in (0, 1, 2, 3, 4, 5, 6, 7, 16, 17) else a
-             for i, a in enumerate(args)]
-
-    def launch():
-        st = fn(*cargs)
-        if st != 0:
-            raise KvrcError(st, "kvrc_paged_norm_rope_cache")
-    return launch
+def kvrc_paged_blk_norm_rope_cache(kv, gamma, cos, sin, block_index, k_cache, ckv_cache,
+                                   ckv_scale=None, *, eps=1e-6, err_count=None, stream=None):
+    """Block-indexed paged mode (PA_BLK_BNSD): block_index [B * ceil(S / block_size)]."""
+    B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
+    _need(block_index, "block_index", (torch.int64,), 1)
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if BS < 1 or block_index.numel() != B * (-(-S // BS)):
+        raise ValueError("block_index must have B * ceil(S / block_size) entries")
+    if tuple(k_cache.shape) != (NB, BS, 1, Dk) or tuple(ckv_cache.shape) != (NB, BS, 1, Dv):
+        raise ValueError("caches must be [num_blocks, block_size, 1, Dk] and [.., Dv]")
+    dt = _cache_dtype(ckv_cache, ckv_scale)
+    if ckv_scale is not None and tuple(ckv_scale.shape) != (NB, BS, 1):
+        raise ValueError("ckv_scale must be [num_blocks, block_size, 1]")
+    st = lib().kvrc_paged_blk_norm_rope_cache(
+        _ptr(kv), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(block_index), _ptr(k_cache),
+        _ptr(ckv_cache), _ptr(ckv_scale), B, S, Dv, Dk, NB, BS, dt, float(eps),
+        _err_ptr(err_count), _stream(stream))
+    _check(st, "kvrc_paged_blk_norm_rope_cache")
 
 
 def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale=None, *,

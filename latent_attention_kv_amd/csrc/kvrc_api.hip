@@ -41,13 +41,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out)
 
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? KVRC_OK : KVRC_ERR_HIP; }
 
-// Shared body of the two norm-rope-cache entry points. `rows` is the number
-// of cache rows; rows_per_batch is 0 for paged caches.
+// Shared body of the norm-rope-cache entry points. `rows` is the number of
+// cache rows; rows_per_batch > 0 selects Norm mode, block_size > 0 the
+// block-indexed mode (one index entry per block_size tokens of a sequence).
 int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *cos, const void *sin,
                                const int64_t *index, void *k_cache, void *ckv_cache,
                                float *ckv_scale, int64_t B, int64_t S, int64_t Dv, int64_t Dk,
-                               int64_t rows, int64_t rows_per_batch, int64_t limit,
-                               int32_t ckv_dtype, float eps, int32_t *err_count,
+                               int64_t rows, int64_t rows_per_batch, int64_t block_size,
+                               int64_t limit, int32_t ckv_dtype, float eps, int32_t *err_count,
                                hipStream_t stream)
 {
     if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8)
@@ -72,12 +73,14 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
         !aligned(ckv_scale, 4) || !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
 
+    const int64_t chunks = block_size > 0 ? (S + block_size - 1) / block_size : 0;
+    const int64_t index_count = block_size > 0 ? B * chunks : T;
     int64_t kbytes, cbytes, sbytes = 0;
     if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (int8 ? 1 : 2), &cbytes) ||
         (int8 && !mul_ok(rows, 4, &sbytes)))
         return KVRC_ERR_SHAPE;
     const Range in[] = {span(kv, T * D * 2), span(gamma, Dv * 2), span(cos, T * Dk * 2),
-                        span(sin, T * Dk * 2), span(index, T * 8)};
+                        span(sin, T * Dk * 2), span(index, index_count * 8)};
     const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
                          span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
@@ -103,6 +106,8 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     a.Dv = Dv;
     a.Dk = Dk;
     a.rows_per_batch = rows_per_batch;
+    a.chunks_per_seq = chunks;
+    a.block_size = block_size;
     a.limit = limit;
     a.cache_rows = rows;
     a.int8 = int8;
@@ -143,8 +148,24 @@ int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void
     if (num_blocks < 0 || block_size < 1 || !mul_ok(num_blocks, block_size, &rows))
         return KVRC_ERR_SHAPE;
     return norm_rope_cache_common(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
-                                  ckv_scale, B, S, Dv, Dk, rows, 0, rows, ckv_dtype, eps,
+                                  ckv_scale, B, S, Dv, Dk, rows, 0, 0, rows, ckv_dtype, eps,
                                   err_count, stream);
+}
+
+int32_t kvrc_paged_blk_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
+                                       const void *sin, const int64_t *block_index,
+                                       void *k_cache, void *ckv_cache, float *ckv_scale,
+                                       int64_t B, int64_t S, int64_t Dv, int64_t Dk,
+                                       int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                                       float eps, int32_t *err_count, hipStream_t stream)
+{
+    int64_t rows;
+    if (num_blocks < 0 || block_size < 1 || block_size > INT32_MAX ||
+        !mul_ok(num_blocks, block_size, &rows))
+        return KVRC_ERR_SHAPE;
+    return norm_rope_cache_common(kv, gamma, cos, sin, block_index, k_cache, ckv_cache,
+                                  ckv_scale, B, S, Dv, Dk, rows, 0, block_size, rows, ckv_dtype,
+                                  eps, err_count, stream);
 }
 
 int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
@@ -159,7 +180,7 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
     // Sc == 0 with B*S > 0: every index must be -1; rows_per_batch stays > 0
     // only when there are rows to address.
     return norm_rope_cache_common(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale, B,
-                                  S, Dv, Dk, rows, Sc > 0 ? Sc : 1, Sc, ckv_dtype, eps,
+                                  S, Dv, Dk, rows, Sc > 0 ? Sc : 1, 0, Sc, ckv_dtype, eps,
                                   err_count, stream);
 }
 

@@ -8,10 +8,12 @@
 
 namespace kvrc {
 
-// One fused norm-rope-cache launch. A token t in [0, T) with index value v
-// writes cache row
-//   rows_per_batch == 0 : v                              (paged mode)
-//   rows_per_batch  > 0 : (t / S) * rows_per_batch + v   (Norm mode)
+// One fused norm-rope-cache launch. Token t = b*S + s in [0, T) reads its index
+// value v from index[t], or from index[b*chunks_per_seq + s/block_size] in
+// block-indexed mode, and writes cache row
+//   paged mode         : v
+//   Norm mode          : b * rows_per_batch + v
+//   block-indexed mode : (v / block_size) * block_size + s % block_size
 // when 0 <= v < limit; v == -1 skips it; any other v is counted in err.
 struct NormRopeCacheArgs {
     const uint16_t *kv;       // [T, Dv + Dk] bf16
@@ -23,7 +25,9 @@ struct NormRopeCacheArgs {
     void *ckv_cache;          // [rows, Dv] bf16 or int8
     float *ckv_scale;         // [rows] (int8 only)
     int64_t T, S, Dv, Dk;
-    int64_t rows_per_batch;   // 0 = paged
+    int64_t rows_per_batch;   // > 0: Norm mode
+    int64_t chunks_per_seq;   // > 0: block-indexed mode (ceil(S / block_size))
+    int64_t block_size;       // block-indexed mode only
     int64_t limit;            // exclusive bound of a valid index value
     int64_t cache_rows;       // rows of each cache (paged: limit; Norm: Bc * Sc)
     bool int8;

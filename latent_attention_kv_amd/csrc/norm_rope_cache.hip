@@ -39,13 +39,32 @@ namespace {
 constexpr int kThreads = KVRC_WG_THREADS;
 constexpr int kWaves = kThreads / 64;
 
+// Position of token t's entry in the index array (T and S fit 32 bits).
+__device__ __forceinline__ int64_t index_pos(const NormRopeCacheArgs &a, int64_t t)
+{
+    if (a.chunks_per_seq == 0)
+        return t;
+    const uint32_t b = (uint32_t)t / (uint32_t)a.S, s = (uint32_t)t % (uint32_t)a.S;
+    return (int64_t)b * a.chunks_per_seq + s / (uint32_t)a.block_size;
+}
+
 // Destination row of token t with index value v, or -1 (skip). Counts
 // invalid index values.
 __device__ __forceinline__ int64_t dest_row(const NormRopeCacheArgs &a, int64_t v, int64_t t,
                                             bool leader)
 {
-    if (v >= 0 && v < a.limit)
-        return a.rows_per_batch ? (t / a.S) * a.rows_per_batch + v : v;
+    if (v >= 0 && v < a.limit) {
+        if (a.rows_per_batch)
+            return (int64_t)((uint32_t)t / (uint32_t)a.S) * a.rows_per_batch + v;
+        if (a.chunks_per_seq) {
+            const uint32_t s = (uint32_t)t % (uint32_t)a.S;
+            const uint64_t bs = (uint64_t)a.block_size;
+            const uint64_t blk = (uint64_t)v < 0xffffffffull
+                ? (uint64_t)((uint32_t)v / (uint32_t)bs) : (uint64_t)v / bs;
+            return (int64_t)(blk * bs + s % (uint32_t)bs);
+        }
+        return v;
+    }
     if (v != -1 && leader && a.err)
         atomicAdd(a.err, 1);
     return -1;
@@ -132,7 +151,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
     // The token's inputs do not depend on its index value, so every load is
     // issued before the index is examined and their latencies overlap; the
     // stores alone are conditional (a skipped token's reads are wasted).
-    const int64_t v = a.index[t];
+    const int64_t v = a.index[index_pos(a, t)];
 
     // ---- loads: norm half, gamma, RoPE half, cos/sin -----------------------
     const uint16_t *xr = a.kv + t * D;
@@ -315,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
     const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (t >= a.T)
         return;
-    const int64_t row = dest_row(a, a.index[t], t, lane == 0);
+    const int64_t row = dest_row(a, a.index[index_pos(a, t)], t, lane == 0);
     if (row < 0)
         return;
     const int64_t Dv = a.Dv, Dk = a.Dk, D = Dv + Dk;

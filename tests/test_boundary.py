@@ -94,6 +94,28 @@ def test_paged_validation(over, want):
     assert paged(**over) == want
 
 
+def paged_blk(**over):
+    a = dict(kv=A["kv"], gamma=A["gamma"], cos=A["cos"], sin=A["sin"], idx=A["idx"], kc=A["kc"],
+             ckv=A["ckv"], scale=None, B=2, S=300, Dv=512, Dk=64, NB=64, BS=128, dt=0, eps=1e-6,
+             err=None, stream=None)
+    a.update(over)
+    return k.lib().kvrc_paged_blk_norm_rope_cache(a["kv"], a["gamma"], a["cos"], a["sin"],
+                                                  a["idx"], a["kc"], a["ckv"], a["scale"], a["B"],
+                                                  a["S"], a["Dv"], a["Dk"], a["NB"], a["BS"],
+                                                  a["dt"], a["eps"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(idx=None), NULL), (dict(BS=0), SHAPE), (dict(NB=-1), SHAPE), (dict(BS=1 << 32), SHAPE),
+    (dict(Dk=12), SHAPE), (dict(dt=1), DTYPE), (dict(idx=A["idx"] + 4), ALIGN),
+    # the index holds B*ceil(S/BS) = 6 entries (48 bytes): a cache starting inside it aliases
+    (dict(kc=A["idx"] + 32), ALIAS),
+    (dict(B=0), OK), (dict(S=0, idx=None), OK),
+])
+def test_paged_blk_validation(over, want):
+    assert paged_blk(**over) == want
+
+
 @pytest.mark.parametrize("over,want", [
     (dict(Bc=1), SHAPE), (dict(Sc=-1), SHAPE), (dict(sin=None), NULL), (dict(Dv=12), SHAPE),
     (dict(dt=1), DTYPE), (dict(ckv=A["ckv"] + 8), ALIGN), (dict(ckv=A["kc"]), ALIAS),

@@ -65,6 +65,10 @@ def run_kvrc_gpu(case, err=None, index_override=None):
         idx = case["slot_mapping"] if index_override is None else index_override
         k.kvrc_paged_norm_rope_cache(*args, dt(idx), caches["k_cache"], caches["ckv_cache"],
                                      caches.get("ckv_scale"), eps=case["eps"], err_count=err)
+    elif case["mode"] == "paged_blk":
+        idx = case["block_index"] if index_override is None else index_override
+        k.kvrc_paged_blk_norm_rope_cache(*args, dt(idx), caches["k_cache"], caches["ckv_cache"],
+                                         caches.get("ckv_scale"), eps=case["eps"], err_count=err)
     else:
         idx = case["index"] if index_override is None else index_override
         k.kvrc_norm_rope_cache(*args, dt(idx), caches["k_cache"], caches["ckv_cache"],
@@ -77,6 +81,16 @@ def written_rows(case):
     if case["mode"] == "paged":
         v = case["slot_mapping"]
         return np.unique(v[v >= 0])
+    if case["mode"] == "paged_blk":
+        S, bs = case["S"], case["block_size"]
+        chunks = -(-S // bs)
+        rows = []
+        for b in range(case["B"]):
+            for s in range(S):
+                v = int(case["block_index"][b * chunks + s // bs])
+                if v >= 0:
+                    rows.append((v // bs) * bs + s % bs)
+        return np.unique(np.array(rows, dtype=np.int64))
     idx = case["index"]
     rows = np.arange(case["B"])[:, None] * case["Sc"] + idx
     return np.unique(rows[idx >= 0])
@@ -91,7 +105,7 @@ def compare_kvrc(case, got, want, *, exact_bf16=False):
         if g.dtype == torch.bfloat16:
             wd = dbf(w)
             d = (ordered(g) - ordered(wd)).abs()
-            n_rows = d.shape[0] * (d.shape[1] if case["mode"] == "paged" else d.shape[2])
+            n_rows = d.shape[0] * (d.shape[2] if case["mode"] == "norm" else d.shape[1])
             per_row = d.reshape(n_rows, -1).amax(dim=1)
             untouched = torch.ones(n_rows, dtype=torch.bool, device=DEV)
             untouched[rows] = False
@@ -479,3 +493,35 @@ def test_int8_exact_ties():
     codes = got["ckv_cache"].cpu().numpy().reshape(-1, Dv)[slots]
     np.testing.assert_array_equal(codes, np.rint(rows).astype(np.int8))     # rint: half to even
     assert np.all(got["ckv_scale"].cpu().numpy().reshape(-1)[slots] == np.float32(1 / 64))
+
+
+
+@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("B,S,BS,offsets", [(8, 4096, 128, False), (3, 300, 64, True),
+                                             (2, 37, 16, False), (5, 1, 16, False)])
+def test_paged_blk_mode(ckv, B, S, BS, offsets):
+    """Block-indexed mode (PA_BLK_BNSD): one entry per chunk of BS tokens,
+    ragged last chunks, skipped chunks, entries with offsets inside the block."""
+    say(f"[parity] paged blk {ckv} B={B} S={S} BS={BS}")
+    chunks = B * (-(-S // BS))
+    case = gen.kvrc_paged_blk_case(960 + S, B=B, S=S, Dv=512, Dk=64,
+                                   num_blocks=max(2 * chunks, 64), block_size=BS, ckv_dtype=ckv,
+                                   n_skip=min(2, chunks - 1), entry_offsets=offsets)
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
+def test_paged_blk_named_workload_and_invalid_entries():
+    case = gen.make_config("prefill_paged_blk")
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+    small = gen.kvrc_paged_blk_case(970, B=2, S=100, Dv=512, Dk=64, num_blocks=16,
+                                    block_size=32)
+    idx = small["block_index"].copy()
+    idx[1] = 16 * 32                   # out of range: its 32 tokens are skipped and counted
+    idx[3] = -7                        # out of range: batch 0's last chunk has 100 - 96 = 4 tokens
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_kvrc_gpu(small, err=err, index_override=idx)
+    assert int(err.item()) == 32 + 4
+    fixed = idx.copy()
+    fixed[[1, 3]] = -1
+    clean = dict(small, block_index=fixed)
+    compare_kvrc(clean, got, oracle.run_kvrc_case(clean), exact_bf16=True)
