@@ -20,7 +20,7 @@ Conventions
   Angles and cos/sin are evaluated in float64, rounded to float32, and (where
   a bf16 table is wanted) rounded again to bf16.
 * Caches are pre-filled with sentinels that the method never produces:
-  bf16 7.0, int8 -128, scale -1.0.
+  bf16 7.0, int8 -128, FLOAT8 E4M3FN code 0x7f (NaN), scale -1.0.
 """
 from __future__ import annotations
 
@@ -29,10 +29,11 @@ import numpy as np
 BF16_SENTINEL = 0x40E0          # 7.0 in bf16
 BF16_NAN = 0x7FC0
 INT8_SENTINEL = -128
+FP8_SENTINEL = 0x7F             # E4M3FN NaN code
 SCALE_SENTINEL = -1.0
 
 CONFIG_NAMES = ("norm_tiny", "decode_paged", "prefill_paged", "quant_paged", "qsa")
-EXTRA_NAMES = ("prefill_paged_blk",)
+EXTRA_NAMES = ("prefill_paged_blk", "quant_fp8_paged")
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -95,6 +96,17 @@ class CacheSpec:
 # Norm-rope-cache cases
 # ---------------------------------------------------------------------------
 
+def ckv_cache_spec(shape, ckv_dtype):
+    """ckv cache of the given element type ("bf16", "int8" or "fp8" = E4M3FN codes)."""
+    if ckv_dtype == "bf16":
+        return CacheSpec(shape, np.uint16, BF16_SENTINEL)
+    if ckv_dtype == "int8":
+        return CacheSpec(shape, np.int8, INT8_SENTINEL)
+    if ckv_dtype == "fp8":
+        return CacheSpec(shape, np.uint8, FP8_SENTINEL)
+    raise ValueError(ckv_dtype)
+
+
 def _kv_common(g, B, S, Dv, Dk, sigma):
     kv = bf16_bits(g.standard_normal((B, 1, S, Dv + Dk), dtype=np.float32) * np.float32(sigma))
     gamma = bf16_bits(g.uniform(0.5, 1.5, size=(Dv,)).astype(np.float32))
@@ -115,10 +127,9 @@ def kvrc_norm_case(seed, B, S, Dv, Dk, Bc, Sc, n_skip, *, eps=1e-6, sigma=1.0,
         index.reshape(-1)[flat] = -1
     caches = {
         "k_cache": CacheSpec((Bc, 1, Sc, Dk), np.uint16, BF16_SENTINEL),
-        "ckv_cache": CacheSpec((Bc, 1, Sc, Dv), np.uint16 if ckv_dtype == "bf16" else np.int8,
-                               BF16_SENTINEL if ckv_dtype == "bf16" else INT8_SENTINEL),
+        "ckv_cache": ckv_cache_spec((Bc, 1, Sc, Dv), ckv_dtype),
     }
-    if ckv_dtype == "int8":
+    if ckv_dtype != "bf16":
         caches["ckv_scale"] = CacheSpec((Bc, 1, Sc), np.float32, SCALE_SENTINEL)
     return dict(mode="norm", kv=kv, gamma=gamma, cos=cos, sin=sin, index=index,
                 caches=caches, B=B, S=S, Dv=Dv, Dk=Dk, Bc=Bc, Sc=Sc, eps=float(eps),
@@ -160,11 +171,9 @@ def kvrc_paged_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6, sig
     cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
     caches = {
         "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
-        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv),
-                               np.uint16 if ckv_dtype == "bf16" else np.int8,
-                               BF16_SENTINEL if ckv_dtype == "bf16" else INT8_SENTINEL),
+        "ckv_cache": ckv_cache_spec((num_blocks, block_size, 1, Dv), ckv_dtype),
     }
-    if ckv_dtype == "int8":
+    if ckv_dtype != "bf16":
         caches["ckv_scale"] = CacheSpec((num_blocks, block_size, 1), np.float32, SCALE_SENTINEL)
     return dict(mode="paged", kv=kv, gamma=gamma, cos=cos, sin=sin, slot_mapping=slots,
                 caches=caches, B=B, S=S, Dv=Dv, Dk=Dk, num_blocks=num_blocks,
@@ -192,11 +201,9 @@ def kvrc_paged_blk_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6,
     cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
     caches = {
         "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
-        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv),
-                               np.uint16 if ckv_dtype == "bf16" else np.int8,
-                               BF16_SENTINEL if ckv_dtype == "bf16" else INT8_SENTINEL),
+        "ckv_cache": ckv_cache_spec((num_blocks, block_size, 1, Dv), ckv_dtype),
     }
-    if ckv_dtype == "int8":
+    if ckv_dtype != "bf16":
         caches["ckv_scale"] = CacheSpec((num_blocks, block_size, 1), np.float32, SCALE_SENTINEL)
     return dict(mode="paged_blk", kv=kv, gamma=gamma, cos=cos, sin=sin,
                 block_index=np.ascontiguousarray(entries), caches=caches, B=B, S=S, Dv=Dv,
@@ -274,6 +281,11 @@ def make_config(name: str, seed: int | None = None):
     if name == "qsa":
         return qsa_case(5 if seed is None else seed, N=32, L=2048, Di=128, Dr=64, kbs=64,
                         past_max=8192, Bcap=160)
+    if name == "quant_fp8_paged":
+        # the quantised-cache batch with a FLOAT8 E4M3FN ckv cache
+        return kvrc_paged_case(7 if seed is None else seed, B=64, S=1024, Dv=512, Dk=64,
+                               num_blocks=4096, block_size=128, slot_kind="table",
+                               sigma=2.0, ckv_dtype="fp8")
     if name == "prefill_paged_blk":
         # the prefill batch in block-indexed form: one entry per 128-token chunk
         return kvrc_paged_blk_case(6 if seed is None else seed, B=8, S=4096, Dv=512, Dk=64,
@@ -282,7 +294,8 @@ def make_config(name: str, seed: int | None = None):
 
 
 def kvrc_bytes_per_written_token(Dv: int, Dk: int, ckv_dtype: str) -> int:
-    """Algorithmic bytes one written token moves: kv + cos/sin + slot + outputs."""
+    """Algorithmic bytes one written token moves: kv + cos/sin + slot + outputs
+    (a quantised ckv row is one byte per value plus its float32 scale)."""
     reads = 2 * (Dv + Dk) + 2 * 2 * Dk + 8
     writes = (2 * Dv if ckv_dtype == "bf16" else Dv + 4) + 2 * Dk
     return reads + writes

@@ -66,6 +66,12 @@ def _load():
     lib.orc_qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64,
                                     I64, I64, F, I]
     lib.orc_qsa_block_key.argtypes = [P, I64, I64, P, P, P, I64, F, P, P]
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = F
+    lib.orc_e4m3_encode.argtypes = [F]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_quant_row_fp8.argtypes = [P, I64, P, P]
+    lib.orc_e4m3_encode_array.argtypes = [P, P, I64, I]
     lib.orc_f32_to_bf16_array.argtypes = [P, P, I64]
     lib.orc_bf16_to_f32_array.argtypes = [P, P, I64]
     lib.orc_max_threads.restype = I
@@ -135,6 +141,29 @@ def quant_row(y):
     return code, np.float32(scale[0])
 
 
+def e4m3_decode(code) -> np.float32:
+    return np.float32(_load().orc_e4m3_decode(int(code) & 0xFF))
+
+
+def e4m3_encode(v) -> int:
+    return int(_load().orc_e4m3_encode(float(np.float32(v))))
+
+
+def e4m3_encode_array(v, nthreads=None) -> np.ndarray:
+    v = _f32(v)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().orc_e4m3_encode_array(_p(v), _p(out), v.size, nthreads or max_threads())
+    return out
+
+
+def quant_row_fp8(y):
+    y = _f32(y)
+    code = np.empty(y.shape, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.float32)
+    _load().orc_quant_row_fp8(_p(y), y.size, _p(code), _p(scale))
+    return code, np.float32(scale[0])
+
+
 def token_outputs(kv_row, gamma, cos_row, sin_row, Dv, Dk, eps=1e-6):
     """float32 (pre-rounding) outputs of one token: rmsnorm(Dv) and rope(Dk)."""
     kv_row = np.ascontiguousarray(kv_row, dtype=np.uint16)
@@ -170,6 +199,11 @@ def _check(rc):
         raise OracleError(f"oracle status {rc}: {STATUS.get(rc, '?')}")
 
 
+def _ckv_kind(ckv_cache) -> int:
+    """0: bf16 bits (uint16), 1: int8 codes, 2: FLOAT8 E4M3FN codes (uint8)."""
+    return {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[ckv_cache.dtype]
+
+
 def paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
                           ckv_scale=None, *, eps=1e-6, nthreads=None):
     """Update k_cache / ckv_cache (/ ckv_scale) in place. Shapes:
@@ -179,7 +213,7 @@ def paged_norm_rope_cache(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
     Dk = cos.shape[-1]
     Dv = D - Dk
     NB, BS = k_cache.shape[0], k_cache.shape[1]
-    int8 = ckv_cache.dtype == np.int8
+    int8 = _ckv_kind(ckv_cache)
     rc = _load().orc_paged_norm_rope_cache(
         _p(kv), _p(gamma), _p(cos), _p(sin), _p(slot_mapping), _p(k_cache), _p(ckv_cache),
         _p(ckv_scale), B, S, Dv, Dk, NB, BS, int(int8), eps,
@@ -194,7 +228,7 @@ def paged_blk_norm_rope_cache(kv, gamma, cos, sin, block_index, k_cache, ckv_cac
     Dk = cos.shape[-1]
     Dv = D - Dk
     NB, BS = k_cache.shape[0], k_cache.shape[1]
-    int8 = ckv_cache.dtype == np.int8
+    int8 = _ckv_kind(ckv_cache)
     rc = _load().orc_paged_blk_norm_rope_cache(
         _p(kv), _p(gamma), _p(cos), _p(sin), _p(block_index), _p(k_cache), _p(ckv_cache),
         _p(ckv_scale), B, S, Dv, Dk, NB, BS, int(int8), eps, nthreads or max_threads())
@@ -208,7 +242,7 @@ def norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale=No
     Dk = cos.shape[-1]
     Dv = D - Dk
     Bc, Sc = k_cache.shape[0], k_cache.shape[2]
-    int8 = ckv_cache.dtype == np.int8
+    int8 = _ckv_kind(ckv_cache)
     rc = _load().orc_norm_rope_cache(
         _p(kv), _p(gamma), _p(cos), _p(sin), _p(index), _p(k_cache), _p(ckv_cache),
         _p(ckv_scale), B, S, Dv, Dk, Bc, Sc, int(int8), eps, nthreads or max_threads())

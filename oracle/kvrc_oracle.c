@@ -37,6 +37,9 @@
 #include <omp.h>
 #endif
 
+/* ckv cache element types (the oracle's own numbering). */
+enum { ORC_CKV_BF16 = 0, ORC_CKV_INT8 = 1, ORC_CKV_FP8 = 2 };
+
 /* Oracle status codes (its own; unrelated to the library's). */
 enum {
     ORC_OK = 0,
@@ -178,6 +181,90 @@ void orc_quant_row(const float *y, int64_t n, int8_t *code, float *scale)
     *scale = sc;
 }
 
+/*
+ * FLOAT8 E4M3FN (one of the ckv cache types of aclnnKvRmsNormRopeCache,
+ * quantisation scenario 1): sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds the subnormals m * 2^-9; no infinities; codes
+ * 0x7f / 0xff are NaN, so the largest finite magnitude is 0x7e = 1.75 * 2^8 =
+ * 448.
+ */
+float orc_e4m3_decode(uint8_t c)
+{
+    int e = (c >> 3) & 0xf, m = c & 7;
+    float mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexpf((float)m, -9);
+    else
+        mag = ldexpf((float)(8 + m), e - 10);
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* The 127 finite non-negative E4M3FN values, indexed by code (increasing). */
+static void e4m3_table(float t[127])
+{
+    for (int c = 0; c < 127; ++c)
+        t[c] = orc_e4m3_decode((uint8_t)c);
+}
+
+/*
+ * Code of the E4M3FN value nearest to v, ties to the even code; magnitudes
+ * beyond 448 give 448 (saturation; the quantiser below never produces them).
+ * The nearest value is found by bisection of the decoded table.
+ */
+static uint8_t e4m3_nearest(const float t[127], float v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= t[126])
+        return sign | 126;
+    int lo = 0, hi = 126;                     /* t[lo] <= a < t[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (t[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = a - t[lo], dh = t[hi] - a;
+    int c = dl < dh ? lo : dh < dl ? hi : ((lo & 1) ? hi : lo);
+    return sign | (uint8_t)c;
+}
+
+uint8_t orc_e4m3_encode(float v)
+{
+    float t[127];
+    e4m3_table(t);
+    return e4m3_nearest(t, v);
+}
+
+/*
+ * Per-row dynamic FLOAT8 E4M3FN quantisation. READING: the pages give no
+ * scale rule for the float8 caches; by analogy with RowMax(abs)/127 for int8
+ * (aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula: the row maximum
+ * maps to the largest code), scale = RowMax(|y|) / 448 and code =
+ * E4M3FN(y / scale) to nearest, ties to even. An all-zero row stores scale 0
+ * and codes 0x00.
+ */
+void orc_quant_row_fp8(const float *y, int64_t n, uint8_t *code, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(y[i]);
+        if (a > amax)
+            amax = a;
+    }
+    float sc = amax / 448.0f;
+    float t[127];
+    e4m3_table(t);
+    for (int64_t i = 0; i < n; ++i)
+        code[i] = sc == 0.0f ? (uint8_t)0 : e4m3_nearest(t, y[i] / sc);
+    *scale = sc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Fused norm-rope-cache                                                    */
 /* ------------------------------------------------------------------------ */
@@ -190,16 +277,19 @@ void orc_quant_row(const float *y, int64_t n, int8_t *code, float *scale)
  */
 static void token_to_row(const uint16_t *kv, const float *g, const uint16_t *cs,
                          const uint16_t *sn, int64_t Dv, int64_t Dk, float eps,
-                         int ckv_int8, int64_t row, uint16_t *k_cache, void *ckv_cache,
+                         int ckv_kind, int64_t row, uint16_t *k_cache, void *ckv_cache,
                          float *ckv_scale, float *xbuf, float *ybuf, float *cbuf, float *sbuf)
 {
     /* left Dv columns: rmsNorm */
     for (int64_t i = 0; i < Dv; ++i)
         xbuf[i] = orc_bf16_to_f32(kv[i]);
     orc_rmsnorm_f32(xbuf, g, Dv, eps, ybuf);
-    if (ckv_int8) {
+    if (ckv_kind == ORC_CKV_INT8) {
         int8_t *dst = (int8_t *)ckv_cache + row * Dv;
         orc_quant_row(ybuf, Dv, dst, &ckv_scale[row]);
+    } else if (ckv_kind == ORC_CKV_FP8) {
+        uint8_t *dst = (uint8_t *)ckv_cache + row * Dv;
+        orc_quant_row_fp8(ybuf, Dv, dst, &ckv_scale[row]);
     } else {
         uint16_t *dst = (uint16_t *)ckv_cache + row * Dv;
         for (int64_t i = 0; i < Dv; ++i)
@@ -241,7 +331,7 @@ static int check_indices(const int64_t *idx, int64_t n, int64_t limit)
 
 static int run_tokens(const uint16_t *kv, const uint16_t *gamma, const uint16_t *cs,
                       const uint16_t *sn, const int64_t *dest_row, int64_t T, int64_t Dv,
-                      int64_t Dk, float eps, int ckv_int8, uint16_t *k_cache, void *ckv_cache,
+                      int64_t Dk, float eps, int ckv_kind, uint16_t *k_cache, void *ckv_cache,
                       float *ckv_scale, int nthreads)
 {
     float *g = (float *)malloc(sizeof(float) * (size_t)Dv);
@@ -265,7 +355,7 @@ static int run_tokens(const uint16_t *kv, const uint16_t *gamma, const uint16_t 
             if (dest_row[t] < 0)
                 continue;                       /* index -1: token skipped */
             token_to_row(kv + t * (Dv + Dk), g, cs + t * Dk, sn + t * Dk, Dv, Dk, eps,
-                         ckv_int8, dest_row[t], k_cache, ckv_cache, ckv_scale, xbuf, ybuf,
+                         ckv_kind, dest_row[t], k_cache, ckv_cache, ckv_scale, xbuf, ybuf,
                          cbuf, sbuf);
         }
         free(xbuf);
@@ -290,12 +380,12 @@ int orc_paged_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const u
                               const uint16_t *sn, const int64_t *slot_mapping,
                               uint16_t *k_cache, void *ckv_cache, float *ckv_scale,
                               int64_t B, int64_t S, int64_t Dv, int64_t Dk,
-                              int64_t num_blocks, int64_t block_size, int ckv_int8, float eps,
+                              int64_t num_blocks, int64_t block_size, int ckv_kind, float eps,
                               int nthreads)
 {
     if (B < 0 || S < 0 || Dv < 1 || Dk < 2 || (Dk & 1) || num_blocks < 0 || block_size < 1)
         return ORC_BAD_ARG;
-    if (ckv_int8 && !ckv_scale)
+    if (ckv_kind < 0 || ckv_kind > 2 || (ckv_kind != ORC_CKV_BF16 && !ckv_scale))
         return ORC_BAD_ARG;
     int64_t T = B * S;
     if (T == 0)
@@ -313,7 +403,7 @@ int orc_paged_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const u
             dest[t] = (blk * block_size + off) * 1 + 0;   /* [blk, off, head 0] */
         }
     }
-    rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_int8, k_cache, ckv_cache,
+    rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_kind, k_cache, ckv_cache,
                     ckv_scale, nthreads);
     free(dest);
     return rc;
@@ -329,12 +419,12 @@ int orc_paged_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const u
 int orc_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const uint16_t *cs,
                         const uint16_t *sn, const int64_t *index, uint16_t *k_cache,
                         void *ckv_cache, float *ckv_scale, int64_t B, int64_t S, int64_t Dv,
-                        int64_t Dk, int64_t Bc, int64_t Sc, int ckv_int8, float eps,
+                        int64_t Dk, int64_t Bc, int64_t Sc, int ckv_kind, float eps,
                         int nthreads)
 {
     if (B < 0 || S < 0 || Dv < 1 || Dk < 2 || (Dk & 1) || Bc < B || Sc < 0)
         return ORC_BAD_ARG;
-    if (ckv_int8 && !ckv_scale)
+    if (ckv_kind < 0 || ckv_kind > 2 || (ckv_kind != ORC_CKV_BF16 && !ckv_scale))
         return ORC_BAD_ARG;
     int64_t T = B * S;
     if (T == 0)
@@ -350,7 +440,7 @@ int orc_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, const uint16_
             int64_t v = index[b * S + s];
             dest[b * S + s] = v < 0 ? -1 : (b * 1 + 0) * Sc + v;   /* [b, head 0, v] */
         }
-    int rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_int8, k_cache, ckv_cache,
+    int rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_kind, k_cache, ckv_cache,
                         ckv_scale, nthreads);
     free(dest);
     return rc;
@@ -369,12 +459,12 @@ int orc_paged_blk_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, con
                                   const uint16_t *sn, const int64_t *block_index,
                                   uint16_t *k_cache, void *ckv_cache, float *ckv_scale,
                                   int64_t B, int64_t S, int64_t Dv, int64_t Dk,
-                                  int64_t num_blocks, int64_t block_size, int ckv_int8,
+                                  int64_t num_blocks, int64_t block_size, int ckv_kind,
                                   float eps, int nthreads)
 {
     if (B < 0 || S < 0 || Dv < 1 || Dk < 2 || (Dk & 1) || num_blocks < 0 || block_size < 1)
         return ORC_BAD_ARG;
-    if (ckv_int8 && !ckv_scale)
+    if (ckv_kind < 0 || ckv_kind > 2 || (ckv_kind != ORC_CKV_BF16 && !ckv_scale))
         return ORC_BAD_ARG;
     int64_t T = B * S;
     if (T == 0)
@@ -400,7 +490,7 @@ int orc_paged_blk_norm_rope_cache(const uint16_t *kv, const uint16_t *gamma, con
             int64_t v = block_index[b * chunks + s / block_size];
             dest[b * S + s] = v < 0 ? -1 : (v / block_size) * block_size + s % block_size;
         }
-    rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_int8, k_cache, ckv_cache,
+    rc = run_tokens(kv, gamma, cs, sn, dest, T, Dv, Dk, eps, ckv_kind, k_cache, ckv_cache,
                     ckv_scale, nthreads);
     free(dest);
     return rc;
@@ -597,6 +687,20 @@ int orc_max_threads(void)
 }
 
 /* Array forms of the format conversions, for the tests. */
+void orc_e4m3_encode_array(const float *src, uint8_t *dst, int64_t n, int nthreads)
+{
+    float t[127];
+    e4m3_table(t);
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = e4m3_nearest(t, src[i]);
+    (void)nthreads;
+}
+
 void orc_f32_to_bf16_array(const float *src, uint16_t *dst, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)

@@ -47,6 +47,9 @@ def _expected_rows(case):
         if case["ckv_dtype"] == "int8":
             code, scale = oracle.quant_row(yn)
             rows[flat] = (oracle.f32_to_bf16(yr), code, scale)
+        elif case["ckv_dtype"] == "fp8":
+            code, scale = oracle.quant_row_fp8(yn)
+            rows[flat] = (oracle.f32_to_bf16(yr), code, scale)
         else:
             rows[flat] = (oracle.f32_to_bf16(yr), oracle.f32_to_bf16(yn), None)
     return rows
@@ -71,7 +74,7 @@ def _assert_same(a, b):
         np.testing.assert_array_equal(a[k].view(np.uint8), b[k].view(np.uint8), err_msg=k)
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", ["bf16", "int8", "fp8"])
 def test_paged_scatter_brute_force(ckv):
     case = gen.kvrc_paged_case(41, B=3, S=37, Dv=64, Dk=16, num_blocks=16, block_size=16,
                                slot_kind="random", skip_frac=0.2, ckv_dtype=ckv, max_pos=4096)
@@ -91,7 +94,7 @@ def test_paged_table_layout_brute_force():
     _assert_same(oracle.run_kvrc_case(case), _brute(case))
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", ["bf16", "int8", "fp8"])
 def test_norm_scatter_brute_force(ckv):
     case = gen.kvrc_norm_case(43, B=3, S=10, Dv=64, Dk=16, Bc=4, Sc=24, n_skip=4, ckv_dtype=ckv)
     # the same index value in two batches is legal (separate namespaces)
@@ -156,7 +159,7 @@ def test_threads_do_not_change_result():
     _assert_same(a, b)
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("S,offsets", [(64, False), (40, False), (37, True)])
 def test_paged_blk_scatter_brute_force(ckv, S, offsets):
     """Block-indexed mode (PA_BLK_BNSD): ragged last chunk, skipped chunks and
