@@ -61,6 +61,9 @@ WORKLOAD_TEXT = {
                     "unique random slots, 5% skipped (-1)",
     "quant_paged": "paged int8 ckv cache: B=64, S=1024, D=576 bf16 (sigma 2), ckv int8 "
                    "[4096,128,1,512] + fp32 scale [4096,128,1], k bf16 [4096,128,1,64]",
+    "quant_fp8_paged": "paged FLOAT8 E4M3FN ckv cache: B=64, S=1024, D=576 bf16 (sigma 2), "
+                       "ckv E4M3FN [4096,128,1,512] + fp32 scale [4096,128,1], "
+                       "k bf16 [4096,128,1,64]",
     "norm_tiny": "Norm cache mode: B=2, S=16, D=576, caches [2,1,32,d] bf16",
     "prefill_paged_blk": "paged prefill, block-indexed (PA_BLK_BNSD): B=8, S=4096 (32768 "
                          "tokens), D=576 bf16, one index entry per 128-token chunk, caches "
@@ -153,7 +156,8 @@ def build_sets(case, R, dev):
                 s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
                                      device=dev).view(torch.bfloat16)
             else:
-                tdt = torch.int8 if spec.dtype == np.int8 else torch.float32
+                tdt = {np.dtype(np.int8): torch.int8, np.dtype(np.uint8): torch.uint8,
+                       np.dtype(np.float32): torch.float32}[spec.dtype]
                 s[name] = torch.full(spec.shape, spec.fill, dtype=tdt, device=dev)
         sets.append(s)
     return sets

@@ -51,8 +51,9 @@ typedef enum kvrc_status {
 
 /* Element type of the ckv cache. */
 typedef enum kvrc_cache_dtype {
-    KVRC_CACHE_BF16 = 0, /* bf16 rows, no scale                                  */
-    KVRC_CACHE_INT8 = 1  /* int8 codes + one float32 scale per row               */
+    KVRC_CACHE_BF16 = 0,    /* bf16 rows, no scale                               */
+    KVRC_CACHE_INT8 = 1,    /* int8 codes + one float32 scale per row            */
+    KVRC_CACHE_FP8_E4M3 = 2 /* FLOAT8 E4M3FN codes + one float32 scale per row   */
 } kvrc_cache_dtype;
 
 /* Static, human-readable name of a status code. Never NULL. */
@@ -66,9 +67,11 @@ int32_t kvrc_version(void);
  *
  * Source: aclnnKvRmsNormRopeCache (Description; Formulas (1) interleaveRope and
  * (2) rmsNorm; restrictions on index for the PA / PA_BNSD cache modes;
- * quantisation scenario 1 for an int8 ckv cache) with the per-row scale rule
- * RowMax(abs)/127 and round of aclnnMlaPrologV3WeightNz (Dequant Scale Query
- * Nope formula).
+ * quantisation scenario 1 for an int8 or FLOAT8 E4M3FN ckv cache) with the
+ * per-row scale rule RowMax(abs)/127 and round of aclnnMlaPrologV3WeightNz
+ * (Dequant Scale Query Nope formula). The source gives no scale rule for the
+ * float8 cache; this library reads it as the same rule with 448, the largest
+ * finite E4M3FN value, in place of 127.
  *
  * For every token t = b*S + s of kv[B, 1, S, Dv+Dk]:
  *   v = slot_mapping[t]; v == -1 skips the token (nothing is written for it;
@@ -78,8 +81,11 @@ int32_t kvrc_version(void);
  *        x1 = x[0::2], x2 = x[1::2], kr = cat(x1,x2)*cos + cat(-x2,x1)*sin
  *   ckv_cache[v / block_size, v % block_size, 0, :] = bf16(y)      (BF16), or
  *        int8 codes rint(y / scale) with scale = max|y| / 127 stored to
- *        ckv_scale[v / block_size, v % block_size, 0]             (INT8;
- *        an all-zero row stores scale 0 and codes 0)
+ *        ckv_scale[v / block_size, v % block_size, 0]             (INT8), or
+ *        E4M3FN codes of y / scale (nearest, ties to the even code, +-448
+ *        beyond) with scale = max|y| / 448 stored likewise   (FP8_E4M3);
+ *        y / scale is the correctly rounded float32 quotient, and an
+ *        all-zero row stores scale 0 and codes 0
  *   k_cache[v / block_size, v % block_size, 0, :] = bf16(kr)
  * The sum of squares uses a fixed order: 64 partial sums, partial l adding
  * the squares of the 8-element chunks c = l, l+64, ... in order, folded in
@@ -92,9 +98,9 @@ int32_t kvrc_version(void);
  *   cos, sin      bf16  [B, 1, S, Dk]        one full-width row per token
  *   slot_mapping  int64 [B*S]                -1 or unique in [0, num_blocks*block_size)
  *   k_cache       bf16  [num_blocks, block_size, 1, Dk]
- *   ckv_cache     bf16 or int8 [num_blocks, block_size, 1, Dv]
+ *   ckv_cache     bf16, int8 or E4M3FN (uint8 codes) [num_blocks, block_size, 1, Dv]
  *   ckv_scale     float32 [num_blocks, block_size, 1]; must be NULL for BF16
- *                 and non-NULL for INT8
+ *                 and non-NULL for INT8 and FP8_E4M3
  *   Dv, Dk        multiples of 8, >= 8 (Dk even is the source's rule; 8 is
  *                 this library's vector width)
  *   eps           added to the mean square
@@ -147,8 +153,8 @@ int32_t kvrc_paged_blk_norm_rope_cache(const void *kv, const void *gamma, const 
  *
  *   index      int64 [B, S]                 -1 skips; unique within a batch row
  *   k_cache    bf16  [Bc, 1, Sc, Dk]
- *   ckv_cache  bf16 or int8 [Bc, 1, Sc, Dv]
- *   ckv_scale  float32 [Bc, 1, Sc] (INT8 only, else NULL)
+ *   ckv_cache  bf16, int8 or E4M3FN [Bc, 1, Sc, Dv]
+ *   ckv_scale  float32 [Bc, 1, Sc] (INT8 and FP8_E4M3 only, else NULL)
  * Token (b, s) with v = index[b, s] >= 0 writes row [b, 0, v] of each cache.
  * Other arguments, the returned status and err_count are as for
  * kvrc_paged_norm_rope_cache.

@@ -3,9 +3,9 @@
  *
  * Not part of the method. The kernels of libkvrc reach results bit-identical
  * to the float32 definition only if their building blocks round exactly as
- * IEEE float32 does; this entry point runs those building blocks on the GPU
+ * IEEE float32 does; these entry points run those building blocks on the GPU
  * for caller-chosen operands so that a test can compare them with the host's
- * IEEE results.
+ * IEEE results and with the float8 format's definition.
  */
 #ifndef KVRC_SELFTEST_H
 #define KVRC_SELFTEST_H
@@ -32,6 +32,17 @@ extern "C" {
  */
 int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_shared, float *q_ieee,
                             float *root, int64_t n, hipStream_t stream);
+
+/*
+ * For i in [0, n): code[i] = the FLOAT8 E4M3FN code the kernels store for the
+ * float32 quotient x[i] (nearest E4M3FN value, ties to the even code,
+ * magnitudes beyond 448 saturating to +-448; the sign bit of the code is the
+ * sign of x[i], also for a zero result). x is float32 device memory (16-byte
+ * aligned), code uint8 device memory (4-byte aligned, not overlapping x);
+ * n must be a multiple of 4. Returns KVRC_OK, KVRC_ERR_NULL, KVRC_ERR_SHAPE,
+ * KVRC_ERR_ALIGN, KVRC_ERR_ALIAS or KVRC_ERR_HIP. Asynchronous on `stream`.
+ */
+int32_t kvrc_selftest_e4m3(const float *x, uint8_t *code, int64_t n, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ is not on the GPU, the call raises.
 Entry points (same names as the C ABI in ``include/kvrc.h``):
   * kvrc_paged_norm_rope_cache - RMSNorm + interleaved RoPE + scatter into
     paged caches [num_blocks, block_size, 1, d] (aclnnKvRmsNormRopeCache,
-    PA_BNSD cache mode)
+    PA_BNSD cache mode); the ckv cache holds bf16 rows, or int8 / FLOAT8
+    E4M3FN codes with a float32 scale per row
   * kvrc_paged_blk_norm_rope_cache - the same with one index entry per block
     of tokens (PA_BLK_BNSD cache mode)
   * kvrc_norm_rope_cache       - the same into contiguous caches
@@ -23,15 +24,17 @@ import os
 import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
-           "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith", "KvrcError", "lib",
-           "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "EXPORTED_SYMBOLS"]
+           "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
+           "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
+           "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so")
 CACHE_BF16 = 0
 CACHE_INT8 = 1
+CACHE_FP8_E4M3 = 2
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache", "qsa_prepare",
-                    "kvrc_selftest_arith")
+                    "kvrc_selftest_arith", "kvrc_selftest_e4m3")
 
 _lib = None
 
@@ -68,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_prepare.restype = I32
     L.kvrc_selftest_arith.argtypes = [P, P, P, P, P, I64, P]
     L.kvrc_selftest_arith.restype = I32
+    L.kvrc_selftest_e4m3.argtypes = [P, P, I64, P]
+    L.kvrc_selftest_e4m3.restype = I32
     _lib = L
     return L
 
@@ -122,13 +127,18 @@ def _kv_shapes(kv, gamma, cos, sin):
     return B, S, Dv, Dk
 
 
+# ckv cache element types: bf16 rows, int8 codes, or FLOAT8 E4M3FN codes
+# (torch.float8_e4m3fn, or their raw bytes as torch.uint8).
+_CKV = (torch.bfloat16, torch.int8, torch.float8_e4m3fn, torch.uint8)
+
+
 def _cache_dtype(ckv_cache, ckv_scale):
-    if ckv_cache.dtype == torch.int8:
-        _need(ckv_scale, "ckv_scale", (torch.float32,))
-        return CACHE_INT8
-    if ckv_scale is not None:
-        raise ValueError("ckv_scale is only used with an int8 ckv cache")
-    return CACHE_BF16
+    if ckv_cache.dtype == torch.bfloat16:
+        if ckv_scale is not None:
+            raise ValueError("ckv_scale is only used with a quantised (int8 / fp8) ckv cache")
+        return CACHE_BF16
+    _need(ckv_scale, "ckv_scale", (torch.float32,))
+    return CACHE_INT8 if ckv_cache.dtype == torch.int8 else CACHE_FP8_E4M3
 
 
 def _err_ptr(err_count):
@@ -149,7 +159,7 @@ def _paged_args(kv, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, ckv_scale
     B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
     _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
     _need(k_cache, "k_cache", _BF16, 4)
-    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    _need(ckv_cache, "ckv_cache", _CKV, 4)
     NB, BS = k_cache.shape[0], k_cache.shape[1]
     if slot_mapping.numel() != B * S:
         raise ValueError("slot_mapping must have B*S entries")
@@ -177,7 +187,7 @@ def kvrc_paged_blk_norm_rope_cache(kv, gamma, cos, sin, block_index, k_cache, ck
     B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
     _need(block_index, "block_index", (torch.int64,), 1)
     _need(k_cache, "k_cache", _BF16, 4)
-    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    _need(ckv_cache, "ckv_cache", _CKV, 4)
     NB, BS = k_cache.shape[0], k_cache.shape[1]
     if BS < 1 or block_index.numel() != B * (-(-S // BS)):
         raise ValueError("block_index must have B * ceil(S / block_size) entries")
@@ -199,7 +209,7 @@ def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_sca
     B, S, Dv, Dk = _kv_shapes(kv, gamma, cos, sin)
     _need(index, "index", (torch.int64,), 2)
     _need(k_cache, "k_cache", _BF16, 4)
-    _need(ckv_cache, "ckv_cache", (torch.bfloat16, torch.int8), 4)
+    _need(ckv_cache, "ckv_cache", _CKV, 4)
     Bc, Sc = k_cache.shape[0], k_cache.shape[2]
     if tuple(index.shape) != (B, S):
         raise ValueError("index must be [B, S]")
@@ -224,6 +234,16 @@ def kvrc_selftest_arith(a, b, q_shared, q_ieee, root, *, stream=None):
     st = lib().kvrc_selftest_arith(_ptr(a), _ptr(b), _ptr(q_shared), _ptr(q_ieee), _ptr(root),
                                    a.numel(), _stream(stream))
     _check(st, "kvrc_selftest_arith")
+
+
+def kvrc_selftest_e4m3(x, code, *, stream=None):
+    """E4M3FN conversion self-test (include/kvrc_selftest.h): float32 x -> uint8 codes."""
+    _need(x, "x", (torch.float32,), 1)
+    _need(code, "code", (torch.uint8,), 1)
+    if code.numel() != x.numel():
+        raise ValueError("x and code must have the same length")
+    _check(lib().kvrc_selftest_e4m3(_ptr(x), _ptr(code), x.numel(), _stream(stream)),
+           "kvrc_selftest_e4m3")
 
 
 def qsa_prepare(raw_index_keys, block_keys, key_length, rope_cos, rope_sin, k_norm_weight,

@@ -140,6 +140,7 @@ __device__ __forceinline__ float fold_max(float v)
 // ---------------------------------------------------------------------------
 constexpr float kFastDivLo = 0x1p-60f;
 constexpr float kFastDivHi = 0x1p60f;
+constexpr float kFastDivDividendLo = 0x1p-64f;
 // Bit pattern of 2^-120: a square x*x at or above it means |x| >= 2^-60.
 constexpr uint32_t kMinSquareBits = 0x03800000u;
 
@@ -171,6 +172,31 @@ __device__ __forceinline__ u32x2 pack_low_bytes8(const uint32_t (&w)[8])
     const uint32_t c = __builtin_amdgcn_perm(w[5], w[4], 0x0c0c0400u);
     const uint32_t d = __builtin_amdgcn_perm(w[7], w[6], 0x04000c0cu);
     return u32x2{a | b, c | d};
+}
+
+// Four float32 values -> four FLOAT8 E4M3FN codes (OCP format: 4 exponent
+// bits with bias 7, 3 mantissa bits, largest finite value 448, no
+// infinities), bytes 0..3 of the result in argument order. Each value is
+// rounded to the nearest E4M3FN value, ties to the even code; magnitudes
+// beyond 448 saturate to +-448. v_med3_f32 does the saturation (it keeps the
+// sign of zero) and v_cvt_pk_fp8_f32, which on gfx950 converts to the OCP
+// E4M3FN format with round to nearest even, the rounding.
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -kE4m3Max, kE4m3Max);
+    b = __builtin_amdgcn_fmed3f(b, -kE4m3Max, kE4m3Max);
+    c = __builtin_amdgcn_fmed3f(c, -kE4m3Max, kE4m3Max);
+    d = __builtin_amdgcn_fmed3f(d, -kE4m3Max, kE4m3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ u32x2 e4m3_pack8(const float (&q)[8])
+{
+    return u32x2{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
 }
 
 // Pack eight int8 codes (given as float integral values in [-127, 127]).

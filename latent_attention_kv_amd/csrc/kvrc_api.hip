@@ -51,7 +51,8 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
                                int64_t limit, int32_t ckv_dtype, float eps, int32_t *err_count,
                                hipStream_t stream)
 {
-    if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8)
+    if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8 &&
+        ckv_dtype != KVRC_CACHE_FP8_E4M3)
         return KVRC_ERR_DTYPE;
     if (B < 0 || S < 0 || rows < 0 || limit < 0)
         return KVRC_ERR_SHAPE;
@@ -65,8 +66,8 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
 
     if (!kv || !gamma || !cos || !sin || !index || !k_cache || !ckv_cache)
         return KVRC_ERR_NULL;
-    const bool int8 = ckv_dtype == KVRC_CACHE_INT8;
-    if (int8 != (ckv_scale != nullptr))
+    const bool quant = ckv_dtype != KVRC_CACHE_BF16;   // one byte per element + scale
+    if (quant != (ckv_scale != nullptr))
         return KVRC_ERR_DTYPE;
     if (!aligned(kv, 16) || !aligned(gamma, 16) || !aligned(cos, 16) || !aligned(sin, 16) ||
         !aligned(index, 8) || !aligned(k_cache, 16) || !aligned(ckv_cache, 16) ||
@@ -76,8 +77,8 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     const int64_t chunks = block_size > 0 ? (S + block_size - 1) / block_size : 0;
     const int64_t index_count = block_size > 0 ? B * chunks : T;
     int64_t kbytes, cbytes, sbytes = 0;
-    if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (int8 ? 1 : 2), &cbytes) ||
-        (int8 && !mul_ok(rows, 4, &sbytes)))
+    if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (quant ? 1 : 2), &cbytes) ||
+        (quant && !mul_ok(rows, 4, &sbytes)))
         return KVRC_ERR_SHAPE;
     const Range in[] = {span(kv, T * D * 2), span(gamma, Dv * 2), span(cos, T * Dk * 2),
                         span(sin, T * Dk * 2), span(index, index_count * 8)};
@@ -110,7 +111,7 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     a.block_size = block_size;
     a.limit = limit;
     a.cache_rows = rows;
-    a.int8 = int8;
+    a.ckv = ckv_dtype;
     a.eps = eps;
     a.err = err_count;
     (void)hipGetLastError();                  // start from a clean error state
@@ -135,7 +136,7 @@ const char *kvrc_status_string(int32_t status)
     }
 }
 
-int32_t kvrc_version(void) { return 100; }
+int32_t kvrc_version(void) { return 101; }
 
 int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                    const void *sin, const int64_t *slot_mapping, void *k_cache,

@@ -8,6 +8,9 @@
 
 namespace kvrc {
 
+// Element type of the ckv cache rows (the values of kvrc_cache_dtype).
+enum CkvKind : int { kCkvBf16 = 0, kCkvInt8 = 1, kCkvFp8 = 2 };
+
 // One fused norm-rope-cache launch. Token t = b*S + s in [0, T) reads its index
 // value v from index[t], or from index[b*chunks_per_seq + s/block_size] in
 // block-indexed mode, and writes cache row
@@ -22,15 +25,15 @@ struct NormRopeCacheArgs {
     const uint16_t *sin;      // [T, Dk] bf16
     const int64_t *index;     // [T]
     uint16_t *k_cache;        // [rows, Dk] bf16
-    void *ckv_cache;          // [rows, Dv] bf16 or int8
-    float *ckv_scale;         // [rows] (int8 only)
+    void *ckv_cache;          // [rows, Dv] bf16, int8 or E4M3FN codes
+    float *ckv_scale;         // [rows] (int8 and E4M3FN only)
     int64_t T, S, Dv, Dk;
     int64_t rows_per_batch;   // > 0: Norm mode
     int64_t chunks_per_seq;   // > 0: block-indexed mode (ceil(S / block_size))
     int64_t block_size;       // block-indexed mode only
     int64_t limit;            // exclusive bound of a valid index value
     int64_t cache_rows;       // rows of each cache (paged: limit; Norm: Bc * Sc)
-    bool int8;
+    int ckv;                  // CkvKind
     float eps;
     int32_t *err;             // nullable
 };

@@ -2,10 +2,13 @@
 //
 // Computes, per token (aclnnKvRmsNormRopeCache, Description and Formulas (1)
 // interleaveRope, (2) rmsNorm; int8 rows use the RowMax(abs)/127 + round rule
-// of aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula):
+// of aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula, and FLOAT8
+// E4M3FN rows, a ckv cache type of quantisation scenario 1, the same rule
+// with 448, the largest E4M3FN value, in place of 127):
 //   y  = (x / sqrt(sum(x*x)/Dv + eps)) * gamma          on kv[t, 0:Dv]
 //   kr = cat(x1, x2) * cos + cat(-x2, x1) * sin          on kv[t, Dv:Dv+Dk]
-//   ckv_cache[row] = bf16(y)  or  int8 rint(y / (max|y| / 127)) + scale
+//   ckv_cache[row] = bf16(y), or int8 rint(y / (max|y| / 127)) + scale,
+//                    or E4M3FN(y / (max|y| / 448)) + scale
 //   k_cache[row]   = bf16(kr)
 //
 // Design (HBM-bound; nothing here is a dense contraction, so no MFMA):
@@ -21,8 +24,8 @@
 //     consecutive outputs: one contiguous store per lane;
 //   * sqrt is correctly rounded and x/rms, amax/127, y/scale are correctly
 //     rounded divisions (IEEE, or the shared-divisor form of
-//     device_common.hpp on its domain), so the outputs and the int8 codes are
-//     bit-identical to the float32 definition.
+//     device_common.hpp on its domain), so the outputs and the int8 and
+//     E4M3FN codes are bit-identical to the float32 definition.
 //
 // The specialised kernel handles Dv = 512, Dk = 64 (the DeepSeek-V3 latent
 // key row); every other multiple-of-8 shape takes the generic kernel (one
@@ -134,7 +137,7 @@ class CacheWriter {
 // ---------------------------------------------------------------------------
 // Dv = 512, Dk = 64: TPW token rows per wavefront.
 // ---------------------------------------------------------------------------
-template <int TPW, bool INT8, bool BUF, int NT>
+template <int TPW, int CKV, bool BUF, int NT>
 __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
 {
     constexpr int DV = 512, DK = 64, D = DV + DK;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
         }
     }
 
-    if constexpr (INT8) {
+    if constexpr (CKV == kCkvInt8) {
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
@@ -298,6 +301,46 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
                 dst.store(row * DV + 8 * (l + LPT * j), pack_low_bytes8(cb[j]));
+            if (l == 0)
+                a.ckv_scale[row] = scale;
+        }
+    } else if constexpr (CKV == kCkvFp8) {
+        float amax = 0.0f;
+        uint32_t tiny = 0;                // some |y| of this lane below 2^-64
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                amax = fmaxf(amax, fabsf(y[j][e]));
+                tiny |= fabsf(y[j][e]) < kFastDivDividendLo;
+            }
+        amax = fold_max<LPT>(amax);
+        const float scale = amax / kE4m3Max;
+        // q = RN(y / scale), then the nearest E4M3FN code. The shared-divisor
+        // division needs scale in its divisor domain and |y| >= 2^-64 (the
+        // quotient stays within 449 here, so no upper bound on |y| applies);
+        // zeros and tiny values take IEEE division, which also keeps the
+        // sign of a zero quotient.
+        float q[NCH][8];
+        if (fast_div_divisor_ok(scale) && !tiny) {
+            const float rs = 1.0f / scale;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    q[j][e] = div_rn_shared(y[j][e], scale, rs);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    q[j][e] = scale == 0.0f ? 0.0f : y[j][e] / scale;
+        }
+        if (write) {
+            const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV);
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                dst.store(row * DV + 8 * (l + LPT * j), e4m3_pack8(q[j]));
             if (l == 0)
                 a.ckv_scale[row] = scale;
         }
@@ -352,7 +395,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
     const float ms = ss / (float)Dv;
     const float rms = sqrtf(ms + a.eps);
 
-    if (a.int8) {
+    if (a.ckv != kCkvBf16) {
+        const bool fp8 = a.ckv == kCkvFp8;
         float amax = 0.0f;
         for (int64_t c = lane; c < nch; c += 64) {
             float x[8], g[8];
@@ -364,8 +408,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
             }
         }
         amax = fold_max<64>(amax);
-        const float scale = amax / 127.0f;
-        int8_t *dst = static_cast<int8_t *>(a.ckv_cache) + row * Dv;
+        const float scale = amax / (fp8 ? kE4m3Max : 127.0f);
+        uint8_t *dst = static_cast<uint8_t *>(a.ckv_cache) + row * Dv;
         for (int64_t c = lane; c < nch; c += 64) {
             float x[8], g[8], code[8];
             unpack8(*reinterpret_cast<const uint4 *>(xr + 8 * c), x);
@@ -373,9 +417,11 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
             for (int e = 0; e < 8; ++e) {
                 const float q = x[e] / rms;
                 const float yv = q * g[e];
-                code[e] = scale == 0.0f ? 0.0f : rintf(yv / scale);
+                const float qs = scale == 0.0f ? 0.0f : yv / scale;
+                code[e] = fp8 ? qs : rintf(qs);
             }
-            *reinterpret_cast<uint2 *>(dst + 8 * c) = pack_codes8(code);
+            *reinterpret_cast<uint2 *>(dst + 8 * c) =
+                fp8 ? to_uint2(e4m3_pack8(code)) : pack_codes8(code);
         }
         if (lane == 0)
             a.ckv_scale[row] = scale;
@@ -405,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
     }
 }
 
-template <int TPW, bool INT8, int NT>
+template <int TPW, int CKV, int NT>
 hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
 {
     const int64_t tokens_per_wg = (int64_t)(NT / 64) * TPW;
@@ -413,13 +459,13 @@ hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
     // Buffer descriptors hold 32-bit sizes and offsets: each cache must be
     // smaller than 4 GiB for the sc1 buffer stores.
     const int64_t rows = a.cache_rows;
-    const bool buf = rows * 512 * (INT8 ? 1 : 2) <= (int64_t)UINT32_MAX &&
+    const bool buf = rows * 512 * (CKV == kCkvBf16 ? 2 : 1) <= (int64_t)UINT32_MAX &&
                      rows * 64 * 2 <= (int64_t)UINT32_MAX;
     if (buf)
-        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8, true, NT>), dim3((uint32_t)grid),
+        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, CKV, true, NT>), dim3((uint32_t)grid),
                            dim3(NT), 0, stream, a);
     else
-        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, INT8, false, NT>), dim3((uint32_t)grid),
+        hipLaunchKernelGGL((norm_rope_cache_d576<TPW, CKV, false, NT>), dim3((uint32_t)grid),
                            dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
@@ -435,6 +481,9 @@ hipError_t launch_d576(const NormRopeCacheArgs &a, hipStream_t stream)
 #ifndef KVRC_TPW_INT8
 #define KVRC_TPW_INT8 2
 #endif
+#ifndef KVRC_TPW_FP8
+#define KVRC_TPW_FP8 2
+#endif
 
 // Up to this many tokens (a decode step) the chip is far from full: one row
 // per wavefront in one-wavefront workgroups spreads the rows over the most
@@ -445,11 +494,18 @@ constexpr int64_t kSmallBatchTokens = 2048;
 hipError_t launch_norm_rope_cache(const NormRopeCacheArgs &a, hipStream_t stream)
 {
     if (a.Dv == 512 && a.Dk == 64) {
-        if (a.T <= kSmallBatchTokens)
-            return a.int8 ? launch_d576<1, true, 64>(a, stream)
-                          : launch_d576<1, false, 64>(a, stream);
-        return a.int8 ? launch_d576<KVRC_TPW_INT8, true, kThreads>(a, stream)
-                      : launch_d576<KVRC_TPW_BF16, false, kThreads>(a, stream);
+        if (a.T <= kSmallBatchTokens) {
+            switch (a.ckv) {
+            case kCkvInt8: return launch_d576<1, kCkvInt8, 64>(a, stream);
+            case kCkvFp8: return launch_d576<1, kCkvFp8, 64>(a, stream);
+            default: return launch_d576<1, kCkvBf16, 64>(a, stream);
+            }
+        }
+        switch (a.ckv) {
+        case kCkvInt8: return launch_d576<KVRC_TPW_INT8, kCkvInt8, kThreads>(a, stream);
+        case kCkvFp8: return launch_d576<KVRC_TPW_FP8, kCkvFp8, kThreads>(a, stream);
+        default: return launch_d576<KVRC_TPW_BF16, kCkvBf16, kThreads>(a, stream);
+        }
     }
     const int64_t grid = (a.T + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(norm_rope_cache_generic, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);

@@ -24,6 +24,17 @@ __global__ __launch_bounds__(256) void arith_kernel(const float *__restrict__ a,
     }
 }
 
+// Four quotients per thread, converted exactly as the kernels convert them.
+__global__ __launch_bounds__(256) void e4m3_kernel(const float4 *__restrict__ x,
+                                                   uint32_t *__restrict__ code, int64_t n4)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 v = x[i];
+        code[i] = kvrc::e4m3_pack4(v.x, v.y, v.z, v.w);
+    }
+}
+
 bool overlaps(const void *p, const void *q, int64_t bytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
@@ -57,5 +68,27 @@ extern "C" int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_
     (void)hipGetLastError();
     hipLaunchKernelGGL(arith_kernel, dim3(grid), dim3(256), 0, stream, a, b, q_shared, q_ieee,
                        root, n);
+    return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
+}
+
+extern "C" int32_t kvrc_selftest_e4m3(const float *x, uint8_t *code, int64_t n, hipStream_t stream)
+{
+    if (n < 0 || n % 4)
+        return KVRC_ERR_SHAPE;
+    if (n == 0)
+        return KVRC_OK;
+    if (!x || !code)
+        return KVRC_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(code) % 4)
+        return KVRC_ERR_ALIGN;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ca = reinterpret_cast<uintptr_t>(code);
+    if (ca < xa + (uintptr_t)(n * 4) && xa < ca + (uintptr_t)n)
+        return KVRC_ERR_ALIAS;
+    const int64_t n4 = n / 4;
+    const int64_t blocks = (n4 + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(e4m3_kernel, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(x), reinterpret_cast<uint32_t *>(code), n4);
     return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
 }

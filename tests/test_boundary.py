@@ -39,7 +39,7 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 100
+    assert k.lib().kvrc_version() == 101
 
 
 def test_status_strings():
@@ -82,7 +82,11 @@ def norm(**over):
     (dict(Dv=510), SHAPE), (dict(Dk=4), SHAPE), (dict(Dk=60), SHAPE), (dict(Dv=0), SHAPE),
     (dict(B=-1), SHAPE), (dict(S=-2), SHAPE), (dict(NB=-1), SHAPE), (dict(BS=0), SHAPE),
     (dict(B=1 << 20, S=1 << 20), SHAPE),
-    (dict(dt=2), DTYPE), (dict(dt=1), DTYPE), (dict(scale=A["scale"]), DTYPE),
+    (dict(dt=3), DTYPE), (dict(dt=-1), DTYPE), (dict(dt=1), DTYPE), (dict(dt=2), DTYPE),
+    (dict(scale=A["scale"]), DTYPE), (dict(dt=3, scale=A["scale"]), DTYPE),
+    (dict(dt=2, scale=A["scale"] + 2), ALIGN),
+    # an E4M3FN cache holds one byte per element: 64 rows * 512 B
+    (dict(dt=2, scale=A["ckv"] + 64 * 512 - 16), ALIAS),
     (dict(kv=A["kv"] + 8), ALIGN), (dict(cos=A["cos"] + 2), ALIGN), (dict(idx=A["idx"] + 4), ALIGN),
     (dict(kc=A["kc"] + 8), ALIGN), (dict(dt=1, scale=A["scale"] + 2), ALIGN),
     (dict(err=A["err"] + 2), ALIGN),
@@ -154,6 +158,16 @@ def qsa(**over):
 ])
 def test_qsa_validation(over, want):
     assert qsa(**over) == want
+
+
+@pytest.mark.parametrize("x,code,n,want", [
+    (A["kv"], A["ckv"], 3, SHAPE), (A["kv"], A["ckv"], -4, SHAPE), (None, A["ckv"], 4, NULL),
+    (A["kv"], None, 4, NULL), (A["kv"] + 4, A["ckv"], 4, ALIGN), (A["kv"], A["ckv"] + 2, 4, ALIGN),
+    (A["kv"], A["kv"] + 12, 4, ALIAS), (A["kv"] + 16, A["kv"], 64, ALIAS),
+    (A["kv"], A["ckv"], 0, OK), (None, None, 0, OK),
+])
+def test_selftest_e4m3_validation(x, code, n, want):
+    assert k.lib().kvrc_selftest_e4m3(x, code, n, None) == want
 
 
 def test_binding_refuses_cpu_tensors():

@@ -8,12 +8,16 @@ correctly rounded quotient on its domain 2^-60 <= b <= 2^60,
 (b) against the device's IEEE division: exhaustively over every bf16
 numerator in the domain (the kv values the norm divides) for 2^15 divisors,
 and on 2^30 random float32 numerators (the quantisation divides float32 y).
+(c) The float32 -> E4M3FN conversion of the fp8 rows equals the oracle's
+encoder on every code value, every midpoint and its float32 neighbours, the
+saturation range and random float32 values.
 """
 import numpy as np
 import pytest
 import torch
 
 import latent_attention_kv_amd as k
+import oracle
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -116,3 +120,55 @@ def test_device_ieee_division_and_sqrt_match_host():
     np.testing.assert_array_equal(qi.cpu().numpy().view(np.int32), want_q.view(np.int32))
     _, _, rt = run(torch.from_numpy(np.abs(a)).to(DEV), torch.from_numpy(b).to(DEV))
     np.testing.assert_array_equal(rt.cpu().numpy().view(np.int32), want_r.view(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# float32 -> FLOAT8 E4M3FN conversion of the kernels against the oracle's
+# encoder (nearest value by search over the decoded code table, ties to the
+# even code, saturating at 448; itself pinned to the format's definition).
+# ---------------------------------------------------------------------------
+
+def e4m3_codes_gpu(x):
+    xs = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+    code = torch.empty(xs.numel(), dtype=torch.uint8, device=DEV)
+    k.kvrc_selftest_e4m3(xs, code)
+    torch.cuda.synchronize()
+    return code.cpu().numpy()
+
+
+def check_e4m3(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    pad = (-x.size) % 4
+    x = np.concatenate([x, np.zeros(pad, np.float32)])
+    got, want = e4m3_codes_gpu(x), oracle.e4m3_encode_array(x)
+    bad = np.flatnonzero(got != want)
+    if bad.size:
+        i = bad[0]
+        pytest.fail(f"{bad.size} mismatches, e.g. x={x[i]!r} ({x.view(np.uint32)[i]:#010x}) "
+                    f"gpu={got[i]:#04x} oracle={want[i]:#04x}")
+
+
+def test_e4m3_values_midpoints_and_neighbours():
+    t = np.array([oracle.e4m3_decode(c) for c in range(127)], dtype=np.float32)
+    mids = ((t[:-1].astype(np.float64) + t[1:]) / 2).astype(np.float32)
+    pts = [t, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+           np.nextafter(t, np.float32(0)), np.nextafter(t, np.float32(1e9))]
+    big = np.array([448.0, 448.00003, 460.0, 463.99997, 464.0, 465.0, 480.0, 1e6, 3.4e38],
+                   np.float32)
+    tiny = np.array([0.0, 2.0 ** -10, np.nextafter(np.float32(2.0 ** -10), np.float32(1)),
+                     np.nextafter(np.float32(2.0 ** -10), np.float32(0)), 2.0 ** -11, 1e-20,
+                     1e-38, 1e-45, 2.0 ** -126], np.float32)
+    x = np.concatenate(pts + [big, tiny])
+    check_e4m3(np.concatenate([x, -x]))
+
+
+def test_e4m3_random_float32():
+    rng = np.random.Generator(np.random.PCG64(8))
+    n = 1 << 24
+    # every exponent from float32 denormals to beyond the E4M3FN range
+    x = (rng.uniform(1, 2, n) * np.exp2(rng.integers(-150, 12, n))).astype(np.float32)
+    x[rng.random(n) < 0.5] *= -1
+    check_e4m3(x)
+    bits = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    check_e4m3(y[np.isfinite(y)])

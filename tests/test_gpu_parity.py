@@ -116,8 +116,8 @@ def compare_kvrc(case, got, want, *, exact_bf16=False):
             max_ulp = max(max_ulp, m)
             off += int((d > 0).sum().item())
             del d, wd
-        elif g.dtype == torch.int8:
-            assert torch.equal(g, dt(w)), f"{name}: int8 codes differ"
+        elif g.dtype in (torch.int8, torch.uint8):
+            assert torch.equal(g, dt(w)), f"{name}: int8 / E4M3FN codes differ"
         else:
             wd = dt(w)
             assert torch.equal(torch.isnan(g), torch.isnan(wd))
@@ -126,7 +126,8 @@ def compare_kvrc(case, got, want, *, exact_bf16=False):
     return max_ulp, off
 
 
-NAMED_KVRC = ["norm_tiny", "decode_paged", "prefill_paged", "quant_paged"]
+NAMED_KVRC = ["norm_tiny", "decode_paged", "prefill_paged", "quant_paged", "quant_fp8_paged"]
+CKV = ["bf16", "int8", "fp8"]
 
 
 @pytest.mark.parametrize("name", NAMED_KVRC)
@@ -156,7 +157,7 @@ GENERIC_SHAPES = [(8, 8), (64, 16), (128, 32), (520, 72), (1024, 128), (512, 128
 
 
 @pytest.mark.parametrize("dv,dk", GENERIC_SHAPES)
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 def test_other_shapes_paged(dv, dk, ckv):
     say(f"[parity] paged Dv={dv} Dk={dk} {ckv}")
     case = gen.kvrc_paged_case(100 + dv + dk, B=3, S=37, Dv=dv, Dk=dk, num_blocks=16,
@@ -166,7 +167,7 @@ def test_other_shapes_paged(dv, dk, ckv):
 
 
 @pytest.mark.parametrize("B,S", [(1, 1), (1, 5), (3, 7), (2, 333), (7, 129)])
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 def test_ragged_token_counts_d576(B, S, ckv):
     say(f"[parity] d576 ragged B={B} S={S} {ckv}")
     case = gen.kvrc_paged_case(200 + B * S, B=B, S=S, Dv=512, Dk=64, num_blocks=64,
@@ -174,7 +175,7 @@ def test_ragged_token_counts_d576(B, S, ckv):
     compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 @pytest.mark.parametrize("dv,dk", [(512, 64), (64, 16)])
 def test_norm_mode(ckv, dv, dk):
     say(f"[parity] norm mode Dv={dv} Dk={dk} {ckv}")
@@ -184,7 +185,7 @@ def test_norm_mode(ckv, dv, dk):
 
 
 @pytest.mark.parametrize("sigma", [1e15, 1e-20, 1e-25, 3e-3])
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 def test_extreme_magnitudes(sigma, ckv):
     """Large rows, rows whose squares are float32 denormals, small rows."""
     say(f"[parity] sigma={sigma} {ckv}")
@@ -193,7 +194,7 @@ def test_extreme_magnitudes(sigma, ckv):
     compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 def test_zero_rows_and_zero_eps(ckv):
     case = gen.kvrc_paged_case(401, B=2, S=40, Dv=512, Dk=64, num_blocks=8, block_size=16,
                                slot_kind="random", ckv_dtype=ckv)
@@ -407,7 +408,7 @@ def test_graph_replays_match_eager():
                      exact_bf16=True)
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+@pytest.mark.parametrize("ckv", CKV)
 @pytest.mark.parametrize("T", [96, 4096])
 def test_cache_larger_than_4gib(ckv, T):
     """Caches of 4 GiB or more take the plain-global-store path (with both the
@@ -435,9 +436,10 @@ def test_cache_larger_than_4gib(ckv, T):
                                          device=DEV).view(torch.bfloat16)
         scale = None
     else:
-        caches["ckv_cache"] = torch.full((NB, BS, 1, Dv), gen.INT8_SENTINEL, dtype=torch.int8,
-                                         device=DEV)
+        caches["ckv_cache"] = torch.from_numpy(gen.ckv_cache_spec((1,), ckv).numpy()).to(DEV) \
+            .expand(NB, BS, 1, Dv).contiguous()
         scale = torch.full((NB, BS, 1), gen.SCALE_SENTINEL, dtype=torch.float32, device=DEV)
+    ckv_sentinel = gen.ckv_cache_spec((1,), ckv).fill
     k.kvrc_paged_norm_rope_cache(dbf(small["kv"]), dbf(small["gamma"]), dbf(small["cos"]),
                                  dbf(small["sin"]), dt(slots), caches["k_cache"],
                                  caches["ckv_cache"], scale, eps=small["eps"])
@@ -453,8 +455,8 @@ def test_cache_larger_than_4gib(ckv, T):
             in_rows = int((g[idx].view(torch.int16) != sentinel).sum().item())
         else:
             assert torch.equal(g[idx], dt(w)), name
-            changed = int((g != gen.INT8_SENTINEL).sum().item())
-            in_rows = int((g[idx] != gen.INT8_SENTINEL).sum().item())
+            changed = int((g != ckv_sentinel).sum().item())
+            in_rows = int((g[idx] != ckv_sentinel).sum().item())
         assert changed == in_rows, f"{name}: bytes outside the written rows changed"
     if scale is not None:
         sv = scale.view(-1)
@@ -496,7 +498,45 @@ def test_int8_exact_ties():
 
 
 
-@pytest.mark.parametrize("ckv", ["bf16", "int8"])
+def test_fp8_exact_ties():
+    """Rows whose quotients y/scale are exact midpoints between neighbouring
+    E4M3FN values: eps makes mean(x^2) + eps = 64^2 (rms = 64 exactly),
+    gamma = 1 and max|x| = 448, hence y = x/64, scale = 7/448 = 1/64 and
+    y/scale = x; each midpoint must take the even code. (All squares are
+    multiples of 1/4 and the sums stay below 2^21, so every partial sum is
+    exact in float32.)"""
+    rng = gen.rng_for(952)
+    Dv, Dk, T = 512, 64, 64
+    mids = [k + 0.5 for k in range(8, 16)] + list(range(17, 32, 2)) + list(range(34, 64, 4)) + \
+        list(range(68, 128, 8)) + list(range(136, 256, 16))
+    vals = np.array(mids + [-m for m in mids] + list(range(272, 448, 32)), np.float32)
+    base = np.zeros(Dv, np.float32)
+    base[0] = 448.0
+    base[1:1 + len(vals)] = vals
+    ss = float(np.sum(base.astype(np.float64) ** 2))
+    ms = np.float32(ss / Dv)
+    assert ss < 2.0 ** 21 and float(ms) * Dv == ss and ms < 4096
+    eps = float(np.float32(4096.0) - ms)
+    assert np.float32(ms + np.float32(eps)) == 4096.0
+    rows = np.stack([rng.permutation(base) for _ in range(T)])
+    kv = np.concatenate([rows, rng.standard_normal((T, Dk)).astype(np.float32)], axis=1)
+    case = gen.kvrc_paged_case(953, B=1, S=T, Dv=Dv, Dk=Dk, num_blocks=4, block_size=32,
+                               slot_kind="random", ckv_dtype="fp8")
+    case["kv"] = gen.bf16_bits(kv).reshape(1, 1, T, Dv + Dk)
+    assert np.array_equal(gen.bits_to_f32(case["kv"]).reshape(T, -1)[:, :Dv], rows)
+    case["gamma"] = gen.bf16_bits(np.ones(Dv, np.float32))
+    case["eps"] = eps
+    want = oracle.run_kvrc_case(case)
+    got = run_kvrc_gpu(case)
+    compare_kvrc(case, got, want, exact_bf16=True)
+    slots = case["slot_mapping"]
+    codes = got["ckv_cache"].cpu().numpy().reshape(-1, Dv)[slots]
+    np.testing.assert_array_equal(codes, oracle.e4m3_encode_array(rows.reshape(-1)).reshape(T, Dv))
+    assert np.all(codes[rows == 8.5] == 0x50) and np.all(codes[rows == 17.0] == 0x58)
+    assert np.all(got["ckv_scale"].cpu().numpy().reshape(-1)[slots] == np.float32(1 / 64))
+
+
+@pytest.mark.parametrize("ckv", CKV)
 @pytest.mark.parametrize("B,S,BS,offsets", [(8, 4096, 128, False), (3, 300, 64, True),
                                              (2, 37, 16, False), (5, 1, 16, False)])
 def test_paged_blk_mode(ckv, B, S, BS, offsets):
