@@ -164,8 +164,11 @@ void orc_rope_f32(const float *x, const float *cs, const float *sn, int64_t d, f
  * READINGS: the row is the float32 y before any bf16 rounding; round is
  * half-to-even (the pages write their formulas in torch notation, whose
  * round is half-to-even); an all-zero row stores scale 0 and codes 0.
- * |code| <= 127 always holds (y/scale <= 127*(1+2^-23) in magnitude), so no
- * clamp is applied.
+ * While scale is a normal float32, |y/scale| <= 127*(1+2^-23) and the codes
+ * fit int8. When RowMax/127 underflows into the subnormals the rounded scale
+ * can be far below RowMax/127 and the quotient can pass 127: the codes then
+ * saturate at +-127 (the row maximum maps to the largest code, the intent of
+ * the rule).
  */
 void orc_quant_row(const float *y, int64_t n, int8_t *code, float *scale)
 {
@@ -176,8 +179,10 @@ void orc_quant_row(const float *y, int64_t n, int8_t *code, float *scale)
             amax = a;
     }
     float sc = amax / 127.0f;
-    for (int64_t i = 0; i < n; ++i)
-        code[i] = sc == 0.0f ? (int8_t)0 : (int8_t)rintf(y[i] / sc);
+    for (int64_t i = 0; i < n; ++i) {
+        float r = sc == 0.0f ? 0.0f : rintf(y[i] / sc);
+        code[i] = (int8_t)(r > 127.0f ? 127.0f : r < -127.0f ? -127.0f : r);
+    }
     *scale = sc;
 }
 

@@ -139,3 +139,16 @@ def test_fp8_rows_end_to_end(mode):
         assert sc[r] == scale
     untouched = np.setdiff1d(np.arange(ck.shape[0]), list(rows_of.values()))
     assert np.all(ck[untouched] == gen.FP8_SENTINEL) and np.all(sc[untouched] == gen.SCALE_SENTINEL)
+
+
+def test_quant_row_fp8_subnormal_scale():
+    """RowMax/448 = 1.43 * 2^-149 rounds to the subnormal 2^-149: y/scale is
+    640 for the row maximum, which saturates to 448 (0x7e); 300 takes the
+    nearest value 288 (0x79); a row maximum below 224 * 2^-149 gives scale 0
+    and all-zero codes."""
+    u = np.float32(2.0 ** -149)
+    code, scale = oracle.quant_row_fp8(np.array([640, 300, -500, 0, -1], np.float32) * u)
+    assert scale == u
+    np.testing.assert_array_equal(code, np.array([0x7E, 0x79, 0xFE, 0x00, 0xB8], dtype=np.uint8))
+    code, scale = oracle.quant_row_fp8(np.array([200, -3], np.float32) * u)
+    assert scale == 0 and np.all(code == 0)

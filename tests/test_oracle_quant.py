@@ -88,3 +88,13 @@ def test_quant_end_to_end_exact_ties():
     oracle.paged_norm_rope_cache(kvb, gamma, cs, cs, slots, kc, ck, sc, eps=eps)
     np.testing.assert_array_equal(ck.reshape(T, Dv), np.rint(rows).astype(np.int8))
     assert np.all(sc == np.float32(1 / 64))
+
+
+def test_quant_subnormal_scale_saturates():
+    """RowMax/127 = 1.40 * 2^-149 rounds to the subnormal 2^-149, so y/scale
+    reaches 178 for the row maximum: codes saturate at +-127 (the row maximum
+    maps to the largest code); elements below 127 * scale keep rint(y/scale)."""
+    u = np.float32(2.0 ** -149)
+    code, scale = oracle.quant_row(np.array([178, 100, -150, 0, 3], np.float32) * u)
+    assert scale == u
+    np.testing.assert_array_equal(code, np.array([127, 100, -127, 0, 3], dtype=np.int8))
