@@ -85,7 +85,8 @@ int32_t kvrc_version(void);
  *        E4M3FN codes of y / scale (nearest, ties to the even code, +-448
  *        beyond) with scale = max|y| / 448 stored likewise   (FP8_E4M3);
  *        y / scale is the correctly rounded float32 quotient, and an
- *        all-zero row stores scale 0 and codes 0
+ *        all-zero row stores scale 0 and codes 0; when scale is a float32
+ *        subnormal the quotient can pass 127 (448): codes saturate there
  *   k_cache[v / block_size, v % block_size, 0, :] = bf16(kr)
  * The sum of squares uses a fixed order: 64 partial sums, partial l adding
  * the squares of the 8-element chunks c = l, l+64, ... in order, folded in

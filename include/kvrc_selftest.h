@@ -37,7 +37,10 @@ int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_shared, flo
  * For i in [0, n): code[i] = the FLOAT8 E4M3FN code the kernels store for the
  * float32 quotient x[i] (nearest E4M3FN value, ties to the even code,
  * magnitudes beyond 448 saturating to +-448; the sign bit of the code is the
- * sign of x[i], also for a zero result). x is float32 device memory (16-byte
+ * sign of x[i], also for a zero result). Magnitudes below 464 take the
+ * hardware conversion directly, as in the kernels' common path; larger ones
+ * are clamped to +-448 first, as the kernels do where a quotient can get
+ * there. x is float32 device memory (16-byte
  * aligned), code uint8 device memory (4-byte aligned, not overlapping x);
  * n must be a multiple of 4. Returns KVRC_OK, KVRC_ERR_NULL, KVRC_ERR_SHAPE,
  * KVRC_ERR_ALIGN, KVRC_ERR_ALIAS or KVRC_ERR_HIP. Asynchronous on `stream`.

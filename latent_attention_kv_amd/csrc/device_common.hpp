@@ -176,22 +176,35 @@ __device__ __forceinline__ u32x2 pack_low_bytes8(const uint32_t (&w)[8])
 
 // Four float32 values -> four FLOAT8 E4M3FN codes (OCP format: 4 exponent
 // bits with bias 7, 3 mantissa bits, largest finite value 448, no
-// infinities), bytes 0..3 of the result in argument order. Each value is
-// rounded to the nearest E4M3FN value, ties to the even code; magnitudes
-// beyond 448 saturate to +-448. v_med3_f32 does the saturation (it keeps the
-// sign of zero) and v_cvt_pk_fp8_f32, which on gfx950 converts to the OCP
-// E4M3FN format with round to nearest even, the rounding.
+// infinities), bytes 0..3 of the result in argument order: each value is
+// rounded to the nearest E4M3FN value, ties to the even code, with the sign
+// of the input (v_cvt_pk_fp8_f32, which on gfx950 converts to the OCP format
+// with round to nearest even). Valid for |x| < 464: up to there the nearest
+// value under that rounding is at most 448, the largest code (464 is the
+// midpoint between 448 and 480, where the format has no finite value).
+// Callers clamp (e4m3_clamp) wherever a value can reach 464.
 constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float e4m3_clamp(float x)
+{
+    return __builtin_amdgcn_fmed3f(x, -kE4m3Max, kE4m3Max);    // keeps the sign of zero
+}
 
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
 {
-    a = __builtin_amdgcn_fmed3f(a, -kE4m3Max, kE4m3Max);
-    b = __builtin_amdgcn_fmed3f(b, -kE4m3Max, kE4m3Max);
-    c = __builtin_amdgcn_fmed3f(c, -kE4m3Max, kE4m3Max);
-    d = __builtin_amdgcn_fmed3f(d, -kE4m3Max, kE4m3Max);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
+}
+
+// True when t (a normal float32 with |t| >= 2^-6) lies within [-4, +3]
+// float32 ulps of a midpoint between two neighbouring E4M3FN values. In that
+// range every E4M3FN value has 3 mantissa bits, so the midpoints are the
+// floats whose 20 low mantissa bits are 0x80000; the midpoints sit mid-binade,
+// so t, the midpoint and anything a few ulps from them share one binade.
+__device__ __forceinline__ bool e4m3_near_midpoint(float t)
+{
+    return ((__float_as_uint(t) + 4u) & 0xffff8u) == 0x80000u;
 }
 
 __device__ __forceinline__ u32x2 e4m3_pack8(const float (&q)[8])

@@ -8,7 +8,9 @@
 //   y  = (x / sqrt(sum(x*x)/Dv + eps)) * gamma          on kv[t, 0:Dv]
 //   kr = cat(x1, x2) * cos + cat(-x2, x1) * sin          on kv[t, Dv:Dv+Dk]
 //   ckv_cache[row] = bf16(y), or int8 rint(y / (max|y| / 127)) + scale,
-//                    or E4M3FN(y / (max|y| / 448)) + scale
+//                    or E4M3FN(y / (max|y| / 448)) + scale (codes saturate
+//                    at +-127 / +-448 where a subnormal scale lets the
+//                    quotient pass them)
 //   k_cache[row]   = bf16(kr)
 //
 // Design (HBM-bound; nothing here is a dense contraction, so no MFMA):
@@ -289,12 +291,16 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
                         cb[j][e] = __float_as_uint(w);
                 }
         } else {
+            // scale 0, tiny or huge: IEEE division. A scale rounded to a
+            // float32 subnormal can push |y / scale| past 127: saturate.
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    cb[j][e] = __float_as_uint(
-                        (scale == 0.0f ? 0.0f : y[j][e] / scale) + kRoundMagic);
+                for (int e = 0; e < 8; ++e) {
+                    const float qv = scale == 0.0f ? 0.0f : y[j][e] / scale;
+                    cb[j][e] = __float_as_uint(__builtin_amdgcn_fmed3f(qv, -127.0f, 127.0f) +
+                                               kRoundMagic);
+                }
         }
         if (write) {
             const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV);
@@ -306,35 +312,63 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
         }
     } else if constexpr (CKV == kCkvFp8) {
         float amax = 0.0f;
-        uint32_t tiny = 0;                // some |y| of this lane below 2^-64
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 8; ++e)
                 amax = fmaxf(amax, fabsf(y[j][e]));
-                tiny |= fabsf(y[j][e]) < kFastDivDividendLo;
-            }
         amax = fold_max<LPT>(amax);
         const float scale = amax / kE4m3Max;
-        // q = RN(y / scale), then the nearest E4M3FN code. The shared-divisor
-        // division needs scale in its divisor domain and |y| >= 2^-64 (the
-        // quotient stays within 449 here, so no upper bound on |y| applies);
-        // zeros and tiny values take IEEE division, which also keeps the
-        // sign of a zero quotient.
+        // The code is that of Q = RN(y / scale). In the shared-divisor domain
+        // of scale, t = RN(y * RN(1/scale)) is within |Q| * (2^-23 + 2^-48)
+        // of y / scale, so t and Q lie less than 2.5 ulps apart; the rounding
+        // to E4M3FN is monotonic, so both get the same code unless a midpoint
+        // between two E4M3FN values lies within 2.5 ulps of t. Lanes holding
+        // such an element, or one below 2^-6 (the E4M3FN subnormal range,
+        // whose midpoints have other bit patterns), redo the quotients
+        // exactly. Everywhere here |t| and |Q| stay below 448 * (1 + 2^-22),
+        // inside the conversion's range.
         float q[NCH][8];
-        if (fast_div_divisor_ok(scale) && !tiny) {
+        if (fast_div_divisor_ok(scale)) {
             const float rs = 1.0f / scale;
+            bool redo = false;
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    q[j][e] = div_rn_shared(y[j][e], scale, rs);
+                for (int e = 0; e < 8; ++e) {
+                    const float t = y[j][e] * rs;
+                    q[j][e] = t;
+                    redo |= (fabsf(t) < 0x1p-6f) | e4m3_near_midpoint(t);
+                }
+            if (redo) {
+                bool tiny = false;        // shared-divisor domain: |y| >= 2^-64
+#pragma unroll
+                for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        tiny |= fabsf(y[j][e]) < kFastDivDividendLo;
+                if (!tiny) {
+#pragma unroll
+                    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            q[j][e] = div_rn_shared(y[j][e], scale, rs);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            q[j][e] = y[j][e] / scale;
+                }
+            }
         } else {
+            // scale 0 (an all-zero row: codes 0), tiny or huge: IEEE division;
+            // a scale rounded to a float32 denormal can push |Q| past 448.
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    q[j][e] = scale == 0.0f ? 0.0f : y[j][e] / scale;
+                    q[j][e] = scale == 0.0f ? 0.0f : e4m3_clamp(y[j][e] / scale);
         }
         if (write) {
             const CacheWriter<BUF> dst(a.ckv_cache, a.cache_rows * DV);
@@ -418,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_cache_generic(NormRopeCach
                 const float q = x[e] / rms;
                 const float yv = q * g[e];
                 const float qs = scale == 0.0f ? 0.0f : yv / scale;
-                code[e] = fp8 ? qs : rintf(qs);
+                code[e] = fp8 ? e4m3_clamp(qs) : rintf(__builtin_amdgcn_fmed3f(qs, -127.0f, 127.0f));
             }
             *reinterpret_cast<uint2 *>(dst + 8 * c) =
                 fp8 ? to_uint2(e4m3_pack8(code)) : pack_codes8(code);

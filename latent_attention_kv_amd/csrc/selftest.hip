@@ -24,14 +24,23 @@ __global__ __launch_bounds__(256) void arith_kernel(const float *__restrict__ a,
     }
 }
 
-// Four quotients per thread, converted exactly as the kernels convert them.
+// Four quotients per thread. Magnitudes below 464 go straight to the
+// conversion (as on the kernels' path where the quotient is known to stay
+// below 448 * (1 + 2^-22)); larger ones are clamped first, as the kernels do
+// wherever a quotient can reach 464.
+__device__ __forceinline__ float selftest_e4m3_operand(float x)
+{
+    return fabsf(x) < 464.0f ? x : kvrc::e4m3_clamp(x);
+}
+
 __global__ __launch_bounds__(256) void e4m3_kernel(const float4 *__restrict__ x,
                                                    uint32_t *__restrict__ code, int64_t n4)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         const float4 v = x[i];
-        code[i] = kvrc::e4m3_pack4(v.x, v.y, v.z, v.w);
+        code[i] = kvrc::e4m3_pack4(selftest_e4m3_operand(v.x), selftest_e4m3_operand(v.y),
+                                   selftest_e4m3_operand(v.z), selftest_e4m3_operand(v.w));
     }
 }
 

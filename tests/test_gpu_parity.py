@@ -206,6 +206,28 @@ def test_zero_rows_and_zero_eps(ckv):
     compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
 
 
+@pytest.mark.parametrize("ckv", CKV)
+def test_subnormal_outputs_and_scales(ckv):
+    """x ~ 2^-35 with eps = 1 (rms = 1) and gamma = 2^-107 put y near 2^-142:
+    bf16 outputs are subnormal, and the int8 / E4M3FN scales RowMax/127 and
+    RowMax/448 round to float32 subnormals (or to 0), so quotients pass 127
+    or 448 in some rows and the codes saturate."""
+    say(f"[parity] subnormal scales {ckv}")
+    case = gen.kvrc_paged_case(407, B=4, S=64, Dv=512, Dk=64, num_blocks=16, block_size=32,
+                               slot_kind="random", ckv_dtype=ckv)
+    rng = gen.rng_for(408)
+    x = rng.standard_normal((256, 576)).astype(np.float32) * np.float32(2.0 ** -35)
+    x *= np.exp2(rng.uniform(-3, 3, (256, 1))).astype(np.float32)
+    case["kv"] = gen.bf16_bits(x).reshape(4, 1, 64, 576)
+    case["gamma"] = gen.bf16_bits(np.full(512, 2.0 ** -107, np.float32))
+    case["eps"] = 1.0
+    want = oracle.run_kvrc_case(case)
+    if ckv != "bf16":
+        sc = want["ckv_scale"].reshape(-1)[case["slot_mapping"][case["slot_mapping"] >= 0]]
+        assert np.any((sc > 0) & (sc < np.float32(2.0 ** -126)))
+    compare_kvrc(case, run_kvrc_gpu(case), want, exact_bf16=True)
+
+
 def test_all_skipped_and_empty():
     case = gen.kvrc_paged_case(402, B=2, S=9, Dv=512, Dk=64, num_blocks=4, block_size=16,
                                slot_kind="random")
