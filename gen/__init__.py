@@ -33,7 +33,7 @@ FP8_SENTINEL = 0x7F             # E4M3FN NaN code
 SCALE_SENTINEL = -1.0
 
 CONFIG_NAMES = ("norm_tiny", "decode_paged", "prefill_paged", "quant_paged", "qsa")
-EXTRA_NAMES = ("prefill_paged_blk", "quant_fp8_paged")
+EXTRA_NAMES = ("prefill_paged_blk", "quant_fp8_paged", "mla_kv_head")
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -212,6 +212,55 @@ def kvrc_paged_blk_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6,
 
 
 # ---------------------------------------------------------------------------
+# MLA kv-path head cases
+# ---------------------------------------------------------------------------
+
+def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=0.875,
+                     slot_kind="table", skip_frac=0.0, max_pos=32768, x_sigma=1.0):
+    """Inputs of the MLA kv-path head for T = B*S tokens of hidden size He.
+
+    x [T, He] bf16 ~ N(0, x_sigma); the fused projection weight
+    w [576, He] bf16 ~ N(0, 1/He) (random init, row j produces output
+    column j: rows 0..511 the compressed kv, rows 512..575 the rope key);
+    gamma ~ U(0.5, 1.5); alpha a float32 scalar; cos/sin [T, 64] bf16 and the
+    slot mapping as in kvrc_paged_case (table or random slots); bf16 paged
+    caches [num_blocks, block_size, 1, d].
+    """
+    Dv, Dk = 512, 64
+    g = rng_for(seed)
+    T = B * S
+    x = bf16_bits(g.standard_normal((T, He), dtype=np.float32) * np.float32(x_sigma))
+    w = bf16_bits(g.standard_normal((Dv + Dk, He), dtype=np.float32)
+                  * np.float32(1.0 / np.sqrt(He)))
+    gamma = bf16_bits(g.uniform(0.5, 1.5, size=(Dv,)).astype(np.float32))
+    if slot_kind == "table":
+        per_seq = -(-S // block_size)
+        blocks = g.choice(num_blocks, size=B * per_seq, replace=False).reshape(B, per_seq)
+        s = np.arange(S)
+        slots = (blocks[:, s // block_size] * block_size + (s % block_size)[None, :]).reshape(T)
+        positions = np.broadcast_to(np.arange(S), (B, S))
+    elif slot_kind == "random":
+        slots = g.choice(num_blocks * block_size, size=T, replace=False)
+        positions = g.integers(0, max_pos, size=(B, S))
+    else:
+        raise ValueError(slot_kind)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    n_skip = int(round(skip_frac * T))
+    if n_skip:
+        slots[g.choice(T, size=n_skip, replace=False)] = -1
+    cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
+    caches = {
+        "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
+        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv), np.uint16, BF16_SENTINEL),
+    }
+    return dict(mode="mla_paged", x=x, w=w, gamma=gamma, alpha=float(np.float32(alpha)),
+                cos=np.ascontiguousarray(cos.reshape(T, Dk)),
+                sin=np.ascontiguousarray(sin.reshape(T, Dk)), slot_mapping=slots,
+                caches=caches, B=B, S=S, T=T, He=He, Dv=Dv, Dk=Dk, num_blocks=num_blocks,
+                block_size=block_size, eps=float(eps))
+
+
+# ---------------------------------------------------------------------------
 # QSA block-key cases
 # ---------------------------------------------------------------------------
 
@@ -286,6 +335,10 @@ def make_config(name: str, seed: int | None = None):
         return kvrc_paged_case(7 if seed is None else seed, B=64, S=1024, Dv=512, Dk=64,
                                num_blocks=4096, block_size=128, slot_kind="table",
                                sigma=2.0, ckv_dtype="fp8")
+    if name == "mla_kv_head":
+        # the prefill batch through the MLA kv-path head (DeepSeek-V3 hidden 7168)
+        return mla_kv_head_case(8 if seed is None else seed, B=8, S=4096, He=7168,
+                                num_blocks=8192, block_size=128)
     if name == "prefill_paged_blk":
         # the prefill batch in block-indexed form: one entry per 128-token chunk
         return kvrc_paged_blk_case(6 if seed is None else seed, B=8, S=4096, Dv=512, Dk=64,

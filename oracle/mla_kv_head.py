@@ -1,0 +1,127 @@
+"""CPU oracle of the MLA kv-path head: projection, RmsNorm scaled by alpha_kv,
+RoPE, paged cache scatter.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``): only the tests,
+``__graft_entry__.smoke()`` and the bench's CPU-baseline leg may use it; the
+library never imports it and shares no code with it.
+
+Source: aclnnMlaPrologV3WeightNz (Interface function: the third path, x times
+W^DKV, RmsNorm, times the key scale factor alpha_kv, into the cache; the
+fourth path, x times W^KR, ROPE, into the other cache; Formula: RmsNorm
+formula, c^KV = alpha_kv * RmsNorm(x W^DKV), k^C = Cache(c^KV),
+k^R = Cache(ROPE(x W^KR))), with the interleaved RoPE of
+aclnnKvRmsNormRopeCache (Formula (1) interleaveRope) and its paged cache
+placement (restrictions on index, PA_BNSD: slot -1 skips the token).
+
+Readings (the pages fix none of these):
+  * precision: float64 throughout; the bf16 inputs widen exactly, the
+    products x_k * w_kj of two bf16 values are exact, the projection is one
+    float64 matrix product (a library routine), and each output is rounded to
+    bf16 (nearest, ties to even) once, directly from float64;
+  * the projection output is not rounded before the norm (the head is one
+    fused step, as in the pages' formula);
+  * alpha_kv is a scalar applied to the RmsNorm output, gamma included:
+    y = alpha_kv * (gamma * c / RMS(c)) with RMS(c) = sqrt(mean(c^2) + eps);
+  * the weight is one [576, He] matrix: row j < 512 is column j of W^DKV,
+    row 512 + i is column i of W^KR (the rope key input);
+  * RoPE is the interleaved one, with per-token cos / sin rows [T, 64].
+
+Every function is pinned in ``tests/test_oracle_mla.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DV, DK = 512, 64
+
+
+class MlaOracleError(RuntimeError):
+    pass
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(v) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round to nearest, ties to even, in one
+    step (no float32 intermediate, which could round twice)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.float64)
+    fin = np.isfinite(v)
+    a = np.abs(v)
+    normal = fin & (a >= 2.0 ** -126)
+    # normal range: 8 significant bits
+    m, e = np.frexp(np.where(normal, v, 1.0))          # v = m * 2^e, 0.5 <= |m| < 1
+    out[normal] = np.ldexp(np.rint(m * 256.0), e - 8)[normal]
+    # subnormal range: multiples of 2^-133
+    sub = fin & ~normal
+    out[sub] = np.rint(v[sub] * 2.0 ** 133) * 2.0 ** -133
+    out[~fin] = v[~fin]
+    # largest finite bf16 is (2 - 2^-7) * 2^127; anything rounding above it is inf
+    big = fin & (np.abs(out) >= 2.0 ** 128)
+    out[big] = np.copysign(np.inf, v[big])
+    with np.errstate(over="ignore"):
+        f = out.astype(np.float32)                       # exact: out is a bf16 value
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    bits[np.isnan(v)] = 0x7FC0
+    return bits
+
+
+def kv_project(x, w) -> np.ndarray:
+    """c = x @ W^T in float64: x [T, He], w [576, He] bf16 -> [T, 576]."""
+    return bf16_to_f64(x) @ bf16_to_f64(w).T
+
+
+def kv_head_rows(x, w, gamma, alpha, cos, sin, eps):
+    """Per-token float64 outputs: y [T, 512] = alpha * RmsNorm(c[:, :512]) and
+    kr [T, 64] = RoPE(c[:, 512:]) with the token's cos / sin rows."""
+    c = kv_project(x, w)
+    if c.shape[1] != DV + DK:
+        raise MlaOracleError("the weight must have 576 rows")
+    cv, cr = c[:, :DV], c[:, DV:]
+    ms = np.sum(cv * cv, axis=1) / DV
+    rms = np.sqrt(ms + float(eps))
+    g = bf16_to_f64(gamma)
+    y = float(alpha) * ((cv / rms[:, None]) * g[None, :])
+    x1, x2 = cr[:, 0::2], cr[:, 1::2]
+    cs, sn = bf16_to_f64(cos), bf16_to_f64(sin)
+    kr = np.concatenate([x1, x2], axis=1) * cs + np.concatenate([-x2, x1], axis=1) * sn
+    return y, kr
+
+
+def check_slots(slot_mapping, rows):
+    v = np.asarray(slot_mapping, dtype=np.int64)
+    if np.any((v < -1) | (v >= rows)):
+        raise MlaOracleError("slot out of range")
+    valid = v[v >= 0]
+    if np.unique(valid).size != valid.size:
+        raise MlaOracleError("duplicate slot")
+
+
+def mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slot_mapping, k_cache, ckv_cache, eps):
+    """Writes bf16(y) and bf16(kr) of every token with slot v >= 0 to row v of
+    ckv_cache [NB, BS, 1, 512] and k_cache [NB, BS, 1, 64] (uint16 bits, in
+    place); -1 skips the token; other rows keep their bytes."""
+    kc = k_cache.reshape(-1, DK)
+    ck = ckv_cache.reshape(-1, DV)
+    check_slots(slot_mapping, ck.shape[0])
+    v = np.asarray(slot_mapping, dtype=np.int64)
+    if v.size == 0:
+        return
+    y, kr = kv_head_rows(x, w, gamma, alpha, cos, sin, eps)
+    keep = v >= 0
+    ck[v[keep]] = f64_to_bf16(y[keep])
+    kc[v[keep]] = f64_to_bf16(kr[keep])
+
+
+def run_mla_case(case):
+    """Runs a gen.mla_kv_head_case on fresh sentinel-filled caches."""
+    caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+    mla_kv_head_paged(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                      case["sin"], case["slot_mapping"], caches["k_cache"],
+                      caches["ckv_cache"], case["eps"])
+    return caches

@@ -1,0 +1,152 @@
+"""Pins of the MLA kv-path head oracle (aclnnMlaPrologV3WeightNz, the third
+and fourth paths: c^KV = alpha_kv * RmsNorm(x W^DKV) into the ckv cache,
+k^R = ROPE(x W^KR) into the k cache).
+
+* float64 -> bf16 rounding: hand-worked ties, a double-rounding trap,
+  subnormal ties, overflow (tests/golden/bf16_round_hand.json);
+* the projection: exact rational sums on a small case;
+* identity weights reduce the head to the fused norm-rope-cache of the
+  aclnnKvRmsNormRopeCache page, whose float32 oracle is pinned separately;
+* alpha: a power of two scales every output exactly;
+* the RMS invariant of the normalised rows; RoPE special angles;
+* scatter: -1 skips, untouched rows keep their bytes, bad slots rejected.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from oracle import mla_kv_head as M
+from tests._util import golden
+
+
+def test_f64_to_bf16_hand_worked():
+    for c in golden("bf16_round_hand.json")["cases"]:
+        got = int(M.f64_to_bf16(np.array([float(c["value"])]))[0])
+        assert got == int(c["bits"], 16), c["note"]
+    assert int(M.f64_to_bf16(np.array([np.nan]))[0]) & 0x7FFF > 0x7F80
+    assert int(M.f64_to_bf16(np.array([-0.0]))[0]) == 0x8000
+
+
+def test_f64_to_bf16_matches_nearest_search():
+    """Against a brute-force nearest search over all finite bf16 values of
+    the same binade (ties: even fraction)."""
+    rng = gen.rng_for(80)
+    v = rng.standard_normal(3000) * np.exp2(rng.integers(-130, 120, 3000))
+    allb = np.arange(0x8000, dtype=np.uint16)
+    allv = M.bf16_to_f64(allb)
+    fin = np.isfinite(allv)
+    allb, allv = allb[fin], allv[fin]
+    got = M.f64_to_bf16(v)
+    for x, gb in zip(v, got):
+        d = np.abs(allv - abs(x))
+        best = allb[d == d.min()]
+        b = best[0] if best.size == 1 else best[best % 2 == 0][0]
+        assert int(gb) == (int(b) | (0x8000 if x < 0 else 0)), x
+
+
+def test_projection_exact_small():
+    """c[t, j] = sum_k x[t, k] w[j, k] as exact rationals; the float64
+    product is within its summation bound 64 * 2^-53 * sum |x w|."""
+    rng = gen.rng_for(81)
+    x = gen.bf16_bits(rng.standard_normal((3, 64)).astype(np.float32))
+    w = gen.bf16_bits(rng.standard_normal((576, 64)).astype(np.float32))
+    c = M.kv_project(x, w)
+    xf, wf = M.bf16_to_f64(x), M.bf16_to_f64(w)
+    for t in range(3):
+        for j in (0, 1, 17, 511, 512, 575):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xf[t], wf[j]))
+            bound = 64 * 2.0 ** -53 * float(np.sum(np.abs(xf[t] * wf[j])))
+            assert abs(float(exact) - c[t, j]) <= bound
+
+
+def _identity_case(seed, T, alpha=1.0):
+    """He = 576 with W = I: c equals the token's own 576 inputs."""
+    case = gen.mla_kv_head_case(seed, B=1, S=T, He=576, num_blocks=4, block_size=64,
+                                slot_kind="random", alpha=alpha)
+    case["w"] = gen.bf16_bits(np.eye(576, dtype=np.float32))
+    return case
+
+
+def test_identity_weights_reduce_to_norm_rope_cache():
+    """With W = I the head is the fused norm-rope-cache of the
+    aclnnKvRmsNormRopeCache page on kv = x (alpha 1): the float64 head and
+    the float32 fused oracle agree within one bf16 ulp everywhere and are
+    equal almost everywhere (they differ only where float32 rounding error
+    crosses a bf16 rounding boundary)."""
+    T = 200
+    case = _identity_case(82, T)
+    got = M.run_mla_case(case)
+    kc = np.full((4, 64, 1, 64), gen.BF16_SENTINEL, np.uint16)
+    ck = np.full((4, 64, 1, 512), gen.BF16_SENTINEL, np.uint16)
+    oracle.paged_norm_rope_cache(case["x"].reshape(1, 1, T, 576), case["gamma"],
+                                 case["cos"].reshape(1, 1, T, 64), case["sin"].reshape(1, 1, T, 64),
+                                 case["slot_mapping"], kc, ck, eps=case["eps"])
+    from tests._util import bf16_ulp_diff
+    for a, b in ((got["ckv_cache"], ck), (got["k_cache"], kc)):
+        d = bf16_ulp_diff(a.reshape(-1), b.reshape(-1))
+        assert d.max() <= 1 and np.mean(d == 0) > 0.99
+    # RoPE of exact inputs with per-element exact products: bit-equal
+    np.testing.assert_array_equal(got["k_cache"], kc)
+
+
+def test_alpha_power_of_two_is_exact():
+    T = 64
+    a1 = M.run_mla_case(_identity_case(83, T, alpha=1.0))
+    a2 = M.run_mla_case(_identity_case(83, T, alpha=2.0))
+    y1 = M.bf16_to_f64(a1["ckv_cache"])
+    y2 = M.bf16_to_f64(a2["ckv_cache"])
+    written = y1 != 7.0
+    np.testing.assert_array_equal(y2[written], 2 * y1[written])
+    np.testing.assert_array_equal(a1["k_cache"], a2["k_cache"])
+
+
+def test_rms_invariant_and_rope_angles():
+    rng = gen.rng_for(84)
+    case = gen.mla_kv_head_case(85, B=2, S=8, He=256, num_blocks=4, block_size=16,
+                                alpha=0.75)
+    y, kr = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                           case["sin"], case["eps"])
+    c = M.kv_project(case["x"], case["w"])
+    ms = np.mean(c[:, :512] ** 2, axis=1)
+    g = M.bf16_to_f64(case["gamma"])
+    lhs = np.sqrt(np.mean((y / (0.75 * g)) ** 2, axis=1))
+    np.testing.assert_allclose(lhs, np.sqrt(ms / (ms + case["eps"])), rtol=1e-12)
+    # zero angle: kr is the de-interleaved rope input; quarter turn: (-x2, x1)
+    one = np.full((16, 64), 0x3F80, np.uint16)
+    zero = np.zeros((16, 64), np.uint16)
+    _, k0 = M.kv_head_rows(case["x"], case["w"], case["gamma"], 1.0, one, zero, case["eps"])
+    _, k1 = M.kv_head_rows(case["x"], case["w"], case["gamma"], 1.0, zero, one, case["eps"])
+    r = c[:, 512:]
+    np.testing.assert_array_equal(k0, np.concatenate([r[:, 0::2], r[:, 1::2]], axis=1))
+    np.testing.assert_array_equal(k1, np.concatenate([-r[:, 1::2], r[:, 0::2]], axis=1))
+    # pair norms are preserved by any angle
+    p_in = r[:, 0::2] ** 2 + r[:, 1::2] ** 2
+    p_out = kr[:, :32] ** 2 + kr[:, 32:] ** 2
+    np.testing.assert_allclose(p_out, p_in, rtol=1e-2)          # bf16 cos/sin: |c^2+s^2-1| < 1e-2
+
+
+def test_scatter_skips_and_untouched_rows():
+    case = gen.mla_kv_head_case(86, B=2, S=30, He=128, num_blocks=8, block_size=16,
+                                slot_kind="random", skip_frac=0.2)
+    got = M.run_mla_case(case)
+    v = case["slot_mapping"]
+    y, kr = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                           case["sin"], case["eps"])
+    ck, kc = got["ckv_cache"].reshape(-1, 512), got["k_cache"].reshape(-1, 64)
+    for t, s in enumerate(v):
+        if s >= 0:
+            np.testing.assert_array_equal(ck[s], M.f64_to_bf16(y[t]))
+            np.testing.assert_array_equal(kc[s], M.f64_to_bf16(kr[t]))
+    untouched = np.setdiff1d(np.arange(ck.shape[0]), v[v >= 0])
+    assert np.all(ck[untouched] == gen.BF16_SENTINEL) and np.all(kc[untouched] == gen.BF16_SENTINEL)
+    bad = dict(case, slot_mapping=v.copy())
+    bad["slot_mapping"][3] = bad["slot_mapping"][5] = 7
+    with pytest.raises(M.MlaOracleError, match="duplicate"):
+        M.run_mla_case(bad)
+    bad["slot_mapping"] = v.copy()
+    bad["slot_mapping"][0] = 8 * 16
+    with pytest.raises(M.MlaOracleError, match="range"):
+        M.run_mla_case(bad)
