@@ -50,8 +50,9 @@ _COMMON_SOURCES = ["latent_attention_kv_amd/csrc/device_common.hpp",
 KERNEL_SOURCES = {
     "kvrc": ["latent_attention_kv_amd/csrc/norm_rope_cache.hip"] + _COMMON_SOURCES,
     "qsa": ["latent_attention_kv_amd/csrc/qsa_prepare.hip"] + _COMMON_SOURCES,
+    "mla": ["latent_attention_kv_amd/csrc/mla_kv_head.hip"] + _COMMON_SOURCES,
 }
-KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel"}
+KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel", "mla": "mla_kv_head_kernel"}
 
 WORKLOAD_TEXT = {
     "prefill_paged": "paged prefill: B=8, S=4096 (32768 tokens), kv [8,1,4096,576] bf16 "
@@ -69,11 +70,15 @@ WORKLOAD_TEXT = {
                          "tokens), D=576 bf16, one index entry per 128-token chunk, caches "
                          "[8192,128,1,512] + [8192,128,1,64] bf16",
     "qsa": "QSAPrepare block keys: N=32, L=2048, Di=128, Dr=64, key_block_size=64",
+    "mla_kv_head": "MLA kv-path head: T=32768 tokens (B=8, S=4096), x [32768,7168] bf16 times "
+                   "the fused projection [576,7168] bf16 (random init) on the matrix cores, "
+                   "alpha_kv 0.875, RMSNorm + RoPE, PA_BNSD caches [8192,128,1,512/64] bf16",
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def kernel_family(workload: str) -> str:
-    return "qsa" if workload == "qsa" else "kvrc"
+    return {"qsa": "qsa", "mla_kv_head": "mla"}.get(workload, "kvrc")
 
 
 def source_hash(workload: str) -> str:
@@ -86,9 +91,19 @@ def source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
+def algorithmic_flops(case) -> int:
+    """Multiply-add work of the projection: 2 * T * 576 * He (MLA head only)."""
+    return 2 * case["T"] * 576 * case["He"] if case.get("mode") == "mla_paged" else 0
+
+
 def algorithmic_bytes(case) -> tuple[int, int]:
     """(bytes per launch, tokens per launch) the method must move."""
     import gen
+    if case.get("mode") == "mla_paged":
+        T, He = case["T"], case["He"]
+        written = int((case["slot_mapping"] >= 0).sum())
+        return (T * He * 2 + 576 * He * 2 + T * (2 * 2 * 64 + 8) + written * (1024 + 128)
+                + 1024, T)
     if "raw_index_keys" in case:
         N, L, Di, Dr, kbs = case["N"], case["L"], case["Di"], case["Dr"], case["kbs"]
         total = 0
@@ -133,6 +148,17 @@ def build_sets(case, R, dev):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     sets = []
+    if case.get("mode") == "mla_paged":
+        base = dict(x=dbf(case["x"]), w=dbf(case["w"]), gamma=dbf(case["gamma"]),
+                    cos=dbf(case["cos"]), sin=dbf(case["sin"]), idx=dt(case["slot_mapping"]))
+        for i in range(R):
+            s = {k: (v.clone() if i else v) for k, v in base.items()}
+            for name, spec in case["caches"].items():
+                fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
+                s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
+                                     device=dev).view(torch.bfloat16)
+            sets.append(s)
+        return sets
     if "raw_index_keys" in case:
         base = dict(raw=dbf(case["raw_index_keys"]), kl=dt(case["key_length"]),
                     rc=dt(case["rope_cos"]), rs=dt(case["rope_sin"]), w=dbf(case["k_norm_weight"]),
@@ -165,7 +191,11 @@ def build_sets(case, R, dev):
 
 def launch(case, s):
     import latent_attention_kv_amd as k
-    if "raw_index_keys" in case:
+    if case.get("mode") == "mla_paged":
+        k.kvrc_mla_kv_head_paged(s["x"], s["w"], s["gamma"], s["cos"], s["sin"], s["idx"],
+                                 s["k_cache"], s["ckv_cache"], alpha_kv=case["alpha"],
+                                 eps=case["eps"])
+    elif "raw_index_keys" in case:
         k.qsa_prepare(s["raw"], s["bk"], s["kl"], s["rc"], s["rs"], s["w"], s["praw"], s["prope"],
                       s["nraw"], s["nrope"], key_block_size=case["kbs"], eps=case["eps"])
     elif case["mode"] == "paged":
@@ -188,6 +218,24 @@ def cpu_baseline(case, seconds=10.0):
     import oracle
     threads = oracle.max_threads()
     n, busy = 0, 0.0
+    if case.get("mode") == "mla_paged":
+        from oracle import mla_kv_head as M
+        sample = 2048
+        caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+        args = (case["x"][:sample], case["w"], case["gamma"], case["alpha"], case["cos"][:sample],
+                case["sin"][:sample], case["slot_mapping"][:sample], caches["k_cache"],
+                caches["ckv_cache"], case["eps"])
+        while busy < seconds or n == 0:
+            s0 = time.perf_counter()
+            M.mla_kv_head_paged(*args)
+            busy += time.perf_counter() - s0
+            n += 1
+        threads = _blas_threads()
+        return {"value": round(sample * n / busy, 1), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"the first {sample} tokens of the batch run {n} times by the float64 "
+                          f"oracle ({busy:.1f} s; the projection is numpy's float64 matrix "
+                          f"product over {threads} BLAS threads)"}
     if "raw_index_keys" in case:
         while busy < seconds or n == 0:
             s0 = time.perf_counter()
@@ -219,6 +267,18 @@ def cpu_baseline(case, seconds=10.0):
             "sample": f"the full batch ({tokens} tokens) run {n} times by the oracle "
                       f"({busy:.1f} s; input generation and cache allocation excluded), "
                       f"OpenMP over tokens"}
+
+
+def _blas_threads() -> int:
+    """Threads of numpy's BLAS (the float64 oracle's matrix product)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(n[0])
+    except Exception:
+        pass
+    return os.cpu_count() or 1
 
 
 def read_traffic(workload):
@@ -411,6 +471,23 @@ def main(argv=None):
         torch.cuda.synchronize()
 
     achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
+    flops = algorithmic_flops(case)
+    if flops:
+        tflops = flops / (kernel_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": read_traffic(args.workload),
+                    "algorithmic_flops_per_launch": flops,
+                    "algorithmic_bytes_per_launch": bytes_per_launch,
+                    "hbm_gbps_at_algorithmic_bytes": round(achieved, 1),
+                    "kernel_us": round(kernel_us, 3)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": read_traffic(args.workload),
+                    "algorithmic_bytes_per_launch": bytes_per_launch,
+                    "kernel_us": round(kernel_us, 3)}
     line = {
         "metric": METRIC,
         "value": round(tokens / secs, 1),
@@ -422,16 +499,12 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if flops else "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                    "tokens_per_step": tokens, "io_dtype": "bf16",
                    "buffer_sets_rotated": R, "graph": not args.no_graph},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic(args.workload),
-                     "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "kernel_us": round(kernel_us, 3)},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

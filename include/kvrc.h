@@ -1,7 +1,8 @@
 /*
  * kvrc.h - C ABI of the MI355X (gfx950) library for latent-attention KV
  * preprocessing: the fused RMSNorm + interleaved RoPE + cache scatter of the
- * per-token key row, and QSAPrepare block-key compression.
+ * per-token key row, the MLA kv-path head that produces that row from the
+ * hidden state, and QSAPrepare block-key compression.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -165,6 +166,51 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                              void *ckv_cache, float *ckv_scale, int64_t B, int64_t S, int64_t Dv,
                              int64_t Dk, int64_t Bc, int64_t Sc, int32_t ckv_dtype, float eps,
                              int32_t *err_count, hipStream_t stream);
+
+/*
+ * kvrc_mla_kv_head_paged - the kv path of the MLA prologue: projection, then
+ * the normalised key into the ckv cache and the rotated key into the k cache.
+ *
+ * Source: aclnnMlaPrologV3WeightNz (Interface function, third and fourth
+ * paths; Formula: RmsNorm formula, c^KV = alpha_kv * RmsNorm(x W^DKV),
+ * k^C = Cache(c^KV), k^R = Cache(ROPE(x W^KR))); the RoPE is Formula (1)
+ * interleaveRope of aclnnKvRmsNormRopeCache, the placement its PA_BNSD rule.
+ *
+ * For every token t of x[T, He]:
+ *   c  = x[t] . W^T, float32 accumulation of the exact bf16 products (c is
+ *        not rounded before the norm);
+ *   y  = alpha_kv * ((c[0:512] / sqrt(mean(c[0:512]^2) + eps)) * gamma)
+ *   kr = interleaved RoPE of c[512:576] with cos[t], sin[t] (as in
+ *        kvrc_paged_norm_rope_cache)
+ *   v = slot_mapping[t]; v == -1 skips the token;
+ *   ckv_cache[v / block_size, v % block_size, 0, :] = bf16(y)
+ *   k_cache[v / block_size, v % block_size, 0, :]   = bf16(kr)
+ * The projection runs on the matrix cores in an order of its own, so the
+ * outputs are not bit-reproducible against another summation order; they
+ * are deterministic for a given He (independent of T and of the launch).
+ *
+ * Arguments:
+ *   x             bf16 [T, He]
+ *   w_dkv_kr      bf16 [576, He]: row j < 512 is column j of W^DKV, row
+ *                 512 + i is column i of W^KR (the layout of a [out, in]
+ *                 linear layer whose 576 outputs are the two weights side by
+ *                 side)
+ *   gamma         bf16 [512]
+ *   alpha_kv      the key scale factor (a float32 scalar)
+ *   cos, sin      bf16 [T, 64]
+ *   slot_mapping  int64 [T]    -1 or unique in [0, num_blocks*block_size)
+ *   k_cache       bf16 [num_blocks, block_size, 1, 64]
+ *   ckv_cache     bf16 [num_blocks, block_size, 1, 512]
+ *   He            a multiple of 32, >= 32; T <= 2^31 - 1
+ * Returns KVRC_OK (also when T == 0: nothing is launched), or an error
+ * status with nothing written; outputs must not overlap inputs; err_count
+ * counts slots outside [-1, num_blocks*block_size).
+ */
+int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
+                               float alpha_kv, const void *cos, const void *sin,
+                               const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
+                               int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
+                               float eps, int32_t *err_count, hipStream_t stream);
 
 /*
  * qsa_prepare - one index key per complete key block, for sparse attention.

@@ -14,6 +14,10 @@ Entry points (same names as the C ABI in ``include/kvrc.h``):
     of tokens (PA_BLK_BNSD cache mode)
   * kvrc_norm_rope_cache       - the same into contiguous caches
     [Bc, 1, Sc, d] (Norm cache mode)
+  * kvrc_mla_kv_head_paged     - the MLA kv-path head: x [T, He] times the
+    fused [576, He] projection on the matrix cores, then alpha_kv * RMSNorm,
+    RoPE and the paged scatter (aclnnMlaPrologV3WeightNz, third and fourth
+    paths)
   * qsa_prepare                - block keys (openvino.opset17.qsa_prepare)
 """
 from __future__ import annotations
@@ -24,7 +28,7 @@ import os
 import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
-           "kvrc_norm_rope_cache", "qsa_prepare", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
+           "kvrc_norm_rope_cache", "kvrc_mla_kv_head_paged", "qsa_prepare", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
            "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -33,8 +37,9 @@ CACHE_BF16 = 0
 CACHE_INT8 = 1
 CACHE_FP8_E4M3 = 2
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
-                    "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache", "qsa_prepare",
-                    "kvrc_selftest_arith", "kvrc_selftest_e4m3")
+                    "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
+                    "kvrc_mla_kv_head_paged", "qsa_prepare", "kvrc_selftest_arith",
+                    "kvrc_selftest_e4m3")
 
 _lib = None
 
@@ -66,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32,
                                        F, P, P]
     L.kvrc_norm_rope_cache.restype = I32
+    L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, F, P,
+                                         P]
+    L.kvrc_mla_kv_head_paged.restype = I32
     L.qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F,
                               P, P]
     L.qsa_prepare.restype = I32
@@ -222,6 +230,38 @@ def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_sca
                                     _ptr(k_cache), _ptr(ckv_cache), _ptr(ckv_scale), B, S, Dv, Dk,
                                     Bc, Sc, dt, float(eps), _err_ptr(err_count), _stream(stream))
     _check(st, "kvrc_norm_rope_cache")
+
+
+def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, *,
+                           alpha_kv=1.0, eps=1e-6, err_count=None, stream=None):
+    """MLA kv-path head into paged bf16 caches: x [T, He], w_dkv_kr [576, He],
+    gamma [512], cos / sin [T, 64], slot_mapping [T]; k_cache
+    [NB, BS, 1, 64] and ckv_cache [NB, BS, 1, 512] are updated in place."""
+    _need(x, "x", _BF16, 2)
+    _need(w_dkv_kr, "w_dkv_kr", _BF16, 2)
+    _need(gamma, "gamma", _BF16, 1)
+    _need(cos, "cos", _BF16, 2)
+    _need(sin, "sin", _BF16, 2)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", _BF16, 4)
+    T, He = x.shape
+    if tuple(w_dkv_kr.shape) != (576, He):
+        raise ValueError("w_dkv_kr must be [576, He]")
+    if tuple(gamma.shape) != (512,):
+        raise ValueError("gamma must be [512]")
+    if tuple(cos.shape) != (T, 64) or tuple(sin.shape) != (T, 64):
+        raise ValueError("cos / sin must be [T, 64]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have T entries")
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
+        raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
+    st = lib().kvrc_mla_kv_head_paged(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
+                                      _ptr(cos), _ptr(sin), _ptr(slot_mapping), _ptr(k_cache),
+                                      _ptr(ckv_cache), T, He, NB, BS, float(eps),
+                                      _err_ptr(err_count), _stream(stream))
+    _check(st, "kvrc_mla_kv_head_paged")
 
 
 def kvrc_selftest_arith(a, b, q_shared, q_ieee, root, *, stream=None):

@@ -136,7 +136,7 @@ const char *kvrc_status_string(int32_t status)
     }
 }
 
-int32_t kvrc_version(void) { return 101; }
+int32_t kvrc_version(void) { return 102; }
 
 int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                    const void *sin, const int64_t *slot_mapping, void *k_cache,
@@ -183,6 +183,59 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
     return norm_rope_cache_common(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_scale, B,
                                   S, Dv, Dk, rows, Sc > 0 ? Sc : 1, 0, Sc, ckv_dtype, eps,
                                   err_count, stream);
+}
+
+int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
+                               float alpha_kv, const void *cos, const void *sin,
+                               const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
+                               int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
+                               float eps, int32_t *err_count, hipStream_t stream)
+{
+    int64_t rows;
+    if (T < 0 || T > (int64_t)INT32_MAX || He < kvrc::kMlaHeadK || He % kvrc::kMlaHeadK ||
+        num_blocks < 0 || block_size < 1 || !mul_ok(num_blocks, block_size, &rows))
+        return KVRC_ERR_SHAPE;
+    int64_t xbytes, wbytes, kbytes, cbytes;
+    if (!mul_ok(T, He * 2, &xbytes) || !mul_ok(576, He * 2, &wbytes) ||
+        !mul_ok(rows, 64 * 2, &kbytes) || !mul_ok(rows, 512 * 2, &cbytes))
+        return KVRC_ERR_SHAPE;
+    if (T == 0)
+        return KVRC_OK;                       // empty input: caches untouched
+    if (!x || !w_dkv_kr || !gamma || !cos || !sin || !slot_mapping || !k_cache || !ckv_cache)
+        return KVRC_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_dkv_kr, 16) || !aligned(gamma, 16) || !aligned(cos, 16) ||
+        !aligned(sin, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
+        !aligned(ckv_cache, 16) || !aligned(err_count, 4))
+        return KVRC_ERR_ALIGN;
+    const Range in[] = {span(x, xbytes), span(w_dkv_kr, wbytes), span(gamma, 1024),
+                        span(cos, T * 128), span(sin, T * 128), span(slot_mapping, T * 8)};
+    const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes),
+                         span(err_count, err_count ? 4 : 0)};
+    for (const Range &o : out) {
+        for (const Range &i : in)
+            if (overlap(o, i))
+                return KVRC_ERR_ALIAS;
+        for (const Range &o2 : out)
+            if (&o2 != &o && overlap(o, o2))
+                return KVRC_ERR_ALIAS;
+    }
+    kvrc::MlaKvHeadArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint16_t *>(w_dkv_kr);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.cos = static_cast<const uint16_t *>(cos);
+    a.sin = static_cast<const uint16_t *>(sin);
+    a.slot = slot_mapping;
+    a.k_cache = static_cast<uint16_t *>(k_cache);
+    a.ckv_cache = static_cast<uint16_t *>(ckv_cache);
+    a.T = T;
+    a.He = He;
+    a.cache_rows = rows;
+    a.alpha = alpha_kv;
+    a.eps = eps;
+    a.err = err_count;
+    (void)hipGetLastError();
+    return launch_status(kvrc::launch_mla_kv_head(a, stream));
 }
 
 int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t *key_length,

@@ -60,6 +60,26 @@ struct QsaArgs {
 
 hipError_t launch_qsa_prepare(const QsaArgs &a, hipStream_t stream);
 
+// One MLA kv-path head launch (see kvrc_mla_kv_head_paged in kvrc.h).
+struct MlaKvHeadArgs {
+    const uint16_t *x;        // [T, He] bf16
+    const uint16_t *w;        // [576, He] bf16
+    const uint16_t *gamma;    // [512] bf16
+    const uint16_t *cos;      // [T, 64] bf16
+    const uint16_t *sin;      // [T, 64] bf16
+    const int64_t *slot;      // [T]
+    uint16_t *k_cache;        // [cache_rows, 64] bf16
+    uint16_t *ckv_cache;      // [cache_rows, 512] bf16
+    int64_t T, He, cache_rows;
+    float alpha, eps;
+    int32_t *err;             // nullable
+};
+
+hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream);
+
+// K granularity of the MLA head kernel (He must be a multiple of it).
+constexpr int64_t kMlaHeadK = 32;
+
 // Largest Di qsa_prepare accepts (bounded by the per-lane accumulators).
 constexpr int64_t kQsaMaxDi = 4096;
 

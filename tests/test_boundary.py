@@ -39,7 +39,7 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 101
+    assert k.lib().kvrc_version() == 102
 
 
 def test_status_strings():
@@ -127,6 +127,36 @@ def test_paged_blk_validation(over, want):
 ])
 def test_norm_validation(over, want):
     assert norm(**over) == want
+
+
+M = {name: (i + 40) << 32 for i, name in enumerate(
+    ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err"])}
+
+
+def mla(**over):
+    a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
+             slot=M["slot"], kc=M["kc"], ckv=M["ckv"], T=300, He=7168, NB=64, BS=128, eps=1e-6,
+             err=None, stream=None)
+    a.update(over)
+    return k.lib().kvrc_mla_kv_head_paged(a["x"], a["w"], a["gamma"], a["alpha"], a["cos"],
+                                          a["sin"], a["slot"], a["kc"], a["ckv"], a["T"], a["He"],
+                                          a["NB"], a["BS"], a["eps"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(gamma=None), NULL), (dict(cos=None), NULL),
+    (dict(sin=None), NULL), (dict(slot=None), NULL), (dict(kc=None), NULL), (dict(ckv=None), NULL),
+    (dict(He=0), SHAPE), (dict(He=16), SHAPE), (dict(He=7160), SHAPE), (dict(T=-1), SHAPE),
+    (dict(T=1 << 31), SHAPE), (dict(NB=-1), SHAPE), (dict(BS=0), SHAPE),
+    (dict(x=M["x"] + 8), ALIGN), (dict(w=M["w"] + 2), ALIGN), (dict(slot=M["slot"] + 4), ALIGN),
+    (dict(ckv=M["ckv"] + 8), ALIGN), (dict(err=M["err"] + 1), ALIGN),
+    # x holds 300 * 7168 * 2 bytes: a cache starting inside it aliases
+    (dict(kc=M["x"] + 4096), ALIAS), (dict(ckv=M["w"]), ALIAS), (dict(kc=M["ckv"] + 16), ALIAS),
+    (dict(err=M["kc"]), ALIAS),
+    (dict(T=0), OK), (dict(T=0, x=None, kc=None), OK),
+])
+def test_mla_validation(over, want):
+    assert mla(**over) == want
 
 
 Q = {name: (i + 20) << 32 for i, name in enumerate(

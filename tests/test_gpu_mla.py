@@ -1,0 +1,190 @@
+"""GPU parity of the MLA kv-path head (kvrc_mla_kv_head_paged) against the
+float64 oracle (oracle/mla_kv_head.py) on the same seeded inputs.
+
+The projection runs on the matrix cores with float32 accumulation in an order
+of its own, so the bar is derived from the arithmetic instead of bit
+equality. With He products per output, each exact (bf16 x bf16), any float32
+summation order (round to nearest or toward zero) keeps
+    |c_gpu - c| <= e = 2 He u / (1 - He u) * sum_k |x_k w_k|,   u = 2^-24;
+propagated through the mean square (512 float32 squares and adds), the
+square root and the division, the scaling by alpha * gamma and the RoPE
+products, it bounds |y_gpu - y| by dy; the bf16 output then lies within
+dy + 1/2 bf16 ulp of the float64 value. Every written element must meet that
+bound, and, because the bound is loose (it allows for worst-case cancellation
+in the sums), at least 99.5 % of the outputs must equal the float64 value
+rounded to bf16 (a correct float32 path misses it only where its error of
+about 1e-6 relative straddles a bf16 rounding boundary). Placement and every
+byte no token addresses: bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import latent_attention_kv_amd as k
+from oracle import mla_kv_head as M
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+U = 2.0 ** -24
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _native_library_loaded():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert k.lib()._name == k.LIB_PATH
+    yield
+
+
+def dbf(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def run_mla_gpu(case, slots=None, err=None):
+    caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
+    slots = case["slot_mapping"] if slots is None else slots
+    k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
+                             dbf(case["sin"]), torch.from_numpy(slots).to(DEV),
+                             caches["k_cache"], caches["ckv_cache"], alpha_kv=case["alpha"],
+                             eps=case["eps"], err_count=err)
+    torch.cuda.synchronize()
+    return {n: t.view(torch.int16).cpu().numpy().view(np.uint16) for n, t in caches.items()}
+
+
+def ulp_bf16(v):
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def expected_with_bounds(case):
+    """float64 outputs (oracle) and the per-element bound on |bf16 gpu - value|."""
+    y, kr = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                           case["sin"], case["eps"])
+    X, W = M.bf16_to_f64(case["x"]), M.bf16_to_f64(case["w"])
+    C = X @ W.T
+    A = np.abs(X) @ np.abs(W).T
+    He = X.shape[1]
+    e = (2 * He * U / (1 - He * U)) * A
+    cv, ev = C[:, :512], e[:, :512]
+    ssq = np.sum(cv * cv, axis=1)
+    dss = np.sum(2 * np.abs(cv) * ev + ev * ev, axis=1) + 520 * U * np.sum((np.abs(cv) + ev) ** 2, axis=1)
+    ms = ssq / 512
+    den = ms + case["eps"]
+    drel = np.divide(dss / 512, 2 * den, out=np.full_like(den, np.inf), where=den > 0) + 4 * U
+    rms = np.sqrt(den)
+    g = np.abs(M.bf16_to_f64(case["gamma"]))[None, :]
+    a = abs(case["alpha"])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dy = a * g * (ev / rms[:, None] + np.abs(cv) / rms[:, None] * drel[:, None]) * 1.01 \
+            + 4 * U * np.abs(y)
+    r, er = C[:, 512:], e[:, 512:]
+    cs, sn = np.abs(M.bf16_to_f64(case["cos"])), np.abs(M.bf16_to_f64(case["sin"]))
+    ev_, od_ = np.concatenate([er[:, 0::2], er[:, 1::2]], 1), np.concatenate([er[:, 1::2], er[:, 0::2]], 1)
+    rv_, ro_ = np.concatenate([r[:, 0::2], r[:, 1::2]], 1), np.concatenate([r[:, 1::2], r[:, 0::2]], 1)
+    dk = (cs * ev_ + sn * od_) * 1.01 + 3 * U * (np.abs(rv_) * cs + np.abs(ro_) * sn)
+    tol_y = dy + 0.5 * ulp_bf16(np.abs(y) + dy)
+    tol_k = dk + 0.5 * ulp_bf16(np.abs(kr) + dk)
+    return y, kr, tol_y, tol_k
+
+
+def compare_mla(case, got, slots=None):
+    """Returns (fraction of outputs equal to the rounded float64 value, worst
+    error / bound)."""
+    slots = case["slot_mapping"] if slots is None else slots
+    y, kr, tol_y, tol_k = expected_with_bounds(case)
+    ck, kc = got["ckv_cache"].reshape(-1, 512), got["k_cache"].reshape(-1, 64)
+    t_idx = np.flatnonzero(slots >= 0)
+    rows = slots[t_idx]
+    equal, total, worst = 0, 0, 0.0
+    for gbits, want, tol in ((ck[rows], y[t_idx], tol_y[t_idx]), (kc[rows], kr[t_idx], tol_k[t_idx])):
+        gv = M.bf16_to_f64(gbits)
+        err = np.abs(gv - want)
+        bad = ~(err <= tol)
+        if bad.any():
+            i = np.argwhere(bad)[0]
+            pytest.fail(f"{int(bad.sum())} outputs beyond the bound, e.g. token "
+                        f"{t_idx[i[0]]} col {i[1]}: gpu {gv[tuple(i)]!r} want {want[tuple(i)]!r} "
+                        f"bound {tol[tuple(i)]!r}")
+        worst = max(worst, float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0)
+        wbits = M.f64_to_bf16(want)
+        same = (gbits == wbits) | (((gbits & 0x7FFF) == 0) & ((wbits & 0x7FFF) == 0))
+        equal += int(np.sum(same))
+        total += gbits.size
+    frac = equal / max(total, 1)
+    assert total - equal <= max(3, int(0.005 * total)), \
+        f"only {frac:.5f} of the outputs equal the float64 value rounded to bf16"
+    untouched = np.setdiff1d(np.arange(ck.shape[0]), rows)
+    assert np.all(ck[untouched] == gen.BF16_SENTINEL) and np.all(kc[untouched] == gen.BF16_SENTINEL), \
+        "bytes outside the written rows changed"
+    return frac, worst
+
+
+def test_mla_named_workload_full_size():
+    say("[mla] workload mla_kv_head (T=32768, He=7168)")
+    case = gen.make_config("mla_kv_head")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_mla_gpu(case, err=err)
+    assert int(err.item()) == 0
+    frac, worst = compare_mla(case, got)
+    say(f"[mla] equal to the rounded float64 value: {frac:.6f}; worst error / bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("B,S,He", [(1, 1, 32), (1, 5, 64), (2, 100, 96), (1, 129, 512),
+                                    (3, 257, 1024), (2, 300, 7168), (1, 128, 2048)])
+def test_mla_shapes_and_ragged_tails(B, S, He):
+    say(f"[mla] B={B} S={S} He={He}")
+    case = gen.mla_kv_head_case(500 + S + He, B=B, S=S, He=He, num_blocks=64, block_size=32,
+                                slot_kind="random", skip_frac=0.1)
+    frac, worst = compare_mla(case, run_mla_gpu(case))
+    say(f"[mla] equal fraction {frac:.5f}, worst error / bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("alpha,eps,x_sigma", [(0.0, 1e-6, 1.0), (-1.5, 1e-6, 1.0),
+                                               (3.0, 1.0, 1.0), (1.0, 1e-6, 1e-3),
+                                               (1.0, 1e-6, 300.0)])
+def test_mla_alpha_eps_magnitudes(alpha, eps, x_sigma):
+    say(f"[mla] alpha={alpha} eps={eps} x_sigma={x_sigma}")
+    case = gen.mla_kv_head_case(520, B=2, S=200, He=1024, num_blocks=32, block_size=32,
+                                slot_kind="random", alpha=alpha, eps=eps, x_sigma=x_sigma)
+    compare_mla(case, run_mla_gpu(case))
+
+
+def test_mla_zero_rows():
+    case = gen.mla_kv_head_case(521, B=1, S=150, He=512, num_blocks=16, block_size=16,
+                                slot_kind="random")
+    case["x"][:7] = 0
+    case["x"][140:] = 0x8000                       # negative zeros
+    compare_mla(case, run_mla_gpu(case))
+
+
+def test_mla_invalid_slots_are_skipped_and_counted():
+    case = gen.mla_kv_head_case(522, B=1, S=300, He=256, num_blocks=32, block_size=16,
+                                slot_kind="random", skip_frac=0.05)
+    slots = case["slot_mapping"].copy()
+    slots[[3, 130, 299]] = [32 * 16, -2, 1 << 40]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_mla_gpu(case, slots=slots, err=err)
+    assert int(err.item()) == 3
+    fixed = slots.copy()
+    fixed[[3, 130, 299]] = -1
+    compare_mla(case, got, slots=fixed)
+
+
+def test_mla_deterministic_across_launch_sizes():
+    """A token's outputs do not depend on T or on its position in the batch
+    (same He): the first 130 tokens of a batch equal the same tokens alone."""
+    case = gen.mla_kv_head_case(523, B=1, S=400, He=1024, num_blocks=32, block_size=16,
+                                slot_kind="random")
+    full = run_mla_gpu(case)
+    part = dict(case, x=case["x"][:130], cos=case["cos"][:130], sin=case["sin"][:130],
+                slot_mapping=case["slot_mapping"][:130], T=130, S=130)
+    sub = run_mla_gpu(part)
+    rows = case["slot_mapping"][:130]
+    np.testing.assert_array_equal(full["ckv_cache"].reshape(-1, 512)[rows],
+                                  sub["ckv_cache"].reshape(-1, 512)[rows])
+    np.testing.assert_array_equal(full["k_cache"].reshape(-1, 64)[rows],
+                                  sub["k_cache"].reshape(-1, 64)[rows])
