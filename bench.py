@@ -359,7 +359,14 @@ def ingest_profile(args) -> int:
            f"{st['MaxNs']} |", "",
            f"Algorithmic bytes per launch: {alg} ({tokens} tokens) -> "
            f"{alg / avg_s / 1e9:.1f} GB/s at the average duration "
-           f"({alg / avg_s / 8e12 * 100:.1f} % of 8 TB/s).", "",
+           f"({alg / avg_s / 8e12 * 100:.1f} % of 8 TB/s).", ""]
+    flops = algorithmic_flops(gen.make_config(w))
+    if flops:
+        md += [f"Algorithmic flops per launch: {flops} (2 * T * 576 * He) -> "
+               f"{flops / avg_s / 1e12:.1f} TFLOP/s at the average duration "
+               f"({flops / avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS * 100:.1f} % of the "
+               f"{MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s bf16 dense peak).", ""]
+    md += [
            "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
            "| counter | KiB per dispatch | on the 1 GiB copy | scale | bytes per dispatch |",
            "|---|---|---|---|---|"]

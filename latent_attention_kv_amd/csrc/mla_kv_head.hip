@@ -18,15 +18,27 @@
 // workgroup owns 128 whole token rows, so the row-wise norm, the RoPE and
 // the scatter run on the accumulators without writing c to memory:
 //   * 8 wavefronts = 2 (rows) x 4 (columns); wavefront (wm, wn) accumulates
-//     rows 64 wm .. +64 and columns 144 wn .. +144 as 4 x 9 tiles of 16 x 16;
-//   * K advances 32 at a time: the 128 x 32 slice of x and the 576 x 32 slice
-//     of W are staged in LDS (double-buffered, rows padded to 80 bytes so
-//     that the 16-byte fragment reads of 16 lanes cover all 64 banks once);
-//     the next slice is loaded into registers while the current one feeds
-//     the MFMAs;
-//   * epilogue: squares of the 512 kv columns are reduced across lanes and
-//     wavefronts, the rows are normalised and rotated in registers, staged
-//     as bf16 rows in LDS and written with 16-byte stores per cache row.
+//     rows 64 wm .. +64 and columns 144 wn .. +144 as 4 x 9 tiles of 16 x 16
+//     (144 accumulator registers, two wavefronts per SIMD);
+//   * K advances 32 at a time through 3 LDS stages (x slice 128 x 32, W slice
+//     576 x 32, 44 KiB), filled by direct global -> LDS loads
+//     (global_load_lds_dwordx4: no staging registers, no LDS store
+//     instructions) two steps ahead of the MFMAs; each wavefront waits only
+//     for its own loads of the step about to be used, then one barrier
+//     publishes them;
+//   * within a step the next B fragment read and one load of step + 2 are
+//     issued between groups of 4 MFMAs, so their issue overlaps the matrix
+//     pipe instead of preceding it;
+//   * staged rows are 64 bytes with their four 16-byte pieces permuted by
+//     (row / 4) mod 4, so the 16 lanes of a fragment read cover all 64 banks;
+//   * epilogue: a 4 x 4 transpose among neighbouring lanes turns each
+//     accumulator tile into row pieces of 4 columns; squares are reduced per
+//     row across lanes and wavefronts; rows are normalised and rotated in
+//     registers, staged as bf16 in LDS with 8-byte writes and scattered with
+//     16-byte stores per cache row.
+// Measured on MI355X for T = 32768, He = 7168: about 350 us per call
+// (770 TFLOP/s); the operand stream through the texture path, not the
+// matrix cores, bounds this tile shape.
 #include "kvrc_launch.hpp"
 
 namespace kvrc {
@@ -34,76 +46,117 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRows = 128;                 // token rows per workgroup
 constexpr int kCols = 576;                 // projection outputs (512 + 64)
 constexpr int kNorm = 512;
 constexpr int kRope = 64;
-constexpr int kThreads = 512;              // 8 wavefronts
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kKt = (int)kMlaHeadK;        // K per stage (one MFMA K)
-constexpr int kLdsRow = 80;                // bytes per staged row (64 + 16 pad)
-constexpr int kStageA = kRows * kLdsRow;   // 10240
-constexpr int kStageB = kCols * kLdsRow;   // 46080
-constexpr int kStage = kStageA + kStageB;  // 56320
-constexpr int kChunks = (kRows + kCols) * (kKt * 2 / 16);   // 16-byte pieces per stage: 2816
-constexpr int kFull = kChunks / kThreads;                          // 5 pieces for every thread
-constexpr int kTail = kChunks - kFull * kThreads;                  // + 1 for the first 256
-constexpr int kLoadIters = kFull + 1;
-static_assert(kTail > 0 && kTail % 64 == 0, "tail pieces fill whole wavefronts");
+constexpr int kRowBytes = kKt * 2;         // 64
+constexpr int kStageA = kRows * kRowBytes; // 8192
+constexpr int kStageB = kCols * kRowBytes; // 36864
+constexpr int kStage = kStageA + kStageB;  // 45056
+constexpr int kStages = 3;
+constexpr int kBlocks = kStage / 1024;     // 1 KiB blocks per stage (one load instruction each)
+// the 44 blocks of a stage: wavefronts 0-3 load 6 each, wavefronts 4-7 load 5
+static_assert(4 * 6 + 4 * 5 == kBlocks, "block split");
+constexpr int kMaxBlocksPerWave = 6;
 constexpr int kMt = 4, kNt = 9;            // 16 x 16 tiles per wavefront
-// epilogue staging: bf16 rows of 512 (+8 pad) and 64 (+8 pad) values
+constexpr int kWaveCols = kNt * 16;        // 144
+// epilogue staging: bf16 rows of 512 (+8 pad) and 64 (+8 pad) values, then
+// the per-wavefront square sums
 constexpr int kCkvLds = (kNorm + 8) * 2;   // 1040 bytes per row
 constexpr int kKLds = (kRope + 8) * 2;     // 144 bytes per row
-constexpr int kLdsBytes = 2 * kStage > kRows * (kCkvLds + kKLds) + 4 * kRows * 4
-                              ? 2 * kStage
-                              : kRows * (kCkvLds + kKLds) + 4 * kRows * 4;
+constexpr int kRedOff = kRows * (kCkvLds + kKLds);
+constexpr int kEpiBytes = kRedOff + 4 * kRows * 4;
+constexpr int kLdsBytes = kStages * kStage > kEpiBytes ? kStages * kStage : kEpiBytes;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the unused counters at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float v)
+// Piece permutation of a staged row: piece c of row r sits in slot
+// c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const f32x2 p = {v, 0.0f};
-    const bf16x2 r = __builtin_convertvector(p, bf16x2);
-    return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__global__ __launch_bounds__(kThreads) void mla_kv_head_kernel(MlaKvHeadArgs a)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 4 x 4 transpose among lanes 4q .. 4q+3: lane 4q + i holds column i of a
+// 4 x 4 block (v[j] = row j) and ends with row i (v[c] = column c).
+__device__ __forceinline__ void quad_transpose(f32x4 &v, int lane)
+{
+    const int b = lane & 1, d = (lane >> 1) & 1;
+    // step 1 (partner lane ^ 1): keep rows with bit 0 == b, take the
+    // partner's column for them
+    const float r0 = __shfl_xor(b ? v[0] : v[1], 1, 64);
+    const float r1 = __shfl_xor(b ? v[2] : v[3], 1, 64);
+    // now: rows b and 2 + b, columns (lane & 2) + {0, 1}
+    const float e0 = b ? r0 : v[0], e1 = b ? v[1] : r0;     // row b
+    const float e2 = b ? r1 : v[2], e3 = b ? v[3] : r1;     // row 2 + b
+    // step 2 (partner lane ^ 2): keep row 2d + b, take the partner's two
+    // columns of it
+    const float s0 = __shfl_xor(d ? e0 : e2, 2, 64);
+    const float s1 = __shfl_xor(d ? e1 : e3, 2, 64);
+    if (d) {
+        v[0] = s0; v[1] = s1; v[2] = e2; v[3] = e3;
+    } else {
+        v[0] = e0; v[1] = e1; v[2] = s0; v[3] = s1;
+    }
+}
+
+__global__ __launch_bounds__(kThreads)
+void mla_kv_head_kernel(MlaKvHeadArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
+    const int nblk = wave < 4 ? 6 : 5;
+    const int blk0 = wave < 4 ? 6 * wave : 24 + 5 * (wave - 4);
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int64_t T = a.T, He = a.He;
 
-    // ---- global -> register loads of one K slice ------------------------
-    // piece q < 512: x row q / 4, 16-byte piece q % 4; else W row (q-512) / 4.
-    // Pieces q = tid + 512 i: i < kFull for every thread, i = kFull for the
-    // first kTail threads (whole wavefronts). Rows past T read row T-1
+    // ---- direct global -> LDS loads ---------------------------------------
+    // Wavefront w fills nblk 1 KiB blocks from blk0 on in each stage;
+    // block b < 8 holds x rows 16 b .. +16, block b >= 8 W rows 16 (b - 8) ..
+    // +16. Lane l writes byte 16 l of the block: row 16 b' + l / 4, slot l % 4,
+    // i.e. piece (l % 4) ^ swz(row) of that row. Rows past T read row T - 1
     // (valid memory; their results are dropped).
-    const uint4 *src[kLoadIters];
-    int dst[kLoadIters];
+    const uint16_t *src[kMaxBlocksPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoadIters; ++i) {
-        const int q = (i < kFull || tid < kTail) ? tid + i * kThreads : 0;
-        const int r = q >> 2, c = q & 3;
-        if (r < kRows) {
+    for (int i = 0; i < kMaxBlocksPerWave; ++i) {
+        const int b = blk0 + (i < nblk ? i : 0);
+        const int r = (b < kStageA / 1024 ? b : b - kStageA / 1024) * 16 + (lane >> 2);
+        const int piece = (lane & 3) ^ swz(r);
+        if (b < kStageA / 1024) {
             int64_t t = row0 + r;
             t = t < T ? t : T - 1;
-            src[i] = reinterpret_cast<const uint4 *>(a.x + t * He) + c;
-            dst[i] = r * kLdsRow + c * 16;
+            src[i] = a.x + t * He + piece * 8;
         } else {
-            const int n = r - kRows;
-            src[i] = reinterpret_cast<const uint4 *>(a.w + (int64_t)n * He) + c;
-            dst[i] = kStageA + n * kLdsRow + c * 16;
+            src[i] = a.w + (int64_t)r * He + piece * 8;
         }
     }
-    const bool tail = tid < kTail;
-    static_assert(kFull == 5, "the staging registers below are spelled out for 5 + 1 pieces");
-    uint4 s0, s1, s2, s3, s4, s5;       // named, so that they stay in registers
+    auto issue = [&](int stage, int64_t k0) {
+        unsigned char *base = smem + stage * kStage + blk0 * 1024;
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void *)(base + i * 1024), 16, 0, 0);
+        if (nblk == 6)
+            __builtin_amdgcn_global_load_lds(src[5] + k0, (lds_void *)(base + 5 * 1024), 16, 0, 0);
+    };
 
     f32x4 acc[kMt][kNt];
 #pragma unroll
@@ -112,125 +165,136 @@ __global__ __launch_bounds__(kThreads) void mla_kv_head_kernel(MlaKvHeadArgs a)
         for (int n = 0; n < kNt; ++n)
             acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // fragment addresses inside a stage: lane l reads row (l % 16) of its
-    // tile, K elements 8 (l / 16) .. +8
-    const int fr = lane & 15, fk = (lane >> 4) * 16;
-    const int a_off = (64 * wm + fr) * kLdsRow + fk;
-    const int b_off = kStageA + (144 * wn + fr) * kLdsRow + fk;
+    // fragment reads: lane l takes row (l % 16) of a tile, K piece l / 16
+    // (tile row offsets are multiples of 16, so swz of the row is swz(l % 16))
+    const int fr = lane & 15, fc = lane >> 4;
+    const int a_off = (64 * wm + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
+    const int b_off = kStageA + (kWaveCols * wn + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
 
     const int64_t nk = He / kKt;
-#define KVRC_LOAD_SLICE(k0)                                                    \
-    do {                                                                       \
-        const int64_t off_ = (k0) / 8;            /* in 16-byte pieces */      \
-        s0 = src[0][off_];                                                     \
-        s1 = src[1][off_];                                                     \
-        s2 = src[2][off_];                                                     \
-        s3 = src[3][off_];                                                     \
-        s4 = src[4][off_];                                                     \
-        if (tail)                                                              \
-            s5 = src[5][off_];                                                 \
-    } while (0)
-#define KVRC_STORE_SLICE(buf)                                                  \
-    do {                                                                       \
-        unsigned char *base_ = smem + (buf) * kStage;                          \
-        *reinterpret_cast<uint4 *>(base_ + dst[0]) = s0;                       \
-        *reinterpret_cast<uint4 *>(base_ + dst[1]) = s1;                       \
-        *reinterpret_cast<uint4 *>(base_ + dst[2]) = s2;                       \
-        *reinterpret_cast<uint4 *>(base_ + dst[3]) = s3;                       \
-        *reinterpret_cast<uint4 *>(base_ + dst[4]) = s4;                       \
-        if (tail)                                                              \
-            *reinterpret_cast<uint4 *>(base_ + dst[5]) = s5;                   \
-    } while (0)
-    KVRC_LOAD_SLICE(0);
-    KVRC_STORE_SLICE(0);
-    __syncthreads();
+    issue(0, 0);
+    if (nk > 1)
+        issue(1, kKt);
     for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < nk)
-            KVRC_LOAD_SLICE((kt + 1) * kKt);
-        const unsigned char *base = smem + buf * kStage;
-        bf16x8 af[kMt];
+        // this wavefront's loads of step kt are done (those of kt + 1 may be
+        // in flight); the barrier publishes every wavefront's, and tells that
+        // all are past step kt - 1, whose stage is refilled next
+        asm volatile("" ::: "memory");
+        if (kt + 1 < nk) {
+            if (nblk == 6)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+        } else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const bool more = kt + 2 < nk;
+        unsigned char *dbase = smem + (int)((kt + 2) % kStages) * kStage + blk0 * 1024;
+        const int64_t k0 = (kt + 2) * kKt;
+        const unsigned char *base = smem + (int)(kt % kStages) * kStage;
+        bf16x8 af[kMt], bf[2];
 #pragma unroll
         for (int m = 0; m < kMt; ++m)
-            af[m] = *reinterpret_cast<const bf16x8 *>(base + a_off + m * 16 * kLdsRow);
+            af[m] = *reinterpret_cast<const bf16x8 *>(base + a_off + m * 16 * kRowBytes);
+        bf[0] = *reinterpret_cast<const bf16x8 *>(base + b_off);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
-            const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(base + b_off + n * 16 * kLdsRow);
+            if (n + 1 < kNt)
+                bf[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(base + b_off + (n + 1) * 16 * kRowBytes);
+            if (n < 6 && more && (n < 5 || nblk == 6))
+                __builtin_amdgcn_global_load_lds(src[n] + k0, (lds_void *)(dbase + n * 1024), 16, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < kMt; ++m)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf, acc[m][n], 0, 0, 0);
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf[n & 1], acc[m][n], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk)
-            KVRC_STORE_SLICE(buf ^ 1);
-        __syncthreads();
     }
-#undef KVRC_LOAD_SLICE
-#undef KVRC_STORE_SLICE
+    __syncthreads();                          // every stage read: LDS reused below
 
     // ---- epilogue -----------------------------------------------------------
-    // acc[m][n][j] is c[row][col] with row = 64 wm + 16 m + 4 (lane / 16) + j,
-    // col = 144 wn + 16 n + lane % 16.
-    float *red = reinterpret_cast<float *>(smem + kRows * (kCkvLds + kKLds));   // [4][128]
+    // After the transpose, acc[m][n][e] is c[row][col] with
+    //   row = 16 m + 4 (lane / 16) + lane % 4,
+    //   col = 144 w + 16 n + 4 ((lane % 16) / 4) + e.
+#pragma unroll
+    for (int m = 0; m < kMt; ++m)
+#pragma unroll
+        for (int n = 0; n < kNt; ++n)
+            quad_transpose(acc[m][n], lane);
+    const int rsub = 4 * (lane >> 4) + (lane & 3);       // row within a 16-row tile
+    const int cq = 4 * ((lane & 15) >> 2);               // first column within a tile
+    float *red = reinterpret_cast<float *>(smem + kRedOff);     // [4 column quarters][128]
+    const int ntn = wn < 3 ? kNt : 5;                    // tiles holding kv (not rope) columns
+#pragma unroll
+    for (int m = 0; m < kMt; ++m) {
+        float s = 0.0f;
+#pragma unroll
+        for (int n = 0; n < kNt; ++n)
+            if (n < ntn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s += acc[m][n][e] * acc[m][n][e];
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 8, 64);
+        if (cq == 0)
+            red[wn * kRows + 64 * wm + 16 * m + rsub] = s;
+    }
+    __syncthreads();
+
     unsigned char *ckv_lds = smem;
     unsigned char *k_lds = smem + kRows * kCkvLds;
-    const int lr = (lane >> 4) * 4;                       // first row of this lane in a tile
-    const int lc = lane & 15;
-    const int ntn = wn < 3 ? kNt : 5;                     // tiles holding kv (not rope) columns
-#pragma unroll
-    for (int m = 0; m < kMt; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float s = 0.0f;
-#pragma unroll
-            for (int n = 0; n < kNt; ++n)
-                if (n < ntn)
-                    s += acc[m][n][j] * acc[m][n][j];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 4, 64);
-            s += __shfl_xor(s, 8, 64);
-            if (lc == 0)
-                red[wn * kRows + 64 * wm + 16 * m + lr + j] = s;
-        }
-    __syncthreads();
-
     const float alpha = a.alpha;
+    float g[kNt][4];
 #pragma unroll
-    for (int m = 0; m < kMt; ++m)
+    for (int n = 0; n < kNt; ++n) {
+        const int col = kWaveCols * wn + 16 * n + cq;
+        const int gc = col < kNorm ? col : 0;
+        const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + gc);
+        g[n][0] = bf16_lo(gw.x); g[n][1] = bf16_hi(gw.x);
+        g[n][2] = bf16_lo(gw.y); g[n][3] = bf16_hi(gw.y);
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 64 * wm + 16 * m + lr + j;
-            const float ss = (red[r] + red[kRows + r]) + (red[2 * kRows + r] + red[3 * kRows + r]);
-            const float rms = sqrtf(ss / (float)kNorm + a.eps);
-            int64_t t = row0 + r;
-            t = t < T ? t : T - 1;
+    for (int m = 0; m < kMt; ++m) {
+        const int r = 64 * wm + 16 * m + rsub;
+        const float ss = (red[r] + red[kRows + r]) + (red[2 * kRows + r] + red[3 * kRows + r]);
+        const float rr = 1.0f / sqrtf(ss / (float)kNorm + a.eps);
+        int64_t t = row0 + r;
+        t = t < T ? t : T - 1;
 #pragma unroll
-            for (int n = 0; n < kNt; ++n) {
-                const int col = 144 * wn + 16 * n + lc;
-                const float v = acc[m][n][j];
-                if (n < ntn) {
-                    const float g = bf16_to_f32(a.gamma[col]);
-                    const float yv = alpha * ((v / rms) * g);
-                    *reinterpret_cast<uint16_t *>(ckv_lds + r * kCkvLds + col * 2) = f32_to_bf16(yv);
-                } else {
-                    // rope column m2 = col - 512: pair i = m2 / 2; the partner
-                    // of an even column is the next lane and vice versa
-                    const int m2 = col - kNorm;
-                    const float p = __shfl_xor(v, 1, 64);
-                    const int i = m2 >> 1;
-                    const bool odd = m2 & 1;
-                    const int o = odd ? kRope / 2 + i : i;
-                    const float cs = bf16_to_f32(a.cos[t * kRope + o]);
-                    const float sn = bf16_to_f32(a.sin[t * kRope + o]);
-                    const float kr = odd ? v * cs + p * sn : v * cs - p * sn;
-                    *reinterpret_cast<uint16_t *>(k_lds + r * kKLds + o * 2) = f32_to_bf16(kr);
-                }
+        for (int n = 0; n < kNt; ++n) {
+            const f32x4 v = acc[m][n];
+            if (n < ntn) {
+                const int col = kWaveCols * wn + 16 * n + cq;
+                const uint2 o = {pack_bf16(alpha * ((v[0] * rr) * g[n][0]),
+                                           alpha * ((v[1] * rr) * g[n][1])),
+                                 pack_bf16(alpha * ((v[2] * rr) * g[n][2]),
+                                           alpha * ((v[3] * rr) * g[n][3]))};
+                *reinterpret_cast<uint2 *>(ckv_lds + r * kCkvLds + col * 2) = o;
+            } else {
+                // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
+                // and (2 i0 + 2, 2 i0 + 3) give outputs i0, i0 + 1 and
+                // 32 + i0, 33 + i0
+                const int i0 = 8 * (n - 5) + cq / 2;
+                const uint32_t c0 = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + i0);
+                const uint32_t c1 = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + 32 + i0);
+                const uint32_t s0 = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + i0);
+                const uint32_t s1 = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + 32 + i0);
+                const float lo0 = v[0] * bf16_lo(c0) - v[1] * bf16_lo(s0);
+                const float lo1 = v[2] * bf16_hi(c0) - v[3] * bf16_hi(s0);
+                const float hi0 = v[1] * bf16_lo(c1) + v[0] * bf16_lo(s1);
+                const float hi1 = v[3] * bf16_hi(c1) + v[2] * bf16_hi(s1);
+                *reinterpret_cast<uint32_t *>(k_lds + r * kKLds + i0 * 2) = pack_bf16(lo0, lo1);
+                *reinterpret_cast<uint32_t *>(k_lds + r * kKLds + (32 + i0) * 2) =
+                    pack_bf16(hi0, hi1);
             }
         }
+    }
     __syncthreads();
 
-    // ---- scatter: wavefront w writes rows w, w + 8, ... ---------------------
-    for (int r = wave; r < kRows; r += kThreads / 64) {
+    // ---- scatter: wavefront w writes rows w, w + 4, ... ---------------------
+    for (int r = wave; r < kRows; r += kWaves) {
         const int64_t t = row0 + r;
         if (t >= T)
             break;
