@@ -33,7 +33,7 @@ FP8_SENTINEL = 0x7F             # E4M3FN NaN code
 SCALE_SENTINEL = -1.0
 
 CONFIG_NAMES = ("norm_tiny", "decode_paged", "prefill_paged", "quant_paged", "qsa")
-EXTRA_NAMES = ("prefill_paged_blk", "quant_fp8_paged", "mla_kv_head")
+EXTRA_NAMES = ("prefill_paged_blk", "quant_fp8_paged", "mla_kv_head", "qsa_select")
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -261,6 +261,39 @@ def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=
 
 
 # ---------------------------------------------------------------------------
+# Block selection over QSA block keys
+# ---------------------------------------------------------------------------
+
+def qsa_select_case(seed, N, H, Di, Bcap, kbs, sel_ratio, cmp_ratio, topk, *, kl_lo=None,
+                    kl_hi=None, key_length_count=None, scale=None, key_sigma=1.0):
+    """One query per sequence and head, q [N, H, Di] ~ N(0,1) bf16, scored
+    against block keys [N, Bcap, Di] ~ N(0, key_sigma) bf16; the rows at or
+    beyond a sequence's block count are NaN (never to be read).
+    key_length ~ U{kl_lo .. kl_hi - 1} (default: 0 .. Bcap * kbs), so a
+    sequence has key_length // kbs complete blocks. scale defaults to
+    1 / sqrt(Di)."""
+    g = rng_for(seed)
+    if kl_lo is None:
+        kl_lo = 0
+    if kl_hi is None:
+        kl_hi = Bcap * kbs + 1
+    q = bf16_bits(g.standard_normal((N, H, Di), dtype=np.float32))
+    keys = bf16_bits(g.standard_normal((N, Bcap, Di), dtype=np.float32) * np.float32(key_sigma))
+    kl = g.integers(kl_lo, kl_hi, size=N).astype(np.int64)
+    if key_length_count == 1:
+        kl = kl[:1].copy()
+    for n in range(N):
+        nb = int(kl[n % len(kl)]) // kbs
+        keys[n, nb:] = BF16_NAN
+    Jcap = (Bcap + sel_ratio + cmp_ratio - 3) // sel_ratio + 1 if Bcap > 0 else 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(Di)
+    return dict(query=q, block_keys=keys, key_length=kl, N=N, H=H, Di=Di, Bcap=Bcap, kbs=kbs,
+                sel_ratio=sel_ratio, cmp_ratio=cmp_ratio, topk=topk, Jcap=Jcap,
+                scale=float(np.float32(scale)))
+
+
+# ---------------------------------------------------------------------------
 # QSA block-key cases
 # ---------------------------------------------------------------------------
 
@@ -339,6 +372,12 @@ def make_config(name: str, seed: int | None = None):
         # the prefill batch through the MLA kv-path head (DeepSeek-V3 hidden 7168)
         return mla_kv_head_case(8 if seed is None else seed, B=8, S=4096, He=7168,
                                 num_blocks=8192, block_size=128)
+    if name == "qsa_select":
+        # decode-time block selection: 128 sequences, 64 query heads, up to
+        # 256 blocks of 64 tokens, selection blocks of 128 tokens, top 16
+        return qsa_select_case(9 if seed is None else seed, N=128, H=64, Di=128, Bcap=256,
+                               kbs=64, sel_ratio=2, cmp_ratio=1, topk=16, kl_lo=4096,
+                               kl_hi=16385)
     if name == "prefill_paged_blk":
         # the prefill batch in block-indexed form: one entry per 128-token chunk
         return kvrc_paged_blk_case(6 if seed is None else seed, B=8, S=4096, Dv=512, Dk=64,
