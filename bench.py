@@ -51,8 +51,10 @@ KERNEL_SOURCES = {
     "kvrc": ["latent_attention_kv_amd/csrc/norm_rope_cache.hip"] + _COMMON_SOURCES,
     "qsa": ["latent_attention_kv_amd/csrc/qsa_prepare.hip"] + _COMMON_SOURCES,
     "mla": ["latent_attention_kv_amd/csrc/mla_kv_head.hip"] + _COMMON_SOURCES,
+    "sel": ["latent_attention_kv_amd/csrc/qsa_select.hip"] + _COMMON_SOURCES,
 }
-KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel", "mla": "mla_kv_head_kernel"}
+KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel", "mla": "mla_kv_head_kernel",
+               "sel": "qsa_select_kernel"}
 
 WORKLOAD_TEXT = {
     "prefill_paged": "paged prefill: B=8, S=4096 (32768 tokens), kv [8,1,4096,576] bf16 "
@@ -73,12 +75,15 @@ WORKLOAD_TEXT = {
     "mla_kv_head": "MLA kv-path head: T=32768 tokens (B=8, S=4096), x [32768,7168] bf16 times "
                    "the fused projection [576,7168] bf16 (random init) on the matrix cores, "
                    "alpha_kv 0.875, RMSNorm + RoPE, PA_BNSD caches [8192,128,1,512/64] bf16",
+    "qsa_select": "block selection: N=128 sequences x 1 query token, H=64 heads, Di=128, block "
+                  "keys [128,256,128] bf16 (key_length U[4096,16384), key_block_size 64), "
+                  "selection blocks of 2 key blocks, top 16",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def kernel_family(workload: str) -> str:
-    return {"qsa": "qsa", "mla_kv_head": "mla"}.get(workload, "kvrc")
+    return {"qsa": "qsa", "mla_kv_head": "mla", "qsa_select": "sel"}.get(workload, "kvrc")
 
 
 def source_hash(workload: str) -> str:
@@ -99,6 +104,14 @@ def algorithmic_flops(case) -> int:
 def algorithmic_bytes(case) -> tuple[int, int]:
     """(bytes per launch, tokens per launch) the method must move."""
     import gen
+    if "block_keys" in case and "query" in case:
+        total = 0
+        kl = case["key_length"]
+        for n in range(case["N"]):
+            nb = int(kl[n % len(kl)]) // case["kbs"]
+            total += case["H"] * case["Di"] * 2 + nb * case["Di"] * 2 + 8
+            total += case["Jcap"] * 4 + case["topk"] * 4
+        return total, case["N"]
     if case.get("mode") == "mla_paged":
         T, He = case["T"], case["He"]
         written = int((case["slot_mapping"] >= 0).sum())
@@ -148,6 +161,14 @@ def build_sets(case, R, dev):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     sets = []
+    if "block_keys" in case and "query" in case:
+        base = dict(q=dbf(case["query"]), keys=dbf(case["block_keys"]), kl=dt(case["key_length"]))
+        for i in range(R):
+            s = {k: (v.clone() if i else v) for k, v in base.items()}
+            s["scores"] = torch.zeros(case["N"], case["Jcap"], dtype=torch.float32, device=dev)
+            s["idx"] = torch.zeros(case["N"], case["topk"], dtype=torch.int32, device=dev)
+            sets.append(s)
+        return sets
     if case.get("mode") == "mla_paged":
         base = dict(x=dbf(case["x"]), w=dbf(case["w"]), gamma=dbf(case["gamma"]),
                     cos=dbf(case["cos"]), sin=dbf(case["sin"]), idx=dt(case["slot_mapping"]))
@@ -191,7 +212,11 @@ def build_sets(case, R, dev):
 
 def launch(case, s):
     import latent_attention_kv_amd as k
-    if case.get("mode") == "mla_paged":
+    if "block_keys" in case and "query" in case:
+        k.qsa_select_topk(s["q"], s["keys"], s["kl"], s["scores"], s["idx"],
+                          key_block_size=case["kbs"], sel_ratio=case["sel_ratio"],
+                          cmp_ratio=case["cmp_ratio"], scale=case["scale"])
+    elif case.get("mode") == "mla_paged":
         k.kvrc_mla_kv_head_paged(s["x"], s["w"], s["gamma"], s["cos"], s["sin"], s["idx"],
                                  s["k_cache"], s["ckv_cache"], alpha_kv=case["alpha"],
                                  eps=case["eps"])
@@ -218,6 +243,17 @@ def cpu_baseline(case, seconds=10.0):
     import oracle
     threads = oracle.max_threads()
     n, busy = 0, 0.0
+    if "block_keys" in case and "query" in case:
+        from oracle import qsa_select as Sel
+        while busy < seconds or n == 0:
+            s0 = time.perf_counter()
+            Sel.run_select_case(case)
+            busy += time.perf_counter() - s0
+            n += 1
+        return {"value": round(case["N"] * n / busy, 1), "unit": "tokens/s",
+                "cores": _blas_threads(), "kind": "oracle",
+                "sample": f"the full batch ({case['N']} query tokens) run {n} times by the "
+                          f"float64 oracle ({busy:.1f} s; numpy, one sequence at a time)"}
     if case.get("mode") == "mla_paged":
         from oracle import mla_kv_head as M
         sample = 2048

@@ -2,7 +2,8 @@
  * kvrc.h - C ABI of the MI355X (gfx950) library for latent-attention KV
  * preprocessing: the fused RMSNorm + interleaved RoPE + cache scatter of the
  * per-token key row, the MLA kv-path head that produces that row from the
- * hidden state, and QSAPrepare block-key compression.
+ * hidden state, QSAPrepare block-key compression, and block selection over
+ * those keys.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -258,6 +259,55 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
                     float *next_incomplete_rope, int64_t N, int64_t L, int64_t Di, int64_t Dr,
                     int64_t Bcap, int64_t key_block_size, float eps, int32_t *err_count,
                     hipStream_t stream);
+
+/*
+ * qsa_select_topk - block selection for sparse attention: each sequence's
+ * query heads are scored against its block keys and the best selection
+ * blocks are returned.
+ *
+ * Source: aclnnNsaCompressAttentionInfer (Description and Formulas: P_cmp =
+ * Softmax(scale * query . key^T); P_slc[j] = sum over m < l'/d and n < l/d of
+ * P_cmp[(l'/d) j - m - n]; the sum over the G heads that share a key head;
+ * topkIndices = topk). The compressed keys are the block keys written by
+ * qsa_prepare (one per complete block of key_block_size tokens).
+ *
+ * For every sequence n (single-token inference: one query per head, which
+ * sees all complete blocks):
+ *   K = key_length[n] (key_length[0] when key_length_count == 1),
+ *   nb = K / key_block_size blocks, i < nb;
+ *   P_cmp[h][i] = softmax over i of scale * query[n, h] . block_keys[n, i]
+ *   Q[i] = sum over the H heads of P_cmp[h][i]  (the block keys have one head)
+ *   scores[n, j] = sum_{m < sel_ratio} sum_{c < cmp_ratio} Q[sel_ratio * j - m - c]
+ *       (terms outside [0, nb) are 0) for j < J = (nb + sel_ratio + cmp_ratio
+ *       - 3) / sel_ratio + 1 (J = 0 when nb = 0); scores[n, j] = 0 for
+ *       J <= j < Jcap;
+ *   indices[n, :] = the topk j < J of largest score, by descending score,
+ *       equal scores by ascending j; -1 after the first min(topk, J).
+ * Float32 arithmetic (bf16 products accumulated on the matrix cores, the
+ * device's exp2f on scores scaled by log2 e); deterministic.
+ *
+ * Arguments:
+ *   query         bf16 [N, H, Di]        H a multiple of 16 (<= 1024)
+ *   block_keys    bf16 [N, Bcap, Di]     Di a multiple of 32 (<= 4096); rows
+ *                                        >= nb are not read
+ *   key_length    int64 [key_length_count], count 1 or N; read on the device
+ *   scale         the score scale (e.g. 1 / sqrt(Di))
+ *   sel_ratio     l'/d >= 1 (selection block / key block), cmp_ratio l/d >= 1
+ *   scores        float32 [N, Jcap] out, Jcap = (Bcap + sel_ratio + cmp_ratio - 3)
+ *                 / sel_ratio + 1 (0 when Bcap = 0)
+ *   indices       int32 [N, topk] out
+ * The working set (H + 16) (2 Di + 16) + 64 H + 4 (6 H + Bcap + Jcap) bytes
+ * (q, one 16-row key tile and its scores) must fit one workgroup's LDS (about
+ * 160 KiB), else KVRC_ERR_SHAPE. Returns KVRC_OK (also
+ * when N == 0), or an error status with nothing written; outputs must not
+ * overlap inputs. A sequence with K < 0 or nb > Bcap gets scores 0 and
+ * indices -1 and counts once in err_count.
+ */
+int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t *key_length,
+                        int64_t key_length_count, float scale, int64_t N, int64_t H, int64_t Di,
+                        int64_t Bcap, int64_t key_block_size, int64_t sel_ratio,
+                        int64_t cmp_ratio, int64_t topk, float *scores, int32_t *indices,
+                        int32_t *err_count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ Entry points (same names as the C ABI in ``include/kvrc.h``):
     RoPE and the paged scatter (aclnnMlaPrologV3WeightNz, third and fourth
     paths)
   * qsa_prepare                - block keys (openvino.opset17.qsa_prepare)
+  * qsa_select_topk            - block selection over those keys: softmax
+    scores, selection pooling, head sum, top-k (aclnnNsaCompressAttentionInfer)
 """
 from __future__ import annotations
 
@@ -28,8 +30,8 @@ import os
 import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
-           "kvrc_norm_rope_cache", "kvrc_mla_kv_head_paged", "qsa_prepare", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
-           "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
+           "kvrc_norm_rope_cache", "kvrc_mla_kv_head_paged", "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
+           "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so")
@@ -38,8 +40,8 @@ CACHE_INT8 = 1
 CACHE_FP8_E4M3 = 2
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
-                    "kvrc_mla_kv_head_paged", "qsa_prepare", "kvrc_selftest_arith",
-                    "kvrc_selftest_e4m3")
+                    "kvrc_mla_kv_head_paged", "qsa_prepare", "qsa_select_topk",
+                    "kvrc_selftest_arith", "kvrc_selftest_e4m3")
 
 _lib = None
 
@@ -74,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, F, P,
                                          P]
     L.kvrc_mla_kv_head_paged.restype = I32
+    L.qsa_select_topk.argtypes = [P, P, P, I64, F, I64, I64, I64, I64, I64, I64, I64, I64, P, P,
+                                  P, P]
+    L.qsa_select_topk.restype = I32
     L.qsa_prepare.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F,
                               P, P]
     L.qsa_prepare.restype = I32
@@ -326,3 +331,37 @@ def qsa_prepare(raw_index_keys, block_keys, key_length, rope_cos, rope_sin, k_no
                            _ptr(next_incomplete_raw_keys), _ptr(next_incomplete_rope), N, L, Di,
                            Dr, Bcap, kbs, float(eps), _err_ptr(err_count), _stream(stream))
     _check(st, "qsa_prepare")
+
+
+def select_blocks_capacity(Bcap: int, sel_ratio: int, cmp_ratio: int) -> int:
+    """Jcap: selection-score columns for a block-key capacity Bcap."""
+    return (Bcap + sel_ratio + cmp_ratio - 3) // sel_ratio + 1 if Bcap > 0 else 0
+
+
+def qsa_select_topk(query, block_keys, key_length, scores, indices, *, key_block_size,
+                    sel_ratio=1, cmp_ratio=1, scale=None, err_count=None, stream=None):
+    """Block selection: query [N, H, Di] and block_keys [N, Bcap, Di] (bf16),
+    key_length [N] or [1]; writes scores [N, Jcap] (float32) and indices
+    [N, topk] (int32). scale defaults to 1 / sqrt(Di)."""
+    _need(query, "query", _BF16, 3)
+    _need(block_keys, "block_keys", _BF16, 3)
+    _need(key_length, "key_length", (torch.int64,), 1)
+    _need(scores, "scores", (torch.float32,), 2)
+    _need(indices, "indices", (torch.int32,), 2)
+    N, H, Di = query.shape
+    Bcap = block_keys.shape[1]
+    if tuple(block_keys.shape) != (N, Bcap, Di):
+        raise ValueError("block_keys must be [N, Bcap, Di]")
+    jcap = select_blocks_capacity(Bcap, int(sel_ratio), int(cmp_ratio))
+    if tuple(scores.shape) != (N, jcap):
+        raise ValueError(f"scores must be [N, {jcap}]")
+    if indices.shape[0] != N:
+        raise ValueError("indices must be [N, topk]")
+    if scale is None:
+        scale = 1.0 / float(Di) ** 0.5
+    st = lib().qsa_select_topk(_ptr(query), _ptr(block_keys), _ptr(key_length),
+                               key_length.numel(), float(scale), N, H, Di, Bcap,
+                               int(key_block_size), int(sel_ratio), int(cmp_ratio),
+                               indices.shape[1], _ptr(scores), _ptr(indices),
+                               _err_ptr(err_count), _stream(stream))
+    _check(st, "qsa_select_topk")

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkvrc.so")
 SOURCES = ["kvrc_api.hip", "norm_rope_cache.hip", "qsa_prepare.hip", "mla_kv_head.hip",
-           "selftest.hip"]
+           "qsa_select.hip", "selftest.hip"]
 
 # -ffp-contract=off: every float operation rounds once (no fused multiply-add),
 #   which the fixed arithmetic order of the kernels relies on.

@@ -136,7 +136,7 @@ const char *kvrc_status_string(int32_t status)
     }
 }
 
-int32_t kvrc_version(void) { return 102; }
+int32_t kvrc_version(void) { return 103; }
 
 int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                    const void *sin, const int64_t *slot_mapping, void *k_cache,
@@ -236,6 +236,76 @@ int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *
     a.err = err_count;
     (void)hipGetLastError();
     return launch_status(kvrc::launch_mla_kv_head(a, stream));
+}
+
+int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t *key_length,
+                        int64_t key_length_count, float scale, int64_t N, int64_t H, int64_t Di,
+                        int64_t Bcap, int64_t key_block_size, int64_t sel_ratio,
+                        int64_t cmp_ratio, int64_t topk, float *scores, int32_t *indices,
+                        int32_t *err_count, hipStream_t stream)
+{
+    if (N < 0 || N > (int64_t)INT32_MAX || H < 16 || H % 16 || H > 1024 || Di < 32 || Di % 32 ||
+        Di > 4096 || Bcap < 0 || Bcap > (1 << 24) || key_block_size < 1 || sel_ratio < 1 ||
+        cmp_ratio < 1 || sel_ratio > 1024 || cmp_ratio > 1024 || topk < 0 ||
+        topk > (int64_t)INT32_MAX)
+        return KVRC_ERR_SHAPE;
+    if (key_length_count != 1 && key_length_count != N)
+        return KVRC_ERR_SHAPE;
+    const int64_t jcap = Bcap > 0 ? (Bcap + sel_ratio + cmp_ratio - 3) / sel_ratio + 1 : 0;
+    // key rows staged per chunk: as many 16-row tiles as fit (up to the
+    // capacity), at least one
+    constexpr int64_t kLdsBudget = 160 * 1024 - 256;
+    const int64_t fixed = kvrc::qsa_select_lds_bytes(H, Di, Bcap, jcap, 0);
+    const int64_t per_row = Di * 2 + 16 + 4 * H;       // a staged key row and its H scores
+    const int64_t fit = fixed < kLdsBudget ? (kLdsBudget - fixed) / per_row / 16 * 16 : 0;
+    const int64_t want = (Bcap + 15) / 16 * 16;
+    const int64_t chunk = want < fit ? want : fit;
+    if (chunk < 16)
+        return KVRC_ERR_SHAPE;
+    int64_t qbytes, kbytes, sbytes, ibytes;
+    if (!mul_ok(N, H * Di * 2, &qbytes) || !mul_ok(N, Bcap * Di * 2, &kbytes) ||
+        !mul_ok(N, jcap * 4, &sbytes) || !mul_ok(N, topk * 4, &ibytes))
+        return KVRC_ERR_SHAPE;
+    if (N == 0)
+        return KVRC_OK;
+    if (!query || !block_keys || !key_length || (sbytes && !scores) || (ibytes && !indices))
+        return KVRC_ERR_NULL;
+    if (!aligned(query, 16) || !aligned(block_keys, 16) || !aligned(key_length, 8) ||
+        !aligned(scores, 4) || !aligned(indices, 4) || !aligned(err_count, 4))
+        return KVRC_ERR_ALIGN;
+    const Range in[] = {span(query, qbytes), span(block_keys, kbytes),
+                        span(key_length, key_length_count * 8)};
+    const Range out[] = {span(scores, sbytes), span(indices, ibytes),
+                         span(err_count, err_count ? 4 : 0)};
+    for (const Range &o : out) {
+        for (const Range &i : in)
+            if (overlap(o, i))
+                return KVRC_ERR_ALIAS;
+        for (const Range &o2 : out)
+            if (&o2 != &o && overlap(o, o2))
+                return KVRC_ERR_ALIAS;
+    }
+    kvrc::QsaSelectArgs a;
+    a.query = static_cast<const uint16_t *>(query);
+    a.keys = static_cast<const uint16_t *>(block_keys);
+    a.key_length = key_length;
+    a.klc = key_length_count;
+    a.scale = scale;
+    a.N = N;
+    a.H = H;
+    a.Di = Di;
+    a.Bcap = Bcap;
+    a.kbs = key_block_size;
+    a.sel = sel_ratio;
+    a.cmp = cmp_ratio;
+    a.topk = topk;
+    a.Jcap = jcap;
+    a.chunk = chunk;
+    a.scores = scores;
+    a.indices = indices;
+    a.err = err_count;
+    (void)hipGetLastError();
+    return launch_status(kvrc::launch_qsa_select(a, stream));
 }
 
 int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t *key_length,

@@ -80,6 +80,23 @@ hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream);
 // K granularity of the MLA head kernel (He must be a multiple of it).
 constexpr int64_t kMlaHeadK = 32;
 
+// One block-selection launch (see qsa_select_topk in kvrc.h).
+struct QsaSelectArgs {
+    const uint16_t *query;        // [N, H, Di] bf16
+    const uint16_t *keys;         // [N, Bcap, Di] bf16
+    const int64_t *key_length;    // [klc]
+    int64_t klc;
+    float scale;
+    int64_t N, H, Di, Bcap, kbs, sel, cmp, topk, Jcap;
+    int64_t chunk;                // key rows staged in LDS at a time (multiple of 16)
+    float *scores;                // [N, Jcap]
+    int32_t *indices;             // [N, topk]
+    int32_t *err;                 // nullable
+};
+
+hipError_t launch_qsa_select(const QsaSelectArgs &a, hipStream_t stream);
+int64_t qsa_select_lds_bytes(int64_t H, int64_t Di, int64_t Bcap, int64_t Jcap, int64_t chunk);
+
 // Largest Di qsa_prepare accepts (bounded by the per-lane accumulators).
 constexpr int64_t kQsaMaxDi = 4096;
 

@@ -39,7 +39,7 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 102
+    assert k.lib().kvrc_version() == 103
 
 
 def test_status_strings():
@@ -157,6 +157,34 @@ def mla(**over):
 ])
 def test_mla_validation(over, want):
     assert mla(**over) == want
+
+
+SL = {name: (i + 60) << 32 for i, name in enumerate(["q", "k", "kl", "sc", "ix", "err"])}
+
+
+def select(**over):
+    a = dict(q=SL["q"], k=SL["k"], kl=SL["kl"], klc=4, scale=0.1, N=4, H=64, Di=128, Bcap=256,
+             kbs=64, sel=2, cmp=1, topk=16, sc=SL["sc"], ix=SL["ix"], err=None, stream=None)
+    a.update(over)
+    return k.lib().qsa_select_topk(a["q"], a["k"], a["kl"], a["klc"], a["scale"], a["N"], a["H"],
+                                   a["Di"], a["Bcap"], a["kbs"], a["sel"], a["cmp"], a["topk"],
+                                   a["sc"], a["ix"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(kl=None), NULL), (dict(sc=None), NULL),
+    (dict(ix=None), NULL),
+    (dict(H=8), SHAPE), (dict(H=40), SHAPE), (dict(Di=48), SHAPE), (dict(Di=0), SHAPE),
+    (dict(kbs=0), SHAPE), (dict(sel=0), SHAPE), (dict(cmp=0), SHAPE), (dict(topk=-1), SHAPE),
+    (dict(klc=2), SHAPE), (dict(N=-1), SHAPE), (dict(Bcap=-1), SHAPE),
+    (dict(H=1024, Di=4096), SHAPE),                   # working set beyond one workgroup's LDS
+    (dict(q=SL["q"] + 8), ALIGN), (dict(kl=SL["kl"] + 4), ALIGN), (dict(sc=SL["sc"] + 2), ALIGN),
+    (dict(ix=SL["ix"] + 1), ALIGN),
+    (dict(sc=SL["q"] + 64), ALIAS), (dict(ix=SL["sc"] + 16), ALIAS), (dict(err=SL["ix"]), ALIAS),
+    (dict(N=0, klc=1), OK), (dict(N=0, klc=0, q=None, sc=None), OK),
+])
+def test_select_validation(over, want):
+    assert select(**over) == want
 
 
 Q = {name: (i + 20) << 32 for i, name in enumerate(
