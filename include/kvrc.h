@@ -296,9 +296,11 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
  *   scores        float32 [N, Jcap] out, Jcap = (Bcap + sel_ratio + cmp_ratio - 3)
  *                 / sel_ratio + 1 (0 when Bcap = 0)
  *   indices       int32 [N, topk] out
- * The working set (H + 16) (2 Di + 16) + 64 H + 4 (6 H + Bcap + Jcap) bytes
- * (q, one 16-row key tile and its scores) must fit one workgroup's LDS (about
- * 160 KiB), else KVRC_ERR_SHAPE. Returns KVRC_OK (also
+ * A NaN score is never selected: its position, after those of every other
+ * block, holds -1.
+ * The working set (H + 16) (2 Di + 16) + 80 H + 4 (Bcap + Jcap + 6) bytes
+ * (q, one 16-row key tile, per-head partial results, the block scores) must
+ * fit one workgroup's LDS (about 160 KiB), else KVRC_ERR_SHAPE. Returns KVRC_OK (also
  * when N == 0), or an error status with nothing written; outputs must not
  * overlap inputs. A sequence with K < 0 or nb > Bcap gets scores 0 and
  * indices -1 and counts once in err_count.

@@ -256,7 +256,7 @@ int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t
     // capacity), at least one
     constexpr int64_t kLdsBudget = 160 * 1024 - 256;
     const int64_t fixed = kvrc::qsa_select_lds_bytes(H, Di, Bcap, jcap, 0);
-    const int64_t per_row = Di * 2 + 16 + 4 * H;       // a staged key row and its H scores
+    const int64_t per_row = Di * 2 + 16 + H / 2;       // a staged key row, per-tile head results
     const int64_t fit = fixed < kLdsBudget ? (kLdsBudget - fixed) / per_row / 16 * 16 : 0;
     const int64_t want = (Bcap + 15) / 16 * 16;
     const int64_t chunk = want < fit ? want : fit;

@@ -96,6 +96,8 @@ struct QsaSelectArgs {
 
 hipError_t launch_qsa_select(const QsaSelectArgs &a, hipStream_t stream);
 int64_t qsa_select_lds_bytes(int64_t H, int64_t Di, int64_t Bcap, int64_t Jcap, int64_t chunk);
+// true when (H, Di, Bcap) runs on the compile-time fast path
+bool qsa_select_fast_path(int64_t H, int64_t Di, int64_t Bcap);
 
 // Largest Di qsa_prepare accepts (bounded by the per-lane accumulators).
 constexpr int64_t kQsaMaxDi = 4096;

@@ -11,20 +11,25 @@
 //   indices   = the topk largest P[j], descending, equal scores by ascending j,
 //               -1 where fewer than topk blocks exist
 //
-// Design (one 256-thread workgroup per sequence):
+// Design (one 512-thread workgroup per sequence):
 //   * the scores are a dense contraction (H x nb x Di), so they run on the
-//     matrix cores (v_mfma_f32_16x16x32_bf16) from q [H, Di] staged in LDS;
-//     wavefront w takes the 16-block tiles w, w + 4, ...;
-//   * the sequence's keys pass through LDS in chunks of up to `chunk` rows,
-//     each loaded by all threads at once (one memory latency per chunk);
-//     every staged 16-row tile feeds all head tiles;
-//   * the chunk's scores stay in LDS in log2 units (scale * log2 e * q . k),
-//     so the softmax is a maximum, exp2 and a sum per head, and the head
-//     sum Q[i] takes one reciprocal per head; a sequence that fits one chunk
-//     takes one sweep of the matrix cores, a longer one three (maxima, sums,
-//     Q), each recomputing the chunk's scores;
-//   * pooling on LDS; the top-k on wavefront 0 alone: one arg-max of
-//     (score, -index) per selected block, with no workgroup barrier.
+//     matrix cores (v_mfma_f32_16x16x32_bf16) from q [H, Di] and the keys
+//     staged in LDS; wavefront w takes the 16-block column tiles w, w + 8, ...
+//     and every head tile of each;
+//   * a tile's accumulator holds 4 heads x 16 blocks per 16-lane row, so a
+//     head's maximum or sum over a tile's blocks is four DPP steps inside the
+//     row; per-tile results go to LDS and are combined in tile order;
+//   * scores in log2 units (scale * log2 e * q . k): the softmax is a
+//     maximum, exp2 and a sum per head, and Q takes one reciprocal per head;
+//   * when the sequence's keys fit one LDS chunk and its tiles fit the
+//     registers (kMaxTiles per wavefront), the scores are computed once and
+//     held in registers through the maximum, the exp2 and the head sum;
+//     otherwise the keys pass through LDS in chunks, once per sweep (maxima,
+//     sums, Q), and every sweep recomputes its tiles;
+//   * pooling on LDS; top-k by rank: each candidate counts the candidates
+//     ahead of it (higher score, or equal score and lower index) and lands at
+//     that position; above kRankMax candidates, repeated arg-max on one
+//     wavefront.
 // Float32 throughout (exp2f of the device library); deterministic: every
 // reduction has a fixed order.
 #include "kvrc_launch.hpp"
@@ -35,221 +40,134 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRankMax = 2048;
+constexpr int kMaxTiles = 16;            // score tiles a wavefront holds in registers
 
-// rows x pieces 16-byte pieces of a row-major bf16 matrix (row length Di) into
-// LDS rows of rowb bytes; each thread issues kBatch loads before it stores
-// any, so a batch costs one memory latency. Loads and stores are
-// unconditional (indices past the end repeat the last piece) so that the
-// batch stays in registers.
-constexpr int kBatch = 8;
+// rows_a rows of a, then rows of b (row-major bf16, row length Di, 16-byte
+// pieces) into consecutive LDS rows of rowb bytes. Each thread issues kBatch
+// loads before it stores any, so a batch costs one memory latency. Indices
+// past the end repeat the last piece (load and store), so every load and
+// store is unconditional: a conditional store lets the compiler move its load
+// into the branch, after the wait for the previous one.
+constexpr int kBatch = 12;
 
-__device__ __forceinline__ const uint4 *piece_src(const uint16_t *src, int c, int pieces, int Di)
+struct RowSrc {
+    const uint16_t *a, *b;
+    int rows_a, pieces, Di;
+    __device__ __forceinline__ const uint4 *at(int c) const
+    {
+        const int row = c / pieces, off = (c % pieces) * 8;
+        const uint16_t *p = row < rows_a ? a + (int64_t)row * Di : b + (int64_t)(row - rows_a) * Di;
+        return reinterpret_cast<const uint4 *>(p + off);
+    }
+};
+
+// one piece of the batch: load (index past the end -> the last piece) and store
+#define KVRC_SEL_LOAD(i) const uint4 v##i = *src.at(min(c0 + (i) * kThreads, total - 1));
+#define KVRC_SEL_STORE(i)                                                                    \
+    {                                                                                        \
+        const int c = min(c0 + (i) * kThreads, total - 1);                                   \
+        *reinterpret_cast<uint4 *>(dst + (c / pieces) * rowb + (c % pieces) * 16) = v##i;    \
+    }
+
+__device__ __forceinline__ void copy_rows(unsigned char *dst, const RowSrc &src, int rows, int rowb,
+                                          int tid)
 {
-    return reinterpret_cast<const uint4 *>(src + (int64_t)(c / pieces) * Di + (c % pieces) * 8);
-}
-
-__device__ __forceinline__ uint4 *piece_dst(unsigned char *dst, int c, int pieces, int rowb)
-{
-    return reinterpret_cast<uint4 *>(dst + (c / pieces) * rowb + (c % pieces) * 16);
-}
-
-__device__ __forceinline__ void copy_rows(unsigned char *dst, const uint16_t *src, int rows,
-                                          int pieces, int rowb, int Di, int tid)
-{
-    static_assert(kBatch == 8, "the batch below is spelled out for 8 pieces");
+    static_assert(kBatch == 12, "the batch below is spelled out for 12 pieces");
+    const int pieces = src.pieces;
     const int total = rows * pieces;
     for (int c0 = tid; c0 < total; c0 += kThreads * kBatch) {
-        // past the end: the last piece again (loads and stores stay unconditional,
-        // so the batch lives in named registers)
-        const int c1 = min(c0 + 1 * kThreads, total - 1), c2 = min(c0 + 2 * kThreads, total - 1);
-        const int c3 = min(c0 + 3 * kThreads, total - 1), c4 = min(c0 + 4 * kThreads, total - 1);
-        const int c5 = min(c0 + 5 * kThreads, total - 1), c6 = min(c0 + 6 * kThreads, total - 1);
-        const int c7 = min(c0 + 7 * kThreads, total - 1);
-        const uint4 v0 = *piece_src(src, c0, pieces, Di), v1 = *piece_src(src, c1, pieces, Di);
-        const uint4 v2 = *piece_src(src, c2, pieces, Di), v3 = *piece_src(src, c3, pieces, Di);
-        const uint4 v4 = *piece_src(src, c4, pieces, Di), v5 = *piece_src(src, c5, pieces, Di);
-        const uint4 v6 = *piece_src(src, c6, pieces, Di), v7 = *piece_src(src, c7, pieces, Di);
-        *piece_dst(dst, c0, pieces, rowb) = v0;
-        *piece_dst(dst, c1, pieces, rowb) = v1;
-        *piece_dst(dst, c2, pieces, rowb) = v2;
-        *piece_dst(dst, c3, pieces, rowb) = v3;
-        *piece_dst(dst, c4, pieces, rowb) = v4;
-        *piece_dst(dst, c5, pieces, rowb) = v5;
-        *piece_dst(dst, c6, pieces, rowb) = v6;
-        *piece_dst(dst, c7, pieces, rowb) = v7;
+        KVRC_SEL_LOAD(0) KVRC_SEL_LOAD(1) KVRC_SEL_LOAD(2) KVRC_SEL_LOAD(3)
+        KVRC_SEL_LOAD(4) KVRC_SEL_LOAD(5) KVRC_SEL_LOAD(6) KVRC_SEL_LOAD(7)
+        KVRC_SEL_LOAD(8) KVRC_SEL_LOAD(9) KVRC_SEL_LOAD(10) KVRC_SEL_LOAD(11)
+        __builtin_amdgcn_sched_barrier(0);               // every load issued before the first wait
+        KVRC_SEL_STORE(0) KVRC_SEL_STORE(1) KVRC_SEL_STORE(2) KVRC_SEL_STORE(3)
+        KVRC_SEL_STORE(4) KVRC_SEL_STORE(5) KVRC_SEL_STORE(6) KVRC_SEL_STORE(7)
+        KVRC_SEL_STORE(8) KVRC_SEL_STORE(9) KVRC_SEL_STORE(10) KVRC_SEL_STORE(11)
     }
 }
+#undef KVRC_SEL_LOAD
+#undef KVRC_SEL_STORE
 
-__global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
+// DPP inside a 16-lane row: xor 1, xor 2 (quad permutes), then the half-row
+// and row mirrors; after the four steps every lane of the row holds the
+// reduction of all 16 (the same value in every lane: each step combines two
+// equal partial results, and + and max are commutative)
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v)
 {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n = blockIdx.x;
-    const int H = (int)a.H, Di = (int)a.Di;
-    const int Jcap = (int)a.Jcap, KC = (int)a.chunk;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
 
-    // LDS: q [H][Di] and a key chunk [KC][Di] (bf16 rows padded by 16 bytes),
-    // the chunk's scores S [H][KC + 4] (float32, log2 units), head max and
-    // reciprocal sums [H] x 2, Q [Bcap], P [Jcap]
-    const int rowb = Di * 2 + 16;
-    const int srow = KC + 4;
-    unsigned char *q_lds = smem;
-    unsigned char *k_lds = smem + H * rowb;
-    float *S = reinterpret_cast<float *>(k_lds + KC * rowb);
-    float *hmax = S + H * srow;
-    float *hrz = hmax + H;
-    float *Q = hrz + H;                        // [Bcap]
-    float *P = Q + a.Bcap;                     // [Jcap]
+__device__ __forceinline__ float row_max16(float v)
+{
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    return fmaxf(v, dpp<kDppMirror>(v));
+}
 
+__device__ __forceinline__ float row_sum16(float v)
+{
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    return v + dpp<kDppMirror>(v);
+}
+
+// one 16 x 16 tile: rows = heads (fragment of q at qa), columns = blocks
+// (fragment of the staged keys at kr). Di >= 32 (checked on the host): a
+// do-while leaves no path on which no MFMA runs, whose join with the MFMA path
+// made the compiler read the first accumulator register without the wait
+// states an MFMA result needs.
+__device__ __forceinline__ f32x4 score_tile(const unsigned char *qa, const unsigned char *kr, int Di)
+{
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int k0 = 0;
+    do {
+        const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(kr + k0 * 2);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(qa + k0 * 2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, acc, 0, 0, 0);
+        k0 += 32;
+    } while (k0 < Di);
+    return acc;
+}
+
+// The sequence's block count nb = key_length / kbs, or -1 for an invalid
+// length (negative, or more blocks than the capacity): such a sequence gets
+// scores 0 and indices -1 here and counts once in the error counter.
+__device__ __forceinline__ int sequence_blocks(const QsaSelectArgs &a, int64_t n, float *scores,
+                                               int32_t *out_idx, int tid)
+{
     const int64_t K = a.key_length[a.klc == 1 ? 0 : n];
-    const int64_t nb64 = K >= 0 ? K / a.kbs : -1;
-    float *scores = a.scores + n * Jcap;
-    int32_t *out_idx = a.indices + n * a.topk;
-    if (nb64 < 0 || nb64 > a.Bcap) {
-        // invalid length: the sequence gets empty outputs and is counted
-        for (int j = tid; j < Jcap; j += kThreads)
-            scores[j] = 0.0f;
-        for (int p = tid; p < a.topk; p += kThreads)
-            out_idx[p] = -1;
-        if (tid == 0 && a.err)
-            atomicAdd(a.err, 1);
-        return;
-    }
-    const int nb = (int)nb64;
-    const int sel = (int)a.sel, cmpr = (int)a.cmp;
-    const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
-    const int pieces = Di / 8;                  // 16-byte pieces per row
-    // scores in log2 units: softmax(x) = exp2(x log2(e) - max) / sum
-    const float scale2 = a.scale * 1.44269504088896341f;
+    const int64_t nb = K >= 0 ? K / a.kbs : -1;
+    if (nb >= 0 && nb <= a.Bcap)
+        return (int)nb;
+    for (int j = tid; j < a.Jcap; j += kThreads)
+        scores[j] = 0.0f;
+    for (int p = tid; p < a.topk; p += kThreads)
+        out_idx[p] = -1;
+    if (tid == 0 && a.err)
+        atomicAdd(a.err, 1);
+    return -1;
+}
 
-    copy_rows(q_lds, a.query + n * (int64_t)H * Di, H, pieces, rowb, Di, tid);
-    for (int h = tid; h < H; h += kThreads) {
-        hmax[h] = -INFINITY;
-        hrz[h] = 0.0f;
-    }
-    for (int i = tid; i < a.Bcap; i += kThreads)
-        Q[i] = 0.0f;
-
-    const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;      // fragment row, first K element
-
-    // keys [c0, c0 + rows) -> LDS, then S[h][i] = scale2 * q_h . k_(c0+i) for
-    // i < rows (tiles of 16 x 16 on the matrix cores; wavefront w takes the
-    // 16-row tiles w, w + 4, ...; the lanes of rows past `rows` are not stored)
-    auto chunk_scores = [&](int c0, int rows) {
-        __syncthreads();                                 // the previous chunk is used up
-        copy_rows(k_lds, kn + (int64_t)c0 * Di, rows, pieces, rowb, Di, tid);
-        __syncthreads();
-        const int ntile = (rows + 15) / 16;
-        for (int jt = wave; jt < ntile; jt += kWaves) {
-            const unsigned char *kr = k_lds + (16 * jt + fr) * rowb + fk * 2;
-            for (int ht = 0; ht < H / 16; ++ht) {
-                const unsigned char *qa = q_lds + (16 * ht + fr) * rowb + fk * 2;
-                // Di >= 32 (checked on the host): a do-while leaves no zero-trip
-                // path, whose join with the MFMA path made the compiler read
-                // the first accumulator register without the wait states an
-                // MFMA result needs (it returned the stale initial value)
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                int k0 = 0;
-                do {
-                    const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(kr + k0 * 2);
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(qa + k0 * 2);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, acc, 0, 0, 0);
-                    k0 += 32;
-                } while (k0 < Di);
-                const int i = 16 * jt + fr;
-                if (i < rows) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        S[(16 * ht + 4 * (lane >> 4) + r) * srow + i] = scale2 * acc[r];
-                }
-            }
-        }
-        __syncthreads();
-    };
-    // per head (wavefront w takes heads w, w + 4, ...; lanes stride the rows):
-    // the running maximum over this chunk's rows
-    auto chunk_max = [&](int rows) {
-        for (int h = wave; h < H; h += kWaves) {
-            float m = -INFINITY;
-            for (int i = lane; i < rows; i += 64)
-                m = fmaxf(m, S[h * srow + i]);
-#pragma unroll
-            for (int x = 32; x >= 1; x >>= 1)
-                m = fmaxf(m, __shfl_xor(m, x, 64));
-            if (lane == 0)
-                hmax[h] = fmaxf(hmax[h], m);
-        }
-    };
-    // per head: exp2(S - max) in place, its sum added to hrz (turned into
-    // 1 / sum once every chunk is in)
-    auto chunk_exp_sum = [&](int rows) {
-        for (int h = wave; h < H; h += kWaves) {
-            const float m = hmax[h];
-            float z = 0.0f;
-            for (int i = lane; i < rows; i += 64) {
-                const float e = exp2f(S[h * srow + i] - m);
-                S[h * srow + i] = e;
-                z += e;
-            }
-#pragma unroll
-            for (int x = 32; x >= 1; x >>= 1)
-                z += __shfl_xor(z, x, 64);
-            if (lane == 0)
-                hrz[h] += z;
-        }
-    };
-    // Q[c0 + i] = sum_h S[h][i] / sum_h with S holding exp2(s - max)
-    auto chunk_q = [&](int c0, int rows) {
-        for (int i = tid; i < rows; i += kThreads) {
-            float q = 0.0f;
-            for (int h = 0; h < H; ++h)
-                q += S[h * srow + i] * hrz[h];
-            Q[c0 + i] = q;
-        }
-    };
-    auto finish_sums = [&]() {
-        __syncthreads();
-        for (int h = tid; h < H; h += kThreads)
-            hrz[h] = 1.0f / hrz[h];
-        __syncthreads();
-    };
-
-    if (nb > 0 && nb <= KC) {
-        // the whole sequence in one chunk: one sweep of the matrix cores
-        chunk_scores(0, nb);
-        chunk_max(nb);
-        __syncthreads();
-        chunk_exp_sum(nb);
-        finish_sums();
-        chunk_q(0, nb);
-    } else if (nb > KC) {
-        for (int c0 = 0; c0 < nb; c0 += KC) {
-            chunk_scores(c0, min(KC, nb - c0));
-            chunk_max(min(KC, nb - c0));
-        }
-        for (int c0 = 0; c0 < nb; c0 += KC) {
-            chunk_scores(c0, min(KC, nb - c0));
-            chunk_exp_sum(min(KC, nb - c0));
-        }
-        finish_sums();
-        for (int c0 = 0; c0 < nb; c0 += KC) {
-            chunk_scores(c0, min(KC, nb - c0));
-            for (int h = wave; h < H; h += kWaves) {
-                const float m = hmax[h];
-                for (int i = lane; i < min(KC, nb - c0); i += 64)
-                    S[h * srow + i] = exp2f(S[h * srow + i] - m);
-            }
-            __syncthreads();
-            chunk_q(c0, min(KC, nb - c0));
-        }
-    }
-    __syncthreads();
-
-    // ---- pooling ------------------------------------------------------------
-    for (int j = tid; j < Jcap; j += kThreads) {
+// Pooling of Q [nb] into the J selection-block scores, and the top-k. Q is
+// complete in LDS (the caller's barrier); P [Jcap rounded up to 4] is LDS
+// scratch.
+__device__ __forceinline__ void pool_and_select(const QsaSelectArgs &a, const float *Q, float *P,
+                                                int nb, int J, float *scores, int32_t *out_idx,
+                                                int tid, int lane, int wave)
+{
+    const int sel = (int)a.sel, cmpr = (int)a.cmp, Jcap = (int)a.Jcap;
+    const int Jcap4 = (Jcap + 3) / 4 * 4;
+    for (int j = tid; j < Jcap4; j += kThreads) {
         float v = 0.0f;
         if (j < J) {
             for (int mm = 0; mm < sel; ++mm)
@@ -259,10 +177,36 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
                         v += Q[i];
                 }
         }
-        scores[j] = v;
-        P[j] = j < J ? v : -1.0f;                        // -1: not a candidate
+        if (j < Jcap)
+            scores[j] = v;
+        // -1 marks what is never selected: blocks past J and NaN scores
+        P[j] = j < J && v == v ? v : -1.0f;
     }
     __syncthreads();
+    if (J <= kRankMax) {
+        // ---- top-k by rank: position of block j = the number of blocks ahead
+        // of it; the ranks of the J blocks are 0 .. J-1, each once. A NaN
+        // score (-1) ranks after every real one and leaves its position -1;
+        // the entries from J up to the next multiple of 4 are -1 with larger
+        // indices, so they are never ahead of a block.
+        const int J4 = (J + 3) / 4 * 4;
+        for (int j = tid; j < J; j += kThreads) {
+            const float v = P[j];
+            int rank = 0;
+#pragma unroll 4
+            for (int jj = 0; jj < J4; jj += 4) {
+                const f32x4 u = *reinterpret_cast<const f32x4 *>(P + jj);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    rank += (u[x] > v) | ((u[x] == v) & (jj + x < j));
+            }
+            if (rank < a.topk)
+                out_idx[rank] = v >= 0.0f ? j : -1;
+        }
+        for (int p = J + tid; p < a.topk; p += kThreads)
+            out_idx[p] = -1;
+        return;
+    }
     if (wave != 0)
         return;
 
@@ -303,22 +247,447 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
     }
 }
 
+__global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
+{
+    // no contraction: scale2 * acc - max is rounded alike wherever it is
+    // computed
+#pragma clang fp contract(off)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = blockIdx.x;
+    const int H = (int)a.H, Di = (int)a.Di;
+    const int Jcap = (int)a.Jcap, KC = (int)a.chunk;
+
+    // LDS: q [H][Di] and a key chunk [KC][Di] (bf16 rows padded by 16 bytes),
+    // per-wavefront head maxima and sums [kWaves][H] x 2, the combined head
+    // maxima and reciprocal sums [H] x 2, per-tile head maxima and sums
+    // [KC / 16][H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4)
+    const int rowb = Di * 2 + 16;
+    unsigned char *q_lds = smem;
+    unsigned char *k_lds = smem + H * rowb;
+    float *wmax = reinterpret_cast<float *>(k_lds + KC * rowb);
+    float *wsum = wmax + kWaves * H;
+    float *hmax = wsum + kWaves * H;
+    float *hrz = hmax + H;
+    float *tmax = hrz + H;
+    float *tsum = tmax + (KC / 16) * H;
+    float *Q = tsum + (KC / 16) * H;
+    float *P = Q + (a.Bcap + 3) / 4 * 4;
+
+    float *scores = a.scores + n * Jcap;
+    int32_t *out_idx = a.indices + n * a.topk;
+    const int nb = sequence_blocks(a, n, scores, out_idx, tid);
+    if (nb < 0)
+        return;
+    const int sel = (int)a.sel, cmpr = (int)a.cmp;
+    const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
+    const int pieces = Di / 8;                  // 16-byte pieces per row
+    const int HT = H / 16;
+    // scores in log2 units: softmax(x) = exp2(x log2(e) - max) / sum
+    const float scale2 = a.scale * 1.44269504088896341f;
+
+    const uint16_t *qn = a.query + n * (int64_t)H * Di;
+    const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
+    const int fr = lane & 15, g = lane >> 4;             // fragment row / column, lane group
+    const int fk = g * 8;                                // first K element of the fragment
+    const int ntile = (nb + 15) / 16;                    // column tiles of the sequence
+    const bool in_regs = nb > 0 && nb <= KC && HT * ((ntile + kWaves - 1) / kWaves) <= kMaxTiles;
+
+    if (in_regs) {
+        copy_rows(q_lds, RowSrc{qn, kn, H, pieces, Di}, H + nb, rowb, tid);
+        __syncthreads();
+        // this wavefront's tiles: t -> (column tile jt, head tile ht), ht fastest
+        const int T = wave < ntile ? ((ntile - 1 - wave) / kWaves + 1) * HT : 0;
+        f32x4 e[kMaxTiles];
+        {
+            int ht = 0, jt = wave;
+#pragma unroll
+            for (int t = 0; t < kMaxTiles; ++t) {
+                if (t < T) {
+                    const f32x4 acc = score_tile(q_lds + (16 * ht + fr) * rowb + fk * 2,
+                                                 k_lds + (16 * jt + fr) * rowb + fk * 2, Di);
+                    const bool ok = 16 * jt + fr < nb;
+                    f32x4 mx;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        e[t][q] = scale2 * acc[q];
+                        mx[q] = row_max16(ok ? e[t][q] : -INFINITY);
+                    }
+                    if (fr == 0)
+                        *reinterpret_cast<f32x4 *>(tmax + jt * H + 16 * ht + 4 * g) = mx;
+                    if (++ht == HT) {
+                        ht = 0;
+                        jt += kWaves;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        for (int h = tid; h < H; h += kThreads) {
+            float v = -INFINITY;
+            for (int jt = 0; jt < ntile; ++jt)
+                v = fmaxf(v, tmax[jt * H + h]);
+            hmax[h] = v;
+        }
+        __syncthreads();
+        {
+            int ht = 0, jt = wave;
+#pragma unroll
+            for (int t = 0; t < kMaxTiles; ++t) {
+                if (t < T) {
+                    const bool ok = 16 * jt + fr < nb;
+                    const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
+                    f32x4 zs;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        e[t][q] = ok ? exp2f(e[t][q] - m[q]) : 0.0f;
+                        zs[q] = row_sum16(e[t][q]);
+                    }
+                    if (fr == 0)
+                        *reinterpret_cast<f32x4 *>(tsum + jt * H + 16 * ht + 4 * g) = zs;
+                    if (++ht == HT) {
+                        ht = 0;
+                        jt += kWaves;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        for (int h = tid; h < H; h += kThreads) {
+            float v = 0.0f;
+            for (int jt = 0; jt < ntile; ++jt)
+                v += tsum[jt * H + h];
+            hrz[h] = 1.0f / v;
+        }
+        __syncthreads();
+        {
+            int ht = 0, jt = wave;
+            float qv = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kMaxTiles; ++t) {
+                if (t < T) {
+                    const f32x4 rz = *reinterpret_cast<const f32x4 *>(hrz + 16 * ht + 4 * g);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        qv += e[t][q] * rz[q];
+                    if (++ht == HT) {
+                        // the 4 lane groups hold the same block for different heads
+                        qv += __shfl_xor(qv, 16, 64);
+                        qv += __shfl_xor(qv, 32, 64);
+                        if (g == 0 && 16 * jt + fr < nb)
+                            Q[16 * jt + fr] = qv;
+                        qv = 0.0f;
+                        ht = 0;
+                        jt += kWaves;
+                    }
+                }
+            }
+        }
+    } else if (nb > 0) {
+        for (int i = tid; i < kWaves * H; i += kThreads) {
+            wmax[i] = -INFINITY;
+            wsum[i] = 0.0f;
+        }
+        const int nchunk = (nb + KC - 1) / KC;
+        // sweep 0: head maxima; sweep 1: head sums of exp2(s - max); sweep 2: Q
+        for (int sweep = 0; sweep < 3; ++sweep) {
+            for (int c = 0; c < nchunk; ++c) {
+                const int c0 = c * KC, rows = min(KC, nb - c0);
+                __syncthreads();                         // the previous chunk is used up
+                if (sweep == 0 && c == 0)
+                    copy_rows(q_lds, RowSrc{qn, kn, H, pieces, Di}, H + rows, rowb, tid);
+                else
+                    copy_rows(k_lds, RowSrc{kn + (int64_t)c0 * Di, nullptr, rows, pieces, Di},
+                              rows, rowb, tid);
+                __syncthreads();
+                const int ctile = (rows + 15) / 16;
+                if (wave >= ctile)
+                    continue;
+                if (sweep < 2) {
+                    for (int ht = 0; ht < HT; ++ht) {
+                        const unsigned char *qa = q_lds + (16 * ht + fr) * rowb + fk * 2;
+                        const int h0 = 16 * ht + 4 * g;  // this lane's 4 heads
+                        const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + h0);
+                        f32x4 r = sweep == 0 ? f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}
+                                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        for (int jt = wave; jt < ctile; jt += kWaves) {
+                            const f32x4 acc = score_tile(qa, k_lds + (16 * jt + fr) * rowb + fk * 2, Di);
+                            const bool ok = 16 * jt + fr < rows;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float s = scale2 * acc[q];
+                                if (sweep == 0)
+                                    r[q] = ok ? fmaxf(r[q], s) : r[q];
+                                else
+                                    r[q] += ok ? exp2f(s - m[q]) : 0.0f;
+                            }
+                        }
+                        float *dst = (sweep == 0 ? wmax : wsum) + wave * H + h0;
+                        f32x4 old = *reinterpret_cast<const f32x4 *>(dst);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            old[q] = sweep == 0 ? fmaxf(old[q], row_max16(r[q])) : old[q] + row_sum16(r[q]);
+                        if (fr == 0)
+                            *reinterpret_cast<f32x4 *>(dst) = old;
+                    }
+                } else {
+                    for (int jt = wave; jt < ctile; jt += kWaves) {
+                        const unsigned char *kr = k_lds + (16 * jt + fr) * rowb + fk * 2;
+                        float qv = 0.0f;
+                        for (int ht = 0; ht < HT; ++ht) {
+                            const int h0 = 16 * ht + 4 * g;
+                            const f32x4 acc = score_tile(q_lds + (16 * ht + fr) * rowb + fk * 2, kr, Di);
+                            const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + h0);
+                            const f32x4 rz = *reinterpret_cast<const f32x4 *>(hrz + h0);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                qv += exp2f(scale2 * acc[q] - m[q]) * rz[q];
+                        }
+                        qv += __shfl_xor(qv, 16, 64);
+                        qv += __shfl_xor(qv, 32, 64);
+                        const int i = 16 * jt + fr;
+                        if (g == 0 && i < rows)
+                            Q[c0 + i] = qv;
+                    }
+                }
+            }
+            __syncthreads();
+            if (sweep < 2) {
+                // combine the wavefronts in a fixed order; the next sweep's
+                // first staging barrier orders it before any use
+                for (int h = tid; h < H; h += kThreads) {
+                    float v = sweep == 0 ? -INFINITY : 0.0f;
+                    for (int w = 0; w < kWaves; ++w)
+                        v = sweep == 0 ? fmaxf(v, wmax[w * H + h]) : v + wsum[w * H + h];
+                    if (sweep == 0)
+                        hmax[h] = v;
+                    else
+                        hrz[h] = 1.0f / v;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    pool_and_select(a, Q, P, nb, J, scores, out_idx, tid, lane, wave);
+}
+
+// Fast path for the common shapes, all sizes known at compile time: Di = 32 DK,
+// H = 16 HT, and at most JWM column tiles per wavefront (Bcap <= 128 JWM).
+// Each wavefront loads the key fragments of its column tiles straight from
+// memory into registers (no other wavefront needs them), q passes through
+// LDS once, and every score of the sequence stays in registers from the
+// matrix cores to the head sum; per-wavefront head maxima and sums are
+// combined per head in wavefront order.
+template <int DK, int HT, int JWM>
+__global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs a)
+{
+#pragma clang fp contract(off)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int Di = 32 * DK, H = 16 * HT, rowb = 2 * Di + 16, pieces = Di / 8;
+    constexpr int QP = H * pieces, QPT = (QP + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = blockIdx.x;
+
+    // LDS: q [H][Di] (rows padded by 16 bytes), per-wavefront head maxima and
+    // sums [H][kWaves] x 2, the combined head maxima and reciprocal sums
+    // [H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4)
+    unsigned char *q_lds = smem;
+    float *wmax = reinterpret_cast<float *>(smem + H * rowb);
+    float *wsum = wmax + H * kWaves;
+    float *hmax = wsum + H * kWaves;
+    float *hrz = hmax + H;
+    float *Q = hrz + H;
+    float *P = Q + (a.Bcap + 3) / 4 * 4;
+
+    float *scores = a.scores + n * a.Jcap;
+    int32_t *out_idx = a.indices + n * a.topk;
+    const int nb = sequence_blocks(a, n, scores, out_idx, tid);
+    if (nb < 0)
+        return;
+    const int sel = (int)a.sel, cmpr = (int)a.cmp;
+    const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
+
+    if (nb > 0) {
+        const uint16_t *qn = a.query + n * (int64_t)H * Di;
+        const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
+        const int fr = lane & 15, g = lane >> 4;         // fragment row / column, lane group
+        const float scale2 = a.scale * 1.44269504088896341f;
+
+        // q -> registers (issued first), the key fragments of column tiles
+        // wave + 8 jl (rows past the sequence clamped to its last block: they
+        // are computed, never used), then q -> LDS
+        uint4 qs[QPT];
+#pragma unroll
+        for (int b = 0; b < QPT; ++b) {
+            const int c = min(tid + b * kThreads, QP - 1);
+            qs[b] = *reinterpret_cast<const uint4 *>(qn + (c / pieces) * Di + (c % pieces) * 8);
+        }
+        bf16x8 kf[JWM][DK];
+#pragma unroll
+        for (int jl = 0; jl < JWM; ++jl) {
+            const int row = min(16 * (wave + kWaves * jl) + fr, nb - 1);
+#pragma unroll
+            for (int u = 0; u < DK; ++u)
+                kf[jl][u] = *reinterpret_cast<const bf16x8 *>(kn + (int64_t)row * Di + 32 * u + 8 * g);
+        }
+#pragma unroll
+        for (int b = 0; b < QPT; ++b) {
+            const int c = min(tid + b * kThreads, QP - 1);
+            *reinterpret_cast<uint4 *>(q_lds + (c / pieces) * rowb + (c % pieces) * 16) = qs[b];
+        }
+        __syncthreads();
+
+        // scores (log2 units): e[jl][ht] = the tile of head tile ht and column
+        // tile wave + 8 jl
+        f32x4 e[JWM][HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            bf16x8 qf[DK];
+#pragma unroll
+            for (int u = 0; u < DK; ++u)
+                qf[u] = *reinterpret_cast<const bf16x8 *>(q_lds + (16 * ht + fr) * rowb + (32 * u + 8 * g) * 2);
+#pragma unroll
+            for (int jl = 0; jl < JWM; ++jl) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int u = 0; u < DK; ++u)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[u], kf[jl][u], acc, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    e[jl][ht][q] = scale2 * acc[q];
+            }
+        }
+        bool ok[JWM];                                   // this lane's column exists
+#pragma unroll
+        for (int jl = 0; jl < JWM; ++jl)
+            ok[jl] = 16 * (wave + kWaves * jl) + fr < nb;
+
+        // head maxima: over this wavefront's columns, then over the wavefronts
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int jl = 0; jl < JWM; ++jl)
+                    m = ok[jl] ? fmaxf(m, e[jl][ht][q]) : m;
+                m = row_max16(m);
+                if (fr == 0)
+                    wmax[(16 * ht + 4 * g + q) * kWaves + wave] = m;
+            }
+        __syncthreads();
+        for (int h = tid; h < H; h += kThreads) {
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(wmax + h * kWaves);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(wmax + h * kWaves + 4);
+            hmax[h] = fmaxf(fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])),
+                            fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])));
+        }
+        __syncthreads();
+
+        // exp2(s - max) in place; head sums in the same two steps
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float z = 0.0f;
+#pragma unroll
+                for (int jl = 0; jl < JWM; ++jl) {
+                    e[jl][ht][q] = ok[jl] ? exp2f(e[jl][ht][q] - m[q]) : 0.0f;
+                    z += e[jl][ht][q];
+                }
+                z = row_sum16(z);
+                if (fr == 0)
+                    wsum[(16 * ht + 4 * g + q) * kWaves + wave] = z;
+            }
+        }
+        __syncthreads();
+        for (int h = tid; h < H; h += kThreads) {
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(wsum + h * kWaves);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(wsum + h * kWaves + 4);
+            hrz[h] = 1.0f / (lo[0] + lo[1] + lo[2] + lo[3] + hi[0] + hi[1] + hi[2] + hi[3]);
+        }
+        __syncthreads();
+
+        // Q[block] = sum over heads of exp2(s - max) / sum
+#pragma unroll
+        for (int jl = 0; jl < JWM; ++jl) {
+            float qv = 0.0f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const f32x4 rz = *reinterpret_cast<const f32x4 *>(hrz + 16 * ht + 4 * g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    qv += e[jl][ht][q] * rz[q];
+            }
+            // the 4 lane groups hold the same block for different heads
+            qv += __shfl_xor(qv, 16, 64);
+            qv += __shfl_xor(qv, 32, 64);
+            if (g == 0 && ok[jl])
+                Q[16 * (wave + kWaves * jl) + fr] = qv;
+        }
+    }
+    __syncthreads();
+    pool_and_select(a, Q, P, nb, J, scores, out_idx, tid, lane, wave);
+}
+
 }  // namespace
 
 int64_t qsa_select_lds_bytes(int64_t H, int64_t Di, int64_t Bcap, int64_t Jcap, int64_t chunk)
 {
-    return (H + chunk) * (Di * 2 + 16) + 4 * (H * (chunk + 4) + 2 * H + Bcap + Jcap);
+    return (H + chunk) * (Di * 2 + 16) +
+           4 * ((2 * kWaves + 2) * H + 2 * (chunk / 16) * H + (Bcap + 3) / 4 * 4 + (Jcap + 3) / 4 * 4);
+}
+
+namespace {
+
+typedef void (*SelectKernel)(QsaSelectArgs);
+
+// the compiled fast-path shapes: Di / 32 in {2, 4}, H / 16 in {1, 2, 4, 8},
+// column tiles per wavefront in {1, 2, 4} (16 H / 16 x tiles at most)
+#define KVRC_SEL_FAST(DK, HT, JWM)                 \
+    if (dk == (DK) && ht == (HT) && jwm == (JWM)) \
+        return qsa_select_fast_kernel<DK, HT, JWM>;
+#define KVRC_SEL_FAST_HT(DK, HT) KVRC_SEL_FAST(DK, HT, 1) KVRC_SEL_FAST(DK, HT, 2) KVRC_SEL_FAST(DK, HT, 4)
+
+SelectKernel fast_select_kernel(int64_t Di, int64_t H, int64_t Bcap)
+{
+    if (Di % 32 || H % 16)
+        return nullptr;
+    const int64_t dk = Di / 32, ht = H / 16;
+    const int64_t per_wave = ((Bcap + 15) / 16 + kWaves - 1) / kWaves;
+    const int64_t jwm = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 0;
+    KVRC_SEL_FAST_HT(2, 1) KVRC_SEL_FAST_HT(2, 2) KVRC_SEL_FAST_HT(2, 4)
+    KVRC_SEL_FAST(2, 8, 1) KVRC_SEL_FAST(2, 8, 2)
+    KVRC_SEL_FAST_HT(4, 1) KVRC_SEL_FAST_HT(4, 2) KVRC_SEL_FAST_HT(4, 4)
+    KVRC_SEL_FAST(4, 8, 1) KVRC_SEL_FAST(4, 8, 2)
+    return nullptr;
+}
+#undef KVRC_SEL_FAST_HT
+#undef KVRC_SEL_FAST
+
+}  // namespace
+
+bool qsa_select_fast_path(int64_t H, int64_t Di, int64_t Bcap)
+{
+    return fast_select_kernel(Di, H, Bcap) != nullptr;
 }
 
 hipError_t launch_qsa_select(const QsaSelectArgs &a, hipStream_t stream)
 {
-    const int64_t lds = qsa_select_lds_bytes(a.H, a.Di, a.Bcap, a.Jcap, a.chunk);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qsa_select_kernel),
+    SelectKernel k = fast_select_kernel(a.Di, a.H, a.Bcap);
+    int64_t lds;
+    if (k) {
+        lds = a.H * (a.Di * 2 + 16) + 4 * ((2 * kWaves + 2) * a.H + (a.Bcap + 3) / 4 * 4 + (a.Jcap + 3) / 4 * 4);
+    } else {
+        k = qsa_select_kernel;
+        lds = qsa_select_lds_bytes(a.H, a.Di, a.Bcap, a.Jcap, a.chunk);
+    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(qsa_select_kernel, dim3((uint32_t)a.N), dim3(kThreads), (uint32_t)lds,
-                       stream, a);
+    hipLaunchKernelGGL(k, dim3((uint32_t)a.N), dim3(kThreads), (uint32_t)lds, stream, a);
     return hipGetLastError();
 }
 

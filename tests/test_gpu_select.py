@@ -132,9 +132,14 @@ def test_select_named_workload_full_size():
     say(f"[select] median relative score error {med:.2e}")
 
 
+# Both kernels: Di in {64, 128}, H in {16, 32, 64, 128} and Bcap <= 512 (up to
+# 128 Bcap for H = 128) run on the compile-time fast path, the rest (Di 32,
+# 96, 256, H 48, Bcap 1000, and keys beyond one LDS chunk) on the general one.
 @pytest.mark.parametrize("N,H,Di,Bcap,kbs,sel,cmp,topk", [
     (3, 16, 32, 5, 16, 1, 1, 2), (4, 32, 64, 40, 32, 2, 1, 8), (5, 64, 128, 100, 64, 3, 2, 10),
     (2, 128, 256, 300, 64, 4, 1, 16), (3, 16, 128, 1000, 16, 2, 2, 64), (2, 48, 96, 17, 8, 1, 3, 40),
+    (2, 128, 128, 256, 64, 2, 1, 16), (3, 16, 64, 512, 16, 1, 1, 32), (2, 64, 128, 500, 64, 2, 2, 24),
+    (2, 128, 64, 200, 32, 1, 4, 12), (4, 32, 128, 129, 16, 1, 1, 130),
 ])
 def test_select_shapes(N, H, Di, Bcap, kbs, sel, cmp, topk):
     say(f"[select] N={N} H={H} Di={Di} Bcap={Bcap} kbs={kbs} sel={sel} cmp={cmp} topk={topk}")
@@ -203,3 +208,32 @@ def test_select_deterministic():
     b = run_select_gpu(case)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_select_many_candidates_argmax_path():
+    """More than 2048 selection blocks: the one-wavefront arg-max top-k, over
+    keys staged in several chunks."""
+    say("[select] J > 2048, several key chunks")
+    case = gen.qsa_select_case(715, N=2, H=16, Di=32, Bcap=2100, kbs=8, sel_ratio=1, cmp_ratio=1,
+                               topk=24, kl_lo=2060 * 8, kl_hi=2100 * 8 + 1)
+    compare_select(case, *run_select_gpu(case))
+
+
+def test_select_nan_scores_are_never_selected():
+    """A NaN inside a sequence's key rows makes every score of that sequence
+    NaN (the softmax sums take it in): no block is selected, every index is
+    -1; the other sequences are unaffected."""
+    case = gen.qsa_select_case(716, N=3, H=32, Di=64, Bcap=40, kbs=16, sel_ratio=2, cmp_ratio=1,
+                               topk=8, kl_lo=30 * 16, kl_hi=40 * 16 + 1)
+    keys = case["block_keys"].copy()
+    keys[1, 3, 5] = gen.BF16_NAN
+    case = dict(case, block_keys=keys)
+    scores, idx = run_select_gpu(case)
+    nb = int(case["key_length"][1]) // 16
+    J = S.num_selection_blocks(nb, 2, 1)
+    assert np.all(np.isnan(scores[1, :J])) and np.all(scores[1, J:] == 0)
+    assert np.all(idx[1] == -1)
+    rest = [0, 2]
+    ok = dict(case, N=2, query=case["query"][rest], block_keys=keys[rest],
+              key_length=case["key_length"][rest])
+    compare_select(ok, scores[rest], idx[rest])
