@@ -54,7 +54,7 @@ KERNEL_SOURCES = {
     "sel": ["latent_attention_kv_amd/csrc/qsa_select.hip"] + _COMMON_SOURCES,
 }
 KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel", "mla": "mla_kv_head_kernel",
-               "sel": "qsa_select_kernel"}
+               "sel": "qsa_select"}
 
 WORKLOAD_TEXT = {
     "prefill_paged": "paged prefill: B=8, S=4096 (32768 tokens), kv [8,1,4096,576] bf16 "
