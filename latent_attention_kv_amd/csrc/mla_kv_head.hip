@@ -20,12 +20,13 @@
 //   * 8 wavefronts = 2 (rows) x 4 (columns); wavefront (wm, wn) accumulates
 //     rows 64 wm .. +64 and columns 144 wn .. +144 as 4 x 9 tiles of 16 x 16
 //     (144 accumulator registers, two wavefronts per SIMD);
-//   * K advances 32 at a time through 3 LDS stages (x slice 128 x 32, W slice
-//     576 x 32, 44 KiB), filled by direct global -> LDS loads
-//     (global_load_lds_dwordx4: no staging registers, no LDS store
-//     instructions) two steps ahead of the MFMAs; each wavefront waits only
-//     for its own loads of the step about to be used, then one barrier
-//     publishes them;
+//   * K advances 32 at a time; the slices pass through two LDS rings filled
+//     by direct global -> LDS loads (global_load_lds_dwordx4: no staging
+//     registers, no LDS store instructions): W (576 x 32, 36 KiB) in 3
+//     stages two steps ahead of the MFMAs, x (128 x 32, 8 KiB) in 4 stages
+//     three steps ahead, as x streams from HBM while W is shared through L2;
+//     each wavefront waits only for its own loads of the step about to be
+//     used, then one barrier publishes them;
 //   * within a step the next B fragment read and one load of step + 2 are
 //     issued between groups of 4 MFMAs, so their issue overlaps the matrix
 //     pipe instead of preceding it;
@@ -36,8 +37,8 @@
 //     row across lanes and wavefronts; rows are normalised and rotated in
 //     registers, staged as bf16 in LDS with 8-byte writes and scattered with
 //     16-byte stores per cache row.
-// Measured on MI355X for T = 32768, He = 7168: about 350 us per call
-// (770 TFLOP/s); the operand stream through the texture path, not the
+// Measured on MI355X for T = 32768, He = 7168: about 294 us per call
+// (920 TFLOP/s); the operand stream through the texture path, not the
 // matrix cores, bounds this tile shape.
 #include "kvrc_launch.hpp"
 
@@ -60,12 +61,19 @@ constexpr int kKt = (int)kMlaHeadK;        // K per stage (one MFMA K)
 constexpr int kRowBytes = kKt * 2;         // 64
 constexpr int kStageA = kRows * kRowBytes; // 8192
 constexpr int kStageB = kCols * kRowBytes; // 36864
-constexpr int kStage = kStageA + kStageB;  // 45056
-constexpr int kStages = 3;
-constexpr int kBlocks = kStage / 1024;     // 1 KiB blocks per stage (one load instruction each)
-// the 44 blocks of a stage: wavefronts 0-3 load 6 each, wavefronts 4-7 load 5
-static_assert(4 * 6 + 4 * 5 == kBlocks, "block split");
-constexpr int kMaxBlocksPerWave = 6;
+// Two LDS rings: W slices (3 stages, loaded 2 steps ahead) and x slices (4
+// stages, loaded 3 steps ahead: x streams from HBM while W is mostly served
+// by L2; measured on MI355X, leads of 2, 3, 4 and 5 steps for x gave 343,
+// 336, 342 and 347 us per call of 32768 x 7168).
+constexpr int kWStages = 3, kWLead = kWStages - 1;
+constexpr int kXStages = 4, kXLead = kXStages - 1;
+constexpr int kXRing = kWStages * kStageB;             // offset of the x ring
+constexpr int kPipeBytes = kXRing + kXStages * kStageA; // 143360
+// the 8 x blocks and 36 W blocks (1 KiB each, one load instruction) of a
+// step: wavefront w loads x block w, then W blocks (5 each for w < 4, 4 for
+// the others)
+static_assert(kStageA / 1024 == kWaves && 4 * 5 + 4 * 4 == kStageB / 1024, "block split");
+constexpr int kMaxWBlocks = 5;
 constexpr int kMt = 4, kNt = 9;            // 16 x 16 tiles per wavefront
 constexpr int kWaveCols = kNt * 16;        // 144
 // epilogue staging: bf16 rows of 512 (+8 pad) and 64 (+8 pad) values, then
@@ -74,7 +82,7 @@ constexpr int kCkvLds = (kNorm + 8) * 2;   // 1040 bytes per row
 constexpr int kKLds = (kRope + 8) * 2;     // 144 bytes per row
 constexpr int kRedOff = kRows * (kCkvLds + kKLds);
 constexpr int kEpiBytes = kRedOff + 4 * kRows * 4;
-constexpr int kLdsBytes = kStages * kStage > kEpiBytes ? kStages * kStage : kEpiBytes;
+constexpr int kLdsBytes = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the unused counters at their maxima).
@@ -122,41 +130,33 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int wm = wave & 1, wn = wave >> 1;
-    const int nblk = wave < 4 ? 6 : 5;
-    const int blk0 = wave < 4 ? 6 * wave : 24 + 5 * (wave - 4);
+    const int nw = wave < 4 ? 5 : 4;                     // W blocks of this wavefront
+    const int wb0 = wave < 4 ? 5 * wave : 20 + 4 * (wave - 4);
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int64_t T = a.T, He = a.He;
 
     // ---- direct global -> LDS loads ---------------------------------------
-    // Wavefront w fills nblk 1 KiB blocks from blk0 on in each stage;
-    // block b < 8 holds x rows 16 b .. +16, block b >= 8 W rows 16 (b - 8) ..
-    // +16. Lane l writes byte 16 l of the block: row 16 b' + l / 4, slot l % 4,
-    // i.e. piece (l % 4) ^ swz(row) of that row. Rows past T read row T - 1
-    // (valid memory; their results are dropped).
-    const uint16_t *src[kMaxBlocksPerWave];
-#pragma unroll
-    for (int i = 0; i < kMaxBlocksPerWave; ++i) {
-        const int b = blk0 + (i < nblk ? i : 0);
-        const int r = (b < kStageA / 1024 ? b : b - kStageA / 1024) * 16 + (lane >> 2);
-        const int piece = (lane & 3) ^ swz(r);
-        if (b < kStageA / 1024) {
-            int64_t t = row0 + r;
-            t = t < T ? t : T - 1;
-            src[i] = a.x + t * He + piece * 8;
-        } else {
-            src[i] = a.w + (int64_t)r * He + piece * 8;
-        }
+    // A 1 KiB block holds 16 rows of 64 bytes (one K step); lane l writes
+    // byte 16 l: row 16 b + l / 4, slot l % 4, i.e. piece (l % 4) ^ swz(row)
+    // of that row. x block w = token rows 16 w .. +16 (rows past T read row
+    // T - 1: valid memory, results dropped); W block b = W rows 16 b .. +16.
+    const uint16_t *xsrc;
+    {
+        const int r = 16 * wave + (lane >> 2);
+        int64_t t = row0 + r;
+        t = t < T ? t : T - 1;
+        xsrc = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
     }
-    auto issue = [&](int stage, int64_t k0) {
-        unsigned char *base = smem + stage * kStage + blk0 * 1024;
+    const uint16_t *wsrc[kMaxWBlocks];
 #pragma unroll
-        for (int i = 0; i < 5; ++i)
-            __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void *)(base + i * 1024), 16, 0, 0);
-        if (nblk == 6)
-            __builtin_amdgcn_global_load_lds(src[5] + k0, (lds_void *)(base + 5 * 1024), 16, 0, 0);
-    };
+    for (int i = 0; i < kMaxWBlocks; ++i) {
+        const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
+        wsrc[i] = a.w + (int64_t)r * He + ((lane & 3) ^ swz(r)) * 8;
+    }
+    unsigned char *const xdst = smem + kXRing + wave * 1024;     // + stage * kStageA
+    unsigned char *const wdst = smem + wb0 * 1024;               // + stage * kStageB + i KiB
 
     f32x4 acc[kMt][kNt];
 #pragma unroll
@@ -169,42 +169,65 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     // (tile row offsets are multiples of 16, so swz of the row is swz(l % 16))
     const int fr = lane & 15, fc = lane >> 4;
     const int a_off = (64 * wm + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
-    const int b_off = kStageA + (kWaveCols * wn + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
+    const int b_off = (kWaveCols * wn + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
 
-    const int64_t nk = He / kKt;
-    issue(0, 0);
-    if (nk > 1)
-        issue(1, kKt);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        // this wavefront's loads of step kt are done (those of kt + 1 may be
-        // in flight); the barrier publishes every wavefront's, and tells that
-        // all are past step kt - 1, whose stage is refilled next
+    // prologue: x of steps 0 .. kXLead - 1, then W of steps 0 .. kWLead - 1
+    // (this order matters to the waits below)
+    const int nk = (int)(He / kKt);
+    for (int st = 0; st < kXLead && st < nk; ++st)
+        __builtin_amdgcn_global_load_lds(xsrc + st * kKt, (lds_void *)(xdst + st * kStageA), 16, 0, 0);
+    for (int st = 0; st < kWLead && st < nk; ++st) {
+#pragma unroll
+        for (int i = 0; i < kMaxWBlocks; ++i)
+            if (i < nw)
+                __builtin_amdgcn_global_load_lds(wsrc[i] + st * kKt,
+                                                 (lds_void *)(wdst + st * kStageB + i * 1024), 16, 0, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        // This wavefront's loads complete in issue order. Its W blocks of
+        // step kt are its last loads issued before those of step kt - 1
+        // (x of step kt went out kXLead - kWLead steps earlier, before
+        // them), so allowing exactly the
+        // loads of step kt - 1 to stay in flight leaves both x and W of step
+        // kt in LDS; the barrier publishes every wavefront's and tells that
+        // all are past step kt - 1, whose stages are refilled next.
         asm volatile("" ::: "memory");
-        if (kt + 1 < nk) {
-            if (nblk == 6)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
-        } else
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        const int pending = kt == 0 ? (nk > 1 ? nw : 0)
+                                    : (kt + kXLead - 1 < nk ? 1 : 0) + (kt + kWLead - 1 < nk ? nw : 0);
+        switch (pending) {
+        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(6)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(5)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1)); break;
+        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+        }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const bool more = kt + 2 < nk;
-        unsigned char *dbase = smem + (int)((kt + 2) % kStages) * kStage + blk0 * 1024;
-        const int64_t k0 = (kt + 2) * kKt;
-        const unsigned char *base = smem + (int)(kt % kStages) * kStage;
+        const int sx = kt + kXLead, sw = kt + kWLead;    // steps loaded during this one
+        const bool more_x = sx < nk, more_w = sw < nk;
+        unsigned char *const xd = xdst + (sx % kXStages) * kStageA;
+        unsigned char *const wd = wdst + (sw % kWStages) * kStageB;
+        const unsigned char *xbase = smem + kXRing + (kt % kXStages) * kStageA;
+        const unsigned char *wbase = smem + (kt % kWStages) * kStageB;
         bf16x8 af[kMt], bf[2];
 #pragma unroll
         for (int m = 0; m < kMt; ++m)
-            af[m] = *reinterpret_cast<const bf16x8 *>(base + a_off + m * 16 * kRowBytes);
-        bf[0] = *reinterpret_cast<const bf16x8 *>(base + b_off);
+            af[m] = *reinterpret_cast<const bf16x8 *>(xbase + a_off + m * 16 * kRowBytes);
+        bf[0] = *reinterpret_cast<const bf16x8 *>(wbase + b_off);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
             if (n + 1 < kNt)
-                bf[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(base + b_off + (n + 1) * 16 * kRowBytes);
-            if (n < 6 && more && (n < 5 || nblk == 6))
-                __builtin_amdgcn_global_load_lds(src[n] + k0, (lds_void *)(dbase + n * 1024), 16, 0, 0);
+                bf[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(wbase + b_off + (n + 1) * 16 * kRowBytes);
+            // one load between MFMA groups: x first, then the W blocks
+            if (n == 0) {
+                if (more_x)
+                    __builtin_amdgcn_global_load_lds(xsrc + sx * kKt, (lds_void *)xd, 16, 0, 0);
+            } else if (n <= kMaxWBlocks) {
+                if (more_w && n - 1 < nw)
+                    __builtin_amdgcn_global_load_lds(wsrc[n - 1] + sw * kKt,
+                                                     (lds_void *)(wd + (n - 1) * 1024), 16, 0, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < kMt; ++m)
