@@ -33,6 +33,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -86,13 +87,25 @@ def kernel_family(workload: str) -> str:
     return {"qsa": "qsa", "mla_kv_head": "mla", "qsa_select": "sel"}.get(workload, "kvrc")
 
 
+def _code_only(rel: str, text: str) -> str:
+    """The source without comments and blank lines (C++: // and /* */;
+    Python: whole-line # comments), so that editing a comment does not
+    disown counters taken on the same code."""
+    if rel.endswith(".py"):
+        lines = [ln.rstrip() for ln in text.splitlines() if not ln.lstrip().startswith("#")]
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def source_hash(workload: str) -> str:
-    """Hash of the sources that build the workload's kernel (counters taken
-    on another version of them are not reported)."""
+    """Hash of the code that builds the workload's kernel (counters taken on
+    another version of it are not reported)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel_family(workload)]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(rel, f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -449,7 +462,7 @@ def main(argv=None):
     if args.ingest_profile:
         return ingest_profile(args)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence with no exchange; no multi-GPU run exists)",
               file=sys.stderr)
         return 2
