@@ -278,6 +278,194 @@ __global__ __launch_bounds__(kThreads) void qsa_prepare_kernel(QsaArgs a, int64_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Di = 128 and blocks of at most 64 rows: one wavefront per (sequence, new
+// block), lane l owning the dimension pair (2 l, 2 l + 1). Every row of the
+// block is one 256-byte load instruction of the wavefront, all issued before
+// the first is added, and each lane adds its pair down the rows in token
+// order as the rows arrive: no LDS and no barrier. The norm's chunk c (dims
+// 8 c .. 8 c + 7) lies on lanes 4 c .. 4 c + 3; its square sum is taken in
+// element order, then the 16 chunk partials are folded in halves (c + 8,
+// + 4, + 2, + 1): the same operations in the same order as the general
+// kernel, so the keys are bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int kWaveDi = 128;
+constexpr int kWaveMaxRows = 64;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+__global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t nb_max)
+{
+    constexpr int64_t Di = kWaveDi;
+    constexpr int kPairs = kWaveDi / 2;              // = 64 lanes
+    const int lane = threadIdx.x;
+    const uint32_t per = (uint32_t)(nb_max + 1);
+    const int64_t n = blockIdx.x / per;
+    const int64_t j = blockIdx.x % per;
+    const int64_t K = a.key_length[a.klc == 1 ? 0 : n];
+    const int64_t kbs = a.kbs, L = a.L;
+    if (K < L || K / kbs > a.Bcap) {
+        if (j == 0 && lane == 0 && a.err)
+            atomicAdd(a.err, 1);
+        return;
+    }
+    const int64_t P = K - L;
+    const int64_t r = P % kbs;
+    const int64_t Dr = a.rope_cos ? a.Dr : 0;
+
+    if (j == nb_max) {
+        // ---- carry state: tokens [t1, K) of the incomplete block ----------
+        // 16 pieces of 16 bytes per row; 8 per lane in flight; indices past
+        // the end repeat the last piece (load and store), so every load and
+        // store is unconditional
+        const int64_t r2 = K % kbs, t1 = K - r2;
+        const int total = (int)r2 * 16;
+        for (int e0 = lane; e0 < total; e0 += 64 * 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = min(e0 + 64 * k, total - 1);
+                const int64_t tau = t1 + e / 16;
+                const uint16_t *src = tau < P
+                    ? a.past_raw + (n * (kbs - 1) + (tau - (P - r))) * Di
+                    : a.raw + (n * L + (tau - P)) * Di;
+                v[k] = *reinterpret_cast<const u32x4 *>(src + 8 * (e % 16));
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = min(e0 + 64 * k, total - 1);
+                *reinterpret_cast<u32x4 *>(a.next_raw + (n * (kbs - 1) + e / 16) * Di + 8 * (e % 16)) = v[k];
+            }
+        }
+        if (Dr && r2 > 0) {
+            for (int64_t d = lane; d < Dr; d += 64) {
+                float c, sn;
+                if (t1 < P) {
+                    c = a.past_rope[n * 2 * Dr + d];
+                    sn = a.past_rope[n * 2 * Dr + Dr + d];
+                } else {
+                    c = a.rope_cos[(n * L + (t1 - P)) * Dr + d];
+                    sn = a.rope_sin[(n * L + (t1 - P)) * Dr + d];
+                }
+                a.next_rope[n * 2 * Dr + d] = c;
+                a.next_rope[n * 2 * Dr + Dr + d] = sn;
+            }
+        }
+        return;
+    }
+
+    const int64_t b = P / kbs + j;
+    if (b >= K / kbs)
+        return;
+    const int64_t tau0 = b * kbs;                       // first token of the block
+    const int64_t np = tau0 < P ? P - tau0 : 0;         // rows taken from the carried state
+    const uint32_t *past = reinterpret_cast<const uint32_t *>(a.past_raw + n * (kbs - 1) * Di) + lane;
+    const uint32_t *rawn = reinterpret_cast<const uint32_t *>(a.raw + n * L * Di) + lane;
+
+    // ---- every row of the block in flight at once (rows past kbs repeat the
+    // last row: the loads stay unconditional and are added as +0 below) ----
+    uint32_t w[kWaveMaxRows];
+#pragma unroll
+    for (int i = 0; i < kWaveMaxRows; ++i) {
+        const int64_t ii = i < kbs ? i : kbs - 1;
+        const uint32_t *src = ii < np ? past + ii * kPairs : rawn + (tau0 + ii - P) * kPairs;
+        w[i] = stream_load<uint32_t>(src);
+    }
+    // this lane's outputs: dims d0 = 2 lane, d1 = d0 + 1; the RoPE covers
+    // dims [base, 128), output o = d - base
+    const int64_t base = Di - Dr;
+    const int d0 = 2 * lane;
+    const bool rot = Dr && d0 >= base;
+    float c0 = 0.0f, c1 = 0.0f, s0 = 0.0f, s1 = 0.0f;
+    if (rot) {
+        const int64_t o0 = d0 - base;
+        const float *cr, *sr;
+        if (tau0 < P) {
+            cr = a.past_rope + n * 2 * Dr;
+            sr = cr + Dr;
+        } else {
+            cr = a.rope_cos + (n * L + (tau0 - P)) * Dr;
+            sr = a.rope_sin + (n * L + (tau0 - P)) * Dr;
+        }
+        c0 = cr[o0]; c1 = cr[o0 + 1];
+        s0 = sr[o0]; s1 = sr[o0 + 1];
+    }
+    const uint32_t gw = a.weight ? *reinterpret_cast<const uint32_t *>(a.weight + d0) : 0u;
+
+    // ---- block mean: float32 sum down the rows in token order -------------
+    // (a sum that starts at +0 is never -0, so the +0 terms past kbs leave it
+    // unchanged)
+    float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaveMaxRows; ++i) {
+        const uint32_t v = i < kbs ? w[i] : 0u;
+        sum0 = sum0 + bf16_lo(v);
+        sum1 = sum1 + bf16_hi(v);
+    }
+    const float fk = (float)kbs;
+    const float m0 = sum0 / fk, m1 = sum1 / fk;
+
+    // ---- RMS normalisation ------------------------------------------------
+    float z0 = m0, z1 = m1;
+    if (a.weight) {
+        // chunk lane / 4: its 8 elements from the 4 lanes of the quad
+        float x[8];
+        x[0] = dpp_f<0x00>(m0); x[1] = dpp_f<0x00>(m1);     // quad_perm [0,0,0,0]
+        x[2] = dpp_f<0x55>(m0); x[3] = dpp_f<0x55>(m1);     // [1,1,1,1]
+        x[4] = dpp_f<0xAA>(m0); x[5] = dpp_f<0xAA>(m1);     // [2,2,2,2]
+        x[6] = dpp_f<0xFF>(m0); x[7] = dpp_f<0xFF>(m1);     // [3,3,3,3]
+        const float part = chunk_sumsq(x, 0.0f);
+        float pc[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            pc[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), 4 * c));
+#pragma unroll
+        for (int wdt = 16; wdt > 1; wdt /= 2)
+#pragma unroll
+            for (int c = 0; c < wdt / 2; ++c)
+                pc[c] = pc[c] + pc[c + wdt / 2];
+        const float rms = sqrtf(pc[0] / (float)Di + a.eps);
+        z0 = (m0 / rms) * bf16_lo(gw);
+        z1 = (m1 / rms) * bf16_hi(gw);
+    }
+
+    // ---- RoPE of the trailing Dr dims: output o takes the pair (2 i, 2 i + 1)
+    // of the rotated part, i = o mod Dr / 2, held by lane base / 2 + i -------
+    float y0 = z0, y1 = z1;
+    if (Dr) {
+        const int64_t h = Dr / 2;
+        const int64_t o0 = d0 - base, o1 = o0 + 1;
+        const bool up0 = o0 >= h, up1 = o1 >= h;
+        const int src0 = rot ? (int)(base / 2 + (up0 ? o0 - h : o0)) : lane;
+        const int src1 = rot ? (int)(base / 2 + (up1 ? o1 - h : o1)) : lane;
+        const float xe0 = __shfl(z0, src0, 64), xo0 = __shfl(z1, src0, 64);
+        const float xe1 = __shfl(z0, src1, 64), xo1 = __shfl(z1, src1, 64);
+        if (rot) {
+            const float p10 = (up0 ? xo0 : xe0) * c0, p20 = (up0 ? xe0 : xo0) * s0;
+            const float p11 = (up1 ? xo1 : xe1) * c1, p21 = (up1 ? xe1 : xo1) * s1;
+            y0 = up0 ? p10 + p20 : p10 - p20;
+            y1 = up1 ? p11 + p21 : p11 - p21;
+        }
+    }
+
+    // ---- store: the wavefront writes the 256-byte key -----------------------
+    uint32_t *dst = reinterpret_cast<uint32_t *>(a.block_keys + (n * a.Bcap + b) * Di);
+    dst[lane] = pack_bf16x2(y0, y1);
+}
+
+hipError_t launch_wave(const QsaArgs &a, hipStream_t stream)
+{
+    const int64_t nb_max = (a.kbs - 1 + a.L) / a.kbs;
+    const int64_t grid = a.N * (nb_max + 1);
+    hipLaunchKernelGGL(qsa_prepare_wave_kernel, dim3((uint32_t)grid), dim3(64), 0, stream, a,
+                       nb_max);
+    return hipGetLastError();
+}
+
 template <int PPT>
 hipError_t launch_ppt(const QsaArgs &a, hipStream_t stream)
 {
@@ -295,6 +483,8 @@ hipError_t launch_ppt(const QsaArgs &a, hipStream_t stream)
 
 hipError_t launch_qsa_prepare(const QsaArgs &a, hipStream_t stream)
 {
+    if (a.Di == kWaveDi && a.kbs <= kWaveMaxRows)
+        return launch_wave(a, stream);
     const int64_t pairs = a.Di / 2;
     if (pairs <= kThreads) return launch_ppt<1>(a, stream);
     if (pairs <= 2 * kThreads) return launch_ppt<2>(a, stream);

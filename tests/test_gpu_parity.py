@@ -336,9 +336,12 @@ def test_qsa_named_workload_bit_exact():
     compare_qsa(run_qsa_gpu(case), oracle.run_qsa_case(case), exact=True)
 
 
+# Di = 128 with blocks of at most 64 rows runs on the one-wavefront kernel,
+# every other shape on the general one.
 @pytest.mark.parametrize("N,L,Di,Dr,kbs", [
     (4, 100, 128, 64, 16), (3, 7, 64, 16, 16), (5, 1, 32, 8, 4), (2, 300, 1024, 128, 24),
     (6, 65, 8, 2, 3), (1, 2048, 256, 256, 64), (3, 50, 136, 40, 2),
+    (3, 130, 128, 128, 64), (2, 70, 128, 2, 33), (2, 90, 128, 64, 65),
 ])
 @pytest.mark.parametrize("variant", ["full", "no_norm", "no_rope", "plain", "broadcast"])
 def test_qsa_shapes_and_features(N, L, Di, Dr, kbs, variant):
