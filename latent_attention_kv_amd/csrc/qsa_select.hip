@@ -159,14 +159,16 @@ __device__ __forceinline__ int sequence_blocks(const QsaSelectArgs &a, int64_t n
 }
 
 // Pooling of Q [nb] into the J selection-block scores, and the top-k. Q is
-// complete in LDS (the caller's barrier); P [Jcap rounded up to 4] is LDS
-// scratch.
+// complete in LDS (the caller's barrier). LDS scratch: P [Jcap rounded up to
+// 4] (float scores), and for the rank top-k K [up to kRankMax] (64-bit keys)
+// and R [up to kRankMax] (ranks).
 __device__ __forceinline__ void pool_and_select(const QsaSelectArgs &a, const float *Q, float *P,
-                                                int nb, int J, float *scores, int32_t *out_idx,
-                                                int tid, int lane, int wave)
+                                                uint64_t *K, int *R, int nb, int J, float *scores,
+                                                int32_t *out_idx, int tid, int lane, int wave)
 {
     const int sel = (int)a.sel, cmpr = (int)a.cmp, Jcap = (int)a.Jcap;
-    const int Jcap4 = (Jcap + 3) / 4 * 4;
+    const int Jcap4 = (Jcap + 3) / 4 * 4, J4 = (J + 3) / 4 * 4;
+    const bool by_rank = J <= kRankMax;
     for (int j = tid; j < Jcap4; j += kThreads) {
         float v = 0.0f;
         if (j < J) {
@@ -181,27 +183,44 @@ __device__ __forceinline__ void pool_and_select(const QsaSelectArgs &a, const fl
             scores[j] = v;
         // -1 marks what is never selected: blocks past J and NaN scores
         P[j] = j < J && v == v ? v : -1.0f;
+        if (by_rank && j < J4) {
+            // one 64-bit key orders the blocks: score (its bits + 1; scores
+            // are >= +0) above, 2^32 - 1 - j below (equal scores: the lower
+            // index first); NaN scores and the padding past J get 0 / lower
+            // halves only, below every real score
+            const uint32_t hi = j < J && v == v ? (v > 0.0f ? __float_as_uint(v) : 0u) + 1u : 0u;
+            K[j] = j < J ? ((uint64_t)hi << 32) | (0xFFFFFFFFu - (uint32_t)j) : 0ull;
+            R[j] = 0;
+        }
     }
     __syncthreads();
-    if (J <= kRankMax) {
-        // ---- top-k by rank: position of block j = the number of blocks ahead
-        // of it; the ranks of the J blocks are 0 .. J-1, each once. A NaN
-        // score (-1) ranks after every real one and leaves its position -1;
-        // the entries from J up to the next multiple of 4 are -1 with larger
-        // indices, so they are never ahead of a block.
-        const int J4 = (J + 3) / 4 * 4;
-        for (int j = tid; j < J; j += kThreads) {
-            const float v = P[j];
-            int rank = 0;
+
+    if (by_rank) {
+        // ---- top-k by rank: the position of block j is the number of keys
+        // above its own (ranks 0 .. J-1, each once). The count for each block
+        // is split into S segments of the key list, so that the work spreads
+        // over the workgroup; the partial counts are added in LDS (integer,
+        // so the order does not matter).
+        const int S = max(1, min(kThreads / max(J, 1), 16));
+        const int L = ((J4 + S - 1) / S + 1) & ~1;      // keys per segment, even
+        for (int w = tid; w < J * S; w += kThreads) {
+            const int seg = w / J, j = w - seg * J;      // neighbouring lanes: same segment
+            const uint64_t key = K[j];
+            const int lo = seg * L, hi = min(lo + L, J4);
+            int cnt = 0;
 #pragma unroll 4
-            for (int jj = 0; jj < J4; jj += 4) {
-                const f32x4 u = *reinterpret_cast<const f32x4 *>(P + jj);
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    rank += (u[x] > v) | ((u[x] == v) & (jj + x < j));
+            for (int jj = lo; jj < hi; jj += 2) {
+                const ulonglong2 kk = *reinterpret_cast<const ulonglong2 *>(K + jj);
+                cnt += kk.x > key;
+                cnt += kk.y > key;
             }
+            atomicAdd(R + j, cnt);
+        }
+        __syncthreads();
+        for (int j = tid; j < J; j += kThreads) {
+            const int rank = R[j];
             if (rank < a.topk)
-                out_idx[rank] = v >= 0.0f ? j : -1;
+                out_idx[rank] = (K[j] >> 32) != 0 ? j : -1;   // a NaN score leaves -1
         }
         for (int p = J + tid; p < a.topk; p += kThreads)
             out_idx[p] = -1;
@@ -261,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
     // LDS: q [H][Di] and a key chunk [KC][Di] (bf16 rows padded by 16 bytes),
     // per-wavefront head maxima and sums [kWaves][H] x 2, the combined head
     // maxima and reciprocal sums [H] x 2, per-tile head maxima and sums
-    // [KC / 16][H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4)
+    // [KC / 16][H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4), the rank
+    // keys and ranks [min(Jcap rounded up to 4, kRankMax)] (8 + 4 bytes)
     const int rowb = Di * 2 + 16;
     unsigned char *q_lds = smem;
     unsigned char *k_lds = smem + H * rowb;
@@ -273,6 +293,8 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
     float *tsum = tmax + (KC / 16) * H;
     float *Q = tsum + (KC / 16) * H;
     float *P = Q + (a.Bcap + 3) / 4 * 4;
+    uint64_t *K = reinterpret_cast<uint64_t *>(P + (Jcap + 3) / 4 * 4);
+    int *R = reinterpret_cast<int *>(K + min((Jcap + 3) / 4 * 4, kRankMax));
 
     float *scores = a.scores + n * Jcap;
     int32_t *out_idx = a.indices + n * a.topk;
@@ -468,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
         }
     }
     __syncthreads();
-    pool_and_select(a, Q, P, nb, J, scores, out_idx, tid, lane, wave);
+    pool_and_select(a, Q, P, K, R, nb, J, scores, out_idx, tid, lane, wave);
 }
 
 // Fast path for the common shapes, all sizes known at compile time: Di = 32 DK,
@@ -490,7 +512,8 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
 
     // LDS: q [H][Di] (rows padded by 16 bytes), per-wavefront head maxima and
     // sums [H][kWaves] x 2, the combined head maxima and reciprocal sums
-    // [H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4)
+    // [H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4), the rank keys and
+    // ranks [min(Jcap rounded up to 4, kRankMax)] (8 + 4 bytes)
     unsigned char *q_lds = smem;
     float *wmax = reinterpret_cast<float *>(smem + H * rowb);
     float *wsum = wmax + H * kWaves;
@@ -498,6 +521,8 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
     float *hrz = hmax + H;
     float *Q = hrz + H;
     float *P = Q + (a.Bcap + 3) / 4 * 4;
+    uint64_t *K = reinterpret_cast<uint64_t *>(P + (a.Jcap + 3) / 4 * 4);
+    int *R = reinterpret_cast<int *>(K + min((int)(a.Jcap + 3) / 4 * 4, kRankMax));
 
     float *scores = a.scores + n * a.Jcap;
     int32_t *out_idx = a.indices + n * a.topk;
@@ -539,19 +564,36 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
 
         // scores (log2 units): e[jl][ht] = the tile of head tile ht and column
         // tile wave + 8 jl
+        // (the q fragments of QF head tiles, at most 8 fragments = 32
+        // registers, are read before their MFMAs, so the LDS reads overlap
+        // instead of one wait each)
+        constexpr int QF = 8 / DK < HT ? (8 / DK > 0 ? 8 / DK : 1) : HT;   // head tiles per batch
         f32x4 e[JWM][HT];
+        bf16x8 qf[QF][DK];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            bf16x8 qf[DK];
+            if (ht % QF == 0) {
 #pragma unroll
-            for (int u = 0; u < DK; ++u)
-                qf[u] = *reinterpret_cast<const bf16x8 *>(q_lds + (16 * ht + fr) * rowb + (32 * u + 8 * g) * 2);
+                for (int hq = 0; hq < QF; ++hq)
+#pragma unroll
+                    for (int u = 0; u < DK; ++u)
+                        qf[hq][u] = *reinterpret_cast<const bf16x8 *>(
+                            q_lds + (16 * (ht + hq) + fr) * rowb + (32 * u + 8 * g) * 2);
+                // every fragment is needed here: the reads are all issued
+                // before the first MFMA (the scheduler would otherwise trade
+                // them against registers, one wait per read)
+#pragma unroll
+                for (int hq = 0; hq < QF; ++hq)
+#pragma unroll
+                    for (int u = 0; u < DK; ++u)
+                        asm volatile("" ::"v"(qf[hq][u]));
+            }
 #pragma unroll
             for (int jl = 0; jl < JWM; ++jl) {
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int u = 0; u < DK; ++u)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[u], kf[jl][u], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht % QF][u], kf[jl][u], acc, 0, 0, 0);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     e[jl][ht][q] = scale2 * acc[q];
@@ -628,15 +670,17 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
         }
     }
     __syncthreads();
-    pool_and_select(a, Q, P, nb, J, scores, out_idx, tid, lane, wave);
+    pool_and_select(a, Q, P, K, R, nb, J, scores, out_idx, tid, lane, wave);
 }
 
 }  // namespace
 
 int64_t qsa_select_lds_bytes(int64_t H, int64_t Di, int64_t Bcap, int64_t Jcap, int64_t chunk)
 {
+    const int64_t jcap4 = (Jcap + 3) / 4 * 4;
     return (H + chunk) * (Di * 2 + 16) +
-           4 * ((2 * kWaves + 2) * H + 2 * (chunk / 16) * H + (Bcap + 3) / 4 * 4 + (Jcap + 3) / 4 * 4);
+           4 * ((2 * kWaves + 2) * H + 2 * (chunk / 16) * H + (Bcap + 3) / 4 * 4 + jcap4) +
+           12 * (jcap4 < kRankMax ? jcap4 : kRankMax);
 }
 
 namespace {
@@ -678,7 +722,9 @@ hipError_t launch_qsa_select(const QsaSelectArgs &a, hipStream_t stream)
     SelectKernel k = fast_select_kernel(a.Di, a.H, a.Bcap);
     int64_t lds;
     if (k) {
-        lds = a.H * (a.Di * 2 + 16) + 4 * ((2 * kWaves + 2) * a.H + (a.Bcap + 3) / 4 * 4 + (a.Jcap + 3) / 4 * 4);
+        const int64_t jcap4 = (a.Jcap + 3) / 4 * 4;
+        lds = a.H * (a.Di * 2 + 16) + 4 * ((2 * kWaves + 2) * a.H + (a.Bcap + 3) / 4 * 4 + jcap4) +
+              12 * (jcap4 < kRankMax ? jcap4 : kRankMax);
     } else {
         k = qsa_select_kernel;
         lds = qsa_select_lds_bytes(a.H, a.Di, a.Bcap, a.Jcap, a.chunk);
