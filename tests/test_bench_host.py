@@ -21,7 +21,7 @@ def test_bytes_per_written_token():
     # byte per code + float32 scale), k 128 written
     assert gen.kvrc_bytes_per_written_token(512, 64, "bf16") == 2568
     assert gen.kvrc_bytes_per_written_token(512, 64, "int8") == 2060
-    assert gen.kvrc_bytes_per_written_token(512, 64, "fp8_e4m3") == 2060
+    assert gen.kvrc_bytes_per_written_token(512, 64, "fp8") == 2060
 
 
 def test_paged_batch_bytes_count_skips_and_gamma():
