@@ -101,6 +101,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Value of lane (l ^ 1) / (l ^ 2) within each quad of lanes: DPP quad
+// permutes [1, 0, 3, 2] and [2, 3, 0, 1] (VALU moves, no LDS round trip).
+__device__ __forceinline__ float quad_xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
 // 4 x 4 transpose among lanes 4q .. 4q+3: lane 4q + i holds column i of a
 // 4 x 4 block (v[j] = row j) and ends with row i (v[c] = column c).
 __device__ __forceinline__ void quad_transpose(f32x4 &v, int lane)
@@ -108,15 +119,15 @@ __device__ __forceinline__ void quad_transpose(f32x4 &v, int lane)
     const int b = lane & 1, d = (lane >> 1) & 1;
     // step 1 (partner lane ^ 1): keep rows with bit 0 == b, take the
     // partner's column for them
-    const float r0 = __shfl_xor(b ? v[0] : v[1], 1, 64);
-    const float r1 = __shfl_xor(b ? v[2] : v[3], 1, 64);
+    const float r0 = quad_xor1(b ? v[0] : v[1]);
+    const float r1 = quad_xor1(b ? v[2] : v[3]);
     // now: rows b and 2 + b, columns (lane & 2) + {0, 1}
     const float e0 = b ? r0 : v[0], e1 = b ? v[1] : r0;     // row b
     const float e2 = b ? r1 : v[2], e3 = b ? v[3] : r1;     // row 2 + b
     // step 2 (partner lane ^ 2): keep row 2d + b, take the partner's two
     // columns of it
-    const float s0 = __shfl_xor(d ? e0 : e2, 2, 64);
-    const float s1 = __shfl_xor(d ? e1 : e3, 2, 64);
+    const float s0 = quad_xor2(d ? e0 : e2);
+    const float s1 = quad_xor2(d ? e1 : e3);
     if (d) {
         v[0] = s0; v[1] = s1; v[2] = e2; v[3] = e3;
     } else {
