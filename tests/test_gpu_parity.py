@@ -368,6 +368,32 @@ def test_qsa_invalid_lengths_counted():
     assert torch.all(bk[3].view(torch.int16) == gen.BF16_SENTINEL)
 
 
+def test_qsa_invalid_lengths_counted_one_wavefront_kernel():
+    """The same error rule on the Di = 128 kernel: a sequence with K < L or
+    with blocks past Bcap writes nothing and counts once; the others are
+    exact."""
+    case = gen.qsa_case(601, N=4, L=70, Di=128, Dr=64, kbs=32, past_max=100)
+    kl = case["key_length"].copy()
+    kl[0] = 50                                   # K < L
+    kl[2] = 100_000                              # blocks past Bcap
+    case["key_length"] = kl
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bk, _, _ = run_qsa_gpu(case, err=err)
+    assert int(err.item()) == 2
+    assert torch.all(bk[0].view(torch.int16) == gen.BF16_SENTINEL)
+    assert torch.all(bk[2].view(torch.int16) == gen.BF16_SENTINEL)
+    ok = [1, 3]
+    sub = dict(case, N=2, raw_index_keys=case["raw_index_keys"][ok], key_length=kl[ok],
+               rope_cos=case["rope_cos"][ok], rope_sin=case["rope_sin"][ok],
+               past_incomplete_raw_keys=case["past_incomplete_raw_keys"][ok],
+               past_incomplete_rope=case["past_incomplete_rope"][ok],
+               caches={"block_keys": gen.CacheSpec((2,) + case["caches"]["block_keys"].shape[1:],
+                                                   np.uint16, gen.BF16_SENTINEL)})
+    want_bk, _, _ = oracle.run_qsa_case(sub)
+    got = bk[ok].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want_bk)
+
+
 @pytest.mark.parametrize("seed", [700, 701])
 def test_qsa_chained_calls_match_whole_history(seed):
     """Random chunking of each sequence's token stream across calls, with the

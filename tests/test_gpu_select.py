@@ -183,6 +183,22 @@ def test_select_invalid_lengths_counted():
     compare_select(ok, scores[1:2], idx[1:2])
 
 
+def test_select_invalid_lengths_counted_fast_kernel():
+    """The same rule on the compile-time kernel (Di = 128, H = 64)."""
+    case = gen.qsa_select_case(717, N=3, H=64, Di=128, Bcap=50, kbs=16, sel_ratio=2, cmp_ratio=1,
+                               topk=5)
+    kl = case["key_length"].copy()
+    kl[1] = 51 * 16                               # 51 blocks > capacity 50
+    kl[2] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    scores, idx = run_select_gpu(case, err=err, key_length=kl)
+    assert int(err.item()) == 2
+    assert np.all(scores[[1, 2]] == 0) and np.all(idx[[1, 2]] == -1)
+    ok = dict(case, N=1, query=case["query"][:1], block_keys=case["block_keys"][:1],
+              key_length=case["key_length"][:1])
+    compare_select(ok, scores[:1], idx[:1])
+
+
 def test_select_exact_ties_by_ascending_index():
     """Identical key rows give identical scores on both sides: equal scores
     are ranked by ascending block index."""
