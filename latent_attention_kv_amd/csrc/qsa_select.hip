@@ -11,27 +11,29 @@
 //   indices   = the topk largest P[j], descending, equal scores by ascending j,
 //               -1 where fewer than topk blocks exist
 //
-// Design (one 512-thread workgroup per sequence):
+// Design (one 512-thread workgroup per sequence, both kernels):
 //   * the scores are a dense contraction (H x nb x Di), so they run on the
-//     matrix cores (v_mfma_f32_16x16x32_bf16) from q [H, Di] and the keys
-//     staged in LDS; wavefront w takes the 16-block column tiles w, w + 8, ...
-//     and every head tile of each;
+//     matrix cores (v_mfma_f32_16x16x32_bf16); wavefront w takes the
+//     16-block column tiles w, w + 8, ... and every head tile of each;
 //   * a tile's accumulator holds 4 heads x 16 blocks per 16-lane row, so a
 //     head's maximum or sum over a tile's blocks is four DPP steps inside the
-//     row; per-tile results go to LDS and are combined in tile order;
+//     row; partial results are combined per head in a fixed order;
 //   * scores in log2 units (scale * log2 e * q . k): the softmax is a
 //     maximum, exp2 and a sum per head, and Q takes one reciprocal per head;
-//   * when the sequence's keys fit one LDS chunk and its tiles fit the
-//     registers (kMaxTiles per wavefront), the scores are computed once and
-//     held in registers through the maximum, the exp2 and the head sum;
-//     otherwise the keys pass through LDS in chunks, once per sweep (maxima,
-//     sums, Q), and every sweep recomputes its tiles;
-//   * pooling on LDS; top-k by rank: each candidate counts the candidates
-//     ahead of it (higher score, or equal score and lower index) and lands at
-//     that position; above kRankMax candidates, repeated arg-max on one
-//     wavefront.
+//   * qsa_select_fast_kernel (Di / 32, H / 16 and the column tiles per
+//     wavefront known at compile time): each wavefront loads the key
+//     fragments of its own tiles straight into registers, q passes through
+//     LDS once, and all scores stay in registers from the MFMA to Q;
+//   * qsa_select_kernel (every other shape): keys staged in LDS chunks; a
+//     sequence that fits one chunk with few enough tiles per wavefront keeps
+//     its scores in registers, a longer one takes three sweeps over its
+//     chunks (maxima, sums, Q), each recomputing its tiles;
+//   * pooling on LDS; top-k by rank: every block gets a 64-bit key (score
+//     above, index below) and lands at the number of larger keys, counted in
+//     segments spread over the workgroup; above kRankMax candidates,
+//     repeated arg-max on one wavefront.
 // Float32 throughout (exp2f of the device library); deterministic: every
-// reduction has a fixed order.
+// floating-point reduction has a fixed order.
 #include "kvrc_launch.hpp"
 
 namespace kvrc {
