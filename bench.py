@@ -54,7 +54,7 @@ KERNEL_SOURCES = {
     "mla": ["latent_attention_kv_amd/csrc/mla_kv_head.hip"] + _COMMON_SOURCES,
     "sel": ["latent_attention_kv_amd/csrc/qsa_select.hip"] + _COMMON_SOURCES,
 }
-KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare_kernel", "mla": "mla_kv_head_kernel",
+KERNEL_NAME = {"kvrc": "norm_rope_cache", "qsa": "qsa_prepare", "mla": "mla_kv_head_kernel",
                "sel": "qsa_select"}
 
 WORKLOAD_TEXT = {
