@@ -298,8 +298,9 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
  *   indices       int32 [N, topk] out
  * A NaN score is never selected: its position, after those of every other
  * block, holds -1.
- * The working set (H + 16) (2 Di + 16) + 80 H + 4 (Bcap + Jcap + 6) bytes
- * (q, one 16-row key tile, per-head partial results, the block scores) must
+ * The working set (H + 16) (2 Di + 16) + 80 H + 4 (Bcap + Jcap + 6)
+ * + 12 min(Jcap + 3, 2048) bytes (q, one 16-row key tile, per-head partial
+ * results, the block scores and their ranking keys) must
  * fit one workgroup's LDS (about 160 KiB), else KVRC_ERR_SHAPE. Returns KVRC_OK (also
  * when N == 0), or an error status with nothing written; outputs must not
  * overlap inputs. A sequence with K < 0 or nb > Bcap gets scores 0 and
