@@ -134,7 +134,8 @@ def test_mla_named_workload_full_size():
 
 
 @pytest.mark.parametrize("B,S,He", [(1, 1, 32), (1, 5, 64), (2, 100, 96), (1, 129, 512),
-                                    (3, 257, 1024), (2, 300, 7168), (1, 128, 2048)])
+                                    (3, 257, 1024), (2, 300, 7168), (1, 128, 2048),
+                                    (1, 70, 16384)])
 def test_mla_shapes_and_ragged_tails(B, S, He):
     say(f"[mla] B={B} S={S} He={He}")
     case = gen.mla_kv_head_case(500 + S + He, B=B, S=S, He=He, num_blocks=64, block_size=32,

@@ -342,6 +342,7 @@ def test_qsa_named_workload_bit_exact():
     (4, 100, 128, 64, 16), (3, 7, 64, 16, 16), (5, 1, 32, 8, 4), (2, 300, 1024, 128, 24),
     (6, 65, 8, 2, 3), (1, 2048, 256, 256, 64), (3, 50, 136, 40, 2),
     (3, 130, 128, 128, 64), (2, 70, 128, 2, 33), (2, 90, 128, 64, 65),
+    (1, 70, 4096, 64, 32),                                     # the largest Di accepted
 ])
 @pytest.mark.parametrize("variant", ["full", "no_norm", "no_rope", "plain", "broadcast"])
 def test_qsa_shapes_and_features(N, L, Di, Dr, kbs, variant):

@@ -140,6 +140,7 @@ def test_select_named_workload_full_size():
     (2, 128, 256, 300, 64, 4, 1, 16), (3, 16, 128, 1000, 16, 2, 2, 64), (2, 48, 96, 17, 8, 1, 3, 40),
     (2, 128, 128, 256, 64, 2, 1, 16), (3, 16, 64, 512, 16, 1, 1, 32), (2, 64, 128, 500, 64, 2, 2, 24),
     (2, 128, 64, 200, 32, 1, 4, 12), (4, 32, 128, 129, 16, 1, 1, 130),
+    (2, 16, 2048, 64, 16, 2, 1, 8),                             # Di near the LDS limit
 ])
 def test_select_shapes(N, H, Di, Bcap, kbs, sel, cmp, topk):
     say(f"[select] N={N} H={H} Di={Di} Bcap={Bcap} kbs={kbs} sel={sel} cmp={cmp} topk={topk}")
