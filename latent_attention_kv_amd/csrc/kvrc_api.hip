@@ -111,6 +111,8 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     a.block_size = block_size;
     a.limit = limit;
     a.cache_rows = rows;
+    a.div_s = kvrc::make_udiv((uint32_t)S);                  // S <= T < 2^31
+    a.div_bs = kvrc::make_udiv((uint32_t)(block_size > 0 ? block_size : 1));
     a.ckv = ckv_dtype;
     a.eps = eps;
     a.err = err_count;

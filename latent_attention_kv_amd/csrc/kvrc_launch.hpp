@@ -18,6 +18,27 @@ enum CkvKind : int { kCkvBf16 = 0, kCkvInt8 = 1, kCkvFp8 = 2 };
 //   Norm mode          : b * rows_per_batch + v
 //   block-indexed mode : (v / block_size) * block_size + s % block_size
 // when 0 <= v < limit; v == -1 skips it; any other v is counted in err.
+// Unsigned 32-bit division by a divisor fixed for a launch, as a
+// multiply-high (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", the round-up method with the add-and-shift fix-up):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+//   n / d = (t + ((n - t) >> 1)) >> (l - 1),   t = mulhi(n, m),
+// for every 32-bit n and every d >= 2; d = 1 is marked by shift 0.
+struct UDiv {
+    uint32_t magic, shift;
+};
+
+inline UDiv make_udiv(uint32_t d)
+{
+    if (d <= 1)
+        return {0, 0};
+    uint32_t l = 0;
+    while ((uint64_t)1 << l < d)
+        ++l;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return {(uint32_t)m, l};
+}
+
 struct NormRopeCacheArgs {
     const uint16_t *kv;       // [T, Dv + Dk] bf16
     const uint16_t *gamma;    // [Dv] bf16
@@ -33,6 +54,7 @@ struct NormRopeCacheArgs {
     int64_t block_size;       // block-indexed mode only
     int64_t limit;            // exclusive bound of a valid index value
     int64_t cache_rows;       // rows of each cache (paged: limit; Norm: Bc * Sc)
+    UDiv div_s, div_bs;       // division by S and by block_size (both < 2^31)
     int ckv;                  // CkvKind
     float eps;
     int32_t *err;             // nullable

@@ -44,13 +44,22 @@ namespace {
 constexpr int kThreads = KVRC_WG_THREADS;
 constexpr int kWaves = kThreads / 64;
 
+// n / d for a divisor fixed per launch (see make_udiv).
+__device__ __forceinline__ uint32_t udiv(uint32_t n, UDiv d)
+{
+    if (d.shift == 0)
+        return n;                                        // divisor 1
+    const uint32_t t = __umulhi(n, d.magic);
+    return (t + ((n - t) >> 1)) >> (d.shift - 1);
+}
+
 // Position of token t's entry in the index array (T and S fit 32 bits).
 __device__ __forceinline__ int64_t index_pos(const NormRopeCacheArgs &a, int64_t t)
 {
     if (a.chunks_per_seq == 0)
         return t;
-    const uint32_t b = (uint32_t)t / (uint32_t)a.S, s = (uint32_t)t % (uint32_t)a.S;
-    return (int64_t)b * a.chunks_per_seq + s / (uint32_t)a.block_size;
+    const uint32_t b = udiv((uint32_t)t, a.div_s), s = (uint32_t)t - b * (uint32_t)a.S;
+    return (int64_t)b * a.chunks_per_seq + udiv(s, a.div_bs);
 }
 
 // Destination row of token t with index value v, or -1 (skip). Counts
@@ -60,13 +69,13 @@ __device__ __forceinline__ int64_t dest_row(const NormRopeCacheArgs &a, int64_t 
 {
     if (v >= 0 && v < a.limit) {
         if (a.rows_per_batch)
-            return (int64_t)((uint32_t)t / (uint32_t)a.S) * a.rows_per_batch + v;
+            return (int64_t)udiv((uint32_t)t, a.div_s) * a.rows_per_batch + v;
         if (a.chunks_per_seq) {
-            const uint32_t s = (uint32_t)t % (uint32_t)a.S;
-            const uint64_t bs = (uint64_t)a.block_size;
-            const uint64_t blk = (uint64_t)v < 0xffffffffull
-                ? (uint64_t)((uint32_t)v / (uint32_t)bs) : (uint64_t)v / bs;
-            return (int64_t)(blk * bs + s % (uint32_t)bs);
+            const uint32_t s = (uint32_t)t - udiv((uint32_t)t, a.div_s) * (uint32_t)a.S;
+            const uint32_t bs = (uint32_t)a.block_size;
+            const uint64_t blk = (uint64_t)v <= 0xffffffffull
+                ? (uint64_t)udiv((uint32_t)v, a.div_bs) : (uint64_t)v / bs;
+            return (int64_t)(blk * bs + (s - udiv(s, a.div_bs) * bs));
         }
         return v;
     }
