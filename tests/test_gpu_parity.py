@@ -184,6 +184,16 @@ def test_norm_mode(ckv, dv, dk):
     compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
 
 
+@pytest.mark.parametrize("B,S,Sc", [(4, 1, 3), (3, 7, 7), (2, 33, 50), (1, 5, 9)])
+def test_norm_mode_sequence_lengths(B, S, Sc):
+    """Token t belongs to batch t // S: lengths 1, odd and prime, and a cache
+    row count equal to S."""
+    say(f"[parity] norm mode B={B} S={S} Sc={Sc}")
+    case = gen.kvrc_norm_case(330 + S, B=B, S=S, Dv=512, Dk=64, Bc=B + 1, Sc=Sc,
+                              n_skip=min(2, B * S - 1))
+    compare_kvrc(case, run_kvrc_gpu(case), oracle.run_kvrc_case(case), exact_bf16=True)
+
+
 @pytest.mark.parametrize("sigma", [1e15, 1e-20, 1e-25, 3e-3])
 @pytest.mark.parametrize("ckv", CKV)
 def test_extreme_magnitudes(sigma, ckv):
@@ -590,7 +600,9 @@ def test_fp8_exact_ties():
 
 @pytest.mark.parametrize("ckv", CKV)
 @pytest.mark.parametrize("B,S,BS,offsets", [(8, 4096, 128, False), (3, 300, 64, True),
-                                             (2, 37, 16, False), (5, 1, 16, False)])
+                                             (2, 37, 16, False), (5, 1, 16, False),
+                                             (2, 13, 1, False), (4, 97, 7, True),
+                                             (3, 1000, 999, True), (3, 50, 1000, True)])
 def test_paged_blk_mode(ckv, B, S, BS, offsets):
     """Block-indexed mode (PA_BLK_BNSD): one entry per chunk of BS tokens,
     ragged last chunks, skipped chunks, entries with offsets inside the block."""
