@@ -103,22 +103,73 @@ __device__ __forceinline__ float chunk_sumsq(const float (&x)[8], float acc)
 //   p[k] <- p[k] + p[k + w/2], w = G, G/2, ..., 2
 // because lane k and lane k ^ m hold the two operands and float addition is
 // commutative.
-template <int G>
-__device__ __forceinline__ float fold_sum(float v)
+//
+// The exchanges stay on the vector ALU (no LDS round trip):
+//   m = 32: v_permlane32_swap of the value with itself leaves the lower half
+//           in one result and the upper half in the other, in every lane;
+//   m = 16: v_permlane16_swap likewise pairs rows 0/1 and 2/3 of 16 lanes;
+//   m = 8:  DPP row rotate by 8 (lane l reads lane l ^ 8 within its row);
+//   m = 4:  DPP row rotate by 4 reads lane l + 4 or l - 4 (mod 16), which
+//           after the m = 8 step holds the same value as lane l ^ 4;
+//   m = 2, 1: DPP quad permutes [2,3,0,1] and [1,0,3,2].
+// Below G = 16 the m = 4 step needs the exact partner and uses a shuffle.
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v)
 {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1)
-        v = v + __shfl_xor(v, m, 64);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, false);
+}
+
+template <int G, typename Op>
+__device__ __forceinline__ uint32_t fold_lanes(uint32_t v, Op op)
+{
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G: power of two <= 64");
+    if constexpr (G == 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = op(r[0], r[1]);
+    }
+    if constexpr (G >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = op(r[0], r[1]);
+    }
+    if constexpr (G >= 16) {
+        v = op(v, dpp_read<0x128>(v));            // row_ror:8
+        v = op(v, dpp_read<0x124>(v));            // row_ror:4
+    } else if constexpr (G >= 8) {
+        v = op(v, (uint32_t)__shfl_xor((int)v, 4, 64));
+    }
+    if constexpr (G >= 4)
+        v = op(v, dpp_read<0x4E>(v));             // quad_perm [2,3,0,1]
+    if constexpr (G >= 2)
+        v = op(v, dpp_read<0xB1>(v));             // quad_perm [1,0,3,2]
     return v;
 }
 
+struct FloatAdd {
+    __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const
+    {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }
+};
+struct UnsignedMax {
+    __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const
+    {
+        return a > b ? a : b;
+    }
+};
+
+template <int G>
+__device__ __forceinline__ float fold_sum(float v)
+{
+    return __uint_as_float(fold_lanes<G>(__float_as_uint(v), FloatAdd{}));
+}
+
+// Maximum of values that are >= +0 and not NaN (an fmaxf chain started at 0
+// never yields NaN): for those, float order is the unsigned order of the
+// bits, which keeps the fold free of NaN canonicalisation.
 template <int G>
 __device__ __forceinline__ float fold_max(float v)
 {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+    return __uint_as_float(fold_lanes<G>(__float_as_uint(v), UnsignedMax{}));
 }
 
 // ---------------------------------------------------------------------------
@@ -204,7 +255,9 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // so t, the midpoint and anything a few ulps from them share one binade.
 __device__ __forceinline__ bool e4m3_near_midpoint(float t)
 {
-    return ((__float_as_uint(t) + 4u) & 0xffff8u) == 0x80000u;
+    // low 20 bits of bits(t) + 4 in [0x80000, 0x80007], tested as the low 20
+    // bits of bits(t) + 4 - 0x80000 (moved to the top) below 8
+    return ((__float_as_uint(t) + (4u - 0x80000u)) << 12) < (8u << 12);
 }
 
 __device__ __forceinline__ u32x2 e4m3_pack8(const float (&q)[8])

@@ -277,28 +277,40 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
                 amax = fmaxf(amax, fabsf(y[j][e]));
         amax = fold_max<LPT>(amax);
         const float scale = amax / 127.0f;
-        // code = rint(RN(y / scale)), half to even, as the low byte of
-        // bits(q + 1.5*2^23) (adding that constant rounds |q| < 2^22 to an
-        // integer in the low mantissa bits, ties to even). In the
-        // shared-divisor domain of scale the quotient is first approximated
-        // as t = RN(y * RN(1/scale)), within 3*2^-24*127 < 2^-15 of RN(y/scale)
-        // (|y / scale| <= 127 + 2^-16); wherever t lies farther than 2^-15
-        // from a half-integer both round to the same integer, and the few
-        // elements within 2^-15 of one take the exact quotient.
+        // code = rint(RN(y / scale)), half to even. In the shared-divisor
+        // domain of scale, with rs = RN(1/scale) and P = y * rs (exact):
+        //   |P - y/scale| and |RN(y/scale) - y/scale| are both below
+        //   2^-24 * 127.0001 < 2^-17, so |P - RN(y/scale)| < 2^-16;
+        //   RN(P + 1.5*2^23) = 1.5*2^23 + rint(P) (one fma; the low byte of
+        //   its bits is the int8 code of rint(P));
+        //   rint(P) and rint(RN(y/scale)) differ only if a half-integer h lies
+        //   within 2^-16 of P. f = RN(P + 384) lies in (256, 512) with ulp
+        //   2^-15, so its 15 low mantissa bits are frac(P) in units of 2^-15
+        //   and |f - 384 - h| < 2^-15 forces them to 0x4000 exactly.
+        // Lanes with an element whose f has low bits 0x3fff..0x4001 redo their
+        // quotients exactly (elements with |y| below the shared-divisor
+        // dividend range have |quotient| < 2^-4 and code 0 either way).
         uint32_t cb[NCH][8];
         if (fast_div_divisor_ok(scale)) {
             const float rs = 1.0f / scale;
+            // smallest (low 15 bits of f + 0x4001) << 17 over the lane: at most
+            // 2 << 17 exactly when some low bits are 0x3fff, 0x4000 or 0x4001
+            uint32_t dmin = 0xffffffffu;
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float t = y[j][e] * rs;
-                    const float w = t + kRoundMagic;
-                    if (fabsf(t - (w - kRoundMagic)) > 0.5f - 0x1p-15f)
-                        cb[j][e] = __float_as_uint(div_rn_shared(y[j][e], scale, rs) + kRoundMagic);
-                    else
-                        cb[j][e] = __float_as_uint(w);
+                    cb[j][e] = __float_as_uint(__builtin_fmaf(y[j][e], rs, kRoundMagic));
+                    const uint32_t f = __float_as_uint(__builtin_fmaf(y[j][e], rs, 384.0f));
+                    dmin = min(dmin, (f + 0x4001u) << 17);
                 }
+            if (dmin <= (2u << 17)) {
+#pragma unroll
+                for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        cb[j][e] = __float_as_uint(div_rn_shared(y[j][e], scale, rs) + kRoundMagic);
+            }
         } else {
             // scale 0, tiny or huge: IEEE division. A scale rounded to a
             // float32 subnormal can push |y / scale| past 127: saturate.
