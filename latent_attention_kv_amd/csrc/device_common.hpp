@@ -248,17 +248,19 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
-// True when t (a normal float32 with |t| >= 2^-6) lies within [-4, +3]
-// float32 ulps of a midpoint between two neighbouring E4M3FN values. In that
-// range every E4M3FN value has 3 mantissa bits, so the midpoints are the
-// floats whose 20 low mantissa bits are 0x80000; the midpoints sit mid-binade,
-// so t, the midpoint and anything a few ulps from them share one binade.
-__device__ __forceinline__ bool e4m3_near_midpoint(float t)
+// Distance key of t (a normal float32 with |t| >= 2^-6) from the midpoints
+// between neighbouring E4M3FN values: below kE4m3NearKey exactly when t lies
+// within [-4, +3] float32 ulps of a midpoint. In that range every E4M3FN
+// value has 3 mantissa bits, so the midpoints are the floats whose 20 low
+// mantissa bits are 0x80000; the midpoints sit mid-binade, so t, the midpoint
+// and anything a few ulps from them share one binade. The key is the low 20
+// bits of bits(t) + 4 - 0x80000 moved to the top, so a minimum over many t
+// answers for all of them at once.
+__device__ __forceinline__ uint32_t e4m3_midpoint_key(float t)
 {
-    // low 20 bits of bits(t) + 4 in [0x80000, 0x80007], tested as the low 20
-    // bits of bits(t) + 4 - 0x80000 (moved to the top) below 8
-    return ((__float_as_uint(t) + (4u - 0x80000u)) << 12) < (8u << 12);
+    return (__float_as_uint(t) + (4u - 0x80000u)) << 12;
 }
+constexpr uint32_t kE4m3NearKey = 8u << 12;
 
 __device__ __forceinline__ u32x2 e4m3_pack8(const float (&q)[8])
 {

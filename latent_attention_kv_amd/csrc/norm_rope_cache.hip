@@ -352,16 +352,18 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
         float q[NCH][8];
         if (fast_div_divisor_ok(scale)) {
             const float rs = 1.0f / scale;
-            bool redo = false;
+            uint32_t kmin = 0xffffffffu;  // smallest midpoint key of the lane
+            float tmin = __builtin_inff(); // smallest |t| of the lane
 #pragma unroll
             for (int j = 0; j < NCH; ++j)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float t = y[j][e] * rs;
                     q[j][e] = t;
-                    redo |= (fabsf(t) < 0x1p-6f) | e4m3_near_midpoint(t);
+                    kmin = min(kmin, e4m3_midpoint_key(t));
+                    tmin = fminf(tmin, fabsf(t));
                 }
-            if (redo) {
+            if (kmin < kE4m3NearKey || tmin < 0x1p-6f) {
                 bool tiny = false;        // shared-divisor domain: |y| >= 2^-64
 #pragma unroll
                 for (int j = 0; j < NCH; ++j)
