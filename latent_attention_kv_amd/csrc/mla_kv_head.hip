@@ -112,6 +112,16 @@ __device__ __forceinline__ float quad_xor2(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
+// Value of lane (l + 8) / (l + 4) mod 16 within each row of 16 lanes.
+__device__ __forceinline__ float row_ror8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_ror4(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+}
+
 // 4 x 4 transpose among lanes 4q .. 4q+3: lane 4q + i holds column i of a
 // 4 x 4 block (v[j] = row j) and ends with row i (v[c] = column c).
 __device__ __forceinline__ void quad_transpose(f32x4 &v, int lane)
@@ -165,6 +175,15 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     for (int i = 0; i < kMaxWBlocks; ++i) {
         const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
         wsrc[i] = a.w + (int64_t)r * He + ((lane & 3) ^ swz(r)) * 8;
+    }
+    // The cache slots of the rows this wavefront scatters (rows wave + 8 i,
+    // i < 16) are fetched now, lane i holding row i's: their latency hides
+    // behind the K loop instead of preceding each row's stores.
+    int64_t my_slot = -1;
+    {
+        const int64_t t = row0 + wave + kWaves * (lane & 15);
+        if (lane < kRows / kWaves && t < T)
+            my_slot = a.slot[t];
     }
     unsigned char *const xdst = smem + kXRing + wave * 1024;     // + stage * kStageA
     unsigned char *const wdst = smem + wb0 * 1024;               // + stage * kStageB + i KiB
@@ -252,15 +271,34 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     // After the transpose, acc[m][n][e] is c[row][col] with
     //   row = 16 m + 4 (lane / 16) + lane % 4,
     //   col = 144 w + 16 n + 4 ((lane % 16) / 4) + e.
+    const int rsub = 4 * (lane >> 4) + (lane & 3);       // row within a 16-row tile
+    const int cq = 4 * ((lane & 15) >> 2);               // first column within a tile
+    const int ntn = wn < 3 ? kNt : 5;                    // tiles holding kv (not rope) columns
+    // The rope tiles (wn == 3, tiles 5..8) need the cos / sin pairs
+    // (i0, i0 + 1) and (32 + i0, 33 + i0), i0 = 8 (n - 5) + cq / 2: those of
+    // row tile 0 are loaded now, those of row tile m + 1 while row tile m is
+    // computed (two register buffers), so their latencies overlap work.
+    uint32_t rc[2][kNt - 5][4];
+    auto load_rope_tables = [&](int m, uint32_t (&dst)[kNt - 5][4]) {
+        int64_t t = row0 + 64 * wm + 16 * m + rsub;
+        t = t < T ? t : T - 1;
+#pragma unroll
+        for (int k = 0; k < kNt - 5; ++k) {
+            const int i0 = 8 * k + cq / 2;
+            dst[k][0] = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + i0);
+            dst[k][1] = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + 32 + i0);
+            dst[k][2] = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + i0);
+            dst[k][3] = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + 32 + i0);
+        }
+    };
+    if (wn == 3)
+        load_rope_tables(0, rc[0]);
 #pragma unroll
     for (int m = 0; m < kMt; ++m)
 #pragma unroll
         for (int n = 0; n < kNt; ++n)
             quad_transpose(acc[m][n], lane);
-    const int rsub = 4 * (lane >> 4) + (lane & 3);       // row within a 16-row tile
-    const int cq = 4 * ((lane & 15) >> 2);               // first column within a tile
     float *red = reinterpret_cast<float *>(smem + kRedOff);     // [4 column quarters][128]
-    const int ntn = wn < 3 ? kNt : 5;                    // tiles holding kv (not rope) columns
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
         float s = 0.0f;
@@ -270,8 +308,10 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     s += acc[m][n][e] * acc[m][n][e];
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 8, 64);
+        // add the four column quarters of the 16-lane row: DPP row rotates by
+        // 8, then by 4 (after the first step lanes l and l ^ 8 agree)
+        s += row_ror8(s);
+        s += row_ror4(s);
         if (cq == 0)
             red[wn * kRows + 64 * wm + 16 * m + rsub] = s;
     }
@@ -284,18 +324,17 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 #pragma unroll
     for (int n = 0; n < kNt; ++n) {
         const int col = kWaveCols * wn + 16 * n + cq;
-        const int gc = col < kNorm ? col : 0;
-        const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + gc);
+        const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + (col < kNorm ? col : 0));
         g[n][0] = bf16_lo(gw.x); g[n][1] = bf16_hi(gw.x);
         g[n][2] = bf16_lo(gw.y); g[n][3] = bf16_hi(gw.y);
     }
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
+        if (wn == 3 && m + 1 < kMt)
+            load_rope_tables(m + 1, rc[(m + 1) & 1]);
         const int r = 64 * wm + 16 * m + rsub;
         const float ss = (red[r] + red[kRows + r]) + (red[2 * kRows + r] + red[3 * kRows + r]);
         const float rr = 1.0f / sqrtf(ss / (float)kNorm + a.eps);
-        int64_t t = row0 + r;
-        t = t < T ? t : T - 1;
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
             const f32x4 v = acc[m][n];
@@ -310,11 +349,10 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
                 // and (2 i0 + 2, 2 i0 + 3) give outputs i0, i0 + 1 and
                 // 32 + i0, 33 + i0
-                const int i0 = 8 * (n - 5) + cq / 2;
-                const uint32_t c0 = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + i0);
-                const uint32_t c1 = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + 32 + i0);
-                const uint32_t s0 = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + i0);
-                const uint32_t s1 = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + 32 + i0);
+                const int k = n - 5 > 0 ? n - 5 : 0;   // n >= 5 here
+                const int i0 = 8 * k + cq / 2;
+                const uint32_t c0 = rc[m & 1][k][0], c1 = rc[m & 1][k][1];
+                const uint32_t s0 = rc[m & 1][k][2], s1 = rc[m & 1][k][3];
                 const float lo0 = v[0] * bf16_lo(c0) - v[1] * bf16_lo(s0);
                 const float lo1 = v[2] * bf16_hi(c0) - v[3] * bf16_hi(s0);
                 const float hi0 = v[1] * bf16_lo(c1) + v[0] * bf16_lo(s1);
@@ -327,12 +365,16 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
     __syncthreads();
 
-    // ---- scatter: wavefront w writes rows w, w + 4, ... ---------------------
-    for (int r = wave; r < kRows; r += kWaves) {
+    // ---- scatter: wavefront w writes rows w, w + 8, ... ---------------------
+#pragma unroll
+    for (int i = 0; i < kRows / kWaves; ++i) {
+        const int r = wave + kWaves * i;
         const int64_t t = row0 + r;
         if (t >= T)
             break;
-        const int64_t v = a.slot[t];
+        const int64_t v = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(my_slot >> 32), i) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)my_slot, i));
         if (v < 0 || v >= a.cache_rows) {
             if (v != -1 && lane == 0 && a.err)
                 atomicAdd(a.err, 1);
