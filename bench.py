@@ -183,10 +183,15 @@ def build_sets(case, R, dev):
             sets.append(s)
         return sets
     if case.get("mode") == "mla_paged":
+        import latent_attention_kv_amd as kvlib
         base = dict(x=dbf(case["x"]), w=dbf(case["w"]), gamma=dbf(case["gamma"]),
                     cos=dbf(case["cos"]), sin=dbf(case["sin"]), idx=dt(case["slot_mapping"]))
+        # the launches run in order on one stream: one zeroed workspace serves all
+        ws = torch.zeros(kvlib.kvrc_mla_kv_head_workspace_bytes(case["x"].shape[0]),
+                         dtype=torch.uint8, device=dev)
         for i in range(R):
             s = {k: (v.clone() if i else v) for k, v in base.items()}
+            s["ws"] = ws
             for name, spec in case["caches"].items():
                 fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
                 s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
@@ -231,8 +236,8 @@ def launch(case, s):
                           cmp_ratio=case["cmp_ratio"], scale=case["scale"])
     elif case.get("mode") == "mla_paged":
         k.kvrc_mla_kv_head_paged(s["x"], s["w"], s["gamma"], s["cos"], s["sin"], s["idx"],
-                                 s["k_cache"], s["ckv_cache"], alpha_kv=case["alpha"],
-                                 eps=case["eps"])
+                                 s["k_cache"], s["ckv_cache"], workspace=s["ws"],
+                                 alpha_kv=case["alpha"], eps=case["eps"])
     elif "raw_index_keys" in case:
         k.qsa_prepare(s["raw"], s["bk"], s["kl"], s["rc"], s["rs"], s["w"], s["praw"], s["prope"],
                       s["nraw"], s["nrope"], key_block_size=case["kbs"], eps=case["eps"])

@@ -48,7 +48,8 @@ typedef enum kvrc_status {
     KVRC_ERR_DTYPE = 3,  /* cache dtype unknown, or scale pointer does not match */
     KVRC_ERR_ALIGN = 4,  /* a base pointer is not 16-byte aligned                */
     KVRC_ERR_ALIAS = 5,  /* an output overlaps an input it must not overlap      */
-    KVRC_ERR_HIP = 6     /* the HIP runtime refused the launch (e.g. no device)  */
+    KVRC_ERR_HIP = 6,    /* the HIP runtime refused the launch (e.g. no device)  */
+    KVRC_ERR_WORKSPACE = 7 /* the workspace is smaller than the call needs       */
 } kvrc_status;
 
 /* Element type of the ckv cache. */
@@ -169,6 +170,14 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                              int32_t *err_count, hipStream_t stream);
 
 /*
+ * kvrc_mla_kv_head_workspace_bytes - bytes of device workspace that
+ * kvrc_mla_kv_head_paged needs for T tokens (the first phase of the pages'
+ * "workspace size, then execute" convention; 2056 bytes per 256 tokens).
+ * Returns -1 for T < 0 or T > 2^31 - 1, 0 for T == 0.
+ */
+int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
+
+/*
  * kvrc_mla_kv_head_paged - the kv path of the MLA prologue: projection, then
  * the normalised key into the ckv cache and the rotated key into the k cache.
  *
@@ -203,15 +212,28 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
  *   k_cache       bf16 [num_blocks, block_size, 1, 64]
  *   ckv_cache     bf16 [num_blocks, block_size, 1, 512]
  *   He            a multiple of 32, >= 32; T <= 2^31 - 1
+ *   workspace     device memory of at least
+ *                 kvrc_mla_kv_head_workspace_bytes(T) bytes (workspace_bytes
+ *                 gives its size), 16-byte aligned, owned by the caller. It
+ *                 must be all zero when first used; every call that runs to
+ *                 its end leaves it all zero again, so one workspace serves
+ *                 any number of calls in order on a stream (HIP graph
+ *                 replays included). Calls that may run at the same time
+ *                 need separate workspaces.
  * Returns KVRC_OK (also when T == 0: nothing is launched), or an error
- * status with nothing written; outputs must not overlap inputs; err_count
- * counts slots outside [-1, num_blocks*block_size).
+ * status with nothing written: KVRC_ERR_WORKSPACE when workspace_bytes is
+ * too small; outputs (the workspace included) must not overlap inputs or
+ * each other. err_count counts slots outside [-1, num_blocks*block_size),
+ * and also a workgroup whose partner did not publish its partial sums
+ * within about a second (its rows are then not valid; the workspace was
+ * not zero, or another call used it at the same time).
  */
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,
                                const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
                                int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
-                               float eps, int32_t *err_count, hipStream_t stream);
+                               float eps, void *workspace, int64_t workspace_bytes,
+                               int32_t *err_count, hipStream_t stream);
 
 /*
  * qsa_prepare - one index key per complete key block, for sparse attention.

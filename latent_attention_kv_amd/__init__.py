@@ -17,7 +17,8 @@ Entry points (same names as the C ABI in ``include/kvrc.h``):
   * kvrc_mla_kv_head_paged     - the MLA kv-path head: x [T, He] times the
     fused [576, He] projection on the matrix cores, then alpha_kv * RMSNorm,
     RoPE and the paged scatter (aclnnMlaPrologV3WeightNz, third and fourth
-    paths)
+    paths); it takes a caller-owned workspace of
+    kvrc_mla_kv_head_workspace_bytes(T) bytes
   * qsa_prepare                - block keys (openvino.opset17.qsa_prepare)
   * qsa_select_topk            - block selection over those keys: softmax
     scores, selection pooling, head sum, top-k (aclnnNsaCompressAttentionInfer)
@@ -30,7 +31,8 @@ import os
 import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
-           "kvrc_norm_rope_cache", "kvrc_mla_kv_head_paged", "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
+           "kvrc_norm_rope_cache", "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
+           "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -40,7 +42,8 @@ CACHE_INT8 = 1
 CACHE_FP8_E4M3 = 2
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
-                    "kvrc_mla_kv_head_paged", "qsa_prepare", "qsa_select_topk",
+                    "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
+                    "qsa_prepare", "qsa_select_topk",
                     "kvrc_selftest_arith", "kvrc_selftest_e4m3")
 
 _lib = None
@@ -73,8 +76,10 @@ def lib() -> ctypes.CDLL:
     L.kvrc_norm_rope_cache.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32,
                                        F, P, P]
     L.kvrc_norm_rope_cache.restype = I32
+    L.kvrc_mla_kv_head_workspace_bytes.argtypes = [I64]
+    L.kvrc_mla_kv_head_workspace_bytes.restype = I64
     L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, F, P,
-                                         P]
+                                         I64, P, P]
     L.kvrc_mla_kv_head_paged.restype = I32
     L.qsa_select_topk.argtypes = [P, P, P, I64, F, I64, I64, I64, I64, I64, I64, I64, I64, P, P,
                                   P, P]
@@ -237,11 +242,22 @@ def kvrc_norm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, ckv_sca
     _check(st, "kvrc_norm_rope_cache")
 
 
+def kvrc_mla_kv_head_workspace_bytes(T):
+    """Bytes of device workspace kvrc_mla_kv_head_paged needs for T tokens."""
+    n = lib().kvrc_mla_kv_head_workspace_bytes(int(T))
+    if n < 0:
+        raise ValueError("T out of range")
+    return n
+
+
 def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, *,
-                           alpha_kv=1.0, eps=1e-6, err_count=None, stream=None):
+                           workspace, alpha_kv=1.0, eps=1e-6, err_count=None, stream=None):
     """MLA kv-path head into paged bf16 caches: x [T, He], w_dkv_kr [576, He],
     gamma [512], cos / sin [T, 64], slot_mapping [T]; k_cache
-    [NB, BS, 1, 64] and ckv_cache [NB, BS, 1, 512] are updated in place."""
+    [NB, BS, 1, 64] and ckv_cache [NB, BS, 1, 512] are updated in place.
+    workspace: a contiguous device tensor of at least
+    kvrc_mla_kv_head_workspace_bytes(T) bytes, all zero before its first use
+    (each completed call leaves it zero)."""
     _need(x, "x", _BF16, 2)
     _need(w_dkv_kr, "w_dkv_kr", _BF16, 2)
     _need(gamma, "gamma", _BF16, 1)
@@ -262,10 +278,15 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
     NB, BS = k_cache.shape[0], k_cache.shape[1]
     if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
         raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().kvrc_mla_kv_head_paged(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
                                       _ptr(cos), _ptr(sin), _ptr(slot_mapping), _ptr(k_cache),
                                       _ptr(ckv_cache), T, He, NB, BS, float(eps),
-                                      _err_ptr(err_count), _stream(stream))
+                                      _ptr(workspace), ws_bytes, _err_ptr(err_count),
+                                      _stream(stream))
     _check(st, "kvrc_mla_kv_head_paged")
 
 

@@ -134,11 +134,12 @@ const char *kvrc_status_string(int32_t status)
     case KVRC_ERR_ALIGN: return "pointer not aligned";
     case KVRC_ERR_ALIAS: return "output overlaps another buffer";
     case KVRC_ERR_HIP: return "HIP launch failed";
+    case KVRC_ERR_WORKSPACE: return "workspace smaller than required";
     default: return "unknown status";
     }
 }
 
-int32_t kvrc_version(void) { return 103; }
+int32_t kvrc_version(void) { return 104; }
 
 int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                    const void *sin, const int64_t *slot_mapping, void *k_cache,
@@ -187,11 +188,19 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                   err_count, stream);
 }
 
+int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T)
+{
+    if (T < 0 || T > (int64_t)INT32_MAX)
+        return -1;
+    return kvrc::mla_kv_head_workspace_bytes(T);
+}
+
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,
                                const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
                                int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
-                               float eps, int32_t *err_count, hipStream_t stream)
+                               float eps, void *workspace, int64_t workspace_bytes,
+                               int32_t *err_count, hipStream_t stream)
 {
     int64_t rows;
     if (T < 0 || T > (int64_t)INT32_MAX || He < kvrc::kMlaHeadK || He % kvrc::kMlaHeadK ||
@@ -203,16 +212,20 @@ int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *
         return KVRC_ERR_SHAPE;
     if (T == 0)
         return KVRC_OK;                       // empty input: caches untouched
-    if (!x || !w_dkv_kr || !gamma || !cos || !sin || !slot_mapping || !k_cache || !ckv_cache)
+    const int64_t wsbytes = kvrc::mla_kv_head_workspace_bytes(T);
+    if (workspace_bytes < wsbytes)
+        return KVRC_ERR_WORKSPACE;
+    if (!x || !w_dkv_kr || !gamma || !cos || !sin || !slot_mapping || !k_cache || !ckv_cache ||
+        !workspace)
         return KVRC_ERR_NULL;
     if (!aligned(x, 16) || !aligned(w_dkv_kr, 16) || !aligned(gamma, 16) || !aligned(cos, 16) ||
         !aligned(sin, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
-        !aligned(ckv_cache, 16) || !aligned(err_count, 4))
+        !aligned(ckv_cache, 16) || !aligned(workspace, 16) || !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
     const Range in[] = {span(x, xbytes), span(w_dkv_kr, wbytes), span(gamma, 1024),
                         span(cos, T * 128), span(sin, T * 128), span(slot_mapping, T * 8)};
     const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes),
-                         span(err_count, err_count ? 4 : 0)};
+                         span(workspace, wsbytes), span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
         for (const Range &i : in)
             if (overlap(o, i))
@@ -235,6 +248,7 @@ int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *
     a.cache_rows = rows;
     a.alpha = alpha_kv;
     a.eps = eps;
+    a.workspace = workspace;
     a.err = err_count;
     (void)hipGetLastError();
     return launch_status(kvrc::launch_mla_kv_head(a, stream));

@@ -94,6 +94,7 @@ struct MlaKvHeadArgs {
     uint16_t *ckv_cache;      // [cache_rows, 512] bf16
     int64_t T, He, cache_rows;
     float alpha, eps;
+    void *workspace;          // mla_kv_head_workspace_bytes(T) bytes, zero between calls
     int32_t *err;             // nullable
 };
 
@@ -101,6 +102,11 @@ hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream);
 
 // K granularity of the MLA head kernel (He must be a multiple of it).
 constexpr int64_t kMlaHeadK = 32;
+// Token rows per workgroup pair of the MLA head kernel.
+constexpr int64_t kMlaPairRows = 256;
+// Workspace of one MLA head call: per pair of workgroups, their per-row
+// partial square sums and two ready flags.
+int64_t mla_kv_head_workspace_bytes(int64_t T);
 
 // One block-selection launch (see qsa_select_topk in kvrc.h).
 struct QsaSelectArgs {

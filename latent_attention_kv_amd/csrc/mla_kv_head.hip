@@ -14,32 +14,41 @@
 // the norm).
 //
 // Design: the projection is a dense contraction (2 * 576 * He flops per
-// token), so it runs on the matrix cores (v_mfma_f32_16x16x32_bf16). A
-// workgroup owns 128 whole token rows, so the row-wise norm, the RoPE and
-// the scatter run on the accumulators without writing c to memory:
-//   * 8 wavefronts = 2 (rows) x 4 (columns); wavefront (wm, wn) accumulates
-//     rows 64 wm .. +64 and columns 144 wn .. +144 as 4 x 9 tiles of 16 x 16
-//     (144 accumulator registers, two wavefronts per SIMD);
+// token), so it runs on the matrix cores (v_mfma_f32_16x16x32_bf16). The
+// operands reach a compute unit through its texture path, whose rate bounds
+// this kernel, so the tile is chosen for bytes per flop: a PAIR of
+// workgroups owns 256 token rows, one workgroup per half of the 576 output
+// columns (columns 0..287, and 288..575 with the 64 rope columns). Per K
+// step of 32 a workgroup then streams 16 KiB of x and 18 KiB of W (34 KiB)
+// instead of 8 + 36 KiB for a 128 x 576 tile, for the same matrix work.
+//   * 8 wavefronts = 4 (rows) x 2 (columns); wavefront (wm, wn) accumulates
+//     rows 64 wm .. +64 and columns 144 wn .. +144 of its half as 4 x 9 tiles
+//     of 16 x 16 (144 accumulator registers, two wavefronts per SIMD);
 //   * K advances 32 at a time; the slices pass through two LDS rings filled
 //     by direct global -> LDS loads (global_load_lds_dwordx4: no staging
-//     registers, no LDS store instructions): W (576 x 32, 36 KiB) in 3
-//     stages two steps ahead of the MFMAs, x (128 x 32, 8 KiB) in 4 stages
+//     registers, no LDS store instructions): W (288 x 32, 18 KiB) in 3
+//     stages two steps ahead of the MFMAs, x (256 x 32, 16 KiB) in 4 stages
 //     three steps ahead, as x streams from HBM while W is shared through L2;
 //     each wavefront waits only for its own loads of the step about to be
 //     used, then one barrier publishes them;
-//   * within a step the next B fragment read and one load of step + 2 are
-//     issued between groups of 4 MFMAs, so their issue overlaps the matrix
-//     pipe instead of preceding it;
+//   * the two workgroups of a pair are blockIdx b and b + 8, which the
+//     dispatcher places on the same XCD: their x rows meet in that XCD's L2;
 //   * staged rows are 64 bytes with their four 16-byte pieces permuted by
 //     (row / 4) mod 4, so the 16 lanes of a fragment read cover all 64 banks;
 //   * epilogue: a 4 x 4 transpose among neighbouring lanes turns each
 //     accumulator tile into row pieces of 4 columns; squares are reduced per
-//     row across lanes and wavefronts; rows are normalised and rotated in
-//     registers, staged as bf16 in LDS with 8-byte writes and scattered with
-//     16-byte stores per cache row.
-// Measured on MI355X for T = 32768, He = 7168: about 294 us per call
-// (920 TFLOP/s); the operand stream through the texture path, not the
-// matrix cores, bounds this tile shape.
+//     row across lanes and wavefronts; the two workgroups of the pair swap
+//     their per-row partial sums through the caller's workspace (a ready
+//     flag per half, set after the sums; the partner reads the sums, zeroes
+//     them and clears the flag, so the workspace is all zero again when the
+//     call ends);
+//     rows are normalised and rotated in registers, staged as bf16 in LDS
+//     and scattered with 16-byte stores per cache row piece.
+// The wait for the partner is bounded: past the limit the workgroup counts
+// an error and goes on (its rows are then wrong), so the kernel always ends.
+// A partner is dispatched at most 8 workgroups later on the same XCD, and
+// workgroups retire as soon as their pair has swapped, so both halves of a
+// pair are resident together whenever one of them waits.
 #include "kvrc_launch.hpp"
 
 namespace kvrc {
@@ -51,38 +60,45 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRows = 128;                 // token rows per workgroup
-constexpr int kCols = 576;                 // projection outputs (512 + 64)
+constexpr int kRows = (int)kMlaPairRows;   // token rows per workgroup pair
+constexpr int kHalfCols = 288;             // output columns per workgroup
 constexpr int kNorm = 512;
 constexpr int kRope = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKt = (int)kMlaHeadK;        // K per stage (one MFMA K)
 constexpr int kRowBytes = kKt * 2;         // 64
-constexpr int kStageA = kRows * kRowBytes; // 8192
-constexpr int kStageB = kCols * kRowBytes; // 36864
+constexpr int kStageA = kRows * kRowBytes; // 16384
+constexpr int kStageB = kHalfCols * kRowBytes; // 18432
 // Two LDS rings: W slices (3 stages, loaded 2 steps ahead) and x slices (4
 // stages, loaded 3 steps ahead: x streams from HBM while W is mostly served
-// by L2; measured on MI355X, leads of 2, 3, 4 and 5 steps for x gave 343,
-// 336, 342 and 347 us per call of 32768 x 7168).
+// by L2).
 constexpr int kWStages = 3, kWLead = kWStages - 1;
 constexpr int kXStages = 4, kXLead = kXStages - 1;
-constexpr int kXRing = kWStages * kStageB;             // offset of the x ring
-constexpr int kPipeBytes = kXRing + kXStages * kStageA; // 143360
-// the 8 x blocks and 36 W blocks (1 KiB each, one load instruction) of a
-// step: wavefront w loads x block w, then W blocks (5 each for w < 4, 4 for
-// the others)
-static_assert(kStageA / 1024 == kWaves && 4 * 5 + 4 * 4 == kStageB / 1024, "block split");
-constexpr int kMaxWBlocks = 5;
+constexpr int kXRing = kWStages * kStageB;              // offset of the x ring
+constexpr int kPipeBytes = kXRing + kXStages * kStageA; // 120832
+// the 16 x blocks and 18 W blocks (1 KiB each, one load instruction) of a
+// step: wavefront w loads x blocks 2w, 2w + 1, then W blocks (3 each for
+// w < 2, 2 for the others)
+constexpr int kXBlocks = 2;
+static_assert(kStageA / 1024 == kXBlocks * kWaves && 2 * 3 + 6 * 2 == kStageB / 1024,
+              "block split");
+constexpr int kMaxWBlocks = 3;
 constexpr int kMt = 4, kNt = 9;            // 16 x 16 tiles per wavefront
 constexpr int kWaveCols = kNt * 16;        // 144
-// epilogue staging: bf16 rows of 512 (+8 pad) and 64 (+8 pad) values, then
-// the per-wavefront square sums
-constexpr int kCkvLds = (kNorm + 8) * 2;   // 1040 bytes per row
-constexpr int kKLds = (kRope + 8) * 2;     // 144 bytes per row
-constexpr int kRedOff = kRows * (kCkvLds + kKLds);
-constexpr int kEpiBytes = kRedOff + 4 * kRows * 4;
+constexpr int kRopeTiles = 4;              // tiles 5..8 of the rope wavefront
+// epilogue staging: bf16 rows of 288 (+8 pad) values, then the per-column-
+// wavefront square sums and the full square sums per row
+constexpr int kStageRow = (kHalfCols + 8) * 2;   // 592 bytes per row
+constexpr int kRedOff = kRows * kStageRow;
+constexpr int kSumOff = kRedOff + 2 * kRows * 4;
+constexpr int kEpiBytes = kSumOff + kRows * 4;
 constexpr int kLdsBytes = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
+// bounded wait for the partner's sums (polls with a short sleep in between)
+constexpr int kSpinLimit = 1 << 20;
+// cache-policy operand of a buffer store: sc1 (device scope, write-through)
+constexpr int kStoreSc1 = 16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the unused counters at their maxima).
@@ -152,40 +168,51 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
-    const int wm = wave & 1, wn = wave >> 1;
-    const int nw = wave < 4 ? 5 : 4;                     // W blocks of this wavefront
-    const int wb0 = wave < 4 ? 5 * wave : 20 + 4 * (wave - 4);
-    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int nw = wave < 2 ? 3 : 2;                     // W blocks of this wavefront
+    const int wb0 = wave < 2 ? 3 * wave : 6 + 2 * (wave - 2);
+    // blockIdx b and b + 8 form a pair (same XCD under round-robin dispatch)
+    const int bx = blockIdx.x;
+    const int half = (bx >> 3) & 1;
+    const int64_t pair = (int64_t)(bx >> 4) * 8 + (bx & 7);
     const int64_t T = a.T, He = a.He;
+    const int64_t npairs = (T + kRows - 1) / kRows;
+    if (pair >= npairs)
+        return;                               // padding of the grid: both halves leave
+    const int64_t row0 = pair * kRows;
+    const bool rope_wave = half == 1 && wn == 1;         // columns 432..575 of the output
+    const int ntn = rope_wave ? kNt - kRopeTiles : kNt;  // tiles holding kv (not rope) columns
 
     // ---- direct global -> LDS loads ---------------------------------------
     // A 1 KiB block holds 16 rows of 64 bytes (one K step); lane l writes
     // byte 16 l: row 16 b + l / 4, slot l % 4, i.e. piece (l % 4) ^ swz(row)
-    // of that row. x block w = token rows 16 w .. +16 (rows past T read row
-    // T - 1: valid memory, results dropped); W block b = W rows 16 b .. +16.
-    const uint16_t *xsrc;
-    {
-        const int r = 16 * wave + (lane >> 2);
+    // of that row. x block b = token rows 16 b .. +16 (rows past T read row
+    // T - 1: valid memory, results dropped); W block b = rows 16 b .. +16 of
+    // this half of W.
+    const uint16_t *xsrc[kXBlocks];
+#pragma unroll
+    for (int i = 0; i < kXBlocks; ++i) {
+        const int r = 16 * (kXBlocks * wave + i) + (lane >> 2);
         int64_t t = row0 + r;
         t = t < T ? t : T - 1;
-        xsrc = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
+        xsrc[i] = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
     }
     const uint16_t *wsrc[kMaxWBlocks];
 #pragma unroll
     for (int i = 0; i < kMaxWBlocks; ++i) {
         const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
-        wsrc[i] = a.w + (int64_t)r * He + ((lane & 3) ^ swz(r)) * 8;
+        wsrc[i] = a.w + (int64_t)(kHalfCols * half + r) * He + ((lane & 3) ^ swz(r)) * 8;
     }
     // The cache slots of the rows this wavefront scatters (rows wave + 8 i,
-    // i < 16) are fetched now, lane i holding row i's: their latency hides
+    // i < 32) are fetched now, lane i holding row i's: their latency hides
     // behind the K loop instead of preceding each row's stores.
     int64_t my_slot = -1;
     {
-        const int64_t t = row0 + wave + kWaves * (lane & 15);
+        const int64_t t = row0 + wave + kWaves * (lane & 31);
         if (lane < kRows / kWaves && t < T)
             my_slot = a.slot[t];
     }
-    unsigned char *const xdst = smem + kXRing + wave * 1024;     // + stage * kStageA
+    unsigned char *const xdst = smem + kXRing + wave * kXBlocks * 1024;  // + stage * kStageA
     unsigned char *const wdst = smem + wb0 * 1024;               // + stage * kStageB + i KiB
 
     f32x4 acc[kMt][kNt];
@@ -205,7 +232,10 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     // (this order matters to the waits below)
     const int nk = (int)(He / kKt);
     for (int st = 0; st < kXLead && st < nk; ++st)
-        __builtin_amdgcn_global_load_lds(xsrc + st * kKt, (lds_void *)(xdst + st * kStageA), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kXBlocks; ++i)
+            __builtin_amdgcn_global_load_lds(xsrc[i] + st * kKt,
+                                             (lds_void *)(xdst + st * kStageA + i * 1024), 16, 0, 0);
     for (int st = 0; st < kWLead && st < nk; ++st) {
 #pragma unroll
         for (int i = 0; i < kMaxWBlocks; ++i)
@@ -217,18 +247,19 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         // This wavefront's loads complete in issue order. Its W blocks of
         // step kt are its last loads issued before those of step kt - 1
         // (x of step kt went out kXLead - kWLead steps earlier, before
-        // them), so allowing exactly the
-        // loads of step kt - 1 to stay in flight leaves both x and W of step
-        // kt in LDS; the barrier publishes every wavefront's and tells that
-        // all are past step kt - 1, whose stages are refilled next.
+        // them), so allowing exactly the loads of step kt - 1 to stay in
+        // flight leaves both x and W of step kt in LDS; the barrier
+        // publishes every wavefront's and tells that all are past step
+        // kt - 1, whose stages are refilled next.
         asm volatile("" ::: "memory");
         const int pending = kt == 0 ? (nk > 1 ? nw : 0)
-                                    : (kt + kXLead - 1 < nk ? 1 : 0) + (kt + kWLead - 1 < nk ? nw : 0);
+                                    : (kt + kXLead - 1 < nk ? kXBlocks : 0) +
+                                          (kt + kWLead - 1 < nk ? nw : 0);
         switch (pending) {
-        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(6)); break;
         case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(5)); break;
         case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2)); break;
         default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
         }
         __builtin_amdgcn_s_barrier();
@@ -249,14 +280,15 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         for (int n = 0; n < kNt; ++n) {
             if (n + 1 < kNt)
                 bf[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(wbase + b_off + (n + 1) * 16 * kRowBytes);
-            // one load between MFMA groups: x first, then the W blocks
-            if (n == 0) {
+            // one load between MFMA groups: the x blocks first, then W
+            if (n < kXBlocks) {
                 if (more_x)
-                    __builtin_amdgcn_global_load_lds(xsrc + sx * kKt, (lds_void *)xd, 16, 0, 0);
-            } else if (n <= kMaxWBlocks) {
-                if (more_w && n - 1 < nw)
-                    __builtin_amdgcn_global_load_lds(wsrc[n - 1] + sw * kKt,
-                                                     (lds_void *)(wd + (n - 1) * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(xsrc[n] + sx * kKt, (lds_void *)(xd + n * 1024),
+                                                     16, 0, 0);
+            } else if (n - kXBlocks < kMaxWBlocks) {
+                if (more_w && n - kXBlocks < nw)
+                    __builtin_amdgcn_global_load_lds(wsrc[n - kXBlocks] + sw * kKt,
+                                                     (lds_void *)(wd + (n - kXBlocks) * 1024), 16, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -269,21 +301,20 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 
     // ---- epilogue -----------------------------------------------------------
     // After the transpose, acc[m][n][e] is c[row][col] with
-    //   row = 16 m + 4 (lane / 16) + lane % 4,
-    //   col = 144 w + 16 n + 4 ((lane % 16) / 4) + e.
+    //   row = 64 wm + 16 m + 4 (lane / 16) + lane % 4,
+    //   col = 288 half + 144 wn + 16 n + 4 ((lane % 16) / 4) + e.
     const int rsub = 4 * (lane >> 4) + (lane & 3);       // row within a 16-row tile
     const int cq = 4 * ((lane & 15) >> 2);               // first column within a tile
-    const int ntn = wn < 3 ? kNt : 5;                    // tiles holding kv (not rope) columns
-    // The rope tiles (wn == 3, tiles 5..8) need the cos / sin pairs
+    // The rope tiles (rope wavefront, tiles 5..8) need the cos / sin pairs
     // (i0, i0 + 1) and (32 + i0, 33 + i0), i0 = 8 (n - 5) + cq / 2: those of
     // row tile 0 are loaded now, those of row tile m + 1 while row tile m is
     // computed (two register buffers), so their latencies overlap work.
-    uint32_t rc[2][kNt - 5][4];
-    auto load_rope_tables = [&](int m, uint32_t (&dst)[kNt - 5][4]) {
+    uint32_t rc[2][kRopeTiles][4];
+    auto load_rope_tables = [&](int m, uint32_t (&dst)[kRopeTiles][4]) {
         int64_t t = row0 + 64 * wm + 16 * m + rsub;
         t = t < T ? t : T - 1;
 #pragma unroll
-        for (int k = 0; k < kNt - 5; ++k) {
+        for (int k = 0; k < kRopeTiles; ++k) {
             const int i0 = 8 * k + cq / 2;
             dst[k][0] = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + i0);
             dst[k][1] = *reinterpret_cast<const uint32_t *>(a.cos + t * kRope + 32 + i0);
@@ -291,14 +322,15 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             dst[k][3] = *reinterpret_cast<const uint32_t *>(a.sin + t * kRope + 32 + i0);
         }
     };
-    if (wn == 3)
+    if (rope_wave)
         load_rope_tables(0, rc[0]);
 #pragma unroll
     for (int m = 0; m < kMt; ++m)
 #pragma unroll
         for (int n = 0; n < kNt; ++n)
             quad_transpose(acc[m][n], lane);
-    float *red = reinterpret_cast<float *>(smem + kRedOff);     // [4 column quarters][128]
+    float *red = reinterpret_cast<float *>(smem + kRedOff);     // [2 column wavefronts][256]
+    float *sums = reinterpret_cast<float *>(smem + kSumOff);    // [256]
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
         float s = 0.0f;
@@ -317,39 +349,85 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
     __syncthreads();
 
-    unsigned char *ckv_lds = smem;
-    unsigned char *k_lds = smem + kRows * kCkvLds;
+    // ---- swap the per-row partial sums with the other half of the pair ----
+    // workspace: float part[npairs][2][256], then uint32 flag[npairs][2].
+    // Wavefront 0 does the whole swap (lane l: rows 4l .. 4l + 3), so one
+    // release (its stores, then the flag) and one acquire suffice.
+    if (wave == 0) {
+        float *part = reinterpret_cast<float *>(a.workspace);
+        uint32_t *flag = reinterpret_cast<uint32_t *>(part + npairs * 2 * kRows);
+        float *mine = part + (pair * 2 + half) * kRows + 4 * lane;
+        float *theirs = part + (pair * 2 + (1 - half)) * kRows + 4 * lane;
+        uint32_t *my_flag = flag + pair * 2 + half;
+        uint32_t *their_flag = flag + pair * 2 + (1 - half);
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = red[4 * lane + j] + red[kRows + 4 * lane + j];
+            __hip_atomic_store(mine + j, p[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // release: the wavefront's sums above are visible before the flag
+        if (lane == 0)
+            __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        int spins = 0;
+        if (lane == 0) {
+            while (__hip_atomic_load(their_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+                   spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                ++spins;
+            }
+        }
+        const bool timed_out = __builtin_amdgcn_readfirstlane(spins) >= kSpinLimit;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float q = __hip_atomic_load(theirs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(theirs + j, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the same order in both halves: the sum of columns 0..287 first
+            sums[4 * lane + j] = half == 0 ? p[j] + q : q + p[j];
+        }
+        if (timed_out) {
+            if (lane == 0 && a.err)
+                atomicAdd(a.err, 1);
+        } else if (lane == 0) {
+            // the partner's sums are read and zeroed: clear its flag (the
+            // next use of this pair's area is a later kernel on the stream)
+            __hip_atomic_store(their_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+
+    unsigned char *stage = smem;
     const float alpha = a.alpha;
     float g[kNt][4];
 #pragma unroll
     for (int n = 0; n < kNt; ++n) {
-        const int col = kWaveCols * wn + 16 * n + cq;
+        const int col = kHalfCols * half + kWaveCols * wn + 16 * n + cq;
         const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + (col < kNorm ? col : 0));
         g[n][0] = bf16_lo(gw.x); g[n][1] = bf16_hi(gw.x);
         g[n][2] = bf16_lo(gw.y); g[n][3] = bf16_hi(gw.y);
     }
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
-        if (wn == 3 && m + 1 < kMt)
+        if (rope_wave && m + 1 < kMt)
             load_rope_tables(m + 1, rc[(m + 1) & 1]);
         const int r = 64 * wm + 16 * m + rsub;
-        const float ss = (red[r] + red[kRows + r]) + (red[2 * kRows + r] + red[3 * kRows + r]);
-        const float rr = 1.0f / sqrtf(ss / (float)kNorm + a.eps);
+        const float rr = 1.0f / sqrtf(sums[r] / (float)kNorm + a.eps);
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
             const f32x4 v = acc[m][n];
             if (n < ntn) {
-                const int col = kWaveCols * wn + 16 * n + cq;
+                const int col = kWaveCols * wn + 16 * n + cq;       // within the half
                 const uint2 o = {pack_bf16(alpha * ((v[0] * rr) * g[n][0]),
                                            alpha * ((v[1] * rr) * g[n][1])),
                                  pack_bf16(alpha * ((v[2] * rr) * g[n][2]),
                                            alpha * ((v[3] * rr) * g[n][3]))};
-                *reinterpret_cast<uint2 *>(ckv_lds + r * kCkvLds + col * 2) = o;
+                *reinterpret_cast<uint2 *>(stage + r * kStageRow + col * 2) = o;
             } else {
                 // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
                 // and (2 i0 + 2, 2 i0 + 3) give outputs i0, i0 + 1 and
-                // 32 + i0, 33 + i0
-                const int k = n - 5 > 0 ? n - 5 : 0;   // n >= 5 here
+                // 32 + i0, 33 + i0, staged after the 224 kv columns of the half
+                const int k = n - ntn > 0 ? n - ntn : 0;   // n >= ntn here
                 const int i0 = 8 * k + cq / 2;
                 const uint32_t c0 = rc[m & 1][k][0], c1 = rc[m & 1][k][1];
                 const uint32_t s0 = rc[m & 1][k][2], s1 = rc[m & 1][k][3];
@@ -357,16 +435,31 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 const float lo1 = v[2] * bf16_hi(c0) - v[3] * bf16_hi(s0);
                 const float hi0 = v[1] * bf16_lo(c1) + v[0] * bf16_lo(s1);
                 const float hi1 = v[3] * bf16_hi(c1) + v[2] * bf16_hi(s1);
-                *reinterpret_cast<uint32_t *>(k_lds + r * kKLds + i0 * 2) = pack_bf16(lo0, lo1);
-                *reinterpret_cast<uint32_t *>(k_lds + r * kKLds + (32 + i0) * 2) =
-                    pack_bf16(hi0, hi1);
+                unsigned char *kr = stage + r * kStageRow + (kNorm - kHalfCols) * 2;
+                *reinterpret_cast<uint32_t *>(kr + i0 * 2) = pack_bf16(lo0, lo1);
+                *reinterpret_cast<uint32_t *>(kr + (32 + i0) * 2) = pack_bf16(hi0, hi1);
             }
         }
     }
     __syncthreads();
 
-    // ---- scatter: wavefront w writes rows w, w + 8, ... ---------------------
-#pragma unroll
+    // ---- scatter: wavefront w writes its half of rows w, w + 8, ... --------
+    // half 0: ckv bytes [0, 576) of the row (36 pieces of 16 bytes);
+    // half 1: ckv bytes [576, 1024) (28 pieces), then the k row (8 pieces).
+    // Caches below 4 GiB take sc1 (device scope) buffer stores, which write
+    // through the XCD's L2 instead of leaving the rows dirty there: the
+    // write-backs of the swap above and of the kernel's end then find little
+    // to flush. The descriptors cover exactly the caches.
+    constexpr int kPieces = kHalfCols * 2 / 16;                 // 36
+    constexpr int kCkvPieces1 = (kNorm - kHalfCols) * 2 / 16;   // 28
+    const bool buf = a.cache_rows * kNorm * 2 <= (int64_t)UINT32_MAX;
+    const __amdgpu_buffer_rsrc_t ckv_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.ckv_cache, 0, (int)(uint32_t)(a.cache_rows * kNorm * 2),
+                                          0x00020000);
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.k_cache, 0, (int)(uint32_t)(a.cache_rows * kRope * 2),
+                                          0x00020000);
+#pragma unroll 4
     for (int i = 0; i < kRows / kWaves; ++i) {
         const int r = wave + kWaves * i;
         const int64_t t = row0 + r;
@@ -376,25 +469,50 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                                          (int)(my_slot >> 32), i) << 32) |
                                     (uint32_t)__builtin_amdgcn_readlane((int)my_slot, i));
         if (v < 0 || v >= a.cache_rows) {
-            if (v != -1 && lane == 0 && a.err)
+            if (half == 0 && v != -1 && lane == 0 && a.err)
                 atomicAdd(a.err, 1);
             continue;
         }
-        const uint4 cv = *reinterpret_cast<const uint4 *>(ckv_lds + r * kCkvLds + lane * 16);
-        *reinterpret_cast<uint4 *>(a.ckv_cache + v * kNorm + lane * 8) = cv;
-        if (lane < 8) {
-            const uint4 kv = *reinterpret_cast<const uint4 *>(k_lds + r * kKLds + lane * 16);
-            *reinterpret_cast<uint4 *>(a.k_cache + v * kRope + lane * 8) = kv;
+        if (lane < kPieces) {
+            const uint4 cv = *reinterpret_cast<const uint4 *>(stage + r * kStageRow + lane * 16);
+            const u32x4 w = {cv.x, cv.y, cv.z, cv.w};
+            // lanes below nckv write the ckv row piece, the others the k row
+            // (two stores, each with one descriptor for the whole wavefront)
+            const int nckv = half == 0 ? kPieces : kCkvPieces1;
+            const int64_t ckv_off = v * kNorm * 2 + kHalfCols * 2 * half + lane * 16;
+            const int64_t k_off = v * kRope * 2 + (lane - nckv) * 16;
+            if (lane < nckv) {
+                if (buf)
+                    __builtin_amdgcn_raw_buffer_store_b128(w, ckv_rsrc, (int)(uint32_t)ckv_off, 0,
+                                                           kStoreSc1);
+                else
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(a.ckv_cache) +
+                                               ckv_off) = cv;
+            } else {
+                if (buf)
+                    __builtin_amdgcn_raw_buffer_store_b128(w, k_rsrc, (int)(uint32_t)k_off, 0,
+                                                           kStoreSc1);
+                else
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(a.k_cache) +
+                                               k_off) = cv;
+            }
         }
     }
 }
 
 }  // namespace
 
+int64_t mla_kv_head_workspace_bytes(int64_t T)
+{
+    const int64_t npairs = T > 0 ? (T + kRows - 1) / kRows : 0;
+    return npairs * (2 * kRows * 4 + 2 * 4);
+}
+
 hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)
 {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-    const int64_t grid = (a.T + kRows - 1) / kRows;
+    const int64_t npairs = (a.T + kRows - 1) / kRows;
+    const int64_t grid = 16 * ((npairs + 7) / 8);   // pairs in groups of 8: b and b + 8
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(mla_kv_head_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess)

@@ -20,13 +20,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
            if h.endswith(".h")]
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP = range(7)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP, WORKSPACE = range(8)
 
 
 def header_functions():
     src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t|int64_t)\s*\*?\s*(\w+)\s*\(", src,
+                                 re.M)))
 
 
 def test_exports_match_header():
@@ -39,13 +40,13 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 103
+    assert k.lib().kvrc_version() == 104
 
 
 def test_status_strings():
     L = k.lib()
-    for s in range(7):
-        assert L.kvrc_status_string(s)
+    for s in range(8):
+        assert L.kvrc_status_string(s) != b"unknown status"
     assert L.kvrc_status_string(99) == b"unknown status"
 
 
@@ -130,17 +131,31 @@ def test_norm_validation(over, want):
 
 
 M = {name: (i + 40) << 32 for i, name in enumerate(
-    ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err"])}
+    ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err", "ws"])}
+WS_300 = 2 * (2 * 256 * 4 + 2 * 4)      # 300 tokens: two pairs of workgroups
 
 
 def mla(**over):
     a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
              slot=M["slot"], kc=M["kc"], ckv=M["ckv"], T=300, He=7168, NB=64, BS=128, eps=1e-6,
-             err=None, stream=None)
+             ws=M["ws"], wsb=WS_300, err=None, stream=None)
     a.update(over)
     return k.lib().kvrc_mla_kv_head_paged(a["x"], a["w"], a["gamma"], a["alpha"], a["cos"],
                                           a["sin"], a["slot"], a["kc"], a["ckv"], a["T"], a["He"],
-                                          a["NB"], a["BS"], a["eps"], a["err"], a["stream"])
+                                          a["NB"], a["BS"], a["eps"], a["ws"], a["wsb"], a["err"],
+                                          a["stream"])
+
+
+def test_mla_workspace_bytes():
+    """One pair of workgroups per 256 tokens: 256 partial sums per half and
+    two flags."""
+    f = k.lib().kvrc_mla_kv_head_workspace_bytes
+    assert f(0) == 0
+    assert f(1) == f(256) == 2056
+    assert f(257) == 2 * 2056
+    assert f(32768) == 128 * 2056
+    assert f(-1) == -1 and f(1 << 31) == -1
+    assert f(300) == WS_300
 
 
 @pytest.mark.parametrize("over,want", [
@@ -153,7 +168,9 @@ def mla(**over):
     # x holds 300 * 7168 * 2 bytes: a cache starting inside it aliases
     (dict(kc=M["x"] + 4096), ALIAS), (dict(ckv=M["w"]), ALIAS), (dict(kc=M["ckv"] + 16), ALIAS),
     (dict(err=M["kc"]), ALIAS),
-    (dict(T=0), OK), (dict(T=0, x=None, kc=None), OK),
+    (dict(ws=None), NULL), (dict(ws=M["ws"] + 8), ALIGN), (dict(ws=M["ckv"] + 64), ALIAS),
+    (dict(ws=M["x"]), ALIAS), (dict(wsb=WS_300 - 1), WORKSPACE), (dict(wsb=0), WORKSPACE),
+    (dict(T=0), OK), (dict(T=0, x=None, kc=None), OK), (dict(T=0, ws=None, wsb=0), OK),
 ])
 def test_mla_validation(over, want):
     assert mla(**over) == want

@@ -44,14 +44,24 @@ def dbf(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def run_mla_gpu(case, slots=None, err=None):
+def new_workspace(T):
+    return torch.zeros(max(1, k.kvrc_mla_kv_head_workspace_bytes(T)), dtype=torch.uint8,
+                       device=DEV)
+
+
+def run_mla_gpu(case, slots=None, err=None, workspace=None):
+    """One call; the workspace (fresh unless given) must be all zero again
+    afterwards."""
     caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
     slots = case["slot_mapping"] if slots is None else slots
+    T = case["x"].shape[0]
+    ws = new_workspace(T) if workspace is None else workspace
     k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
                              dbf(case["sin"]), torch.from_numpy(slots).to(DEV),
-                             caches["k_cache"], caches["ckv_cache"], alpha_kv=case["alpha"],
-                             eps=case["eps"], err_count=err)
+                             caches["k_cache"], caches["ckv_cache"], workspace=ws,
+                             alpha_kv=case["alpha"], eps=case["eps"], err_count=err)
     torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
     return {n: t.view(torch.int16).cpu().numpy().view(np.uint16) for n, t in caches.items()}
 
 
@@ -189,3 +199,84 @@ def test_mla_deterministic_across_launch_sizes():
                                   sub["ckv_cache"].reshape(-1, 512)[rows])
     np.testing.assert_array_equal(full["k_cache"].reshape(-1, 64)[rows],
                                   sub["k_cache"].reshape(-1, 64)[rows])
+
+
+@pytest.mark.parametrize("S", [255, 256, 257, 2049, 2305])
+def test_mla_pair_boundaries(S):
+    """256 rows per pair of workgroups, pairs in groups of 8: partial pairs,
+    a padded grid and a ragged last pair."""
+    say(f"[mla] pair boundaries T={S}")
+    case = gen.mla_kv_head_case(530 + S, B=1, S=S, He=64, num_blocks=160, block_size=16,
+                                slot_kind="random", skip_frac=0.05)
+    compare_mla(case, run_mla_gpu(case))
+
+
+def test_mla_many_pairs_beyond_one_dispatch_wave():
+    """More workgroups than the chip holds at once (640 pairs): pairs start
+    while earlier ones still run; no wait times out (err stays 0)."""
+    say("[mla] T=163840 (1280 workgroups)")
+    case = gen.mla_kv_head_case(540, B=4, S=40960, He=64, num_blocks=1400, block_size=128,
+                                slot_kind="random", skip_frac=0.01)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    compare_mla(case, run_mla_gpu(case, err=err))
+    assert int(err.item()) == 0
+
+
+def test_mla_workspace_reused_across_calls_and_graph_replays():
+    """One workspace for consecutive calls and for replays of a captured
+    graph (eager work in between): every result equals the eager call's and
+    the workspace ends zero each time."""
+    say("[mla] workspace reuse and graph replays")
+    a = gen.mla_kv_head_case(550, B=1, S=600, He=256, num_blocks=64, block_size=16,
+                             slot_kind="random")
+    b = gen.mla_kv_head_case(551, B=1, S=600, He=256, num_blocks=64, block_size=16,
+                             slot_kind="random")
+    ws = new_workspace(600)
+    got_a = run_mla_gpu(a, workspace=ws)
+    got_b = run_mla_gpu(b, workspace=ws)
+    compare_mla(a, got_a)
+    compare_mla(b, got_b)
+
+    x, w, gm = dbf(a["x"]), dbf(a["w"]), dbf(a["gamma"])
+    cs, sn = dbf(a["cos"]), dbf(a["sin"])
+    sl = torch.from_numpy(a["slot_mapping"]).to(DEV)
+    kc = dbf(a["caches"]["k_cache"].numpy())
+    ck = dbf(a["caches"]["ckv_cache"].numpy())
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        k.kvrc_mla_kv_head_paged(x, w, gm, cs, sn, sl, kc, ck, workspace=ws,
+                                 alpha_kv=a["alpha"], eps=a["eps"], stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        k.kvrc_mla_kv_head_paged(x, w, gm, cs, sn, sl, kc, ck, workspace=ws,
+                                 alpha_kv=a["alpha"], eps=a["eps"], stream=stream)
+    want_k = got_a["k_cache"]
+    want_c = got_a["ckv_cache"]
+    sentinel = int(np.array([gen.BF16_SENTINEL], dtype=np.uint16).view(np.int16)[0])
+    for rep in range(3):
+        kc.view(torch.int16).fill_(sentinel)
+        ck.view(torch.int16).fill_(sentinel)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0, f"replay {rep}: workspace not left zero"
+        np.testing.assert_array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), want_k)
+        np.testing.assert_array_equal(ck.view(torch.int16).cpu().numpy().view(np.uint16), want_c)
+
+
+def test_mla_workspace_too_small_is_rejected():
+    case = gen.mla_kv_head_case(552, B=1, S=300, He=64, num_blocks=32, block_size=16,
+                                slot_kind="random")
+    need = k.kvrc_mla_kv_head_workspace_bytes(300)
+    ws = torch.zeros(need - 8, dtype=torch.uint8, device=DEV)
+    caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
+    with pytest.raises(k.KvrcError):
+        k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]),
+                                 dbf(case["cos"]), dbf(case["sin"]),
+                                 torch.from_numpy(case["slot_mapping"]).to(DEV),
+                                 caches["k_cache"], caches["ckv_cache"], workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(caches["ckv_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+                  == gen.BF16_SENTINEL)
