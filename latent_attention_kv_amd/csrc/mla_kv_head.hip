@@ -264,6 +264,10 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        // raised wave priority while this step's MFMAs issue (measured
+        // ~1 % faster: the arbiter favours the wavefront feeding the matrix
+        // pipe over the one still waiting on its loads)
+        __builtin_amdgcn_s_setprio(1);
         const int sx = kt + kXLead, sw = kt + kWLead;    // steps loaded during this one
         const bool more_x = sx < nk, more_w = sw < nk;
         unsigned char *const xd = xdst + (sx % kXStages) * kStageA;
@@ -296,6 +300,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf[n & 1], acc[m][n], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();                          // every stage read: LDS reused below
 
