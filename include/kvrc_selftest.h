@@ -34,6 +34,17 @@ int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_shared, flo
                             float *root, int64_t n, hipStream_t stream);
 
 /*
+ * For i in [0, n): recip[i] = the reciprocal routine of the kernels applied to
+ * b[i]: the hardware reciprocal estimate corrected once by Newton-Raphson with
+ * an exact residual. The kernels use it only where b is in [2^-60, 2^60],
+ * where it must equal the IEEE float32 1 / b[i]. b and recip are float32
+ * device memory of n elements (16-byte aligned, not overlapping). Returns
+ * KVRC_OK, KVRC_ERR_NULL, KVRC_ERR_SHAPE (n < 0), KVRC_ERR_ALIGN,
+ * KVRC_ERR_ALIAS or KVRC_ERR_HIP. Asynchronous on `stream`.
+ */
+int32_t kvrc_selftest_recip(const float *b, float *recip, int64_t n, hipStream_t stream);
+
+/*
  * For i in [0, n): code[i] = the FLOAT8 E4M3FN code the kernels store for the
  * float32 quotient x[i] (nearest E4M3FN value, ties to the even code,
  * magnitudes beyond 448 saturating to +-448; the sign bit of the code is the

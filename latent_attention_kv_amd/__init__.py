@@ -32,7 +32,8 @@ import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
            "kvrc_norm_rope_cache", "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
-           "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_e4m3",
+           "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_recip",
+           "kvrc_selftest_e4m3",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
                     "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
                     "qsa_prepare", "qsa_select_topk",
-                    "kvrc_selftest_arith", "kvrc_selftest_e4m3")
+                    "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3")
 
 _lib = None
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_prepare.restype = I32
     L.kvrc_selftest_arith.argtypes = [P, P, P, P, P, I64, P]
     L.kvrc_selftest_arith.restype = I32
+    L.kvrc_selftest_recip.argtypes = [P, P, I64, P]
+    L.kvrc_selftest_recip.restype = I32
     L.kvrc_selftest_e4m3.argtypes = [P, P, I64, P]
     L.kvrc_selftest_e4m3.restype = I32
     _lib = L
@@ -300,6 +303,17 @@ def kvrc_selftest_arith(a, b, q_shared, q_ieee, root, *, stream=None):
     st = lib().kvrc_selftest_arith(_ptr(a), _ptr(b), _ptr(q_shared), _ptr(q_ieee), _ptr(root),
                                    a.numel(), _stream(stream))
     _check(st, "kvrc_selftest_arith")
+
+
+def kvrc_selftest_recip(b, recip, *, stream=None):
+    """Reciprocal self-test (include/kvrc_selftest.h): float32 b -> the
+    kernels' reciprocal of each element."""
+    _need(b, "b", (torch.float32,), 1)
+    _need(recip, "recip", (torch.float32,), 1)
+    if recip.numel() != b.numel():
+        raise ValueError("b and recip must have the same length")
+    _check(lib().kvrc_selftest_recip(_ptr(b), _ptr(recip), b.numel(), _stream(stream)),
+           "kvrc_selftest_recip")
 
 
 def kvrc_selftest_e4m3(x, code, *, stream=None):

@@ -200,6 +200,19 @@ __device__ __forceinline__ bool fast_div_divisor_ok(float b)
     return b >= kFastDivLo && b <= kFastDivHi;    // false for NaN
 }
 
+// RN(1/b) for 2^-60 <= b <= 2^60 without the IEEE division sequence: the
+// hardware estimate y0 (v_rcp_f32, within one ulp of 1/b) and one
+// Newton-Raphson correction with the residual e = 1 - b*y0 (exact in an fma
+// when y0 is that close), y1 = RN(y0 + y0*e). Three VALU operations instead
+// of about eleven; the self-test kvrc_selftest_recip lets a test compare it
+// with IEEE division for every float32 of the domain.
+__device__ __forceinline__ float rcp_rn(float b)
+{
+    const float y0 = __builtin_amdgcn_rcpf(b);
+    const float e = __builtin_fmaf(-b, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
 __device__ __forceinline__ float div_rn_shared(float a, float b, float rb)
 {
     float q = a * rb;
@@ -207,6 +220,16 @@ __device__ __forceinline__ float div_rn_shared(float a, float b, float rb)
     q = __builtin_fmaf(r, rb, q);
     r = __builtin_fmaf(-q, b, a);
     return __builtin_fmaf(r, rb, q);
+}
+
+// RN(amax / d) for a row maximum amax >= 0 and a constant divisor d (127 or
+// 448): the shared-divisor quotient with RN(1/d) folded by the compiler when
+// amax lies in its dividend domain, IEEE division otherwise (0, tiny, huge).
+__device__ __forceinline__ float row_scale(float amax, float d)
+{
+    if (amax >= kFastDivDividendLo && amax <= 0x1p66f)
+        return div_rn_shared(amax, d, 1.0f / d);
+    return amax / d;
 }
 
 // 1.5 * 2^23: for |q| < 2^22, RN(q + kRoundMagic) = kRoundMagic + rint(q)

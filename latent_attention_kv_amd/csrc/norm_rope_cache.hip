@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
     // are inside its domain (|x| >= 2^-60 and |x| <= sqrt(Dv)*rms), else IEEE.
     float y[NCH][8];
     if (fast_div_divisor_ok(rms) && min_sq >= kMinSquareBits) {
-        const float rr = 1.0f / rms;
+        const float rr = rcp_rn(rms);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             float g[8];
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
             for (int e = 0; e < 8; ++e)
                 amax = fmaxf(amax, fabsf(y[j][e]));
         amax = fold_max<LPT>(amax);
-        const float scale = amax / 127.0f;
+        const float scale = row_scale(amax, 127.0f);
         // code = rint(RN(y / scale)), half to even. In the shared-divisor
         // domain of scale, with rs = RN(1/scale) and P = y * rs (exact):
         //   |P - y/scale| and |RN(y/scale) - y/scale| are both below
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
         // dividend range have |quotient| < 2^-4 and code 0 either way).
         uint32_t cb[NCH][8];
         if (fast_div_divisor_ok(scale)) {
-            const float rs = 1.0f / scale;
+            const float rs = rcp_rn(scale);
             // smallest (low 15 bits of f + 0x4001) << 17 over the lane: at most
             // 2 << 17 exactly when some low bits are 0x3fff, 0x4000 or 0x4001
             uint32_t dmin = 0xffffffffu;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
             for (int e = 0; e < 8; ++e)
                 amax = fmaxf(amax, fabsf(y[j][e]));
         amax = fold_max<LPT>(amax);
-        const float scale = amax / kE4m3Max;
+        const float scale = row_scale(amax, kE4m3Max);
         // The code is that of Q = RN(y / scale). In the shared-divisor domain
         // of scale, t = RN(y * RN(1/scale)) is within |Q| * (2^-23 + 2^-48)
         // of y / scale, so t and Q lie less than 2.5 ulps apart; the rounding
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NT) void norm_rope_cache_d576(NormRopeCacheArgs a)
         // inside the conversion's range.
         float q[NCH][8];
         if (fast_div_divisor_ok(scale)) {
-            const float rs = 1.0f / scale;
+            const float rs = rcp_rn(scale);
             uint32_t kmin = 0xffffffffu;  // smallest midpoint key of the lane
             float tmin = __builtin_inff(); // smallest |t| of the lane
 #pragma unroll

@@ -24,6 +24,14 @@ __global__ __launch_bounds__(256) void arith_kernel(const float *__restrict__ a,
     }
 }
 
+__global__ __launch_bounds__(256) void recip_kernel(const float *__restrict__ b,
+                                                    float *__restrict__ r, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        r[i] = kvrc::rcp_rn(b[i]);
+}
+
 // Four quotients per thread. Magnitudes below 464 go straight to the
 // conversion (as on the kernels' path where the quotient is known to stay
 // below 448 * (1 + 2^-22)); larger ones are clamped first, as the kernels do
@@ -77,6 +85,25 @@ extern "C" int32_t kvrc_selftest_arith(const float *a, const float *b, float *q_
     (void)hipGetLastError();
     hipLaunchKernelGGL(arith_kernel, dim3(grid), dim3(256), 0, stream, a, b, q_shared, q_ieee,
                        root, n);
+    return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
+}
+
+extern "C" int32_t kvrc_selftest_recip(const float *b, float *recip, int64_t n, hipStream_t stream)
+{
+    if (n < 0)
+        return KVRC_ERR_SHAPE;
+    if (n == 0)
+        return KVRC_OK;
+    if (!b || !recip)
+        return KVRC_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(b) % 16 || reinterpret_cast<uintptr_t>(recip) % 16)
+        return KVRC_ERR_ALIGN;
+    if (overlaps(b, recip, n * 4))
+        return KVRC_ERR_ALIAS;
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(recip_kernel, dim3(grid), dim3(256), 0, stream, b, recip, n);
     return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
 }
 

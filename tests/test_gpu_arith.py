@@ -8,6 +8,10 @@ correctly rounded quotient on its domain 2^-60 <= b <= 2^60,
 (b) against the device's IEEE division: exhaustively over every bf16
 numerator in the domain (the kv values the norm divides) for 2^15 divisors,
 and on 2^30 random float32 numerators (the quantisation divides float32 y).
+(b') The reciprocal routine (hardware estimate plus one Newton correction)
+equals the host's IEEE 1/b for every float32 b in [2^-60, 2^60], and the
+shared-divisor quotient equals the host's IEEE amax / d for the two row
+scale divisors d = 127 and 448 and every float32 amax in [2^-64, 2^66].
 (c) The float32 -> E4M3FN conversion of the fp8 rows equals the oracle's
 encoder on every code value, every midpoint and its float32 neighbours, the
 saturation range and random float32 values.
@@ -172,3 +176,52 @@ def test_e4m3_random_float32():
     bits = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
     y = bits.view(np.float32)
     check_e4m3(y[np.isfinite(y)])
+
+
+def test_reciprocal_routine_every_float_of_the_domain():
+    """All 1,006,632,961 float32 values in [2^-60, 2^60] (bit patterns
+    0x21800000 .. 0x5D800000), in chunks; expected values are numpy's IEEE
+    float32 division on the host."""
+    lo, hi = 0x21800000, 0x5D800000
+    chunk = 1 << 26
+    b = torch.empty(chunk, dtype=torch.float32, device=DEV)
+    r = torch.empty_like(b)
+    bad = 0
+    for start in range(lo, hi + 1, chunk):
+        n = min(chunk, hi + 1 - start)
+        torch.arange(start, start + n, dtype=torch.int32, device=DEV, out=bits(b[:n]))
+        k.kvrc_selftest_recip(b[:n], r[:n])
+        got = bits(r[:n]).cpu().numpy()
+        hb = np.arange(start, start + n, dtype=np.int64).astype(np.uint32).view(np.float32)
+        want = (np.float32(1.0) / hb).view(np.int32)
+        miss = np.flatnonzero(got != want)
+        if miss.size:
+            print(f"[arith] recip mismatches in chunk at {start:#x}: {miss.size}, first b bits "
+                  f"{start + int(miss[0]):#x}", flush=True)
+        bad += miss.size
+    assert bad == 0
+
+
+@pytest.mark.parametrize("d", [127.0, 448.0])
+def test_row_scale_divisors_every_float_of_the_domain(d):
+    """amax / 127 (int8) and amax / 448 (E4M3FN) by the shared-divisor
+    quotient, for all float32 amax in [2^-64, 2^66] (bit patterns
+    0x1F800000 .. 0x60800000); expected values from numpy on the host."""
+    lo, hi = 0x1F800000, 0x60800000
+    chunk = 1 << 26
+    a = torch.empty(chunk, dtype=torch.float32, device=DEV)
+    b = torch.full((chunk,), d, dtype=torch.float32, device=DEV)
+    qs, qi, rt = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
+    bad = 0
+    for start in range(lo, hi + 1, chunk):
+        n = min(chunk, hi + 1 - start)
+        torch.arange(start, start + n, dtype=torch.int32, device=DEV, out=bits(a[:n]))
+        k.kvrc_selftest_arith(a[:n], b[:n], qs[:n], qi[:n], rt[:n])
+        got = bits(qs[:n]).cpu().numpy()
+        ha = np.arange(start, start + n, dtype=np.int64).astype(np.uint32).view(np.float32)
+        want = (ha / np.float32(d)).view(np.int32)
+        miss = np.flatnonzero(got != want)
+        if miss.size:
+            print(f"[arith] /{d} mismatches in chunk at {start:#x}: {miss.size}", flush=True)
+        bad += miss.size
+    assert bad == 0
