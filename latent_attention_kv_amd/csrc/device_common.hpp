@@ -14,13 +14,11 @@
 
 // Streaming inputs (kv rows, cos/sin rows, read exactly once) are loaded with
 // the non-temporal hint, which keeps them from displacing the shared gamma
-// row and the indices in the caches. Stores use the default policy: on
-// MI355X the non-temporal hint made the cache-row writes slower.
+// row and the indices in the caches. (Cache rows are written through L2 with
+// sc1 stores where the caches fit a buffer descriptor: the non-temporal hint
+// made those writes slower on MI355X.)
 #ifndef KVRC_NT_LOADS
 #define KVRC_NT_LOADS 1
-#endif
-#ifndef KVRC_NT_STORES
-#define KVRC_NT_STORES 0
 #endif
 
 namespace kvrc {
@@ -40,20 +38,9 @@ __device__ __forceinline__ T stream_load(const void *p)
 #endif
 }
 
-template <typename T>
-__device__ __forceinline__ void stream_store(void *p, T v)
-{
-#if KVRC_NT_STORES
-    __builtin_nontemporal_store(v, static_cast<T *>(p));
-#else
-    *static_cast<T *>(p) = v;
-#endif
-}
-
 __device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 __device__ __forceinline__ u32x4 to_u32x4(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
 __device__ __forceinline__ uint2 to_uint2(u32x2 v) { return make_uint2(v.x, v.y); }
-__device__ __forceinline__ u32x2 to_u32x2(uint2 v) { return u32x2{v.x, v.y}; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
