@@ -280,3 +280,42 @@ def test_mla_workspace_too_small_is_rejected():
     torch.cuda.synchronize()
     assert np.all(caches["ckv_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
                   == gen.BF16_SENTINEL)
+
+
+def test_mla_cache_larger_than_4gib():
+    """Caches of 4 GiB or more take the plain-store path of the scatter (the
+    sc1 buffer stores need 32-bit offsets): rows beyond the 32-bit byte
+    offset land exactly and nothing else in the caches changes."""
+    T, He, BS = 300, 256, 128
+    rows_4g = 2 ** 32 // 1024                                  # ckv rows below the 4 GiB offset
+    NB = rows_4g // BS + 64
+    say(f"[mla] cache over 4 GiB: {NB} blocks")
+    case = gen.mla_kv_head_case(560, B=1, S=T, He=He, num_blocks=1, block_size=T,
+                                slot_kind="random", skip_frac=0.05)   # compact slots 0..T-1
+    rng = gen.rng_for(561)
+    lo = rng.choice(rows_4g - 1, size=T // 2, replace=False)
+    hi = rows_4g + rng.choice(NB * BS - rows_4g, size=T - T // 2, replace=False)
+    big = np.concatenate([lo, hi]).astype(np.int64)
+    rng.shuffle(big)
+    big[case["slot_mapping"] < 0] = -1
+    sentinel = int(np.array([gen.BF16_SENTINEL], dtype=np.uint16).view(np.int16)[0])
+    kc = torch.full((NB, BS, 1, 64), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ck = torch.full((NB, BS, 1, 512), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ws = new_workspace(T)
+    k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
+                             dbf(case["sin"]), torch.from_numpy(big).to(DEV), kc, ck,
+                             workspace=ws, alpha_kv=case["alpha"], eps=case["eps"])
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    valid = big >= 0
+    idx = torch.from_numpy(big[valid]).to(DEV)
+    compact = case["slot_mapping"][valid]
+    got = {"ckv_cache": np.full((T, 512), gen.BF16_SENTINEL, np.uint16),
+           "k_cache": np.full((T, 64), gen.BF16_SENTINEL, np.uint16)}
+    for name, t, d in (("ckv_cache", ck, 512), ("k_cache", kc, 64)):
+        rows = t.view(-1, d)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+        got[name][compact] = rows
+        changed = int((t.view(torch.int16) != sentinel).sum().item())
+        in_rows = int((t.view(-1, d)[idx].view(torch.int16) != sentinel).sum().item())
+        assert changed == in_rows, f"{name}: bytes outside the written rows changed"
+    compare_mla(case, got)
