@@ -107,12 +107,24 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// The maximum steps are single v_max_f32_dpp instructions. The values are
+// results of arithmetic (never signalling NaNs), so the IEEE-mode v_max_f32
+// already returns what fmaxf would (a quiet NaN operand yields the other
+// one); written with fmaxf, each step also quiets its DPP operand and loads
+// an unused "old" value, three instructions more. Each step starts with the
+// two wait states a DPP read needs after the VALU write of its source.
 __device__ __forceinline__ float row_max16(float v)
 {
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    v = fmaxf(v, dpp<kDppXor2>(v));
-    v = fmaxf(v, dpp<kDppHalfMirror>(v));
-    return fmaxf(v, dpp<kDppMirror>(v));
+    float r;
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(v));
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                 : "=v"(v) : "v"(r));
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(v));
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
+                 : "=v"(v) : "v"(r));
+    return v;
 }
 
 __device__ __forceinline__ float row_sum16(float v)
