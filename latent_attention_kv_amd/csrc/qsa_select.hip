@@ -640,23 +640,57 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
         }
         __syncthreads();
 
-        // exp2(s - max) in place; head sums in the same two steps
+        // exp2(s - max) in place. exp2f only adjusts arguments below -126
+        // (subnormal results); at or above it, it equals the bare v_exp_f32.
+        // So a lane whose smallest argument is >= -126 (every lane unless
+        // scores spread over 126 in log2 units) takes v_exp_f32 alone.
+        float xmin = 0.0f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                float lo = INFINITY;
+#pragma unroll
+                for (int jl = 0; jl < JWM; ++jl)
+                    lo = ok[jl] ? fminf(lo, e[jl][ht][q]) : lo;
+                xmin = fminf(xmin, lo - m[q]);
+            }
+        }
+        if (xmin < -126.0f) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int jl = 0; jl < JWM; ++jl)
+                        e[jl][ht][q] = ok[jl] ? exp2f(e[jl][ht][q] - m[q]) : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int jl = 0; jl < JWM; ++jl)
+                        e[jl][ht][q] = ok[jl] ? __builtin_amdgcn_exp2f(e[jl][ht][q] - m[q]) : 0.0f;
+            }
+        }
+        // head sums: over this wavefront's columns, then over the wavefronts
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
                 float z = 0.0f;
 #pragma unroll
-                for (int jl = 0; jl < JWM; ++jl) {
-                    e[jl][ht][q] = ok[jl] ? exp2f(e[jl][ht][q] - m[q]) : 0.0f;
+                for (int jl = 0; jl < JWM; ++jl)
                     z += e[jl][ht][q];
-                }
                 z = row_sum16(z);
                 if (fr == 0)
                     wsum[(16 * ht + 4 * g + q) * kWaves + wave] = z;
             }
-        }
         __syncthreads();
         for (int h = tid; h < H; h += kThreads) {
             const f32x4 lo = *reinterpret_cast<const f32x4 *>(wsum + h * kWaves);

@@ -254,3 +254,16 @@ def test_select_nan_scores_are_never_selected():
     ok = dict(case, N=2, query=case["query"][rest], block_keys=keys[rest],
               key_length=case["key_length"][rest])
     compare_select(ok, scores[rest], idx[rest])
+
+
+@pytest.mark.parametrize("scale", [2.0, 8.0])
+def test_select_wide_score_spread(scale):
+    """Logits spread over hundreds of log2 units (a large scale): some or
+    most lanes of the fast kernel meet exp2 arguments below -126, whose
+    results are subnormal or zero, and take exp2f with its subnormal
+    handling instead of the bare v_exp_f32."""
+    say(f"[select] wide score spread, scale {scale}")
+    case = gen.qsa_select_case(717, N=16, H=64, Di=128, Bcap=256, kbs=64, sel_ratio=2,
+                               cmp_ratio=1, topk=16, kl_lo=128 * 64, kl_hi=256 * 64 + 1,
+                               scale=scale)
+    compare_select(case, *run_select_gpu(case))
