@@ -8,6 +8,8 @@
 //   c      = x[t, :] . W^T                       W = [576, He], rows 0..511
 //                                                 W^DKV, rows 512..575 W^KR
 //   y      = alpha * ((c[0:512] / sqrt(mean(c[0:512]^2) + eps)) * gamma)
+//            (evaluated as (c * (1 / rms)) * (alpha * gamma): float32 steps
+//            of their own, within the derived bound like the projection)
 //   kr     = cat(c1, c2) * cos[t] + cat(-c2, c1) * sin[t]   on c[512:576]
 //   ckv_cache[slot[t]] = bf16(y), k_cache[slot[t]] = bf16(kr); slot -1 skips
 // with float32 accumulation of the bf16 products (no rounding of c before
@@ -35,9 +37,10 @@
 //     dispatcher places on the same XCD: their x rows meet in that XCD's L2;
 //   * staged rows are 64 bytes with their four 16-byte pieces permuted by
 //     (row / 4) mod 4, so the 16 lanes of a fragment read cover all 64 banks;
-//   * epilogue: a 4 x 4 transpose among neighbouring lanes turns each
-//     accumulator tile into row pieces of 4 columns; squares are reduced per
-//     row across lanes and wavefronts; the two workgroups of the pair swap
+//   * epilogue: the MFMAs take W as their first operand, so each lane's
+//     accumulators are 4 consecutive output columns of one token row (no
+//     transpose); squares are reduced per row across lanes (permlane swaps)
+//     and wavefronts; the two workgroups of the pair swap
 //     their per-row partial sums through the caller's workspace (a ready
 //     flag per half, set after the sums; the partner reads the sums, zeroes
 //     them and clears the flag, so the workspace is all zero again when the
@@ -116,50 +119,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Value of lane (l ^ 1) / (l ^ 2) within each quad of lanes: DPP quad
-// permutes [1, 0, 3, 2] and [2, 3, 0, 1] (VALU moves, no LDS round trip).
-__device__ __forceinline__ float quad_xor1(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float quad_xor2(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-
-// Value of lane (l + 8) / (l + 4) mod 16 within each row of 16 lanes.
-__device__ __forceinline__ float row_ror8(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_ror4(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-}
-
-// 4 x 4 transpose among lanes 4q .. 4q+3: lane 4q + i holds column i of a
-// 4 x 4 block (v[j] = row j) and ends with row i (v[c] = column c).
-__device__ __forceinline__ void quad_transpose(f32x4 &v, int lane)
-{
-    const int b = lane & 1, d = (lane >> 1) & 1;
-    // step 1 (partner lane ^ 1): keep rows with bit 0 == b, take the
-    // partner's column for them
-    const float r0 = quad_xor1(b ? v[0] : v[1]);
-    const float r1 = quad_xor1(b ? v[2] : v[3]);
-    // now: rows b and 2 + b, columns (lane & 2) + {0, 1}
-    const float e0 = b ? r0 : v[0], e1 = b ? v[1] : r0;     // row b
-    const float e2 = b ? r1 : v[2], e3 = b ? v[3] : r1;     // row 2 + b
-    // step 2 (partner lane ^ 2): keep row 2d + b, take the partner's two
-    // columns of it
-    const float s0 = quad_xor2(d ? e0 : e2);
-    const float s1 = quad_xor2(d ? e1 : e3);
-    if (d) {
-        v[0] = s0; v[1] = s1; v[2] = e2; v[3] = e3;
-    } else {
-        v[0] = e0; v[1] = e1; v[2] = s0; v[3] = s1;
-    }
-}
 
 __global__ __launch_bounds__(kThreads)
 void mla_kv_head_kernel(MlaKvHeadArgs a)
@@ -297,7 +256,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < kMt; ++m)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf[n & 1], acc[m][n], 0, 0, 0);
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[n & 1], af[m], acc[m][n], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -305,11 +264,13 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     __syncthreads();                          // every stage read: LDS reused below
 
     // ---- epilogue -----------------------------------------------------------
-    // After the transpose, acc[m][n][e] is c[row][col] with
-    //   row = 64 wm + 16 m + 4 (lane / 16) + lane % 4,
-    //   col = 288 half + 144 wn + 16 n + 4 ((lane % 16) / 4) + e.
-    const int rsub = 4 * (lane >> 4) + (lane & 3);       // row within a 16-row tile
-    const int cq = 4 * ((lane & 15) >> 2);               // first column within a tile
+    // The MFMAs take the W fragment as their first operand, so a tile is
+    // c^T: acc[m][n][e] is c[row][col] with
+    //   row = 64 wm + 16 m + lane % 16,
+    //   col = 288 half + 144 wn + 16 n + 4 (lane / 16) + e,
+    // four consecutive columns of one token row in each lane.
+    const int rsub = lane & 15;                          // row within a 16-row tile
+    const int cq = 4 * (lane >> 4);                      // first column within a tile
     // The rope tiles (rope wavefront, tiles 5..8) need the cos / sin pairs
     // (i0, i0 + 1) and (32 + i0, 33 + i0), i0 = 8 (n - 5) + cq / 2: those of
     // row tile 0 are loaded now, those of row tile m + 1 while row tile m is
@@ -329,11 +290,6 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     };
     if (rope_wave)
         load_rope_tables(0, rc[0]);
-#pragma unroll
-    for (int m = 0; m < kMt; ++m)
-#pragma unroll
-        for (int n = 0; n < kNt; ++n)
-            quad_transpose(acc[m][n], lane);
     float *red = reinterpret_cast<float *>(smem + kRedOff);     // [2 column wavefronts][256]
     float *sums = reinterpret_cast<float *>(smem + kSumOff);    // [256]
 #pragma unroll
@@ -345,10 +301,17 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     s += acc[m][n][e] * acc[m][n][e];
-        // add the four column quarters of the 16-lane row: DPP row rotates by
-        // 8, then by 4 (after the first step lanes l and l ^ 8 agree)
-        s += row_ror8(s);
-        s += row_ror4(s);
+        // add the four column quarters (lanes l, l ^ 16, l ^ 32, l ^ 48): a
+        // permlane swap of the value with itself leaves the two halves of
+        // the exchange in its two results, in every lane
+        {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s),
+                                                              false, false);
+            s = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
+                                                              false, false);
+            s = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        }
         if (cq == 0)
             red[wn * kRows + 64 * wm + 16 * m + rsub] = s;
     }
@@ -403,14 +366,16 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     __syncthreads();
 
     unsigned char *stage = smem;
+    // alpha_kv * gamma per column, once: each output is then two products,
+    // (c * rr) * (alpha * gamma)
     const float alpha = a.alpha;
     float g[kNt][4];
 #pragma unroll
     for (int n = 0; n < kNt; ++n) {
         const int col = kHalfCols * half + kWaveCols * wn + 16 * n + cq;
         const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + (col < kNorm ? col : 0));
-        g[n][0] = bf16_lo(gw.x); g[n][1] = bf16_hi(gw.x);
-        g[n][2] = bf16_lo(gw.y); g[n][3] = bf16_hi(gw.y);
+        g[n][0] = alpha * bf16_lo(gw.x); g[n][1] = alpha * bf16_hi(gw.x);
+        g[n][2] = alpha * bf16_lo(gw.y); g[n][3] = alpha * bf16_hi(gw.y);
     }
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
@@ -423,10 +388,8 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             const f32x4 v = acc[m][n];
             if (n < ntn) {
                 const int col = kWaveCols * wn + 16 * n + cq;       // within the half
-                const uint2 o = {pack_bf16(alpha * ((v[0] * rr) * g[n][0]),
-                                           alpha * ((v[1] * rr) * g[n][1])),
-                                 pack_bf16(alpha * ((v[2] * rr) * g[n][2]),
-                                           alpha * ((v[3] * rr) * g[n][3]))};
+                const uint2 o = {pack_bf16((v[0] * rr) * g[n][0], (v[1] * rr) * g[n][1]),
+                                 pack_bf16((v[2] * rr) * g[n][2], (v[3] * rr) * g[n][3])};
                 *reinterpret_cast<uint2 *>(stage + r * kStageRow + col * 2) = o;
             } else {
                 // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
