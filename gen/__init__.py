@@ -260,6 +260,40 @@ def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=
                 block_size=block_size, eps=float(eps))
 
 
+def mla_kv_head_blk_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=0.875,
+                         n_skip=0, entry_offsets=False, x_sigma=1.0):
+    """The MLA kv-path head with the block-indexed placement: x [B*S, He]
+    (batch-major), positions 0..S-1 per sequence, one cache-index entry per
+    chunk of block_size tokens (B * ceil(S/block_size) entries naming
+    distinct random blocks: entry = block*block_size, plus a random offset in
+    [0, block_size) when entry_offsets), n_skip entries set to -1."""
+    Dv, Dk = 512, 64
+    g = rng_for(seed)
+    T = B * S
+    x = bf16_bits(g.standard_normal((T, He), dtype=np.float32) * np.float32(x_sigma))
+    w = bf16_bits(g.standard_normal((Dv + Dk, He), dtype=np.float32)
+                  * np.float32(1.0 / np.sqrt(He)))
+    gamma = bf16_bits(g.uniform(0.5, 1.5, size=(Dv,)).astype(np.float32))
+    chunks = -(-S // block_size)
+    blocks = g.choice(num_blocks, size=B * chunks, replace=False)
+    entries = (blocks * block_size).astype(np.int64)
+    if entry_offsets:
+        entries += g.integers(0, block_size, size=entries.shape)
+    if n_skip:
+        entries[g.choice(B * chunks, size=n_skip, replace=False)] = -1
+    positions = np.broadcast_to(np.arange(S), (B, S))
+    cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
+    caches = {
+        "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
+        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv), np.uint16, BF16_SENTINEL),
+    }
+    return dict(mode="mla_paged_blk", x=x, w=w, gamma=gamma, alpha=float(np.float32(alpha)),
+                cos=np.ascontiguousarray(cos.reshape(T, Dk)),
+                sin=np.ascontiguousarray(sin.reshape(T, Dk)),
+                block_index=np.ascontiguousarray(entries), caches=caches, B=B, S=S, T=T, He=He,
+                Dv=Dv, Dk=Dk, num_blocks=num_blocks, block_size=block_size, eps=float(eps))
+
+
 # ---------------------------------------------------------------------------
 # Block selection over QSA block keys
 # ---------------------------------------------------------------------------

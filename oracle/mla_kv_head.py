@@ -11,7 +11,9 @@ fourth path, x times W^KR, ROPE, into the other cache; Formula: RmsNorm
 formula, c^KV = alpha_kv * RmsNorm(x W^DKV), k^C = Cache(c^KV),
 k^R = Cache(ROPE(x W^KR))), with the interleaved RoPE of
 aclnnKvRmsNormRopeCache (Formula (1) interleaveRope) and its paged cache
-placement (restrictions on index, PA_BNSD: slot -1 skips the token).
+placement (restrictions on index, PA_BNSD: slot -1 skips the token), or the
+block-indexed placement (PA_BLK_BSND: one cache-index entry per chunk of
+BlockSize tokens of a sequence).
 
 Readings (the pages fix none of these):
   * precision: float64 throughout; the bf16 inputs widen exactly, the
@@ -118,10 +120,52 @@ def mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slot_mapping, k_cache, ckv_c
     kc[v[keep]] = f64_to_bf16(kr[keep])
 
 
+def block_index_slots(block_index, B, S, block_size, rows):
+    """Per-token cache rows of the block-indexed placement (PA_BLK_BSND:
+    aclnnMlaPrologV3WeightNz, cacheIndex of shape (B, Ceil(S/BlockSize));
+    aclnnKvRmsNormRopeCache, restrictions on index for PA_BLK_BNSD: each entry
+    is -1 or in [0, BlockNum*BlockSize), entry / BlockSize must not repeat).
+    READING (as for the norm-rope-cache operator): entry (b, c) covers tokens
+    s = c*BS .. c*BS + BS - 1 of batch b and names block entry // BS; token
+    (b, s) goes to row (entry // BS) * BS + s % BS; -1 skips the chunk."""
+    chunks = -(-S // block_size) if S > 0 else 0
+    e = np.asarray(block_index, dtype=np.int64).reshape(-1)
+    if e.size != B * chunks:
+        raise MlaOracleError("block_index must hold B * ceil(S / block_size) entries")
+    if np.any((e < -1) | (e >= rows)):
+        raise MlaOracleError("block index entry out of range")
+    blocks = e[e >= 0] // block_size
+    if np.unique(blocks).size != blocks.size:
+        raise MlaOracleError("a block is named twice")
+    slots = np.full(B * S, -1, dtype=np.int64)
+    for b in range(B):
+        for s in range(S):
+            v = e[b * chunks + s // block_size]
+            if v >= 0:
+                slots[b * S + s] = (v // block_size) * block_size + s % block_size
+    return slots
+
+
+def mla_kv_head_paged_blk(x, w, gamma, alpha, cos, sin, block_index, B, S, k_cache, ckv_cache,
+                          eps):
+    """The same head with the block-indexed placement: x, cos, sin hold the
+    B * S tokens batch-major; one block_index entry per chunk of
+    block_size tokens of a sequence (block_size = k_cache.shape[1])."""
+    rows = k_cache.reshape(-1, DK).shape[0]
+    slots = block_index_slots(block_index, B, S, k_cache.shape[1], rows)
+    mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slots, k_cache, ckv_cache, eps)
+
+
 def run_mla_case(case):
-    """Runs a gen.mla_kv_head_case on fresh sentinel-filled caches."""
+    """Runs a gen.mla_kv_head_case (per-token slots) or a
+    gen.mla_kv_head_blk_case (block index) on fresh sentinel-filled caches."""
     caches = {k: spec.numpy() for k, spec in case["caches"].items()}
-    mla_kv_head_paged(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
-                      case["sin"], case["slot_mapping"], caches["k_cache"],
-                      caches["ckv_cache"], case["eps"])
+    if case.get("mode") == "mla_paged_blk":
+        mla_kv_head_paged_blk(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                              case["sin"], case["block_index"], case["B"], case["S"],
+                              caches["k_cache"], caches["ckv_cache"], case["eps"])
+    else:
+        mla_kv_head_paged(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                          case["sin"], case["slot_mapping"], caches["k_cache"],
+                          caches["ckv_cache"], case["eps"])
     return caches

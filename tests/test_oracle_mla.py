@@ -9,7 +9,9 @@ k^R = ROPE(x W^KR) into the k cache).
   aclnnKvRmsNormRopeCache page, whose float32 oracle is pinned separately;
 * alpha: a power of two scales every output exactly;
 * the RMS invariant of the normalised rows; RoPE special angles;
-* scatter: -1 skips, untouched rows keep their bytes, bad slots rejected.
+* scatter: -1 skips, untouched rows keep their bytes, bad slots rejected;
+* the block-indexed placement: a hand-worked token -> row table, rejected
+  entries, and the head equal to the per-token head on those rows.
 """
 from fractions import Fraction
 
@@ -150,3 +152,35 @@ def test_scatter_skips_and_untouched_rows():
     bad["slot_mapping"][0] = 8 * 16
     with pytest.raises(M.MlaOracleError, match="range"):
         M.run_mla_case(bad)
+
+
+def test_block_index_slots_hand_worked():
+    """B = 2 sequences of S = 5 tokens, chunks of 2 (3 per sequence):
+    entries 4 (block 2), 7 (block 3, offset ignored), -1; 0 (block 0),
+    11 (block 5), 2 (block 1). Worked by hand: token (b, s) -> row
+    (entry // 2) * 2 + s % 2."""
+    entries = np.array([4, 7, -1, 0, 11, 2], dtype=np.int64)
+    got = M.block_index_slots(entries, 2, 5, 2, rows=16)
+    np.testing.assert_array_equal(got, [4, 5, 6, 7, -1, 0, 1, 10, 11, 2])
+    with pytest.raises(M.MlaOracleError, match="twice"):
+        M.block_index_slots(np.array([4, 5, -1, 0, 11, 2]), 2, 5, 2, rows=16)   # block 2 twice
+    with pytest.raises(M.MlaOracleError, match="range"):
+        M.block_index_slots(np.array([4, 7, -1, 0, 16, 2]), 2, 5, 2, rows=16)
+    with pytest.raises(M.MlaOracleError, match="entries"):
+        M.block_index_slots(np.array([4, 7, -1, 0, 11]), 2, 5, 2, rows=16)
+
+
+def test_block_indexed_head_equals_per_token_head():
+    case = gen.mla_kv_head_blk_case(87, B=3, S=37, He=64, num_blocks=16, block_size=8,
+                                    n_skip=2, entry_offsets=True)
+    got = M.run_mla_case(case)
+    slots = M.block_index_slots(case["block_index"], 3, 37, 8, rows=16 * 8)
+    per_token = dict(case, mode="mla_paged", slot_mapping=slots)
+    want = M.run_mla_case(per_token)
+    for name in ("ckv_cache", "k_cache"):
+        np.testing.assert_array_equal(got[name], want[name])
+    # the skipped tokens are exactly those of the two -1 chunks (8 tokens, or
+    # 5 for the last chunk of a sequence: 37 = 4 * 8 + 5)
+    sizes = [8, 8, 8, 8, 5] * 3
+    skipped = sum(sz for e, sz in zip(case["block_index"], sizes) if e < 0)
+    assert np.count_nonzero(slots == -1) == skipped
