@@ -236,6 +236,35 @@ int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *
                                int32_t *err_count, hipStream_t stream);
 
 /*
+ * kvrc_mla_kv_head_paged_blk - the same MLA head with the BLOCK-INDEXED paged
+ * placement.
+ *
+ * Source: aclnnMlaPrologV3WeightNz (cacheIndex of shape (B, Ceil(S/BlockSize))
+ * for the PA_BLK_BSND cache mode), with the placement rule of
+ * aclnnKvRmsNormRopeCache's PA_BLK_BNSD mode (restrictions on index: entries
+ * -1 or in [0, num_blocks*block_size), entry / block_size not repeated).
+ *
+ * The T = B * S tokens of x, cos and sin are batch-major (token b*S + s is
+ * position s of sequence b). Entry b * ceil(S / block_size) + c of
+ * block_index covers tokens s in [c * block_size, (c + 1) * block_size) of
+ * sequence b (the last chunk may be partial); it names block
+ * entry / block_size, token (b, s) writes offset s % block_size of that
+ * block, and -1 skips the chunk.
+ *
+ *   block_index  int64 [B * ceil(S / block_size)]
+ * Everything else - shapes, workspace (kvrc_mla_kv_head_workspace_bytes(B*S)
+ * bytes), status and err_count (here an out-of-range entry skips its chunk and
+ * counts once per token of the chunk) - as for kvrc_mla_kv_head_paged.
+ */
+int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const void *gamma,
+                                   float alpha_kv, const void *cos, const void *sin,
+                                   const int64_t *block_index, void *k_cache, void *ckv_cache,
+                                   int64_t B, int64_t S, int64_t He, int64_t num_blocks,
+                                   int64_t block_size, float eps, void *workspace,
+                                   int64_t workspace_bytes, int32_t *err_count,
+                                   hipStream_t stream);
+
+/*
  * qsa_prepare - one index key per complete key block, for sparse attention.
  *
  * Source: openvino.opset17.qsa_prepare (description and Parameters list).

@@ -32,6 +32,7 @@ import torch
 
 __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
            "kvrc_norm_rope_cache", "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
+           "kvrc_mla_kv_head_paged_blk",
            "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_recip",
            "kvrc_selftest_e4m3",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
@@ -44,7 +45,7 @@ CACHE_FP8_E4M3 = 2
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
                     "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
-                    "qsa_prepare", "qsa_select_topk",
+                    "kvrc_mla_kv_head_paged_blk", "qsa_prepare", "qsa_select_topk",
                     "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3")
 
 _lib = None
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, F, P,
                                          I64, P, P]
     L.kvrc_mla_kv_head_paged.restype = I32
+    L.kvrc_mla_kv_head_paged_blk.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                             F, P, I64, P, P]
+    L.kvrc_mla_kv_head_paged_blk.restype = I32
     L.qsa_select_topk.argtypes = [P, P, P, I64, F, I64, I64, I64, I64, I64, I64, I64, I64, P, P,
                                   P, P]
     L.qsa_select_topk.restype = I32
@@ -291,6 +295,45 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
                                       _ptr(workspace), ws_bytes, _err_ptr(err_count),
                                       _stream(stream))
     _check(st, "kvrc_mla_kv_head_paged")
+
+
+def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cache, ckv_cache, *,
+                               workspace, alpha_kv=1.0, eps=1e-6, err_count=None,
+                               stream=None):
+    """MLA kv-path head with the block-indexed placement: x [B, S, He],
+    cos / sin [B, S, 64], block_index [B, ceil(S / block_size)] (or flat);
+    caches and workspace as for kvrc_mla_kv_head_paged (workspace of
+    kvrc_mla_kv_head_workspace_bytes(B * S) bytes)."""
+    _need(x, "x", _BF16, 3)
+    _need(w_dkv_kr, "w_dkv_kr", _BF16, 2)
+    _need(gamma, "gamma", _BF16, 1)
+    _need(cos, "cos", _BF16, 3)
+    _need(sin, "sin", _BF16, 3)
+    _need(block_index, "block_index", (torch.int64,), None)
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", _BF16, 4)
+    B, S, He = x.shape
+    if tuple(w_dkv_kr.shape) != (576, He):
+        raise ValueError("w_dkv_kr must be [576, He]")
+    if tuple(gamma.shape) != (512,):
+        raise ValueError("gamma must be [512]")
+    if tuple(cos.shape) != (B, S, 64) or tuple(sin.shape) != (B, S, 64):
+        raise ValueError("cos / sin must be [B, S, 64]")
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
+        raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
+    if block_index.numel() != B * (-(-S // BS) if S else 0):
+        raise ValueError("block_index must hold B * ceil(S / block_size) entries")
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvrc_mla_kv_head_paged_blk(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
+                                          _ptr(cos), _ptr(sin), _ptr(block_index), _ptr(k_cache),
+                                          _ptr(ckv_cache), B, S, He, NB, BS, float(eps),
+                                          _ptr(workspace), ws_bytes, _err_ptr(err_count),
+                                          _stream(stream))
+    _check(st, "kvrc_mla_kv_head_paged_blk")
 
 
 def kvrc_selftest_arith(a, b, q_shared, q_ieee, root, *, stream=None):

@@ -89,7 +89,9 @@ struct MlaKvHeadArgs {
     const uint16_t *gamma;    // [512] bf16
     const uint16_t *cos;      // [T, 64] bf16
     const uint16_t *sin;      // [T, 64] bf16
-    const int64_t *slot;      // [T]
+    const int64_t *slot;      // [T], or nullptr with block_index
+    const int64_t *block_index; // [B * chunks] (block-indexed placement), or nullptr
+    int64_t S, chunks, block_size; // sequence length and chunks per sequence (block_index)
     uint16_t *k_cache;        // [cache_rows, 64] bf16
     uint16_t *ckv_cache;      // [cache_rows, 512] bf16
     int64_t T, He, cache_rows;

@@ -12,6 +12,8 @@
 //            of their own, within the derived bound like the projection)
 //   kr     = cat(c1, c2) * cos[t] + cat(-c2, c1) * sin[t]   on c[512:576]
 //   ckv_cache[slot[t]] = bf16(y), k_cache[slot[t]] = bf16(kr); slot -1 skips
+//   (slot[t] from a per-token slot mapping, or from one block-index entry
+//   per chunk of BlockSize tokens of a sequence: PA_BLK_BSND)
 // with float32 accumulation of the bf16 products (no rounding of c before
 // the norm).
 //
@@ -164,12 +166,24 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
     // The cache slots of the rows this wavefront scatters (rows wave + 8 i,
     // i < 32) are fetched now, lane i holding row i's: their latency hides
-    // behind the K loop instead of preceding each row's stores.
+    // behind the K loop instead of preceding each row's stores. With the
+    // block-indexed placement the slot of token t = b*S + s is
+    // (entry / BS) * BS + s % BS for the entry of its chunk s / BS; an
+    // entry outside [-1, rows) becomes -2 (counted in the scatter).
     int64_t my_slot = -1;
     {
         const int64_t t = row0 + wave + kWaves * (lane & 31);
-        if (lane < kRows / kWaves && t < T)
-            my_slot = a.slot[t];
+        if (lane < kRows / kWaves && t < T) {
+            if (a.block_index) {
+                const int64_t b = t / a.S, s = t - b * a.S;
+                const int64_t e = a.block_index[b * a.chunks + s / a.block_size];
+                my_slot = e == -1 ? -1
+                        : (e < -1 || e >= a.cache_rows) ? -2
+                        : (e / a.block_size) * a.block_size + s % a.block_size;
+            } else {
+                my_slot = a.slot[t];
+            }
+        }
     }
     unsigned char *const xdst = smem + kXRing + wave * kXBlocks * 1024;  // + stage * kStageA
     unsigned char *const wdst = smem + wb0 * 1024;               // + stage * kStageB + i KiB

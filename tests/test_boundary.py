@@ -40,7 +40,7 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 104
+    assert k.lib().kvrc_version() == 105
 
 
 def test_status_strings():
@@ -144,6 +144,29 @@ def mla(**over):
                                           a["sin"], a["slot"], a["kc"], a["ckv"], a["T"], a["He"],
                                           a["NB"], a["BS"], a["eps"], a["ws"], a["wsb"], a["err"],
                                           a["stream"])
+
+
+def mla_blk(**over):
+    a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
+             idx=M["slot"], kc=M["kc"], ckv=M["ckv"], B=3, S=100, He=7168, NB=64, BS=128,
+             eps=1e-6, ws=M["ws"], wsb=WS_300, err=None, stream=None)
+    a.update(over)
+    return k.lib().kvrc_mla_kv_head_paged_blk(a["x"], a["w"], a["gamma"], a["alpha"], a["cos"],
+                                              a["sin"], a["idx"], a["kc"], a["ckv"], a["B"],
+                                              a["S"], a["He"], a["NB"], a["BS"], a["eps"],
+                                              a["ws"], a["wsb"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(idx=None), NULL), (dict(B=-1), SHAPE), (dict(S=-1), SHAPE), (dict(BS=0), SHAPE),
+    (dict(He=16), SHAPE), (dict(B=1 << 20, S=1 << 12), SHAPE),       # T = 2^32 > 2^31 - 1
+    (dict(idx=M["slot"] + 4), ALIGN), (dict(ws=None), NULL), (dict(wsb=WS_300 - 1), WORKSPACE),
+    # 3 * ceil(100 / 128) = 3 index entries (24 bytes): an output 16 bytes in overlaps
+    (dict(kc=M["slot"] + 16), ALIAS),
+    (dict(B=0), OK), (dict(S=0, idx=None), OK),
+])
+def test_mla_blk_validation(over, want):
+    assert mla_blk(**over) == want
 
 
 def test_mla_workspace_bytes():

@@ -319,3 +319,51 @@ def test_mla_cache_larger_than_4gib():
         in_rows = int((t.view(-1, d)[idx].view(torch.int16) != sentinel).sum().item())
         assert changed == in_rows, f"{name}: bytes outside the written rows changed"
     compare_mla(case, got)
+
+
+def run_mla_blk_gpu(case, index=None, err=None):
+    """One block-indexed call (x, cos, sin as [B, S, ...]); the workspace
+    must be zero again afterwards."""
+    B, S = case["B"], case["S"]
+    caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
+    idx = case["block_index"] if index is None else index
+    ws = new_workspace(B * S)
+    k.kvrc_mla_kv_head_paged_blk(dbf(case["x"]).view(B, S, -1), dbf(case["w"]), dbf(case["gamma"]),
+                                 dbf(case["cos"]).view(B, S, 64), dbf(case["sin"]).view(B, S, 64),
+                                 torch.from_numpy(idx).to(DEV), caches["k_cache"],
+                                 caches["ckv_cache"], workspace=ws, alpha_kv=case["alpha"],
+                                 eps=case["eps"], err_count=err)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+    return {n: t.view(torch.int16).cpu().numpy().view(np.uint16) for n, t in caches.items()}
+
+
+@pytest.mark.parametrize("B,S,BS,offsets,He", [(2, 300, 64, True, 256), (3, 37, 16, False, 64),
+                                               (1, 1, 16, False, 64), (4, 129, 128, True, 512),
+                                               (2, 13, 1, False, 64), (2, 4096, 128, False, 1024)])
+def test_mla_paged_blk(B, S, BS, offsets, He):
+    """Block-indexed placement (PA_BLK_BSND): one entry per chunk of BS
+    tokens, ragged last chunks, skipped chunks, entries with offsets inside
+    the block; the rows come from the oracle's placement."""
+    say(f"[mla] blk B={B} S={S} BS={BS} He={He}")
+    chunks = B * (-(-S // BS))
+    case = gen.mla_kv_head_blk_case(570 + S + BS, B=B, S=S, He=He,
+                                    num_blocks=max(2 * chunks, 16), block_size=BS,
+                                    n_skip=min(2, chunks - 1), entry_offsets=offsets)
+    rows = case["num_blocks"] * BS
+    slots = M.block_index_slots(case["block_index"], B, S, BS, rows)
+    compare_mla(case, run_mla_blk_gpu(case), slots=slots)
+
+
+def test_mla_paged_blk_invalid_entries_counted_per_token():
+    case = gen.mla_kv_head_blk_case(580, B=2, S=100, He=64, num_blocks=16, block_size=32)
+    idx = case["block_index"].copy()                 # 4 chunks per sequence: 32, 32, 32, 4 tokens
+    idx[1] = 16 * 32                                 # out of range: 32 tokens skipped and counted
+    idx[3] = -7                                      # out of range: the 4-token last chunk
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_mla_blk_gpu(case, index=idx, err=err)
+    assert int(err.item()) == 32 + 4
+    fixed = idx.copy()
+    fixed[[1, 3]] = -1
+    slots = M.block_index_slots(fixed, 2, 100, 32, 16 * 32)
+    compare_mla(case, got, slots=slots)
