@@ -216,7 +216,8 @@ def kvrc_paged_blk_case(seed, B, S, Dv, Dk, num_blocks, block_size, *, eps=1e-6,
 # ---------------------------------------------------------------------------
 
 def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=0.875,
-                     slot_kind="table", skip_frac=0.0, max_pos=32768, x_sigma=1.0):
+                     slot_kind="table", skip_frac=0.0, max_pos=32768, x_sigma=1.0,
+                     ckv_dtype="bf16"):
     """Inputs of the MLA kv-path head for T = B*S tokens of hidden size He.
 
     x [T, He] bf16 ~ N(0, x_sigma); the fused projection weight
@@ -251,9 +252,12 @@ def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=
     cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
     caches = {
         "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
-        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv), np.uint16, BF16_SENTINEL),
+        "ckv_cache": ckv_cache_spec((num_blocks, block_size, 1, Dv), ckv_dtype),
     }
-    return dict(mode="mla_paged", x=x, w=w, gamma=gamma, alpha=float(np.float32(alpha)),
+    if ckv_dtype != "bf16":
+        caches["ckv_scale"] = CacheSpec((num_blocks, block_size, 1), np.float32, SCALE_SENTINEL)
+    return dict(mode="mla_paged", ckv_dtype=ckv_dtype, x=x, w=w, gamma=gamma,
+                alpha=float(np.float32(alpha)),
                 cos=np.ascontiguousarray(cos.reshape(T, Dk)),
                 sin=np.ascontiguousarray(sin.reshape(T, Dk)), slot_mapping=slots,
                 caches=caches, B=B, S=S, T=T, He=He, Dv=Dv, Dk=Dk, num_blocks=num_blocks,
@@ -261,7 +265,7 @@ def mla_kv_head_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=
 
 
 def mla_kv_head_blk_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, alpha=0.875,
-                         n_skip=0, entry_offsets=False, x_sigma=1.0):
+                         n_skip=0, entry_offsets=False, x_sigma=1.0, ckv_dtype="bf16"):
     """The MLA kv-path head with the block-indexed placement: x [B*S, He]
     (batch-major), positions 0..S-1 per sequence, one cache-index entry per
     chunk of block_size tokens (B * ceil(S/block_size) entries naming
@@ -285,9 +289,12 @@ def mla_kv_head_blk_case(seed, B, S, He, num_blocks, block_size, *, eps=1e-6, al
     cos, sin = rope_table_bf16(np.asarray(positions).reshape(B, 1, S), Dk)
     caches = {
         "k_cache": CacheSpec((num_blocks, block_size, 1, Dk), np.uint16, BF16_SENTINEL),
-        "ckv_cache": CacheSpec((num_blocks, block_size, 1, Dv), np.uint16, BF16_SENTINEL),
+        "ckv_cache": ckv_cache_spec((num_blocks, block_size, 1, Dv), ckv_dtype),
     }
-    return dict(mode="mla_paged_blk", x=x, w=w, gamma=gamma, alpha=float(np.float32(alpha)),
+    if ckv_dtype != "bf16":
+        caches["ckv_scale"] = CacheSpec((num_blocks, block_size, 1), np.float32, SCALE_SENTINEL)
+    return dict(mode="mla_paged_blk", ckv_dtype=ckv_dtype, x=x, w=w, gamma=gamma,
+                alpha=float(np.float32(alpha)),
                 cos=np.ascontiguousarray(cos.reshape(T, Dk)),
                 sin=np.ascontiguousarray(sin.reshape(T, Dk)),
                 block_index=np.ascontiguousarray(entries), caches=caches, B=B, S=S, T=T, He=He,

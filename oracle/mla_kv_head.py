@@ -26,7 +26,10 @@ Readings (the pages fix none of these):
     y = alpha_kv * (gamma * c / RMS(c)) with RMS(c) = sqrt(mean(c^2) + eps);
   * the weight is one [576, He] matrix: row j < 512 is column j of W^DKV,
     row 512 + i is column i of W^KR (the rope key input);
-  * RoPE is the interleaved one, with per-token cos / sin rows [T, 64].
+  * RoPE is the interleaved one, with per-token cos / sin rows [T, 64];
+  * a quantised ckv cache takes the per-row rule of the norm-rope-cache
+    operator (RowMax/127 and round for int8, RowMax/448 and the nearest
+    E4M3FN value for FLOAT8 E4M3FN) applied to the float64 y.
 
 Every function is pinned in ``tests/test_oracle_mla.py``.
 """
@@ -104,10 +107,14 @@ def check_slots(slot_mapping, rows):
         raise MlaOracleError("duplicate slot")
 
 
-def mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slot_mapping, k_cache, ckv_cache, eps):
-    """Writes bf16(y) and bf16(kr) of every token with slot v >= 0 to row v of
-    ckv_cache [NB, BS, 1, 512] and k_cache [NB, BS, 1, 64] (uint16 bits, in
-    place); -1 skips the token; other rows keep their bytes."""
+def mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slot_mapping, k_cache, ckv_cache, eps,
+                      ckv_scale=None, kind="bf16"):
+    """Writes the ckv row of y and bf16(kr) of every token with slot v >= 0 to
+    row v of ckv_cache [NB, BS, 1, 512] and k_cache [NB, BS, 1, 64] (in
+    place); -1 skips the token; other rows keep their bytes. kind "bf16":
+    bf16(y) (uint16 bits); "int8" / "fp8": the quantize_rows codes (int8, or
+    E4M3FN code bytes) and the float32 of the scale into ckv_scale
+    [NB, BS, 1]."""
     kc = k_cache.reshape(-1, DK)
     ck = ckv_cache.reshape(-1, DV)
     check_slots(slot_mapping, ck.shape[0])
@@ -116,8 +123,72 @@ def mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slot_mapping, k_cache, ckv_c
         return
     y, kr = kv_head_rows(x, w, gamma, alpha, cos, sin, eps)
     keep = v >= 0
-    ck[v[keep]] = f64_to_bf16(y[keep])
+    if kind == "bf16":
+        ck[v[keep]] = f64_to_bf16(y[keep])
+    else:
+        q, scale = quantize_rows(y[keep], kind)
+        ck[v[keep]] = q.astype(np.int8) if kind == "int8" else e4m3_encode(q)
+        ckv_scale.reshape(-1)[v[keep]] = scale.astype(np.float32)
     kc[v[keep]] = f64_to_bf16(kr[keep])
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v):
+    """Nearest FLOAT8 E4M3FN value of float64 v (|v| <= 464), ties to the
+    even code. The format: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+    normal values (1 + m/8) * 2^(E - 7), E = 1..15 (E = 15, m = 7 is NaN, so
+    448 is the largest); subnormals (m/8) * 2^-6. In the binade
+    [2^e, 2^(e+1)) the values are spaced 2^(e-3); below 2^-6 the spacing is
+    2^-9, as in [2^-6, 2^-5)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))        # a = f * 2^ex, f in [0.5, 1)
+    step = np.ldexp(1.0, ex - 1 - 3)
+    return np.copysign(np.rint(a / step) * step, v)
+
+
+def e4m3_encode(q):
+    """Code bytes of E4M3FN values q (as e4m3_round returns them); the sign
+    bit follows the sign of q, also for zeros."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    sign = np.signbit(q).astype(np.uint8) << 7
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = ex - 1                                          # a in [2^e, 2^(e+1))
+    normal = a >= 2.0 ** -6
+    field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, a / np.ldexp(1.0, e - 3) - 8, a / 2.0 ** -9)
+    return (sign | (field.astype(np.uint8) << 3) | mant.astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_decode(code):
+    """Values of E4M3FN code bytes (the format definition above; NaN codes
+    0x7F / 0xFF give NaN)."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    field, mant = (c >> 3) & 0xF, c & 7
+    val = np.where(field > 0, np.ldexp(1.0 + mant / 8.0, field - 7), np.ldexp(mant / 8.0, -6))
+    val = np.where((field == 15) & (mant == 7), np.nan, val)
+    return sign * val
+
+
+def quantize_rows(y, kind):
+    """Per-row quantisation of the ckv rows y [T, 512] (float64), the rule of
+    the norm-rope-cache oracle taken to float64: scale = RowMax(|y|) / 127
+    and code = round(y / scale), half to even (int8; the RowMax/127 + round
+    rule of aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula), or
+    scale = RowMax(|y|) / 448 and the nearest E4M3FN value of y / scale
+    (FLOAT8 E4M3FN). A zero row has scale 0 and codes 0. Returns (codes as
+    float64 values, scale)."""
+    amax = np.max(np.abs(y), axis=1)
+    scale = amax / (127.0 if kind == "int8" else E4M3_MAX)
+    safe = np.where(scale > 0, scale, 1.0)[:, None]
+    qv = y / safe
+    q = np.rint(qv) if kind == "int8" else e4m3_round(qv)
+    q = np.where(scale[:, None] > 0, q, 0.0 * y)
+    return q, scale
 
 
 def block_index_slots(block_index, B, S, block_size, rows):
@@ -147,25 +218,28 @@ def block_index_slots(block_index, B, S, block_size, rows):
 
 
 def mla_kv_head_paged_blk(x, w, gamma, alpha, cos, sin, block_index, B, S, k_cache, ckv_cache,
-                          eps):
+                          eps, ckv_scale=None, kind="bf16"):
     """The same head with the block-indexed placement: x, cos, sin hold the
     B * S tokens batch-major; one block_index entry per chunk of
     block_size tokens of a sequence (block_size = k_cache.shape[1])."""
     rows = k_cache.reshape(-1, DK).shape[0]
     slots = block_index_slots(block_index, B, S, k_cache.shape[1], rows)
-    mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slots, k_cache, ckv_cache, eps)
+    mla_kv_head_paged(x, w, gamma, alpha, cos, sin, slots, k_cache, ckv_cache, eps, ckv_scale,
+                      kind)
 
 
 def run_mla_case(case):
     """Runs a gen.mla_kv_head_case (per-token slots) or a
     gen.mla_kv_head_blk_case (block index) on fresh sentinel-filled caches."""
     caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+    kind = case.get("ckv_dtype", "bf16")
+    scale = caches.get("ckv_scale")
     if case.get("mode") == "mla_paged_blk":
         mla_kv_head_paged_blk(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
                               case["sin"], case["block_index"], case["B"], case["S"],
-                              caches["k_cache"], caches["ckv_cache"], case["eps"])
+                              caches["k_cache"], caches["ckv_cache"], case["eps"], scale, kind)
     else:
         mla_kv_head_paged(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
                           case["sin"], case["slot_mapping"], caches["k_cache"],
-                          caches["ckv_cache"], case["eps"])
+                          caches["ckv_cache"], case["eps"], scale, kind)
     return caches

@@ -11,7 +11,11 @@ k^R = ROPE(x W^KR) into the k cache).
 * the RMS invariant of the normalised rows; RoPE special angles;
 * scatter: -1 skips, untouched rows keep their bytes, bad slots rejected;
 * the block-indexed placement: a hand-worked token -> row table, rejected
-  entries, and the head equal to the per-token head on those rows.
+  entries, and the head equal to the per-token head on those rows;
+* quantised ckv rows: the float64 E4M3FN rounding against the library's
+  float32 conversion on every midpoint and its float32 neighbours, code
+  decoding of all 256 codes, hand-worked int8 / fp8 rows, and the
+  dequantisation error bound of the whole head.
 """
 from fractions import Fraction
 
@@ -184,3 +188,107 @@ def test_block_indexed_head_equals_per_token_head():
     sizes = [8, 8, 8, 8, 5] * 3
     skipped = sum(sz for e, sz in zip(case["block_index"], sizes) if e < 0)
     assert np.count_nonzero(slots == -1) == skipped
+
+
+def _torch_e4m3(v):
+    import torch
+    t = torch.tensor(np.asarray(v, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy(), t.view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_all_codes_match_library():
+    """Every E4M3FN code decodes to the library's value of that code (NaN
+    codes to NaN), and re-encodes to itself."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.tensor(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = M.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    np.testing.assert_array_equal(got[ok], lib[ok])
+    assert np.sum(~ok) == 2 and set(codes[~ok]) == {0x7F, 0xFF}
+    np.testing.assert_array_equal(M.e4m3_encode(M.e4m3_round(got[ok])), codes[ok])
+
+
+def test_e4m3_round_matches_library_on_midpoints_and_random():
+    """The float64 rounding against the library's float32 -> E4M3FN
+    conversion (nearest, ties to even, saturating) on every midpoint between
+    neighbouring values, the midpoints +- one float32 ulp, and random
+    values over the whole range. All these inputs are float32 values, so the
+    library sees the same numbers."""
+    vals = M.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))          # 0 .. 448 ascending
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids32 = mids.astype(np.float32)
+    assert np.all(mids32 == mids)
+    up = np.nextafter(mids32, np.float32(np.inf))
+    dn = np.nextafter(mids32, np.float32(0))
+    rng = np.random.default_rng(5)
+    rnd = (rng.uniform(-1, 1, 20000) * 2.0 ** rng.uniform(-12, np.log2(460), 20000)).astype(np.float32)
+    v = np.concatenate([mids32, up, dn, -mids32, -up, vals.astype(np.float32), rnd,
+                        np.float32([448, 460, 463.9, -463.9, 0.0, -0.0])])
+    want, want_codes = _torch_e4m3(v)
+    got = M.e4m3_round(v.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(M.e4m3_encode(got), want_codes)
+    # ties go to the even code: 17 -> 16, 19 -> 20, 2^-9 * 1.5 -> 2^-9 * 2
+    np.testing.assert_array_equal(M.e4m3_round(np.array([17.0, 19.0, 1.5 * 2.0 ** -9])),
+                                  [16.0, 20.0, 2.0 ** -8])
+
+
+def test_quantize_rows_hand_worked():
+    """int8: row max 254 -> scale 2; 63.5 / 2 = 31.75 -> 32, -127 / 2 = -63.5
+    -> -64 (tie to even), 0.25 / 2 -> 0. fp8: row max 896 -> scale 2;
+    34 / 2 = 17 -> 16 (tie to even), -36 / 2 = -18 exact, 1/256 / 2 = 2^-9
+    (the smallest subnormal); codes 0x7E = (15, 6), 0x58 = (11, 0),
+    0xD9 = sign + (11, 1), 0x01 = subnormal 1 (exponent field, mantissa). A zero row: scale 0, codes 0."""
+    y = np.zeros((2, 512))
+    y[0, :4] = [254.0, -127.0, 63.5, 0.25]
+    q, s = M.quantize_rows(y, "int8")
+    np.testing.assert_array_equal(s, [2.0, 0.0])
+    np.testing.assert_array_equal(q[0, :4], [127, -64, 32, 0])
+    assert not np.any(q[0, 4:]) and not np.any(q[1])
+    y = np.zeros((2, 512))
+    y[0, :4] = [896.0, 34.0, -36.0, 1 / 256]
+    q, s = M.quantize_rows(y, "fp8")
+    np.testing.assert_array_equal(s, [2.0, 0.0])
+    np.testing.assert_array_equal(q[0, :4], [448.0, 16.0, -18.0, 2.0 ** -9])
+    np.testing.assert_array_equal(M.e4m3_encode(q[0, :4]), [0x7E, 0x58, 0xD9, 0x01])
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantised_head_scatter_and_error_bound(kind):
+    """The quantised head writes, at each kept token's row, codes whose
+    dequantised values lie within half a code step of y (a step of the
+    scale for int8; for E4M3FN, relative 2^-4 of the value, or 2^-10 times
+    the scale below the normal range), a code of magnitude 127 (448) at the
+    row maximum, and the float32 of RowMax/127 (/448) as the scale; the k
+    cache is the bf16 path's; untouched rows keep their sentinels."""
+    case = gen.mla_kv_head_case(88, B=2, S=40, He=96, num_blocks=8, block_size=16,
+                                slot_kind="random", skip_frac=0.2, ckv_dtype=kind)
+    got = M.run_mla_case(case)
+    ref = M.run_mla_case(gen.mla_kv_head_case(88, B=2, S=40, He=96, num_blocks=8, block_size=16,
+                                              slot_kind="random", skip_frac=0.2))
+    np.testing.assert_array_equal(got["k_cache"], ref["k_cache"])
+    y, _ = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                          case["sin"], case["eps"])
+    v = case["slot_mapping"]
+    ck = got["ckv_cache"].reshape(-1, 512)
+    sc = got["ckv_scale"].reshape(-1)
+    div = 127.0 if kind == "int8" else 448.0
+    for t, s in enumerate(v):
+        if s < 0:
+            continue
+        amax = np.max(np.abs(y[t]))
+        assert sc[s] == np.float32(amax / div)
+        deq = (ck[s].astype(np.float64) if kind == "int8" else M.e4m3_decode(ck[s])) * (amax / div)
+        err = np.abs(deq - y[t])
+        if kind == "int8":
+            assert np.all(err <= 0.5 * amax / div * (1 + 1e-12))
+        else:
+            bound = np.maximum(np.abs(y[t]) * 2.0 ** -4, 2.0 ** -10 * amax / div)
+            assert np.all(err <= bound * (1 + 1e-12))
+        code = ck[s][int(np.argmax(np.abs(y[t])))]
+        assert abs(float(code) if kind == "int8" else M.e4m3_decode(code)) == div
+    untouched = np.setdiff1d(np.arange(ck.shape[0]), v[v >= 0])
+    sent = gen.INT8_SENTINEL if kind == "int8" else gen.FP8_SENTINEL
+    assert np.all(ck[untouched] == sent) and np.all(sc[untouched] == gen.SCALE_SENTINEL)
