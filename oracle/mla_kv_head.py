@@ -181,13 +181,14 @@ def quantize_rows(y, kind):
     rule of aclnnMlaPrologV3WeightNz, Dequant Scale Query Nope formula), or
     scale = RowMax(|y|) / 448 and the nearest E4M3FN value of y / scale
     (FLOAT8 E4M3FN). A zero row has scale 0 and codes 0. Returns (codes as
-    float64 values, scale)."""
+    float64 values, scale). The zero codes of a zero row are +0 (byte 0x00),
+    as in the norm-rope-cache rule; elsewhere a zero keeps its sign."""
     amax = np.max(np.abs(y), axis=1)
     scale = amax / (127.0 if kind == "int8" else E4M3_MAX)
     safe = np.where(scale > 0, scale, 1.0)[:, None]
     qv = y / safe
     q = np.rint(qv) if kind == "int8" else e4m3_round(qv)
-    q = np.where(scale[:, None] > 0, q, 0.0 * y)
+    q = np.where(scale[:, None] > 0, q, 0.0)
     return q, scale
 
 

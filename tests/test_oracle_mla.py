@@ -292,3 +292,19 @@ def test_quantised_head_scatter_and_error_bound(kind):
     untouched = np.setdiff1d(np.arange(ck.shape[0]), v[v >= 0])
     sent = gen.INT8_SENTINEL if kind == "int8" else gen.FP8_SENTINEL
     assert np.all(ck[untouched] == sent) and np.all(sc[untouched] == gen.SCALE_SENTINEL)
+
+
+def test_quantised_zero_rows_store_zero_scale_and_code_0x00():
+    """alpha = 0 makes every row zero (zeros of both signs, the signs of
+    the projection): scale 0 and code byte 0 everywhere, the rule of the
+    norm-rope-cache operator's zero rows."""
+    for kind in ("int8", "fp8"):
+        case = gen.mla_kv_head_case(89, B=1, S=20, He=64, num_blocks=4, block_size=8,
+                                    alpha=0.0, ckv_dtype=kind)
+        y, _ = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
+                              case["sin"], case["eps"])
+        assert not np.any(y) and np.any(np.signbit(y))
+        got = M.run_mla_case(case)
+        rows = case["slot_mapping"]
+        assert np.all(got["ckv_cache"].reshape(-1, 512)[rows].view(np.uint8) == 0)
+        assert np.all(got["ckv_scale"].reshape(-1)[rows] == 0.0)
