@@ -172,7 +172,8 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
 /*
  * kvrc_mla_kv_head_workspace_bytes - bytes of device workspace that
  * kvrc_mla_kv_head_paged needs for T tokens (the first phase of the pages'
- * "workspace size, then execute" convention; 2056 bytes per 256 tokens).
+ * "workspace size, then execute" convention; 4112 bytes per 256 tokens, for
+ * every ckv cache type).
  * Returns -1 for T < 0 or T > 2^31 - 1, 0 for T == 0.
  */
 int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
@@ -184,7 +185,9 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  * Source: aclnnMlaPrologV3WeightNz (Interface function, third and fourth
  * paths; Formula: RmsNorm formula, c^KV = alpha_kv * RmsNorm(x W^DKV),
  * k^C = Cache(c^KV), k^R = Cache(ROPE(x W^KR))); the RoPE is Formula (1)
- * interleaveRope of aclnnKvRmsNormRopeCache, the placement its PA_BNSD rule.
+ * interleaveRope of aclnnKvRmsNormRopeCache, the placement its PA_BNSD rule,
+ * a quantised ckv cache its quantisation scenario 1 with the RowMax/127 rule
+ * of the Dequant Scale Query Nope formula (448 for FLOAT8 E4M3FN).
  *
  * For every token t of x[T, He]:
  *   c  = x[t] . W^T, float32 accumulation of the exact bf16 products (c is
@@ -193,7 +196,15 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *   kr = interleaved RoPE of c[512:576] with cos[t], sin[t] (as in
  *        kvrc_paged_norm_rope_cache)
  *   v = slot_mapping[t]; v == -1 skips the token;
- *   ckv_cache[v / block_size, v % block_size, 0, :] = bf16(y)
+ *   ckv_cache[v / block_size, v % block_size, 0, :] = bf16(y)       (BF16), or
+ *        int8 codes of y / scale with scale = max|y| / 127 (INT8), or
+ *        E4M3FN codes of y / scale with scale = max|y| / 448 (FP8_E4M3),
+ *        the scale stored to ckv_scale[v / block_size, v % block_size, 0]:
+ *        the per-row rule of kvrc_paged_norm_rope_cache, except that the
+ *        quotient is y * RN(1 / scale) (one more rounding: the outputs of
+ *        this head are not reproducible to the last bit anyway); codes
+ *        round to nearest, ties to even, and saturate at 127 (448); an
+ *        all-zero row stores scale 0 and codes 0
  *   k_cache[v / block_size, v % block_size, 0, :]   = bf16(kr)
  * The projection runs on the matrix cores in an order of its own, so the
  * outputs are not bit-reproducible against another summation order; they
@@ -210,7 +221,10 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *   cos, sin      bf16 [T, 64]
  *   slot_mapping  int64 [T]    -1 or unique in [0, num_blocks*block_size)
  *   k_cache       bf16 [num_blocks, block_size, 1, 64]
- *   ckv_cache     bf16 [num_blocks, block_size, 1, 512]
+ *   ckv_cache     bf16, int8 or E4M3FN (uint8 codes) [num_blocks, block_size, 1, 512]
+ *   ckv_scale     float32 [num_blocks, block_size, 1]; NULL for BF16,
+ *                 non-NULL for INT8 and FP8_E4M3 (else KVRC_ERR_DTYPE)
+ *   ckv_dtype     a kvrc_cache_dtype
  *   He            a multiple of 32, >= 32; T <= 2^31 - 1
  *   workspace     device memory of at least
  *                 kvrc_mla_kv_head_workspace_bytes(T) bytes (workspace_bytes
@@ -231,9 +245,9 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,
                                const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
-                               int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
-                               float eps, void *workspace, int64_t workspace_bytes,
-                               int32_t *err_count, hipStream_t stream);
+                               float *ckv_scale, int64_t T, int64_t He, int64_t num_blocks,
+                               int64_t block_size, int32_t ckv_dtype, float eps, void *workspace,
+                               int64_t workspace_bytes, int32_t *err_count, hipStream_t stream);
 
 /*
  * kvrc_mla_kv_head_paged_blk - the same MLA head with the BLOCK-INDEXED paged
@@ -252,17 +266,17 @@ int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *
  * block, and -1 skips the chunk.
  *
  *   block_index  int64 [B * ceil(S / block_size)]
- * Everything else - shapes, workspace (kvrc_mla_kv_head_workspace_bytes(B*S)
- * bytes), status and err_count (here an out-of-range entry skips its chunk and
+ * Everything else - shapes, the ckv cache types and scale,
+ * workspace (kvrc_mla_kv_head_workspace_bytes(B*S) bytes), status and err_count (here an out-of-range entry skips its chunk and
  * counts once per token of the chunk) - as for kvrc_mla_kv_head_paged.
  */
 int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const void *gamma,
                                    float alpha_kv, const void *cos, const void *sin,
                                    const int64_t *block_index, void *k_cache, void *ckv_cache,
-                                   int64_t B, int64_t S, int64_t He, int64_t num_blocks,
-                                   int64_t block_size, float eps, void *workspace,
-                                   int64_t workspace_bytes, int32_t *err_count,
-                                   hipStream_t stream);
+                                   float *ckv_scale, int64_t B, int64_t S, int64_t He,
+                                   int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                                   float eps, void *workspace, int64_t workspace_bytes,
+                                   int32_t *err_count, hipStream_t stream);
 
 /*
  * qsa_prepare - one index key per complete key block, for sparse attention.

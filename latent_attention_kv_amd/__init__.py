@@ -80,11 +80,11 @@ def lib() -> ctypes.CDLL:
     L.kvrc_norm_rope_cache.restype = I32
     L.kvrc_mla_kv_head_workspace_bytes.argtypes = [I64]
     L.kvrc_mla_kv_head_workspace_bytes.restype = I64
-    L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, F, P,
-                                         I64, P, P]
+    L.kvrc_mla_kv_head_paged.argtypes = [P, P, P, F, P, P, P, P, P, P, I64, I64, I64, I64, I32,
+                                         F, P, I64, P, P]
     L.kvrc_mla_kv_head_paged.restype = I32
-    L.kvrc_mla_kv_head_paged_blk.argtypes = [P, P, P, F, P, P, P, P, P, I64, I64, I64, I64, I64,
-                                             F, P, I64, P, P]
+    L.kvrc_mla_kv_head_paged_blk.argtypes = [P, P, P, F, P, P, P, P, P, P, I64, I64, I64, I64,
+                                             I64, I32, F, P, I64, P, P]
     L.kvrc_mla_kv_head_paged_blk.restype = I32
     L.qsa_select_topk.argtypes = [P, P, P, I64, F, I64, I64, I64, I64, I64, I64, I64, I64, P, P,
                                   P, P]
@@ -257,11 +257,26 @@ def kvrc_mla_kv_head_workspace_bytes(T):
     return n
 
 
-def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, ckv_cache, *,
-                           workspace, alpha_kv=1.0, eps=1e-6, err_count=None, stream=None):
-    """MLA kv-path head into paged bf16 caches: x [T, He], w_dkv_kr [576, He],
+def _mla_caches(k_cache, ckv_cache, ckv_scale):
+    """Checked (NB, BS, ckv dtype) of the MLA head's caches."""
+    _need(k_cache, "k_cache", _BF16, 4)
+    _need(ckv_cache, "ckv_cache", _CKV, 4)
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
+        raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
+    dt = _cache_dtype(ckv_cache, ckv_scale)
+    if ckv_scale is not None and tuple(ckv_scale.shape) != (NB, BS, 1):
+        raise ValueError("ckv_scale must be [num_blocks, block_size, 1]")
+    return NB, BS, dt
+
+
+def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
+                           ckv_scale=None, *, workspace, alpha_kv=1.0, eps=1e-6, err_count=None,
+                           stream=None):
+    """MLA kv-path head into paged caches: x [T, He], w_dkv_kr [576, He],
     gamma [512], cos / sin [T, 64], slot_mapping [T]; k_cache
-    [NB, BS, 1, 64] and ckv_cache [NB, BS, 1, 512] are updated in place.
+    [NB, BS, 1, 64] (bf16) and ckv_cache [NB, BS, 1, 512] (bf16, or int8 /
+    E4M3FN codes with ckv_scale [NB, BS, 1] float32) are updated in place.
     workspace: a contiguous device tensor of at least
     kvrc_mla_kv_head_workspace_bytes(T) bytes, all zero before its first use
     (each completed call leaves it zero)."""
@@ -271,8 +286,7 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
     _need(cos, "cos", _BF16, 2)
     _need(sin, "sin", _BF16, 2)
     _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
-    _need(k_cache, "k_cache", _BF16, 4)
-    _need(ckv_cache, "ckv_cache", _BF16, 4)
+    NB, BS, dt = _mla_caches(k_cache, ckv_cache, ckv_scale)
     T, He = x.shape
     if tuple(w_dkv_kr.shape) != (576, He):
         raise ValueError("w_dkv_kr must be [576, He]")
@@ -282,24 +296,22 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
         raise ValueError("cos / sin must be [T, 64]")
     if slot_mapping.numel() != T:
         raise ValueError("slot_mapping must have T entries")
-    NB, BS = k_cache.shape[0], k_cache.shape[1]
-    if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
-        raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
     if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
             not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().kvrc_mla_kv_head_paged(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
                                       _ptr(cos), _ptr(sin), _ptr(slot_mapping), _ptr(k_cache),
-                                      _ptr(ckv_cache), T, He, NB, BS, float(eps),
+                                      _ptr(ckv_cache), _ptr(ckv_scale), T, He, NB, BS, dt,
+                                      float(eps),
                                       _ptr(workspace), ws_bytes, _err_ptr(err_count),
                                       _stream(stream))
     _check(st, "kvrc_mla_kv_head_paged")
 
 
-def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cache, ckv_cache, *,
-                               workspace, alpha_kv=1.0, eps=1e-6, err_count=None,
-                               stream=None):
+def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cache, ckv_cache,
+                               ckv_scale=None, *, workspace, alpha_kv=1.0, eps=1e-6,
+                               err_count=None, stream=None):
     """MLA kv-path head with the block-indexed placement: x [B, S, He],
     cos / sin [B, S, 64], block_index [B, ceil(S / block_size)] (or flat);
     caches and workspace as for kvrc_mla_kv_head_paged (workspace of
@@ -310,8 +322,7 @@ def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cach
     _need(cos, "cos", _BF16, 3)
     _need(sin, "sin", _BF16, 3)
     _need(block_index, "block_index", (torch.int64,), None)
-    _need(k_cache, "k_cache", _BF16, 4)
-    _need(ckv_cache, "ckv_cache", _BF16, 4)
+    NB, BS, dt = _mla_caches(k_cache, ckv_cache, ckv_scale)
     B, S, He = x.shape
     if tuple(w_dkv_kr.shape) != (576, He):
         raise ValueError("w_dkv_kr must be [576, He]")
@@ -319,9 +330,6 @@ def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cach
         raise ValueError("gamma must be [512]")
     if tuple(cos.shape) != (B, S, 64) or tuple(sin.shape) != (B, S, 64):
         raise ValueError("cos / sin must be [B, S, 64]")
-    NB, BS = k_cache.shape[0], k_cache.shape[1]
-    if tuple(k_cache.shape) != (NB, BS, 1, 64) or tuple(ckv_cache.shape) != (NB, BS, 1, 512):
-        raise ValueError("caches must be [num_blocks, block_size, 1, 64] and [.., 512]")
     if block_index.numel() != B * (-(-S // BS) if S else 0):
         raise ValueError("block_index must hold B * ceil(S / block_size) entries")
     if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
@@ -330,7 +338,8 @@ def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cach
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().kvrc_mla_kv_head_paged_blk(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
                                           _ptr(cos), _ptr(sin), _ptr(block_index), _ptr(k_cache),
-                                          _ptr(ckv_cache), B, S, He, NB, BS, float(eps),
+                                          _ptr(ckv_cache), _ptr(ckv_scale), B, S, He, NB, BS, dt,
+                                          float(eps),
                                           _ptr(workspace), ws_bytes, _err_ptr(err_count),
                                           _stream(stream))
     _check(st, "kvrc_mla_kv_head_paged_blk")

@@ -139,7 +139,7 @@ const char *kvrc_status_string(int32_t status)
     }
 }
 
-int32_t kvrc_version(void) { return 105; }
+int32_t kvrc_version(void) { return 106; }
 
 int32_t kvrc_paged_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
                                    const void *sin, const int64_t *slot_mapping, void *k_cache,
@@ -202,18 +202,24 @@ namespace {
 // [B * ceil(S / block_size)] (index_count entries, T = B * S).
 int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float alpha_kv,
                    const void *cos, const void *sin, const int64_t *index, bool blk, int64_t B,
-                   int64_t S, void *k_cache, void *ckv_cache, int64_t T, int64_t He,
-                   int64_t num_blocks, int64_t block_size, float eps, void *workspace,
-                   int64_t workspace_bytes, int32_t *err_count, hipStream_t stream)
+                   int64_t S, void *k_cache, void *ckv_cache, float *ckv_scale, int64_t T,
+                   int64_t He, int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                   float eps, void *workspace, int64_t workspace_bytes, int32_t *err_count,
+                   hipStream_t stream)
 {
+    if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8 &&
+        ckv_dtype != KVRC_CACHE_FP8_E4M3)
+        return KVRC_ERR_DTYPE;
+    const bool quant = ckv_dtype != KVRC_CACHE_BF16;   // one byte per element + scale
     int64_t rows;
     if (T < 0 || T > (int64_t)INT32_MAX || He < kvrc::kMlaHeadK || He % kvrc::kMlaHeadK ||
         num_blocks < 0 || block_size < 1 || !mul_ok(num_blocks, block_size, &rows))
         return KVRC_ERR_SHAPE;
     int64_t xbytes, wbytes, kbytes, cbytes;
     if (!mul_ok(T, He * 2, &xbytes) || !mul_ok(576, He * 2, &wbytes) ||
-        !mul_ok(rows, 64 * 2, &kbytes) || !mul_ok(rows, 512 * 2, &cbytes))
+        !mul_ok(rows, 64 * 2, &kbytes) || !mul_ok(rows, 512 * (quant ? 1 : 2), &cbytes))
         return KVRC_ERR_SHAPE;
+    const int64_t sbytes = quant ? rows * 4 : 0;
     const int64_t chunks = blk && S > 0 ? (S + block_size - 1) / block_size : 0;
     const int64_t index_count = blk ? B * chunks : T;
     if (T == 0)
@@ -224,13 +230,16 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     if (!x || !w_dkv_kr || !gamma || !cos || !sin || !index || !k_cache || !ckv_cache ||
         !workspace)
         return KVRC_ERR_NULL;
+    if (quant != (ckv_scale != nullptr))
+        return KVRC_ERR_DTYPE;
     if (!aligned(x, 16) || !aligned(w_dkv_kr, 16) || !aligned(gamma, 16) || !aligned(cos, 16) ||
         !aligned(sin, 16) || !aligned(index, 8) || !aligned(k_cache, 16) ||
-        !aligned(ckv_cache, 16) || !aligned(workspace, 16) || !aligned(err_count, 4))
+        !aligned(ckv_cache, 16) || !aligned(ckv_scale, 4) || !aligned(workspace, 16) ||
+        !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
     const Range in[] = {span(x, xbytes), span(w_dkv_kr, wbytes), span(gamma, 1024),
                         span(cos, T * 128), span(sin, T * 128), span(index, index_count * 8)};
-    const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes),
+    const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
                          span(workspace, wsbytes), span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
         for (const Range &i : in)
@@ -252,7 +261,9 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     a.chunks = chunks;
     a.block_size = block_size;
     a.k_cache = static_cast<uint16_t *>(k_cache);
-    a.ckv_cache = static_cast<uint16_t *>(ckv_cache);
+    a.ckv_cache = ckv_cache;
+    a.ckv_scale = ckv_scale;
+    a.ckv = ckv_dtype;
     a.T = T;
     a.He = He;
     a.cache_rows = rows;
@@ -269,29 +280,29 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,
                                const int64_t *slot_mapping, void *k_cache, void *ckv_cache,
-                               int64_t T, int64_t He, int64_t num_blocks, int64_t block_size,
-                               float eps, void *workspace, int64_t workspace_bytes,
-                               int32_t *err_count, hipStream_t stream)
+                               float *ckv_scale, int64_t T, int64_t He, int64_t num_blocks,
+                               int64_t block_size, int32_t ckv_dtype, float eps, void *workspace,
+                               int64_t workspace_bytes, int32_t *err_count, hipStream_t stream)
 {
     return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, slot_mapping, false, 0, 0, k_cache,
-                      ckv_cache, T, He, num_blocks, block_size, eps, workspace, workspace_bytes,
-                      err_count, stream);
+                      ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
+                      workspace, workspace_bytes, err_count, stream);
 }
 
 int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const void *gamma,
                                    float alpha_kv, const void *cos, const void *sin,
                                    const int64_t *block_index, void *k_cache, void *ckv_cache,
-                                   int64_t B, int64_t S, int64_t He, int64_t num_blocks,
-                                   int64_t block_size, float eps, void *workspace,
-                                   int64_t workspace_bytes, int32_t *err_count,
-                                   hipStream_t stream)
+                                   float *ckv_scale, int64_t B, int64_t S, int64_t He,
+                                   int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                                   float eps, void *workspace, int64_t workspace_bytes,
+                                   int32_t *err_count, hipStream_t stream)
 {
     int64_t T;
     if (B < 0 || S < 0 || !mul_ok(B, S, &T))
         return KVRC_ERR_SHAPE;
     return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, block_index, true, B, S, k_cache,
-                      ckv_cache, T, He, num_blocks, block_size, eps, workspace, workspace_bytes,
-                      err_count, stream);
+                      ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
+                      workspace, workspace_bytes, err_count, stream);
 }
 
 int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t *key_length,

@@ -93,7 +93,9 @@ struct MlaKvHeadArgs {
     const int64_t *block_index; // [B * chunks] (block-indexed placement), or nullptr
     int64_t S, chunks, block_size; // sequence length and chunks per sequence (block_index)
     uint16_t *k_cache;        // [cache_rows, 64] bf16
-    uint16_t *ckv_cache;      // [cache_rows, 512] bf16
+    void *ckv_cache;          // [cache_rows, 512] bf16, int8 or E4M3FN codes
+    float *ckv_scale;         // [cache_rows] (int8 / E4M3FN only), else nullptr
+    int32_t ckv;              // kvrc_cache_dtype
     int64_t T, He, cache_rows;
     float alpha, eps;
     void *workspace;          // mla_kv_head_workspace_bytes(T) bytes, zero between calls
@@ -107,7 +109,8 @@ constexpr int64_t kMlaHeadK = 32;
 // Token rows per workgroup pair of the MLA head kernel.
 constexpr int64_t kMlaPairRows = 256;
 // Workspace of one MLA head call: per pair of workgroups, their per-row
-// partial square sums and two ready flags.
+// partial square sums, per-row partial maxima (quantised ckv) and four
+// ready flags.
 int64_t mla_kv_head_workspace_bytes(int64_t T);
 
 // One block-selection launch (see qsa_select_topk in kvrc.h).

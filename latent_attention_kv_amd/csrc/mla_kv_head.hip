@@ -14,6 +14,10 @@
 //   ckv_cache[slot[t]] = bf16(y), k_cache[slot[t]] = bf16(kr); slot -1 skips
 //   (slot[t] from a per-token slot mapping, or from one block-index entry
 //   per chunk of BlockSize tokens of a sequence: PA_BLK_BSND)
+//   or, for a quantised ckv cache (the per-row rule of the norm-rope-cache
+//   operator: scale = RowMax(|y|) / 127 with rounded int8 codes, or
+//   RowMax(|y|) / 448 with the nearest FLOAT8 E4M3FN codes),
+//   ckv_cache[slot[t]] = codes of y * RN(1 / scale), ckv_scale[slot[t]] = scale
 // with float32 accumulation of the bf16 products (no rounding of c before
 // the norm).
 //
@@ -48,12 +52,18 @@
 //     them and clears the flag, so the workspace is all zero again when the
 //     call ends);
 //     rows are normalised and rotated in registers, staged as bf16 in LDS
-//     and scattered with 16-byte stores per cache row piece.
+//     and scattered with 16-byte stores per cache row piece;
+//   * a quantised ckv cache needs the maximum of each row over both halves:
+//     the normalised values stay in the accumulator registers while the
+//     pair swaps per-row partial maxima the same way (second area, second
+//     pair of flags), then the codes are staged (one byte each) and
+//     scattered like the bf16 rows, half 0 also writing the row scale.
 // The wait for the partner is bounded: past the limit the workgroup counts
 // an error and goes on (its rows are then wrong), so the kernel always ends.
 // A partner is dispatched at most 8 workgroups later on the same XCD, and
 // workgroups retire as soon as their pair has swapped, so both halves of a
 // pair are resident together whenever one of them waits.
+#include "device_common.hpp"
 #include "kvrc_launch.hpp"
 
 namespace kvrc {
@@ -61,8 +71,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRows = (int)kMlaPairRows;   // token rows per workgroup pair
@@ -103,7 +111,6 @@ constexpr int kLdsBytes = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
 constexpr int kSpinLimit = 1 << 20;
 // cache-policy operand of a buffer store: sc1 (device scope, write-through)
 constexpr int kStoreSc1 = 16;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the unused counters at their maxima).
@@ -113,18 +120,50 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // c ^ ((r >> 2) & 3).
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+// One exchange of per-row partial values between the two workgroups of a
+// pair, run by wavefront 0 (lane l: rows 4 l .. 4 l + 3): publish p in this
+// half's area of the workspace (then the flag, with release order), wait
+// for the partner's flag (bounded), read its values into q, zero them and
+// clear its flag, so the area is all zero again afterwards. Returns false
+// when the wait timed out (q is then not the partner's).
+__device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, uint32_t *my_flag,
+                                              uint32_t *their_flag, const float (&p)[4],
+                                              float (&q)[4], int lane)
 {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __hip_atomic_store(mine + 4 * lane + j, p[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // release: the wavefront's values above are visible before the flag
+    if (lane == 0)
+        __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    if (lane == 0) {
+        while (__hip_atomic_load(their_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+               spins < kSpinLimit) {
+            __builtin_amdgcn_s_sleep(2);
+            ++spins;
+        }
+    }
+    const bool timed_out = __builtin_amdgcn_readfirstlane(spins) >= kSpinLimit;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[j] = __hip_atomic_load(theirs + 4 * lane + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(theirs + 4 * lane + j, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the partner's values are read and zeroed: clear its flag (the next use
+    // of this area is a later kernel on the stream)
+    if (!timed_out && lane == 0)
+        __hip_atomic_store(their_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return !timed_out;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
+// Q: the ckv cache type (kvrc_cache_dtype: 0 bf16, 1 int8, 2 E4M3FN).
+template <int Q>
 __global__ __launch_bounds__(kThreads)
 void mla_kv_head_kernel(MlaKvHeadArgs a)
 {
+    constexpr int kEsz = Q == 0 ? 2 : 1;        // bytes per ckv element
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -332,50 +371,25 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     __syncthreads();
 
     // ---- swap the per-row partial sums with the other half of the pair ----
-    // workspace: float part[npairs][2][256], then uint32 flag[npairs][2].
-    // Wavefront 0 does the whole swap (lane l: rows 4l .. 4l + 3), so one
-    // release (its stores, then the flag) and one acquire suffice.
+    // workspace: float sums[npairs][2][256], float maxima[npairs][2][256],
+    // then uint32 flags[npairs][4] (sums: halves 0, 1; maxima: halves 0, 1).
+    float *const part = reinterpret_cast<float *>(a.workspace);
+    uint32_t *const flags = reinterpret_cast<uint32_t *>(part + npairs * 4 * kRows);
+    auto area = [&](int round, int h) { return part + ((round * npairs + pair) * 2 + h) * kRows; };
+    auto flag = [&](int round, int h) { return flags + pair * 4 + 2 * round + h; };
     if (wave == 0) {
-        float *part = reinterpret_cast<float *>(a.workspace);
-        uint32_t *flag = reinterpret_cast<uint32_t *>(part + npairs * 2 * kRows);
-        float *mine = part + (pair * 2 + half) * kRows + 4 * lane;
-        float *theirs = part + (pair * 2 + (1 - half)) * kRows + 4 * lane;
-        uint32_t *my_flag = flag + pair * 2 + half;
-        uint32_t *their_flag = flag + pair * 2 + (1 - half);
-        float p[4];
+        float p[4], q[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             p[j] = red[4 * lane + j] + red[kRows + 4 * lane + j];
-            __hip_atomic_store(mine + j, p[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // release: the wavefront's sums above are visible before the flag
-        if (lane == 0)
-            __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        int spins = 0;
-        if (lane == 0) {
-            while (__hip_atomic_load(their_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-                   spins < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(2);
-                ++spins;
-            }
-        }
-        const bool timed_out = __builtin_amdgcn_readfirstlane(spins) >= kSpinLimit;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool ok = pair_exchange(area(0, half), area(0, 1 - half), flag(0, half),
+                                      flag(0, 1 - half), p, q, lane);
+        // the same order in both halves: the sum of columns 0..287 first
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float q = __hip_atomic_load(theirs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(theirs + j, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // the same order in both halves: the sum of columns 0..287 first
-            sums[4 * lane + j] = half == 0 ? p[j] + q : q + p[j];
-        }
-        if (timed_out) {
-            if (lane == 0 && a.err)
-                atomicAdd(a.err, 1);
-        } else if (lane == 0) {
-            // the partner's sums are read and zeroed: clear its flag (the
-            // next use of this pair's area is a later kernel on the stream)
-            __hip_atomic_store(their_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int j = 0; j < 4; ++j)
+            sums[4 * lane + j] = half == 0 ? p[j] + q[j] : q[j] + p[j];
+        if (!ok && lane == 0 && a.err)
+            atomicAdd(a.err, 1);
     }
     __syncthreads();
 
@@ -397,14 +411,22 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             load_rope_tables(m + 1, rc[(m + 1) & 1]);
         const int r = 64 * wm + 16 * m + rsub;
         const float rr = 1.0f / sqrtf(sums[r] / (float)kNorm + a.eps);
+        float mx = 0.0f;                     // max |y| over this lane's columns (quantised)
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
             const f32x4 v = acc[m][n];
             if (n < ntn) {
                 const int col = kWaveCols * wn + 16 * n + cq;       // within the half
-                const uint2 o = {pack_bf16((v[0] * rr) * g[n][0], (v[1] * rr) * g[n][1]),
-                                 pack_bf16((v[2] * rr) * g[n][2], (v[3] * rr) * g[n][3])};
-                *reinterpret_cast<uint2 *>(stage + r * kStageRow + col * 2) = o;
+                const f32x4 y = {(v[0] * rr) * g[n][0], (v[1] * rr) * g[n][1],
+                                 (v[2] * rr) * g[n][2], (v[3] * rr) * g[n][3]};
+                if constexpr (Q == 0) {
+                    const uint2 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                    *reinterpret_cast<uint2 *>(stage + r * kStageRow + col * 2) = o;
+                } else {
+                    acc[m][n] = y;           // coded once the row maximum is known
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])),
+                                         fmaxf(fabsf(y[2]), fabsf(y[3]))));
+                }
             } else {
                 // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
                 // and (2 i0 + 2, 2 i0 + 3) give outputs i0, i0 + 1 and
@@ -417,26 +439,98 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 const float lo1 = v[2] * bf16_hi(c0) - v[3] * bf16_hi(s0);
                 const float hi0 = v[1] * bf16_lo(c1) + v[0] * bf16_lo(s1);
                 const float hi1 = v[3] * bf16_hi(c1) + v[2] * bf16_hi(s1);
-                unsigned char *kr = stage + r * kStageRow + (kNorm - kHalfCols) * 2;
-                *reinterpret_cast<uint32_t *>(kr + i0 * 2) = pack_bf16(lo0, lo1);
-                *reinterpret_cast<uint32_t *>(kr + (32 + i0) * 2) = pack_bf16(hi0, hi1);
+                unsigned char *kr = stage + r * kStageRow + (kNorm - kHalfCols) * kEsz;
+                *reinterpret_cast<uint32_t *>(kr + i0 * 2) = pack_bf16x2(lo0, lo1);
+                *reinterpret_cast<uint32_t *>(kr + (32 + i0) * 2) = pack_bf16x2(hi0, hi1);
             }
+        }
+        if constexpr (Q != 0) {
+            // row maximum of this wavefront's columns: the four column
+            // quarters (lanes l, l ^ 16, l ^ 32, l ^ 48), as for the sums
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                              false, false);
+            mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                              false, false);
+            mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+            if (cq == 0)
+                red[wn * kRows + r] = mx;    // the sums' partials were consumed above
         }
     }
     __syncthreads();
 
+    if constexpr (Q != 0) {
+        // ---- swap the per-row partial maxima, then code the rows ---------
+        if (wave == 0) {
+            float p[4], q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p[j] = fmaxf(red[4 * lane + j], red[kRows + 4 * lane + j]);
+            const bool ok = pair_exchange(area(1, half), area(1, 1 - half), flag(1, half),
+                                          flag(1, 1 - half), p, q, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sums[4 * lane + j] = fmaxf(p[j], q[j]);     // now the row maxima
+            if (!ok && lane == 0 && a.err)
+                atomicAdd(a.err, 1);
+        }
+        __syncthreads();
+        constexpr float kDiv = Q == 1 ? 127.0f : kE4m3Max;
+#pragma unroll
+        for (int m = 0; m < kMt; ++m) {
+            const int r = 64 * wm + 16 * m + rsub;
+            const float scale = row_scale(sums[r], kDiv);
+            // y * RN(1 / scale) (rcp_rn's domain; IEEE division below it,
+            // where a zero row has scale 0 and codes 0)
+            const bool fast = scale >= 0x1p-60f;
+            const float rs = fast ? rcp_rn(scale) : 0.0f;
+#pragma unroll
+            for (int n = 0; n < kNt; ++n) {
+                if (n < ntn) {
+                    float t[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        t[e] = fast ? acc[m][n][e] * rs
+                                    : (scale > 0.0f ? acc[m][n][e] / scale : 0.0f);
+                    uint32_t w;
+                    if constexpr (Q == 1) {
+                        uint32_t b[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)   // low byte of the bits: rint(t), half even
+                            b[e] = __float_as_uint(__builtin_amdgcn_fmed3f(t[e], -127.0f, 127.0f) +
+                                                   kRoundMagic);
+                        w = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) |
+                            __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+                    } else {
+                        w = e4m3_pack4(e4m3_clamp(t[0]), e4m3_clamp(t[1]), e4m3_clamp(t[2]),
+                                       e4m3_clamp(t[3]));
+                    }
+                    const int col = kWaveCols * wn + 16 * n + cq;
+                    *reinterpret_cast<uint32_t *>(stage + r * kStageRow + col) = w;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
     // ---- scatter: wavefront w writes its half of rows w, w + 8, ... --------
-    // half 0: ckv bytes [0, 576) of the row (36 pieces of 16 bytes);
-    // half 1: ckv bytes [576, 1024) (28 pieces), then the k row (8 pieces).
+    // half 0: ckv bytes [0, 576) of the row (36 pieces of 16 bytes; [0, 288),
+    // 18 pieces, for one-byte codes, and the row scale);
+    // half 1: ckv bytes [576, 1024) (28 pieces; [288, 512), 14 pieces), then
+    // the k row (8 pieces).
     // Caches below 4 GiB take sc1 (device scope) buffer stores, which write
     // through the XCD's L2 instead of leaving the rows dirty there: the
     // write-backs of the swap above and of the kernel's end then find little
     // to flush. The descriptors cover exactly the caches.
-    constexpr int kPieces = kHalfCols * 2 / 16;                 // 36
-    constexpr int kCkvPieces1 = (kNorm - kHalfCols) * 2 / 16;   // 28
-    const bool buf = a.cache_rows * kNorm * 2 <= (int64_t)UINT32_MAX;
+    constexpr int kCkvPieces0 = kHalfCols * kEsz / 16;           // 36 (18)
+    constexpr int kCkvPieces1 = (kNorm - kHalfCols) * kEsz / 16;  // 28 (14)
+    constexpr int kKPieces = kRope * 2 / 16;                      // 8
+    const int nckv = half == 0 ? kCkvPieces0 : kCkvPieces1;
+    const int npieces = half == 0 ? kCkvPieces0 : kCkvPieces1 + kKPieces;
+    const int64_t ckv_row = kNorm * kEsz;
+    const bool buf = a.cache_rows * ckv_row <= (int64_t)UINT32_MAX;
     const __amdgpu_buffer_rsrc_t ckv_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(a.ckv_cache, 0, (int)(uint32_t)(a.cache_rows * kNorm * 2),
+        __builtin_amdgcn_make_buffer_rsrc(a.ckv_cache, 0, (int)(uint32_t)(a.cache_rows * ckv_row),
                                           0x00020000);
     const __amdgpu_buffer_rsrc_t k_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(a.k_cache, 0, (int)(uint32_t)(a.cache_rows * kRope * 2),
@@ -455,13 +549,16 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 atomicAdd(a.err, 1);
             continue;
         }
-        if (lane < kPieces) {
+        if constexpr (Q != 0) {
+            if (half == 0 && lane == 63)
+                a.ckv_scale[v] = row_scale(sums[r], Q == 1 ? 127.0f : kE4m3Max);
+        }
+        if (lane < npieces) {
             const uint4 cv = *reinterpret_cast<const uint4 *>(stage + r * kStageRow + lane * 16);
             const u32x4 w = {cv.x, cv.y, cv.z, cv.w};
             // lanes below nckv write the ckv row piece, the others the k row
             // (two stores, each with one descriptor for the whole wavefront)
-            const int nckv = half == 0 ? kPieces : kCkvPieces1;
-            const int64_t ckv_off = v * kNorm * 2 + kHalfCols * 2 * half + lane * 16;
+            const int64_t ckv_off = v * ckv_row + kHalfCols * kEsz * half + lane * 16;
             const int64_t k_off = v * kRope * 2 + (lane - nckv) * 16;
             if (lane < nckv) {
                 if (buf)
@@ -487,7 +584,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 int64_t mla_kv_head_workspace_bytes(int64_t T)
 {
     const int64_t npairs = T > 0 ? (T + kRows - 1) / kRows : 0;
-    return npairs * (2 * kRows * 4 + 2 * 4);
+    return npairs * (4 * kRows * 4 + 4 * 4);
 }
 
 hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)
@@ -495,12 +592,21 @@ hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     const int64_t npairs = (a.T + kRows - 1) / kRows;
     const int64_t grid = 16 * ((npairs + 7) / 8);   // pairs in groups of 8: b and b + 8
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(mla_kv_head_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    const void *fn = a.ckv == 1 ? reinterpret_cast<const void *>(mla_kv_head_kernel<1>)
+                   : a.ckv == 2 ? reinterpret_cast<const void *>(mla_kv_head_kernel<2>)
+                                : reinterpret_cast<const void *>(mla_kv_head_kernel<0>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(mla_kv_head_kernel, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes, stream,
-                       a);
+    if (a.ckv == 1)
+        hipLaunchKernelGGL(mla_kv_head_kernel<1>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
+                           stream, a);
+    else if (a.ckv == 2)
+        hipLaunchKernelGGL(mla_kv_head_kernel<2>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(mla_kv_head_kernel<0>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
+                           stream, a);
     return hipGetLastError();
 }
 

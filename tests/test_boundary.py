@@ -40,7 +40,7 @@ def test_exports_match_header():
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert k.lib().kvrc_version() == 105
+    assert k.lib().kvrc_version() == 106
 
 
 def test_status_strings():
@@ -131,30 +131,30 @@ def test_norm_validation(over, want):
 
 
 M = {name: (i + 40) << 32 for i, name in enumerate(
-    ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err", "ws"])}
-WS_300 = 2 * (2 * 256 * 4 + 2 * 4)      # 300 tokens: two pairs of workgroups
+    ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err", "ws", "sc"])}
+WS_300 = 2 * (4 * 256 * 4 + 4 * 4)      # 300 tokens: two pairs of workgroups
 
 
 def mla(**over):
     a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
-             slot=M["slot"], kc=M["kc"], ckv=M["ckv"], T=300, He=7168, NB=64, BS=128, eps=1e-6,
-             ws=M["ws"], wsb=WS_300, err=None, stream=None)
+             slot=M["slot"], kc=M["kc"], ckv=M["ckv"], sc=None, T=300, He=7168, NB=64, BS=128,
+             dt=0, eps=1e-6, ws=M["ws"], wsb=WS_300, err=None, stream=None)
     a.update(over)
     return k.lib().kvrc_mla_kv_head_paged(a["x"], a["w"], a["gamma"], a["alpha"], a["cos"],
-                                          a["sin"], a["slot"], a["kc"], a["ckv"], a["T"], a["He"],
-                                          a["NB"], a["BS"], a["eps"], a["ws"], a["wsb"], a["err"],
-                                          a["stream"])
+                                          a["sin"], a["slot"], a["kc"], a["ckv"], a["sc"], a["T"],
+                                          a["He"], a["NB"], a["BS"], a["dt"], a["eps"], a["ws"],
+                                          a["wsb"], a["err"], a["stream"])
 
 
 def mla_blk(**over):
     a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
-             idx=M["slot"], kc=M["kc"], ckv=M["ckv"], B=3, S=100, He=7168, NB=64, BS=128,
-             eps=1e-6, ws=M["ws"], wsb=WS_300, err=None, stream=None)
+             idx=M["slot"], kc=M["kc"], ckv=M["ckv"], sc=None, B=3, S=100, He=7168, NB=64,
+             BS=128, dt=0, eps=1e-6, ws=M["ws"], wsb=WS_300, err=None, stream=None)
     a.update(over)
     return k.lib().kvrc_mla_kv_head_paged_blk(a["x"], a["w"], a["gamma"], a["alpha"], a["cos"],
-                                              a["sin"], a["idx"], a["kc"], a["ckv"], a["B"],
-                                              a["S"], a["He"], a["NB"], a["BS"], a["eps"],
-                                              a["ws"], a["wsb"], a["err"], a["stream"])
+                                              a["sin"], a["idx"], a["kc"], a["ckv"], a["sc"],
+                                              a["B"], a["S"], a["He"], a["NB"], a["BS"], a["dt"],
+                                              a["eps"], a["ws"], a["wsb"], a["err"], a["stream"])
 
 
 @pytest.mark.parametrize("over,want", [
@@ -163,6 +163,7 @@ def mla_blk(**over):
     (dict(idx=M["slot"] + 4), ALIGN), (dict(ws=None), NULL), (dict(wsb=WS_300 - 1), WORKSPACE),
     # 3 * ceil(100 / 128) = 3 index entries (24 bytes): an output 16 bytes in overlaps
     (dict(kc=M["slot"] + 16), ALIAS),
+    (dict(dt=2), DTYPE), (dict(dt=2, sc=M["sc"] + 2), ALIGN), (dict(dt=-1), DTYPE),
     (dict(B=0), OK), (dict(S=0, idx=None), OK),
 ])
 def test_mla_blk_validation(over, want):
@@ -170,13 +171,13 @@ def test_mla_blk_validation(over, want):
 
 
 def test_mla_workspace_bytes():
-    """One pair of workgroups per 256 tokens: 256 partial sums per half and
-    two flags."""
+    """One pair of workgroups per 256 tokens: 256 partial sums and 256
+    partial maxima per half, and four flags."""
     f = k.lib().kvrc_mla_kv_head_workspace_bytes
     assert f(0) == 0
-    assert f(1) == f(256) == 2056
-    assert f(257) == 2 * 2056
-    assert f(32768) == 128 * 2056
+    assert f(1) == f(256) == 4112
+    assert f(257) == 2 * 4112
+    assert f(32768) == 128 * 4112
     assert f(-1) == -1 and f(1 << 31) == -1
     assert f(300) == WS_300
 
@@ -194,6 +195,13 @@ def test_mla_workspace_bytes():
     (dict(ws=None), NULL), (dict(ws=M["ws"] + 8), ALIGN), (dict(ws=M["ckv"] + 64), ALIAS),
     (dict(ws=M["x"]), ALIAS), (dict(wsb=WS_300 - 1), WORKSPACE), (dict(wsb=0), WORKSPACE),
     (dict(T=0), OK), (dict(T=0, x=None, kc=None), OK), (dict(T=0, ws=None, wsb=0), OK),
+    # quantised ckv: the scale pointer goes with the type; [rows] float32
+    (dict(dt=3), DTYPE), (dict(dt=1), DTYPE), (dict(dt=2), DTYPE), (dict(sc=M["sc"]), DTYPE),
+    (dict(dt=1, sc=M["sc"] + 2), ALIGN), (dict(dt=1, sc=M["ckv"] + 64), ALIAS),
+    (dict(dt=2, sc=M["kc"]), ALIAS), (dict(dt=1, sc=M["ws"]), ALIAS), (dict(dt=1, sc=M["x"]), ALIAS),
+    # an int8 ckv cache of 64 * 128 rows holds 4 MiB: a scale array 4 bytes before its end
+    # overlaps it
+    (dict(dt=1, sc=M["ckv"] + 64 * 128 * 512 - 4), ALIAS),
 ])
 def test_mla_validation(over, want):
     assert mla(**over) == want

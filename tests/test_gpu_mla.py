@@ -15,6 +15,15 @@ in the sums), at least 99.5 % of the outputs must equal the float64 value
 rounded to bf16 (a correct float32 path misses it only where its error of
 about 1e-6 relative straddles a bf16 rounding boundary). Placement and every
 byte no token addresses: bit-exact.
+
+A quantised ckv cache (int8 codes with scale RowMax/127, E4M3FN codes with
+RowMax/448) is held to the same dy: with dA the largest dy of the row, the
+quotient t = y * d / RowMax the kernel rounds lies within
+    dt = (dy * d / RowMax + |t| * dA / RowMax) * 1.01 + 4 u |t|
+of the float64 one, so its code must lie between the codes of t - dt and
+t + dt (rounding is monotone), the scale within dA / d * 1.01 + 2 u scale;
+each row's largest code is exactly 127 (448), a zero row stores scale 0 and
+code bytes 0, and at least 99.5 % of the codes equal the float64 oracle's.
 """
 import numpy as np
 import pytest
@@ -49,20 +58,35 @@ def new_workspace(T):
                        device=DEV)
 
 
+def dev_cache(arr):
+    """Device copy of a cache array: bf16 bits (uint16), int8 or E4M3FN codes
+    (uint8), float32 scales."""
+    if arr.dtype == np.uint16:
+        return dbf(arr)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def host_cache(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
 def run_mla_gpu(case, slots=None, err=None, workspace=None):
     """One call; the workspace (fresh unless given) must be all zero again
     afterwards."""
-    caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
+    caches = {n: dev_cache(spec.numpy()) for n, spec in case["caches"].items()}
     slots = case["slot_mapping"] if slots is None else slots
     T = case["x"].shape[0]
     ws = new_workspace(T) if workspace is None else workspace
     k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
                              dbf(case["sin"]), torch.from_numpy(slots).to(DEV),
-                             caches["k_cache"], caches["ckv_cache"], workspace=ws,
-                             alpha_kv=case["alpha"], eps=case["eps"], err_count=err)
+                             caches["k_cache"], caches["ckv_cache"], caches.get("ckv_scale"),
+                             workspace=ws, alpha_kv=case["alpha"], eps=case["eps"],
+                             err_count=err)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
-    return {n: t.view(torch.int16).cpu().numpy().view(np.uint16) for n, t in caches.items()}
+    return {n: host_cache(t) for n, t in caches.items()}
 
 
 def ulp_bf16(v):
@@ -70,8 +94,9 @@ def ulp_bf16(v):
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
-def expected_with_bounds(case):
-    """float64 outputs (oracle) and the per-element bound on |bf16 gpu - value|."""
+def head_bounds(case):
+    """float64 outputs (oracle) and the per-element bounds dy, dk on the
+    float32 values of the kernel before any rounding of the outputs."""
     y, kr = M.kv_head_rows(case["x"], case["w"], case["gamma"], case["alpha"], case["cos"],
                            case["sin"], case["eps"])
     X, W = M.bf16_to_f64(case["x"]), M.bf16_to_f64(case["w"])
@@ -96,21 +121,62 @@ def expected_with_bounds(case):
     ev_, od_ = np.concatenate([er[:, 0::2], er[:, 1::2]], 1), np.concatenate([er[:, 1::2], er[:, 0::2]], 1)
     rv_, ro_ = np.concatenate([r[:, 0::2], r[:, 1::2]], 1), np.concatenate([r[:, 1::2], r[:, 0::2]], 1)
     dk = (cs * ev_ + sn * od_) * 1.01 + 3 * U * (np.abs(rv_) * cs + np.abs(ro_) * sn)
-    tol_y = dy + 0.5 * ulp_bf16(np.abs(y) + dy)
-    tol_k = dk + 0.5 * ulp_bf16(np.abs(kr) + dk)
-    return y, kr, tol_y, tol_k
+    return y, kr, dy, dk
 
 
-def compare_mla(case, got, slots=None):
+def compare_quant(kind, codes, scales, y, dy):
+    """Quantised rows (codes [n, 512], scales [n]) against the float64 rows y
+    with bounds dy; returns the fraction of codes equal to the oracle's."""
+    d = 127.0 if kind == "int8" else 448.0
+    amax = np.max(np.abs(y), axis=1)
+    dA = np.max(dy, axis=1)
+    zero = amax == 0
+    assert np.all(scales[zero] == 0) and np.all(codes[zero].view(np.uint8) == 0), \
+        "zero rows must store scale 0 and code bytes 0"
+    nz = ~zero
+    y, dy, amax, dA, codes, scales = y[nz], dy[nz], amax[nz], dA[nz], codes[nz], scales[nz]
+    want_s = amax / d
+    bad = ~(np.abs(scales.astype(np.float64) - want_s) <= dA / d * 1.01 + 2 * U * want_s)
+    assert not bad.any(), f"{int(bad.sum())} scales beyond the bound"
+    t = y * (d / amax)[:, None]
+    dt = (dy * (d / amax)[:, None] + np.abs(t) * (dA / amax)[:, None]) * 1.01 + 4 * U * np.abs(t)
+    if kind == "int8":
+        rnd = lambda v: np.rint(np.clip(v, -d, d))
+        gv = codes.astype(np.float64)
+    else:
+        rnd = lambda v: M.e4m3_round(np.clip(v, -d, d))
+        gv = M.e4m3_decode(codes.view(np.uint8))
+    bad = ~((rnd(t - dt) <= gv) & (gv <= rnd(t + dt)))
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        pytest.fail(f"{int(bad.sum())} codes beyond the bound, e.g. row {i[0]} col {i[1]}: "
+                    f"gpu {gv[tuple(i)]!r} want {rnd(t)[tuple(i)]!r} (t {t[tuple(i)]!r} +- "
+                    f"{dt[tuple(i)]!r})")
+    assert np.all(np.max(np.abs(gv), axis=1) == d), "a row's largest code must be the maximum"
+    q, _ = M.quantize_rows(y, kind)
+    want = q.astype(np.int8) if kind == "int8" else M.e4m3_encode(q)
+    equal = int(np.sum(codes.view(np.uint8) == want.view(np.uint8)))
+    assert codes.size - equal <= max(3, int(0.005 * codes.size)), \
+        f"only {equal / codes.size:.5f} of the codes equal the oracle's"
+    return equal / codes.size if codes.size else 1.0
+
+
+def compare_mla(case, got, slots=None, bounds=None):
     """Returns (fraction of outputs equal to the rounded float64 value, worst
     error / bound)."""
     slots = case["slot_mapping"] if slots is None else slots
-    y, kr, tol_y, tol_k = expected_with_bounds(case)
+    kind = case.get("ckv_dtype", "bf16")
+    y, kr, dy, dk = head_bounds(case) if bounds is None else bounds
+    tol_k = dk + 0.5 * ulp_bf16(np.abs(kr) + dk)
     ck, kc = got["ckv_cache"].reshape(-1, 512), got["k_cache"].reshape(-1, 64)
     t_idx = np.flatnonzero(slots >= 0)
     rows = slots[t_idx]
+    checks = [(kc[rows], kr[t_idx], tol_k[t_idx])]
+    if kind == "bf16":
+        tol_y = dy + 0.5 * ulp_bf16(np.abs(y) + dy)
+        checks.insert(0, (ck[rows], y[t_idx], tol_y[t_idx]))
     equal, total, worst = 0, 0, 0.0
-    for gbits, want, tol in ((ck[rows], y[t_idx], tol_y[t_idx]), (kc[rows], kr[t_idx], tol_k[t_idx])):
+    for gbits, want, tol in checks:
         gv = M.bf16_to_f64(gbits)
         err = np.abs(gv - want)
         bad = ~(err <= tol)
@@ -128,8 +194,13 @@ def compare_mla(case, got, slots=None):
     assert total - equal <= max(3, int(0.005 * total)), \
         f"only {frac:.5f} of the outputs equal the float64 value rounded to bf16"
     untouched = np.setdiff1d(np.arange(ck.shape[0]), rows)
-    assert np.all(ck[untouched] == gen.BF16_SENTINEL) and np.all(kc[untouched] == gen.BF16_SENTINEL), \
+    sentinel = {"bf16": gen.BF16_SENTINEL, "int8": gen.INT8_SENTINEL, "fp8": gen.FP8_SENTINEL}[kind]
+    assert np.all(ck[untouched] == sentinel) and np.all(kc[untouched] == gen.BF16_SENTINEL), \
         "bytes outside the written rows changed"
+    if kind != "bf16":
+        sc = got["ckv_scale"].reshape(-1)
+        assert np.all(sc[untouched] == gen.SCALE_SENTINEL), "scales outside the written rows changed"
+        frac = compare_quant(kind, ck[rows], sc[rows], y[t_idx], dy[t_idx])
     return frac, worst
 
 
@@ -325,17 +396,17 @@ def run_mla_blk_gpu(case, index=None, err=None):
     """One block-indexed call (x, cos, sin as [B, S, ...]); the workspace
     must be zero again afterwards."""
     B, S = case["B"], case["S"]
-    caches = {n: dbf(spec.numpy()) for n, spec in case["caches"].items()}
+    caches = {n: dev_cache(spec.numpy()) for n, spec in case["caches"].items()}
     idx = case["block_index"] if index is None else index
     ws = new_workspace(B * S)
     k.kvrc_mla_kv_head_paged_blk(dbf(case["x"]).view(B, S, -1), dbf(case["w"]), dbf(case["gamma"]),
                                  dbf(case["cos"]).view(B, S, 64), dbf(case["sin"]).view(B, S, 64),
                                  torch.from_numpy(idx).to(DEV), caches["k_cache"],
-                                 caches["ckv_cache"], workspace=ws, alpha_kv=case["alpha"],
-                                 eps=case["eps"], err_count=err)
+                                 caches["ckv_cache"], caches.get("ckv_scale"), workspace=ws,
+                                 alpha_kv=case["alpha"], eps=case["eps"], err_count=err)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
-    return {n: t.view(torch.int16).cpu().numpy().view(np.uint16) for n, t in caches.items()}
+    return {n: host_cache(t) for n, t in caches.items()}
 
 
 @pytest.mark.parametrize("B,S,BS,offsets,He", [(2, 300, 64, True, 256), (3, 37, 16, False, 64),
@@ -367,3 +438,136 @@ def test_mla_paged_blk_invalid_entries_counted_per_token():
     fixed[[1, 3]] = -1
     slots = M.block_index_slots(fixed, 2, 100, 32, 16 * 32)
     compare_mla(case, got, slots=slots)
+
+
+# ---------------------------------------------------------------------------
+# quantised ckv cache (int8 RowMax/127, E4M3FN RowMax/448)
+# ---------------------------------------------------------------------------
+
+def test_mla_quantised_named_workload_full_size():
+    """The named workload's shape (T=32768, He=7168) into int8 and E4M3FN ckv
+    caches; one float64 evaluation serves both."""
+    say("[mla-q] workload mla_kv_head (T=32768, He=7168), int8 and fp8")
+    base = gen.make_config("mla_kv_head")
+    bounds = None
+    for kind in ("int8", "fp8"):
+        case = dict(base, ckv_dtype=kind, caches=dict(
+            base["caches"], ckv_cache=gen.ckv_cache_spec(base["caches"]["ckv_cache"].shape, kind),
+            ckv_scale=gen.CacheSpec(base["caches"]["ckv_cache"].shape[:3], np.float32,
+                                    gen.SCALE_SENTINEL)))
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        got = run_mla_gpu(case, err=err)
+        assert int(err.item()) == 0
+        if bounds is None:
+            bounds = head_bounds(case)
+        frac, _ = compare_mla(case, got, bounds=bounds)
+        say(f"[mla-q] {kind}: codes equal to the oracle's {frac:.6f}")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("B,S,He", [(1, 1, 32), (1, 5, 64), (2, 300, 7168), (3, 257, 1024),
+                                    (1, 2305, 64)])
+def test_mla_quantised_shapes(kind, B, S, He):
+    say(f"[mla-q] {kind} B={B} S={S} He={He}")
+    case = gen.mla_kv_head_case(600 + S + He, B=B, S=S, He=He, num_blocks=160, block_size=32,
+                                slot_kind="random", skip_frac=0.1, ckv_dtype=kind)
+    frac, _ = compare_mla(case, run_mla_gpu(case))
+    say(f"[mla-q] codes equal {frac:.5f}")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("alpha,x_sigma", [(0.0, 1.0), (-1.5, 1.0), (1.0, 1e-3), (1.0, 300.0)])
+def test_mla_quantised_alpha_and_magnitudes(kind, alpha, x_sigma):
+    """alpha = 0: every row zero (scale 0, code bytes 0); a negative alpha;
+    tiny and large inputs (the norm makes the codes scale-free)."""
+    say(f"[mla-q] {kind} alpha={alpha} x_sigma={x_sigma}")
+    case = gen.mla_kv_head_case(620, B=2, S=200, He=1024, num_blocks=32, block_size=32,
+                                slot_kind="random", alpha=alpha, x_sigma=x_sigma, ckv_dtype=kind)
+    compare_mla(case, run_mla_gpu(case))
+
+
+def test_mla_quantised_many_pairs_and_shared_workspace():
+    """1280 workgroups (two exchanges per pair, pairs starting while others
+    run) with no timed-out wait; then a bf16 call and an fp8 call on the same
+    workspace, each leaving it zero."""
+    say("[mla-q] T=163840 int8, then bf16 and fp8 on one workspace")
+    case = gen.mla_kv_head_case(630, B=4, S=40960, He=64, num_blocks=1400, block_size=128,
+                                slot_kind="random", skip_frac=0.01, ckv_dtype="int8")
+    ws = new_workspace(163840)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    compare_mla(case, run_mla_gpu(case, err=err, workspace=ws))
+    assert int(err.item()) == 0
+    for kind in ("bf16", "fp8"):
+        c = gen.mla_kv_head_case(631, B=1, S=700, He=128, num_blocks=64, block_size=16,
+                                 slot_kind="random", ckv_dtype=kind)
+        compare_mla(c, run_mla_gpu(c, err=err, workspace=ws))
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("B,S,BS,offsets,He", [(2, 300, 64, True, 256), (3, 37, 16, False, 64)])
+def test_mla_quantised_paged_blk(kind, B, S, BS, offsets, He):
+    say(f"[mla-q] blk {kind} B={B} S={S} BS={BS} He={He}")
+    chunks = B * (-(-S // BS))
+    case = gen.mla_kv_head_blk_case(640 + S + BS, B=B, S=S, He=He,
+                                    num_blocks=max(2 * chunks, 16), block_size=BS,
+                                    n_skip=min(2, chunks - 1), entry_offsets=offsets,
+                                    ckv_dtype=kind)
+    slots = M.block_index_slots(case["block_index"], B, S, BS, case["num_blocks"] * BS)
+    compare_mla(case, run_mla_blk_gpu(case), slots=slots)
+
+
+def test_mla_quantised_invalid_slots_are_skipped_and_counted():
+    case = gen.mla_kv_head_case(650, B=1, S=300, He=256, num_blocks=32, block_size=16,
+                                slot_kind="random", skip_frac=0.05, ckv_dtype="fp8")
+    slots = case["slot_mapping"].copy()
+    slots[[3, 130, 299]] = [32 * 16, -2, 1 << 40]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_mla_gpu(case, slots=slots, err=err)
+    assert int(err.item()) == 3
+    fixed = slots.copy()
+    fixed[[3, 130, 299]] = -1
+    compare_mla(case, got, slots=fixed)
+
+
+def test_mla_quantised_cache_larger_than_4gib():
+    """An int8 ckv cache of 4 GiB or more (2^23 rows) takes the plain-store
+    path: rows beyond the 32-bit byte offset land exactly, with their scales,
+    and nothing else changes."""
+    T, He, BS = 300, 256, 128
+    rows_4g = 2 ** 32 // 512
+    NB = rows_4g // BS + 64
+    say(f"[mla-q] int8 cache over 4 GiB: {NB} blocks")
+    case = gen.mla_kv_head_case(660, B=1, S=T, He=He, num_blocks=1, block_size=T,
+                                slot_kind="random", skip_frac=0.05, ckv_dtype="int8")
+    rng = gen.rng_for(661)
+    lo = rng.choice(rows_4g - 1, size=T // 2, replace=False)
+    hi = rows_4g + rng.choice(NB * BS - rows_4g, size=T - T // 2, replace=False)
+    big = np.concatenate([lo, hi]).astype(np.int64)
+    rng.shuffle(big)
+    big[case["slot_mapping"] < 0] = -1
+    sentinel = int(np.array([gen.BF16_SENTINEL], dtype=np.uint16).view(np.int16)[0])
+    kc = torch.full((NB, BS, 1, 64), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ck = torch.full((NB, BS, 1, 512), gen.INT8_SENTINEL, dtype=torch.int8, device=DEV)
+    sc = torch.full((NB, BS, 1), gen.SCALE_SENTINEL, dtype=torch.float32, device=DEV)
+    ws = new_workspace(T)
+    k.kvrc_mla_kv_head_paged(dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
+                             dbf(case["sin"]), torch.from_numpy(big).to(DEV), kc, ck, sc,
+                             workspace=ws, alpha_kv=case["alpha"], eps=case["eps"])
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    valid = big >= 0
+    idx = torch.from_numpy(big[valid]).to(DEV)
+    compact = case["slot_mapping"][valid]
+    got = {"ckv_cache": np.full((T, 512), gen.INT8_SENTINEL, np.int8),
+           "k_cache": np.full((T, 64), gen.BF16_SENTINEL, np.uint16),
+           "ckv_scale": np.full(T, gen.SCALE_SENTINEL, np.float32)}
+    got["ckv_cache"][compact] = ck.view(-1, 512)[idx].cpu().numpy()
+    got["k_cache"][compact] = kc.view(-1, 64)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    got["ckv_scale"][compact] = sc.view(-1)[idx].cpu().numpy()
+    for t, d, s_ in ((ck, 512, gen.INT8_SENTINEL), (kc.view(torch.int16), 64, sentinel),
+                     (sc, 1, gen.SCALE_SENTINEL)):
+        changed = int((t != s_).sum().item())
+        in_rows = int((t.reshape(-1, d)[idx] != s_).sum().item())
+        assert changed == in_rows, "bytes outside the written rows changed"
+    compare_mla(case, got)
