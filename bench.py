@@ -76,6 +76,12 @@ WORKLOAD_TEXT = {
     "mla_kv_head": "MLA kv-path head: T=32768 tokens (B=8, S=4096), x [32768,7168] bf16 times "
                    "the fused projection [576,7168] bf16 (random init) on the matrix cores, "
                    "alpha_kv 0.875, RMSNorm + RoPE, PA_BNSD caches [8192,128,1,512/64] bf16",
+    "mla_kv_head_int8": "MLA kv-path head as mla_kv_head (T=32768, He=7168) into an int8 ckv "
+                        "cache [8192,128,1,512] + fp32 scale [8192,128,1] (RowMax/127), k "
+                        "cache bf16 [8192,128,1,64]",
+    "mla_kv_head_fp8": "MLA kv-path head as mla_kv_head (T=32768, He=7168) into a FLOAT8 "
+                       "E4M3FN ckv cache [8192,128,1,512] + fp32 scale [8192,128,1] "
+                       "(RowMax/448), k cache bf16 [8192,128,1,64]",
     "qsa_select": "block selection: N=128 sequences x 1 query token, H=64 heads, Di=128, block "
                   "keys [128,256,128] bf16 (key_length U[4096,16384), key_block_size 64), "
                   "selection blocks of 2 key blocks, top 16",
@@ -84,7 +90,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def kernel_family(workload: str) -> str:
-    return {"qsa": "qsa", "mla_kv_head": "mla", "qsa_select": "sel"}.get(workload, "kvrc")
+    if workload.startswith("mla_kv_head"):
+        return "mla"
+    return {"qsa": "qsa", "qsa_select": "sel"}.get(workload, "kvrc")
 
 
 def _code_only(rel: str, text: str) -> str:
@@ -128,7 +136,8 @@ def algorithmic_bytes(case) -> tuple[int, int]:
     if case.get("mode") == "mla_paged":
         T, He = case["T"], case["He"]
         written = int((case["slot_mapping"] >= 0).sum())
-        return (T * He * 2 + 576 * He * 2 + T * (2 * 2 * 64 + 8) + written * (1024 + 128)
+        ckv_row = 1024 if case.get("ckv_dtype", "bf16") == "bf16" else 512 + 4
+        return (T * He * 2 + 576 * He * 2 + T * (2 * 2 * 64 + 8) + written * (ckv_row + 128)
                 + 1024, T)
     if "raw_index_keys" in case:
         N, L, Di, Dr, kbs = case["N"], case["L"], case["Di"], case["Dr"], case["kbs"]
@@ -192,10 +201,7 @@ def build_sets(case, R, dev):
         for i in range(R):
             s = {k: (v.clone() if i else v) for k, v in base.items()}
             s["ws"] = ws
-            for name, spec in case["caches"].items():
-                fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
-                s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
-                                     device=dev).view(torch.bfloat16)
+            s.update(_cache_tensors(case, dev))
             sets.append(s)
         return sets
     if "raw_index_keys" in case:
@@ -215,17 +221,26 @@ def build_sets(case, R, dev):
                 sin=dbf(case["sin"]), idx=dt(case[idx_name]))
     for _ in range(R):
         s = {k: v.clone() for k, v in base.items()}
-        for name, spec in case["caches"].items():
-            if spec.dtype == np.uint16:
-                fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
-                s[name] = torch.full(spec.shape, fill, dtype=torch.int16,
-                                     device=dev).view(torch.bfloat16)
-            else:
-                tdt = {np.dtype(np.int8): torch.int8, np.dtype(np.uint8): torch.uint8,
-                       np.dtype(np.float32): torch.float32}[spec.dtype]
-                s[name] = torch.full(spec.shape, spec.fill, dtype=tdt, device=dev)
+        s.update(_cache_tensors(case, dev))
         sets.append(s)
     return sets
+
+
+def _cache_tensors(case, dev):
+    """Fresh device caches of the case, filled with their sentinels."""
+    import numpy as np
+    import torch
+    out = {}
+    for name, spec in case["caches"].items():
+        if spec.dtype == np.uint16:
+            fill = int(np.array([spec.fill], dtype=np.uint16).view(np.int16)[0])
+            out[name] = torch.full(spec.shape, fill, dtype=torch.int16,
+                                   device=dev).view(torch.bfloat16)
+        else:
+            tdt = {np.dtype(np.int8): torch.int8, np.dtype(np.uint8): torch.uint8,
+                   np.dtype(np.float32): torch.float32}[spec.dtype]
+            out[name] = torch.full(spec.shape, spec.fill, dtype=tdt, device=dev)
+    return out
 
 
 def launch(case, s):
@@ -236,8 +251,8 @@ def launch(case, s):
                           cmp_ratio=case["cmp_ratio"], scale=case["scale"])
     elif case.get("mode") == "mla_paged":
         k.kvrc_mla_kv_head_paged(s["x"], s["w"], s["gamma"], s["cos"], s["sin"], s["idx"],
-                                 s["k_cache"], s["ckv_cache"], workspace=s["ws"],
-                                 alpha_kv=case["alpha"], eps=case["eps"])
+                                 s["k_cache"], s["ckv_cache"], s.get("ckv_scale"),
+                                 workspace=s["ws"], alpha_kv=case["alpha"], eps=case["eps"])
     elif "raw_index_keys" in case:
         k.qsa_prepare(s["raw"], s["bk"], s["kl"], s["rc"], s["rs"], s["w"], s["praw"], s["prope"],
                       s["nraw"], s["nrope"], key_block_size=case["kbs"], eps=case["eps"])
@@ -278,7 +293,8 @@ def cpu_baseline(case, seconds=10.0):
         caches = {k: spec.numpy() for k, spec in case["caches"].items()}
         args = (case["x"][:sample], case["w"], case["gamma"], case["alpha"], case["cos"][:sample],
                 case["sin"][:sample], case["slot_mapping"][:sample], caches["k_cache"],
-                caches["ckv_cache"], case["eps"])
+                caches["ckv_cache"], case["eps"], caches.get("ckv_scale"),
+                case.get("ckv_dtype", "bf16"))
         while busy < seconds or n == 0:
             s0 = time.perf_counter()
             M.mla_kv_head_paged(*args)

@@ -386,7 +386,7 @@ def qsa_case(seed, N, L, Di, Dr, kbs, *, past_max=8192, Bcap=None, eps=1e-6,
 # ---------------------------------------------------------------------------
 
 def make_config(name: str, seed: int | None = None):
-    """The five named workloads, seeds 1..5 by default."""
+    """The named workloads, each with its own default seed."""
     if name == "norm_tiny":
         return kvrc_norm_case(1 if seed is None else seed, B=2, S=16, Dv=512, Dk=64,
                               Bc=2, Sc=32, n_skip=3)
@@ -413,6 +413,11 @@ def make_config(name: str, seed: int | None = None):
         # the prefill batch through the MLA kv-path head (DeepSeek-V3 hidden 7168)
         return mla_kv_head_case(8 if seed is None else seed, B=8, S=4096, He=7168,
                                 num_blocks=8192, block_size=128)
+    if name in ("mla_kv_head_int8", "mla_kv_head_fp8"):
+        # the same head into an int8 (RowMax/127) or E4M3FN (RowMax/448) ckv cache
+        kind = name.rsplit("_", 1)[1]
+        return mla_kv_head_case((10 if kind == "int8" else 11) if seed is None else seed, B=8,
+                                S=4096, He=7168, num_blocks=8192, block_size=128, ckv_dtype=kind)
     if name == "qsa_select":
         # decode-time block selection: 128 sequences, 64 query heads, up to
         # 256 blocks of 64 tokens, selection blocks of 128 tokens, top 16
