@@ -74,7 +74,9 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
         !aligned(ckv_scale, 4) || !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
 
-    const int64_t chunks = block_size > 0 ? (S + block_size - 1) / block_size : 0;
+    // ceil(S / block_size) without forming S + block_size (block_size may be
+    // near 2^63 when num_blocks is 0)
+    const int64_t chunks = block_size > 0 ? S / block_size + (S % block_size != 0) : 0;
     const int64_t index_count = block_size > 0 ? B * chunks : T;
     int64_t kbytes, cbytes, sbytes = 0;
     if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (quant ? 1 : 2), &cbytes) ||
@@ -220,7 +222,7 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
         !mul_ok(rows, 64 * 2, &kbytes) || !mul_ok(rows, 512 * (quant ? 1 : 2), &cbytes))
         return KVRC_ERR_SHAPE;
     const int64_t sbytes = quant ? rows * 4 : 0;
-    const int64_t chunks = blk && S > 0 ? (S + block_size - 1) / block_size : 0;
+    const int64_t chunks = blk && S > 0 ? S / block_size + (S % block_size != 0) : 0;
     const int64_t index_count = blk ? B * chunks : T;
     if (T == 0)
         return KVRC_OK;                       // empty input: caches untouched

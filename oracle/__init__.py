@@ -1,5 +1,6 @@
 """ctypes binding of the CPU oracle (``oracle/kvrc_oracle.c``); the MLA
-kv-path head oracle (float64, numpy) is ``oracle/mla_kv_head.py``.
+kv-path head and block-selection oracles (float64, numpy) are
+``oracle/mla_kv_head.py`` and ``oracle/qsa_select.py``.
 
 TEST INFRASTRUCTURE ONLY: the plain CPU definition that the HIP library is
 checked against. Only the tests, ``__graft_entry__.smoke()`` and the bench's

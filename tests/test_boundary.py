@@ -164,6 +164,10 @@ def mla_blk(**over):
     # 3 * ceil(100 / 128) = 3 index entries (24 bytes): an output 16 bytes in overlaps
     (dict(kc=M["slot"] + 16), ALIAS),
     (dict(dt=2), DTYPE), (dict(dt=2, sc=M["sc"] + 2), ALIGN), (dict(dt=-1), DTYPE),
+    # no blocks and a block size near 2^63: one chunk per sequence, 3 entries (24 bytes),
+    # so a workspace 16 bytes into the index aliases (the chunk count must not overflow;
+    # the caches hold no rows, so only the workspace can overlap)
+    (dict(NB=0, BS=(1 << 63) - 1, ws=M["slot"] + 16), ALIAS),
     (dict(B=0), OK), (dict(S=0, idx=None), OK),
 ])
 def test_mla_blk_validation(over, want):
