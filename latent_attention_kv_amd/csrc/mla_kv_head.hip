@@ -480,9 +480,9 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         for (int m = 0; m < kMt; ++m) {
             const int r = 64 * wm + 16 * m + rsub;
             const float scale = row_scale(sums[r], kDiv);
-            // y * RN(1 / scale) (rcp_rn's domain; IEEE division below it,
-            // where a zero row has scale 0 and codes 0)
-            const bool fast = scale >= 0x1p-60f;
+            // y * RN(1 / scale) in rcp_rn's domain [2^-60, 2^60]; IEEE
+            // division outside it (a zero row has scale 0 and codes 0)
+            const bool fast = scale >= 0x1p-60f && scale <= 0x1p60f;
             const float rs = fast ? rcp_rn(scale) : 0.0f;
 #pragma unroll
             for (int n = 0; n < kNt; ++n) {

@@ -476,10 +476,13 @@ def test_mla_quantised_shapes(kind, B, S, He):
 
 
 @pytest.mark.parametrize("kind", ["int8", "fp8"])
-@pytest.mark.parametrize("alpha,x_sigma", [(0.0, 1.0), (-1.5, 1.0), (1.0, 1e-3), (1.0, 300.0)])
+@pytest.mark.parametrize("alpha,x_sigma", [(0.0, 1.0), (-1.5, 1.0), (1.0, 1e-3), (1.0, 300.0),
+                                           (2.0 ** 70, 1.0), (2.0 ** -80, 1.0)])
 def test_mla_quantised_alpha_and_magnitudes(kind, alpha, x_sigma):
     """alpha = 0: every row zero (scale 0, code bytes 0); a negative alpha;
-    tiny and large inputs (the norm makes the codes scale-free)."""
+    tiny and large inputs (the norm makes the codes scale-free); alpha 2^70
+    and 2^-80 put the scales above 2^60 and below 2^-60, outside the fast
+    reciprocal's domain (IEEE division there)."""
     say(f"[mla-q] {kind} alpha={alpha} x_sigma={x_sigma}")
     case = gen.mla_kv_head_case(620, B=2, S=200, He=1024, num_blocks=32, block_size=32,
                                 slot_kind="random", alpha=alpha, x_sigma=x_sigma, ckv_dtype=kind)
