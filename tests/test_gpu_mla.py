@@ -353,14 +353,21 @@ def test_mla_workspace_too_small_is_rejected():
                   == gen.BF16_SENTINEL)
 
 
-def test_mla_cache_larger_than_4gib():
+@pytest.mark.parametrize("span", ["over_4gib", "3gib"])
+def test_mla_large_cache_offsets(span):
     """Caches of 4 GiB or more take the plain-store path of the scatter (the
     sc1 buffer stores need 32-bit offsets): rows beyond the 32-bit byte
-    offset land exactly and nothing else in the caches changes."""
+    offset land exactly. A 3 GiB cache takes the buffer stores, whose offsets
+    pass 2^31 there: rows beyond 2 GiB land too. Nothing else in the caches
+    changes."""
     T, He, BS = 300, 256, 128
-    rows_4g = 2 ** 32 // 1024                                  # ckv rows below the 4 GiB offset
-    NB = rows_4g // BS + 64
-    say(f"[mla] cache over 4 GiB: {NB} blocks")
+    if span == "over_4gib":
+        rows_4g = 2 ** 32 // 1024                              # ckv rows below the 4 GiB offset
+        NB = rows_4g // BS + 64
+    else:
+        rows_4g = 2 ** 31 // 1024                              # ckv rows below the 2 GiB offset
+        NB = (3 * 2 ** 30 // 1024) // BS
+    say(f"[mla] large cache ({span}): {NB} blocks")
     case = gen.mla_kv_head_case(560, B=1, S=T, He=He, num_blocks=1, block_size=T,
                                 slot_kind="random", skip_frac=0.05)   # compact slots 0..T-1
     rng = gen.rng_for(561)
@@ -533,14 +540,20 @@ def test_mla_quantised_invalid_slots_are_skipped_and_counted():
     compare_mla(case, got, slots=fixed)
 
 
-def test_mla_quantised_cache_larger_than_4gib():
+@pytest.mark.parametrize("span", ["over_4gib", "3gib"])
+def test_mla_quantised_large_cache_offsets(span):
     """An int8 ckv cache of 4 GiB or more (2^23 rows) takes the plain-store
-    path: rows beyond the 32-bit byte offset land exactly, with their scales,
-    and nothing else changes."""
+    path: rows beyond the 32-bit byte offset land exactly, with their scales;
+    a 3 GiB one takes the buffer stores with offsets past 2^31. Nothing else
+    changes."""
     T, He, BS = 300, 256, 128
-    rows_4g = 2 ** 32 // 512
-    NB = rows_4g // BS + 64
-    say(f"[mla-q] int8 cache over 4 GiB: {NB} blocks")
+    if span == "over_4gib":
+        rows_4g = 2 ** 32 // 512
+        NB = rows_4g // BS + 64
+    else:
+        rows_4g = 2 ** 31 // 512
+        NB = (3 * 2 ** 30 // 512) // BS
+    say(f"[mla-q] int8 large cache ({span}): {NB} blocks")
     case = gen.mla_kv_head_case(660, B=1, S=T, He=He, num_blocks=1, block_size=T,
                                 slot_kind="random", skip_frac=0.05, ckv_dtype="int8")
     rng = gen.rng_for(661)

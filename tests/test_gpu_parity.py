@@ -472,21 +472,28 @@ def test_graph_replays_match_eager():
 
 @pytest.mark.parametrize("ckv", CKV)
 @pytest.mark.parametrize("T", [96, 4096])
-def test_cache_larger_than_4gib(ckv, T):
+@pytest.mark.parametrize("span", ["over_4gib", "3gib"])
+def test_large_cache_offsets(ckv, T, span):
     """Caches of 4 GiB or more take the plain-global-store path (with both the
     small-batch and the large-batch launch shapes): rows beyond the 32-bit
-    byte offset must land exactly, and nothing else may change."""
+    byte offset must land exactly. A 3 GiB cache takes the buffer stores,
+    whose 32-bit offsets pass 2^31 there: rows beyond 2 GiB must land too.
+    Nothing else may change."""
     Dv, Dk, BS = 512, 64, 128
     row_bytes = Dv * (2 if ckv == "bf16" else 1)
-    NB = (2 ** 32 // row_bytes) // BS + 64                    # just over 4 GiB of ckv rows
-    say(f"[parity] cache over 4 GiB: {ckv}, {NB} blocks, {T} tokens")
+    if span == "over_4gib":
+        split = 2 ** 32 // row_bytes                          # first row past the 4 GiB offset
+        NB = split // BS + 64                                 # just over 4 GiB of ckv rows
+    else:
+        split = 2 ** 31 // row_bytes                          # first row past the 2 GiB offset
+        NB = (3 * 2 ** 30 // row_bytes) // BS                 # 3 GiB of ckv rows
+    say(f"[parity] large cache ({span}): {ckv}, {NB} blocks, {T} tokens")
     small = gen.kvrc_paged_case(900, B=2, S=T // 2, Dv=Dv, Dk=Dk, num_blocks=1, block_size=T,
                                 slot_kind="random", ckv_dtype=ckv)
-    # real slots: half below the 4 GiB offset, half above it
+    # real slots: half below the split offset, half above it
     rng = gen.rng_for(901)
-    lo = rng.choice(2 ** 32 // row_bytes - 1, size=T // 2, replace=False)
-    hi = 2 ** 32 // row_bytes + rng.choice(NB * BS - 2 ** 32 // row_bytes, size=T // 2,
-                                           replace=False)
+    lo = rng.choice(split - 1, size=T // 2, replace=False)
+    hi = split + rng.choice(NB * BS - split, size=T // 2, replace=False)
     slots = np.concatenate([lo, hi]).astype(np.int64)
     rng.shuffle(slots)
     want = oracle.run_kvrc_case(small)                        # slot t -> compact row small[t]
