@@ -232,15 +232,23 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *                 must be all zero when first used; every call that runs to
  *                 its end leaves it all zero again, so one workspace serves
  *                 any number of calls in order on a stream (HIP graph
- *                 replays included). Calls that may run at the same time
- *                 need separate workspaces.
+ *                 replays included).
+ * Concurrency: the two workgroups of a pair wait for each other, which
+ * needs the partner to be placed on a compute unit while the first one
+ * waits. Alongside kernels that never wait this holds (their workgroups
+ * finish and free their units). Two MLA head calls running at the same time
+ * on one device (different streams) can fill every unit with workgroups
+ * waiting for partners that cannot be placed: do not overlap MLA head calls
+ * on a device (order them on one stream, or with events), and give calls
+ * on different streams separate workspaces.
  * Returns KVRC_OK (also when T == 0: nothing is launched), or an error
  * status with nothing written: KVRC_ERR_WORKSPACE when workspace_bytes is
  * too small; outputs (the workspace included) must not overlap inputs or
  * each other. err_count counts slots outside [-1, num_blocks*block_size),
  * and also a workgroup whose partner did not publish its partial sums
  * within about a second (its rows are then not valid; the workspace was
- * not zero, or another call used it at the same time).
+ * not zero, another call used it at the same time, or MLA head calls
+ * overlapped on the device).
  */
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,
