@@ -587,3 +587,40 @@ def test_mla_quantised_large_cache_offsets(span):
         in_rows = int((t.reshape(-1, d)[idx] != s_).sum().item())
         assert changed == in_rows, "bytes outside the written rows changed"
     compare_mla(case, got)
+
+
+def test_mla_quantised_graph_replays_reuse_the_workspace():
+    """The two-exchange quantised head captured in a HIP graph: three
+    replays (eager work in between) on one workspace, each equal to the
+    eager call bit for bit, the workspace zero after each."""
+    say("[mla-q] fp8 graph replays")
+    case = gen.mla_kv_head_case(670, B=1, S=600, He=256, num_blocks=64, block_size=16,
+                                slot_kind="random", ckv_dtype="fp8")
+    ws = new_workspace(600)
+    eager = run_mla_gpu(case, workspace=ws)
+    compare_mla(case, eager)
+    x, w, gm = dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"])
+    cs, sn = dbf(case["cos"]), dbf(case["sin"])
+    sl = torch.from_numpy(case["slot_mapping"]).to(DEV)
+    caches = {n: dev_cache(spec.numpy()) for n, spec in case["caches"].items()}
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        k.kvrc_mla_kv_head_paged(x, w, gm, cs, sn, sl, caches["k_cache"], caches["ckv_cache"],
+                                 caches["ckv_scale"], workspace=ws, alpha_kv=case["alpha"],
+                                 eps=case["eps"], stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        k.kvrc_mla_kv_head_paged(x, w, gm, cs, sn, sl, caches["k_cache"], caches["ckv_cache"],
+                                 caches["ckv_scale"], workspace=ws, alpha_kv=case["alpha"],
+                                 eps=case["eps"], stream=stream)
+    for rep in range(3):
+        for n, spec in case["caches"].items():
+            caches[n].copy_(dev_cache(spec.numpy()))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0, f"replay {rep}: workspace not left zero"
+        for n, t in caches.items():
+            np.testing.assert_array_equal(host_cache(t), eager[n], err_msg=f"replay {rep}: {n}")
