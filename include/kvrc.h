@@ -172,7 +172,7 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
 /*
  * kvrc_mla_kv_head_workspace_bytes - bytes of device workspace that
  * kvrc_mla_kv_head_paged needs for T tokens (the first phase of the pages'
- * "workspace size, then execute" convention; 4112 bytes per 256 tokens, for
+ * "workspace size, then execute" convention; 4104 bytes per 256 tokens, for
  * every ckv cache type).
  * Returns -1 for T < 0 or T > 2^31 - 1, 0 for T == 0.
  */
@@ -200,9 +200,11 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *        int8 codes of y / scale with scale = max|y| / 127 (INT8), or
  *        E4M3FN codes of y / scale with scale = max|y| / 448 (FP8_E4M3),
  *        the scale stored to ckv_scale[v / block_size, v % block_size, 0]:
- *        the per-row rule of kvrc_paged_norm_rope_cache, except that the
- *        quotient is y * RN(1 / scale) (one more rounding: the outputs of
- *        this head are not reproducible to the last bit anyway); codes
+ *        the per-row rule of kvrc_paged_norm_rope_cache, except that
+ *        max|y| is taken as RN((1 / rms) * max|c * alpha_kv * gamma|) (the
+ *        maximum before the norm, scaled) and the quotient is
+ *        y * RN(1 / scale) (a few roundings more: the outputs of this head
+ *        are not reproducible to the last bit anyway); codes
  *        round to nearest, ties to even, and saturate at 127 (448); an
  *        all-zero row stores scale 0 and codes 0
  *   k_cache[v / block_size, v % block_size, 0, :]   = bf16(kr)

@@ -109,7 +109,7 @@ constexpr int64_t kMlaHeadK = 32;
 // Token rows per workgroup pair of the MLA head kernel.
 constexpr int64_t kMlaPairRows = 256;
 // Workspace of one MLA head call: per pair of workgroups, their per-row
-// partial square sums, per-row partial maxima (quantised ckv) and four
+// partial square sums, per-row partial maxima (quantised ckv) and two
 // ready flags.
 int64_t mla_kv_head_workspace_bytes(int64_t T);
 

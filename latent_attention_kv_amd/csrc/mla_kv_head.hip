@@ -17,7 +17,9 @@
 //   or, for a quantised ckv cache (the per-row rule of the norm-rope-cache
 //   operator: scale = RowMax(|y|) / 127 with rounded int8 codes, or
 //   RowMax(|y|) / 448 with the nearest FLOAT8 E4M3FN codes),
-//   ckv_cache[slot[t]] = codes of y * RN(1 / scale), ckv_scale[slot[t]] = scale
+//   ckv_cache[slot[t]] = codes of y * RN(1 / scale), ckv_scale[slot[t]] = scale,
+//   with RowMax(|y|) taken as (1 / rms) * max |c * alpha * gamma| (equal to
+//   the maximum of the rounded y up to a few roundings)
 // with float32 accumulation of the bf16 products (no rounding of c before
 // the norm).
 //
@@ -54,10 +56,12 @@
 //     rows are normalised and rotated in registers, staged as bf16 in LDS
 //     and scattered with 16-byte stores per cache row piece;
 //   * a quantised ckv cache needs the maximum of each row over both halves:
-//     the normalised values stay in the accumulator registers while the
-//     pair swaps per-row partial maxima the same way (second area, second
-//     pair of flags), then the codes are staged (one byte each) and
-//     scattered like the bf16 rows, half 0 also writing the row scale.
+//     each half takes its partial maximum of |c * alpha * gamma| with its
+//     square sums, and both travel through the one exchange (a second area
+//     of the workspace); the normalised values stay in the accumulator
+//     registers until the scale is known, then the codes are staged (one
+//     byte each) and scattered like the bf16 rows, half 0 also writing the
+//     row scale.
 // The wait for the partner is bounded: past the limit the workgroup counts
 // an error and goes on (its rows are then wrong), so the kernel always ends.
 // A partner is dispatched at most 8 workgroups later on the same XCD, and
@@ -105,7 +109,10 @@ constexpr int kRopeTiles = 4;              // tiles 5..8 of the rope wavefront
 constexpr int kStageRow = (kHalfCols + 8) * 2;   // 592 bytes per row
 constexpr int kRedOff = kRows * kStageRow;
 constexpr int kSumOff = kRedOff + 2 * kRows * 4;
-constexpr int kEpiBytes = kSumOff + kRows * 4;
+// quantised ckv: per-column-wavefront partial row maxima, then the row maxima
+constexpr int kRedMaxOff = kSumOff + kRows * 4;
+constexpr int kMaxOff = kRedMaxOff + 2 * kRows * 4;
+constexpr int kEpiBytes = kMaxOff + kRows * 4;
 constexpr int kLdsBytes = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
 // bounded wait for the partner's sums (polls with a short sleep in between)
 constexpr int kSpinLimit = 1 << 20;
@@ -120,19 +127,27 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // c ^ ((r >> 2) & 3).
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-// One exchange of per-row partial values between the two workgroups of a
-// pair, run by wavefront 0 (lane l: rows 4 l .. 4 l + 3): publish p in this
-// half's area of the workspace (then the flag, with release order), wait
-// for the partner's flag (bounded), read its values into q, zero them and
-// clear its flag, so the area is all zero again afterwards. Returns false
-// when the wait timed out (q is then not the partner's).
-__device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, uint32_t *my_flag,
+// The exchange of per-row partial values between the two workgroups of a
+// pair, run by wavefront 0 (lane l: rows 4 l .. 4 l + 3): publish p (and p2,
+// with kTwo) in this half's areas of the workspace (then the flag, with
+// release order), wait for the partner's flag (bounded), read its values
+// into q (q2), zero them and clear its flag, so the areas are all zero again
+// afterwards. Returns false when the wait timed out (q, q2 are then not the
+// partner's).
+template <bool kTwo>
+__device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, float *mine2,
+                                              float *theirs2, uint32_t *my_flag,
                                               uint32_t *their_flag, const float (&p)[4],
-                                              float (&q)[4], int lane)
+                                              const float (&p2)[4], float (&q)[4],
+                                              float (&q2)[4], int lane)
 {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
         __hip_atomic_store(mine + 4 * lane + j, p[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kTwo)
+            __hip_atomic_store(mine2 + 4 * lane + j, p2[j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     // release: the wavefront's values above are visible before the flag
     if (lane == 0)
         __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -150,6 +165,12 @@ __device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, uint32
     for (int j = 0; j < 4; ++j) {
         q[j] = __hip_atomic_load(theirs + 4 * lane + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(theirs + 4 * lane + j, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kTwo) {
+            q2[j] = __hip_atomic_load(theirs2 + 4 * lane + j, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(theirs2 + 4 * lane + j, 0.0f, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     // the partner's values are read and zeroed: clear its flag (the next use
     // of this area is a later kernel on the stream)
@@ -345,55 +366,8 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         load_rope_tables(0, rc[0]);
     float *red = reinterpret_cast<float *>(smem + kRedOff);     // [2 column wavefronts][256]
     float *sums = reinterpret_cast<float *>(smem + kSumOff);    // [256]
-#pragma unroll
-    for (int m = 0; m < kMt; ++m) {
-        float s = 0.0f;
-#pragma unroll
-        for (int n = 0; n < kNt; ++n)
-            if (n < ntn)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s += acc[m][n][e] * acc[m][n][e];
-        // add the four column quarters (lanes l, l ^ 16, l ^ 32, l ^ 48): a
-        // permlane swap of the value with itself leaves the two halves of
-        // the exchange in its two results, in every lane
-        {
-            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s),
-                                                              false, false);
-            s = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
-                                                              false, false);
-            s = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-        }
-        if (cq == 0)
-            red[wn * kRows + 64 * wm + 16 * m + rsub] = s;
-    }
-    __syncthreads();
-
-    // ---- swap the per-row partial sums with the other half of the pair ----
-    // workspace: float sums[npairs][2][256], float maxima[npairs][2][256],
-    // then uint32 flags[npairs][4] (sums: halves 0, 1; maxima: halves 0, 1).
-    float *const part = reinterpret_cast<float *>(a.workspace);
-    uint32_t *const flags = reinterpret_cast<uint32_t *>(part + npairs * 4 * kRows);
-    auto area = [&](int round, int h) { return part + ((round * npairs + pair) * 2 + h) * kRows; };
-    auto flag = [&](int round, int h) { return flags + pair * 4 + 2 * round + h; };
-    if (wave == 0) {
-        float p[4], q[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            p[j] = red[4 * lane + j] + red[kRows + 4 * lane + j];
-        const bool ok = pair_exchange(area(0, half), area(0, 1 - half), flag(0, half),
-                                      flag(0, 1 - half), p, q, lane);
-        // the same order in both halves: the sum of columns 0..287 first
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sums[4 * lane + j] = half == 0 ? p[j] + q[j] : q[j] + p[j];
-        if (!ok && lane == 0 && a.err)
-            atomicAdd(a.err, 1);
-    }
-    __syncthreads();
-
-    unsigned char *stage = smem;
+    float *red_max = reinterpret_cast<float *>(smem + kRedMaxOff);  // [2][256] (quantised)
+    float *maxs = reinterpret_cast<float *>(smem + kMaxOff);        // [256] (quantised)
     // alpha_kv * gamma per column, once: each output is then two products,
     // (c * rr) * (alpha * gamma)
     const float alpha = a.alpha;
@@ -407,11 +381,83 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
 #pragma unroll
     for (int m = 0; m < kMt; ++m) {
+        float s = 0.0f;
+        float mx = 0.0f;                     // max |c * alpha * gamma| (quantised ckv)
+#pragma unroll
+        for (int n = 0; n < kNt; ++n)
+            if (n < ntn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s += acc[m][n][e] * acc[m][n][e];
+                    if constexpr (Q != 0)
+                        mx = fmaxf(mx, fabsf(acc[m][n][e] * g[n][e]));
+                }
+        // add the four column quarters (lanes l, l ^ 16, l ^ 32, l ^ 48): a
+        // permlane swap of the value with itself leaves the two halves of
+        // the exchange in its two results, in every lane
+        {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s),
+                                                              false, false);
+            s = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
+                                                              false, false);
+            s = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        }
+        if constexpr (Q != 0) {
+            const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                              false, false);
+            mx = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
+            const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                              false, false);
+            mx = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1]));
+            if (cq == 0)
+                red_max[wn * kRows + 64 * wm + 16 * m + rsub] = mx;
+        }
+        if (cq == 0)
+            red[wn * kRows + 64 * wm + 16 * m + rsub] = s;
+    }
+    __syncthreads();
+
+    // ---- swap the per-row partials with the other half of the pair --------
+    // workspace: float sums[npairs][2][256], float maxima[npairs][2][256]
+    // (quantised ckv only), then uint32 flags[npairs][2].
+    float *const part = reinterpret_cast<float *>(a.workspace);
+    uint32_t *const flags = reinterpret_cast<uint32_t *>(part + npairs * 4 * kRows);
+    auto area = [&](int k, int h) { return part + ((k * npairs + pair) * 2 + h) * kRows; };
+    if (wave == 0) {
+        float p[4], q[4], p2[4], q2[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = red[4 * lane + j] + red[kRows + 4 * lane + j];
+            p2[j] = Q != 0 ? fmaxf(red_max[4 * lane + j], red_max[kRows + 4 * lane + j]) : 0.0f;
+        }
+        const bool ok = pair_exchange<Q != 0>(area(0, half), area(0, 1 - half), area(1, half),
+                                              area(1, 1 - half), flags + pair * 2 + half,
+                                              flags + pair * 2 + (1 - half), p, p2, q, q2, lane);
+        // the same order in both halves: the sum of columns 0..287 first
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sums[4 * lane + j] = half == 0 ? p[j] + q[j] : q[j] + p[j];
+            if constexpr (Q != 0)
+                maxs[4 * lane + j] = fmaxf(p2[j], q2[j]);
+        }
+        if (!ok && lane == 0 && a.err)
+            atomicAdd(a.err, 1);
+    }
+    __syncthreads();
+
+    unsigned char *stage = smem;
+    // 1 / rms of row r (the same expression wherever it is needed) and, for a
+    // quantised ckv cache, the row scale RN(RN(rr * max |c alpha gamma|) / d)
+    auto row_rr = [&](int r) { return 1.0f / sqrtf(sums[r] / (float)kNorm + a.eps); };
+    constexpr float kDiv = Q == 1 ? 127.0f : kE4m3Max;
+    auto row_scale_of = [&](int r) { return row_scale(row_rr(r) * maxs[r], kDiv); };
+#pragma unroll
+    for (int m = 0; m < kMt; ++m) {
         if (rope_wave && m + 1 < kMt)
             load_rope_tables(m + 1, rc[(m + 1) & 1]);
         const int r = 64 * wm + 16 * m + rsub;
-        const float rr = 1.0f / sqrtf(sums[r] / (float)kNorm + a.eps);
-        float mx = 0.0f;                     // max |y| over this lane's columns (quantised)
+        const float rr = row_rr(r);
 #pragma unroll
         for (int n = 0; n < kNt; ++n) {
             const f32x4 v = acc[m][n];
@@ -423,9 +469,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                     const uint2 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
                     *reinterpret_cast<uint2 *>(stage + r * kStageRow + col * 2) = o;
                 } else {
-                    acc[m][n] = y;           // coded once the row maximum is known
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])),
-                                         fmaxf(fabsf(y[2]), fabsf(y[3]))));
+                    acc[m][n] = y;           // coded below, with the row scale
                 }
             } else {
                 // rope columns 2 i0 .. 2 i0 + 3 of c[512:]: pairs (2 i0, 2 i0 + 1)
@@ -444,42 +488,15 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                 *reinterpret_cast<uint32_t *>(kr + (32 + i0) * 2) = pack_bf16x2(hi0, hi1);
             }
         }
-        if constexpr (Q != 0) {
-            // row maximum of this wavefront's columns: the four column
-            // quarters (lanes l, l ^ 16, l ^ 32, l ^ 48), as for the sums
-            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                              false, false);
-            mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                              false, false);
-            mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-            if (cq == 0)
-                red[wn * kRows + r] = mx;    // the sums' partials were consumed above
-        }
     }
     __syncthreads();
 
     if constexpr (Q != 0) {
-        // ---- swap the per-row partial maxima, then code the rows ---------
-        if (wave == 0) {
-            float p[4], q[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                p[j] = fmaxf(red[4 * lane + j], red[kRows + 4 * lane + j]);
-            const bool ok = pair_exchange(area(1, half), area(1, 1 - half), flag(1, half),
-                                          flag(1, 1 - half), p, q, lane);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sums[4 * lane + j] = fmaxf(p[j], q[j]);     // now the row maxima
-            if (!ok && lane == 0 && a.err)
-                atomicAdd(a.err, 1);
-        }
-        __syncthreads();
-        constexpr float kDiv = Q == 1 ? 127.0f : kE4m3Max;
+        // ---- code the rows ------------------------------------------------
 #pragma unroll
         for (int m = 0; m < kMt; ++m) {
             const int r = 64 * wm + 16 * m + rsub;
-            const float scale = row_scale(sums[r], kDiv);
+            const float scale = row_scale_of(r);
             // y * RN(1 / scale) in rcp_rn's domain [2^-60, 2^60]; IEEE
             // division outside it (a zero row has scale 0 and codes 0)
             const bool fast = scale >= 0x1p-60f && scale <= 0x1p60f;
@@ -551,7 +568,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
         }
         if constexpr (Q != 0) {
             if (half == 0 && lane == 63)
-                a.ckv_scale[v] = row_scale(sums[r], Q == 1 ? 127.0f : kE4m3Max);
+                a.ckv_scale[v] = row_scale_of(r);
         }
         if (lane < npieces) {
             const uint4 cv = *reinterpret_cast<const uint4 *>(stage + r * kStageRow + lane * 16);
@@ -584,7 +601,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 int64_t mla_kv_head_workspace_bytes(int64_t T)
 {
     const int64_t npairs = T > 0 ? (T + kRows - 1) / kRows : 0;
-    return npairs * (4 * kRows * 4 + 4 * 4);
+    return npairs * (4 * kRows * 4 + 2 * 4);
 }
 
 hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)

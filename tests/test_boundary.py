@@ -132,7 +132,7 @@ def test_norm_validation(over, want):
 
 M = {name: (i + 40) << 32 for i, name in enumerate(
     ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err", "ws", "sc"])}
-WS_300 = 2 * (4 * 256 * 4 + 4 * 4)      # 300 tokens: two pairs of workgroups
+WS_300 = 2 * (4 * 256 * 4 + 2 * 4)      # 300 tokens: two pairs of workgroups
 
 
 def mla(**over):
@@ -176,12 +176,12 @@ def test_mla_blk_validation(over, want):
 
 def test_mla_workspace_bytes():
     """One pair of workgroups per 256 tokens: 256 partial sums and 256
-    partial maxima per half, and four flags."""
+    partial maxima per half, and two flags."""
     f = k.lib().kvrc_mla_kv_head_workspace_bytes
     assert f(0) == 0
-    assert f(1) == f(256) == 4112
-    assert f(257) == 2 * 4112
-    assert f(32768) == 128 * 4112
+    assert f(1) == f(256) == 4104
+    assert f(257) == 2 * 4104
+    assert f(32768) == 128 * 4104
     assert f(-1) == -1 and f(1 << 31) == -1
     assert f(300) == WS_300
 
