@@ -53,3 +53,20 @@ def test_code_hash_ignores_comments_not_code():
     assert bench._code_only("k.hip", src) != bench._code_only("k.hip", src.replace("+ 1", "+ 2"))
     py = "# note\nx = 1  # trailing\n"
     assert bench._code_only("b.py", py) == "x = 1  # trailing"
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    """Every workload has a committed trace summary and traffic record, taken
+    on the kernel code as it stands (the bench reports no traffic for a
+    record of other code)."""
+    import json
+    import os
+    for w in bench.WORKLOAD_TEXT:
+        path = os.path.join(bench.ROOT, "profiles", f"traffic_{w}.json")
+        assert os.path.exists(path), f"no traffic record for {w}"
+        with open(path) as f:
+            rec = json.load(f)
+        assert rec["source_hash"] == bench.source_hash(w), f"{w}: profile taken on other code"
+        # summaries are named <kernel>_<workload>.md
+        names = os.listdir(os.path.join(bench.ROOT, "profiles"))
+        assert any(name.endswith(f"_{w}.md") for name in names), f"no trace summary for {w}"
