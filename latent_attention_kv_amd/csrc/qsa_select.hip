@@ -23,7 +23,8 @@
 //   * qsa_select_fast_kernel (Di / 32, H / 16 and the column tiles per
 //     wavefront known at compile time): each wavefront loads the key
 //     fragments of its own tiles straight into registers, q passes through
-//     LDS once, and all scores stay in registers from the MFMA to Q;
+//     LDS once (loaded while the key length is read: it does not depend on
+//     it), and all scores stay in registers from the MFMA to Q;
 //   * qsa_select_kernel (every other shape): keys staged in LDS chunks; a
 //     sequence that fits one chunk with few enough tiles per wavefront keeps
 //     its scores in registers, a longer one takes three sweeps over its
@@ -156,10 +157,9 @@ __device__ __forceinline__ f32x4 score_tile(const unsigned char *qa, const unsig
 // The sequence's block count nb = key_length / kbs, or -1 for an invalid
 // length (negative, or more blocks than the capacity): such a sequence gets
 // scores 0 and indices -1 here and counts once in the error counter.
-__device__ __forceinline__ int sequence_blocks(const QsaSelectArgs &a, int64_t n, float *scores,
-                                               int32_t *out_idx, int tid)
+__device__ __forceinline__ int sequence_blocks_of(const QsaSelectArgs &a, int64_t K, float *scores,
+                                                  int32_t *out_idx, int tid)
 {
-    const int64_t K = a.key_length[a.klc == 1 ? 0 : n];
     const int64_t nb = K >= 0 ? K / a.kbs : -1;
     if (nb >= 0 && nb <= a.Bcap)
         return (int)nb;
@@ -170,6 +170,12 @@ __device__ __forceinline__ int sequence_blocks(const QsaSelectArgs &a, int64_t n
     if (tid == 0 && a.err)
         atomicAdd(a.err, 1);
     return -1;
+}
+
+__device__ __forceinline__ int sequence_blocks(const QsaSelectArgs &a, int64_t n, float *scores,
+                                               int32_t *out_idx, int tid)
+{
+    return sequence_blocks_of(a, a.key_length[a.klc == 1 ? 0 : n], scores, out_idx, tid);
 }
 
 // Pooling of Q [nb] into the J selection-block scores, and the top-k. Q is
@@ -540,27 +546,37 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
 
     float *scores = a.scores + n * a.Jcap;
     int32_t *out_idx = a.indices + n * a.topk;
-    const int nb = sequence_blocks(a, n, scores, out_idx, tid);
-    if (nb < 0)
-        return;
-    const int sel = (int)a.sel, cmpr = (int)a.cmp;
-    const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
-
-    if (nb > 0) {
+    // the key length first (a uniform load), then the q rows, which do not
+    // depend on it, so that both latencies overlap
+    const int64_t Klen = __builtin_nontemporal_load(a.key_length + (a.klc == 1 ? 0 : n));
+    {
         const uint16_t *qn = a.query + n * (int64_t)H * Di;
-        const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
-        const int fr = lane & 15, g = lane >> 4;         // fragment row / column, lane group
-        const float scale2 = a.scale * 1.44269504088896341f;
-
-        // q -> registers (issued first), the key fragments of column tiles
-        // wave + 8 jl (rows past the sequence clamped to its last block: they
-        // are computed, never used), then q -> LDS
         uint4 qs[QPT];
 #pragma unroll
         for (int b = 0; b < QPT; ++b) {
             const int c = min(tid + b * kThreads, QP - 1);
             qs[b] = *reinterpret_cast<const uint4 *>(qn + (c / pieces) * Di + (c % pieces) * 8);
         }
+#pragma unroll
+        for (int b = 0; b < QPT; ++b) {
+            const int c = min(tid + b * kThreads, QP - 1);
+            *reinterpret_cast<uint4 *>(q_lds + (c / pieces) * rowb + (c % pieces) * 16) = qs[b];
+        }
+    }
+    const int nb = sequence_blocks_of(a, Klen, scores, out_idx, tid);
+    if (nb < 0)
+        return;
+    const int sel = (int)a.sel, cmpr = (int)a.cmp;
+    const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
+
+    if (nb > 0) {
+        const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
+        const int fr = lane & 15, g = lane >> 4;         // fragment row / column, lane group
+        const float scale2 = a.scale * 1.44269504088896341f;
+
+        // the key fragments of column tiles wave + 8 jl (rows past the
+        // sequence clamped to its last block: they are computed, never
+        // used); q is in LDS already
         bf16x8 kf[JWM][DK];
 #pragma unroll
         for (int jl = 0; jl < JWM; ++jl) {
@@ -568,11 +584,6 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
 #pragma unroll
             for (int u = 0; u < DK; ++u)
                 kf[jl][u] = *reinterpret_cast<const bf16x8 *>(kn + (int64_t)row * Di + 32 * u + 8 * g);
-        }
-#pragma unroll
-        for (int b = 0; b < QPT; ++b) {
-            const int c = min(tid + b * kThreads, QP - 1);
-            *reinterpret_cast<uint4 *>(q_lds + (c / pieces) * rowb + (c % pieces) * 16) = qs[b];
         }
         __syncthreads();
 
