@@ -626,3 +626,18 @@ def test_mla_quantised_graph_replays_reuse_the_workspace():
         assert int(torch.count_nonzero(ws)) == 0, f"replay {rep}: workspace not left zero"
         for n, t in caches.items():
             np.testing.assert_array_equal(host_cache(t), eager[n], err_msg=f"replay {rep}: {n}")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_mla_all_tokens_skipped(kind):
+    """Every slot -1 (a ragged 300-token batch: two pairs, the second
+    partial): the kernel runs and its pairs still exchange, but no cache
+    byte changes, nothing is counted and the workspace ends zero."""
+    case = gen.mla_kv_head_case(680, B=1, S=300, He=128, num_blocks=16, block_size=32,
+                                slot_kind="random", ckv_dtype=kind)
+    slots = np.full(300, -1, dtype=np.int64)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_mla_gpu(case, slots=slots, err=err)
+    assert int(err.item()) == 0
+    for name, spec in case["caches"].items():
+        np.testing.assert_array_equal(got[name], spec.numpy(), err_msg=name)
