@@ -636,3 +636,63 @@ def test_paged_blk_named_workload_and_invalid_entries():
     fixed[[1, 3]] = -1
     clean = dict(small, block_index=fixed)
     compare_kvrc(clean, got, oracle.run_kvrc_case(clean), exact_bf16=True)
+
+
+# Above 2048 tokens the Dv = 512 / Dk = 64 kernel runs two rows per wavefront
+# in 256-thread workgroups (8 rows per workgroup). Token counts that are not a
+# multiple of 8 leave the last workgroup partial: its last wavefront may hold
+# one row, whose upper 32 lanes exit before the lower half folds its sums and
+# maxima over 32 lanes. Odd sequence lengths put batch boundaries inside
+# workgroups and wavefronts.
+RAGGED_LARGE = [(1, 2049), (2, 1025), (5, 411), (17, 241), (7, 4681), (15, 4369)]
+
+
+_RAGGED_BASE = {}
+
+
+def _ragged_case(mode, B, S, ckv):
+    """The inputs depend on (mode, B, S) only; the ckv cache type changes the
+    caches alone, so the drawn inputs are shared across the three types."""
+    key = (mode, B, S)
+    if key not in _RAGGED_BASE:
+        _RAGGED_BASE.clear()
+        T = B * S
+        seed = 1000 + T
+        if mode == "paged":
+            bs = 128
+            base = gen.kvrc_paged_case(seed, B=B, S=S, Dv=512, Dk=64,
+                                       num_blocks=-(-T // bs) + 8, block_size=bs,
+                                       slot_kind="random", skip_frac=0.03)
+        elif mode == "paged_blk":
+            bs = 64
+            base = gen.kvrc_paged_blk_case(seed, B=B, S=S, Dv=512, Dk=64,
+                                           num_blocks=B * -(-S // bs) + 5, block_size=bs,
+                                           n_skip=1, entry_offsets=True)
+        else:
+            base = gen.kvrc_norm_case(seed, B=B, S=S, Dv=512, Dk=64, Bc=B, Sc=S + 3,
+                                      n_skip=max(1, T // 50))
+        _RAGGED_BASE[key] = base
+    base = _RAGGED_BASE[key]
+    case = dict(base, ckv_dtype=ckv)
+    rows = base["caches"]["ckv_cache"].shape
+    case["caches"] = {"k_cache": base["caches"]["k_cache"],
+                      "ckv_cache": gen.ckv_cache_spec(rows, ckv)}
+    if ckv != "bf16":
+        case["caches"]["ckv_scale"] = gen.CacheSpec(rows[:-1], np.float32, gen.SCALE_SENTINEL)
+    return case
+
+
+@pytest.mark.parametrize("ckv", CKV)
+@pytest.mark.parametrize("B,S", RAGGED_LARGE)
+@pytest.mark.parametrize("mode", ["paged", "paged_blk", "norm"])
+def test_large_batch_ragged_tail(ckv, B, S, mode):
+    T = B * S
+    assert T > 2048 and T % 8
+    say(f"[parity] large-batch ragged tail: {mode} {ckv} B={B} S={S} T={T}")
+    case = _ragged_case(mode, B, S, ckv)
+    want = oracle.run_kvrc_case(case)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_kvrc_gpu(case, err=err)
+    compare_kvrc(case, got, want, exact_bf16=True)
+    assert int(err.item()) == 0
+    del got, want
