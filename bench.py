@@ -10,22 +10,29 @@ Measurement:
   * R independent buffer sets (inputs and caches) are rotated so that the
     touched bytes of R consecutive steps exceed the 256 MB Infinity Cache;
     every step therefore reads its inputs from HBM;
-  * the launches are captured once into a HIP graph (one launch per buffer
-    set) and replayed, so host launch overhead does not enter the timing;
-  * HIP events on the launch stream bracket the K timed steps (after W
-    warm-up steps): ms_per_step = elapsed / K, value = tokens / step time,
-    and the kernel's average launch duration is the same elapsed / K (one
-    launch per step; the small gaps between graph launches are included, so
-    it is slightly above rocprofv3's per-dispatch duration);
-  * roofline: algorithmic bytes per launch (bytes the method must move:
-    kv + cos/sin + index + cache rows written) / average launch duration,
-    against the MI355X HBM3E peak of 8 TB/s;
+  * one eager launch per buffer set first (setup: loads the library and
+    checks every argument set); then exactly W warm-up launches in one HIP
+    graph and exactly K timed launches in another, continuing the rotation;
+  * the timed graph is enqueued behind a spin kernel, so that the whole
+    graph is submitted before its first launch starts; HIP events on the
+    launch stream bracket its replay: ms_per_step = elapsed / K,
+    value = tokens / step time, and the kernel's average launch duration is
+    the same elapsed / K (one launch per step, back to back);
+  * roofline: algorithmic bytes (or flops) per launch / average launch
+    duration, against the MI355X HBM3E peak of 8 TB/s (or the bf16 dense
+    matrix peak); rocprof_kernel_us repeats the per-dispatch duration
+    percentiles of the committed rocprofv3 trace of the same kernel code;
   * traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
     scaled by the same counters' reading on a plain copy of known size, read
     from profiles/traffic_<workload>.json and reported only if the kernel
     sources are unchanged since the counters were taken (else null);
-  * cpu_baseline: the CPU oracle on the host cores, on the same batch,
-    repeated for about 10 s (rank 0, one GPU only).
+  * context (same harness, after the timed region): p10 / p50 / p90 of up
+    to 200 of the same launches each timed alone between its own events, the
+    average step of an empty kernel (one workgroup, and the workload's grid)
+    and of a plain device copy moving the same bytes as one launch, each in
+    a graph of K launches like the timed region;
+  * cpu_baseline: the CPU oracle on the host, on the same batch, about 8 s
+    on one thread and 8 s on all the threads it uses, with the CPU model.
 
 Prints one JSON line.
 """
@@ -33,9 +40,10 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -269,24 +277,29 @@ def launch(case, s):
                                s["ckv_cache"], s.get("ckv_scale"), eps=case["eps"])
 
 
-def cpu_baseline(case, seconds=10.0):
-    """The oracle, as it is, on the host cores: the full batch, repeated until
-    about `seconds` of oracle time have run (caches allocated once, outside
-    the timing; each repeat rewrites the same rows with the same values)."""
+def _oracle_run(case, threads, seconds):
+    """Run the oracle, as it is, on the workload until about `seconds` of
+    oracle time have passed: (runs, busy seconds, tokens per run, what ran).
+    `threads` is the oracle's OpenMP thread count (numpy's BLAS threads for
+    the float64 oracles). Caches are allocated once, outside the timing; each
+    run rewrites the same rows with the same values."""
     import oracle
-    threads = oracle.max_threads()
     n, busy = 0, 0.0
-    if "block_keys" in case and "query" in case:
-        from oracle import qsa_select as Sel
+
+    def loop(fn):
+        nonlocal n, busy
         while busy < seconds or n == 0:
             s0 = time.perf_counter()
-            Sel.run_select_case(case)
+            fn()
             busy += time.perf_counter() - s0
             n += 1
-        return {"value": round(case["N"] * n / busy, 1), "unit": "tokens/s",
-                "cores": _blas_threads(), "kind": "oracle",
-                "sample": f"the full batch ({case['N']} query tokens) run {n} times by the "
-                          f"float64 oracle ({busy:.1f} s; numpy, one sequence at a time)"}
+
+    if "block_keys" in case and "query" in case:
+        from oracle import qsa_select as Sel
+        with _blas_limit(threads):
+            loop(lambda: Sel.run_select_case(case))
+        return n, busy, case["N"], (f"the full batch ({case['N']} query tokens), float64 "
+                                    "oracle, numpy, one sequence at a time")
     if case.get("mode") == "mla_paged":
         from oracle import mla_kv_head as M
         sample = 2048
@@ -295,48 +308,69 @@ def cpu_baseline(case, seconds=10.0):
                 case["sin"][:sample], case["slot_mapping"][:sample], caches["k_cache"],
                 caches["ckv_cache"], case["eps"], caches.get("ckv_scale"),
                 case.get("ckv_dtype", "bf16"))
-        while busy < seconds or n == 0:
-            s0 = time.perf_counter()
-            M.mla_kv_head_paged(*args)
-            busy += time.perf_counter() - s0
-            n += 1
-        threads = _blas_threads()
-        return {"value": round(sample * n / busy, 1), "unit": "tokens/s", "cores": threads,
-                "kind": "oracle",
-                "sample": f"the first {sample} tokens of the batch run {n} times by the float64 "
-                          f"oracle ({busy:.1f} s; the projection is numpy's float64 matrix "
-                          f"product over {threads} BLAS threads)"}
+        with _blas_limit(threads):
+            loop(lambda: M.mla_kv_head_paged(*args))
+        return n, busy, sample, (f"the first {sample} tokens of the batch, float64 oracle "
+                                 "(the projection is numpy's float64 matrix product)")
     if "raw_index_keys" in case:
-        while busy < seconds or n == 0:
-            s0 = time.perf_counter()
-            oracle.run_qsa_case(case, nthreads=threads)
-            busy += time.perf_counter() - s0
-            n += 1
+        loop(lambda: oracle.run_qsa_case(case, nthreads=threads))
+        return n, busy, case["N"] * case["L"], ("the full batch, C oracle, OpenMP over "
+                                                "(sequence, block)")
+    caches = {k: spec.numpy() for k, spec in case["caches"].items()}
+    args = (case["kv"], case["gamma"], case["cos"], case["sin"])
+    if case["mode"] == "paged":
+        fn = lambda: oracle.paged_norm_rope_cache(                          # noqa: E731
+            *args, case["slot_mapping"], caches["k_cache"], caches["ckv_cache"],
+            caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
+    elif case["mode"] == "paged_blk":
+        fn = lambda: oracle.paged_blk_norm_rope_cache(                      # noqa: E731
+            *args, case["block_index"], caches["k_cache"], caches["ckv_cache"],
+            caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
     else:
-        caches = {k: spec.numpy() for k, spec in case["caches"].items()}
-        args = (case["kv"], case["gamma"], case["cos"], case["sin"])
-        while busy < seconds or n == 0:
-            s0 = time.perf_counter()
-            if case["mode"] == "paged":
-                oracle.paged_norm_rope_cache(*args, case["slot_mapping"], caches["k_cache"],
-                                             caches["ckv_cache"], caches.get("ckv_scale"),
-                                             eps=case["eps"], nthreads=threads)
-            elif case["mode"] == "paged_blk":
-                oracle.paged_blk_norm_rope_cache(*args, case["block_index"], caches["k_cache"],
-                                                 caches["ckv_cache"], caches.get("ckv_scale"),
-                                                 eps=case["eps"], nthreads=threads)
-            else:
-                oracle.norm_rope_cache(*args, case["index"], caches["k_cache"], caches["ckv_cache"],
-                                       caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
-            busy += time.perf_counter() - s0
-            n += 1
-        del caches
+        fn = lambda: oracle.norm_rope_cache(                                # noqa: E731
+            *args, case["index"], caches["k_cache"], caches["ckv_cache"],
+            caches.get("ckv_scale"), eps=case["eps"], nthreads=threads)
+    loop(fn)
     _, tokens = algorithmic_bytes(case)
-    return {"value": round(tokens * n / busy, 1), "unit": "tokens/s", "cores": threads,
+    return n, busy, tokens, "the full batch, C oracle, OpenMP over tokens"
+
+
+class _blas_limit:
+    """Limit numpy's BLAS threads inside the block (no-op if unavailable)."""
+
+    def __init__(self, n):
+        self.n, self.ctl = n, None
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self.ctl = threadpool_limits(limits=self.n, user_api="blas")
+        except Exception:
+            self.ctl = None
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctl is not None:
+            self.ctl.restore_original_limits()
+        return False
+
+
+def cpu_baseline(case, seconds=8.0):
+    """The oracle, as it is, on the host: one run of about `seconds` on one
+    thread and one on every thread the oracle may use (OpenMP, or numpy's
+    BLAS for the float64 oracles); value and cores are the all-threads run."""
+    import oracle
+    numpy_oracle = ("block_keys" in case and "query" in case) or case.get("mode") == "mla_paged"
+    all_threads = _blas_threads() if numpy_oracle else oracle.max_threads()
+    n1, b1, tok, what = _oracle_run(case, 1, seconds)
+    na, ba, _, _ = _oracle_run(case, all_threads, seconds)
+    return {"value": round(tok * na / ba, 1), "unit": "tokens/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": f"the full batch ({tokens} tokens) run {n} times by the oracle "
-                      f"({busy:.1f} s; input generation and cache allocation excluded), "
-                      f"OpenMP over tokens"}
+            "single_thread_value": round(tok * n1 / b1, 1),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{what}: {tok} tokens per run; {na} runs on {all_threads} threads "
+                      f"({ba:.1f} s) and {n1} runs on 1 thread ({b1:.1f} s); input "
+                      f"generation and cache allocation excluded"}
 
 
 def _blas_threads() -> int:
@@ -396,6 +430,33 @@ def ingest_profile(args) -> int:
            "trace": {"calls": int(st["Calls"]), "avg_ns": float(st["AverageNs"]),
                      "min_ns": float(st["MinNs"]), "max_ns": float(st["MaxNs"])},
            "commands": args.command}
+    # per-dispatch durations from the trace itself: percentiles of the kernel,
+    # and the reference kernels of the same run (empty kernel per grid shape,
+    # the same-bytes copy)
+    import numpy as np
+    trace = _csv_rows(_find_csv(args.trace_dir, "kernel_trace.csv"))
+
+    def durations(pred):
+        return np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+                         if pred(r)], dtype=np.float64)
+
+    d = durations(lambda r: r["Kernel_Name"] == st["Name"])
+    if len(d):
+        for p, v in zip((10, 50, 90), np.percentile(d, [10, 50, 90])):
+            out["trace"][f"p{p}_ns"] = float(v)
+    ctx = {}
+    for r in trace:
+        name = r["Kernel_Name"]
+        if "empty_kernel" in name:
+            key = f"empty_kernel grid {r['Grid_Size_X']} x wg {r['Workgroup_Size_X']}"
+        elif "copy_kernel" in name:
+            key = f"copy_kernel grid {r['Grid_Size_X']}"
+        else:
+            continue
+        ctx.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out["reference_kernels"] = {
+        key: {"calls": len(v), "avg_ns": round(float(np.mean(v)), 1),
+              "p50_ns": float(np.percentile(v, 50))} for key, v in sorted(ctx.items())}
     copy_bytes = 1024 * 2 ** 20
     for counter, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
         rows = _csv_rows(_find_csv(d, "counter_collection.csv"))
@@ -426,7 +487,19 @@ def ingest_profile(args) -> int:
     md += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
            "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|",
            f"| `{st['Name']}` | {st['Calls']} | {float(st['AverageNs']):.1f} | {st['MinNs']} | "
-           f"{st['MaxNs']} |", "",
+           f"{st['MaxNs']} |", ""]
+    tr = out["trace"]
+    if "p50_ns" in tr:
+        md += [f"Per-dispatch duration percentiles (kernel trace): p10 {tr['p10_ns']:.0f} ns, "
+               f"p50 {tr['p50_ns']:.0f} ns, p90 {tr['p90_ns']:.0f} ns.", ""]
+    if out["reference_kernels"]:
+        md += ["Reference kernels of the same run (bench context: empty kernel per grid "
+               "shape = launch floor; plain copy of the same bytes = bandwidth ceiling):", "",
+               "| kernel | calls | avg ns | p50 ns |", "|---|---|---|---|"]
+        md += [f"| {key} | {v['calls']} | {v['avg_ns']} | {v['p50_ns']:.0f} |"
+               for key, v in out["reference_kernels"].items()]
+        md += [""]
+    md += [
            f"Algorithmic bytes per launch: {alg} ({tokens} tokens) -> "
            f"{alg / avg_s / 1e9:.1f} GB/s at the average duration "
            f"({alg / avg_s / 8e12 * 100:.1f} % of 8 TB/s).", ""]
@@ -457,6 +530,155 @@ def ingest_profile(args) -> int:
     return 0
 
 
+def _gate(stream, ms=5.0):
+    """Keep the GPU busy for about `ms` milliseconds on `stream` (a spin
+    kernel), so that the launches enqueued behind it are all submitted before
+    the first of them starts: the timed region then holds GPU work only."""
+    import torch
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(ms * 2.0e6))
+
+
+def _percentiles(xs, ps=(10, 50, 90)):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {f"p{p}": round(float(np.percentile(a, p)), 3) for p in ps}
+
+
+def _time_graph(launches, stream):
+    """Capture `launches` (callables, one launch each) into one HIP graph and
+    time one replay with HIP events on `stream`: (elapsed ms, replay fn)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in launches:
+            f()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _gate(stream)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), g
+
+
+def isolated_launch_times(launches, stream):
+    """Per-launch durations (us): each launch bracketed by its own pair of
+    timing events, behind a short spin kernel so that the launch and its end
+    event are already queued when the start event is reached. Each figure is
+    one launch's execution plus the event pair's own overhead, with the
+    stream otherwise idle."""
+    import torch
+    pairs = []
+    with torch.cuda.stream(stream):
+        for f in launches:
+            torch.cuda._sleep(100000)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    out = _percentiles(d)
+    out["mean"] = round(sum(d) / len(d), 3)
+    out["launches"] = len(d)
+    return out
+
+
+def kvrc_grid(case):
+    """(workgroups, threads) of the norm-rope-cache launch for the workload's
+    shape: Dv = 512 / Dk = 64 runs one row per one-wavefront workgroup up to
+    2048 tokens and 2 rows per wavefront in 256-thread workgroups above;
+    other shapes one row per wavefront in 256-thread workgroups."""
+    T = case["B"] * case["S"]
+    if case["Dv"] == 512 and case["Dk"] == 64:
+        return (T, 64) if T <= 2048 else (-(-T // 8), 256)
+    return -(-T // 4), 256
+
+
+def context_measurements(case, bytes_per_launch, steps, stream, dev):
+    """Reference points measured in the same harness (graph of `steps`
+    launches, events on the launch stream): the launch floor of an empty
+    kernel (one 64-thread workgroup, and the workload's grid where it is the
+    norm-rope-cache kernel), and a plain device copy moving the same bytes as
+    one launch (bytes/2 read, bytes/2 written) over buffers rotated past the
+    Infinity Cache."""
+    import torch
+    import latent_attention_kv_amd as k
+    out = {}
+    ms, _ = _time_graph([lambda: k.kvrc_selftest_empty(1, 64)] * steps, stream)
+    out["empty_kernel_1wg_us"] = round(ms * 1e3 / steps, 3)
+    if kernel_family_of_case(case) == "kvrc":
+        wg, th = kvrc_grid(case)
+        ms, _ = _time_graph([lambda: k.kvrc_selftest_empty(wg, th)] * steps, stream)
+        out["empty_kernel_same_grid_us"] = round(ms * 1e3 / steps, 3)
+        out["same_grid"] = [wg, th]
+    half = (bytes_per_launch // 2) // 16 * 16
+    pairs = max(2, -(-512 * 2 ** 20 // (2 * half)))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev).fill_(1),
+             torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+    launches = [(lambda s=s, d=d: k.kvrc_selftest_copy(s, d)) for s, d in bufs]
+    ms, _ = _time_graph([launches[i % pairs] for i in range(steps)], stream)
+    us = ms * 1e3 / steps
+    out["copy_same_bytes_us"] = round(us, 3)
+    out["copy_same_bytes_gbps"] = round(2 * half / (us * 1e-6) / 1e9, 1)
+    out["copy_bytes_read_and_written"] = 2 * half
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def kernel_family_of_case(case):
+    if "block_keys" in case and "query" in case:
+        return "sel"
+    if case.get("mode") == "mla_paged":
+        return "mla"
+    if "raw_index_keys" in case:
+        return "qsa"
+    return "kvrc"
+
+
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_profile_times(workload):
+    """Per-dispatch durations of the kernel from the committed rocprofv3
+    trace summary (only while the kernel sources are unchanged)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash(workload):
+        return None
+    tr = t.get("trace", {})
+    out = {"avg_us": round(tr["avg_ns"] / 1e3, 3), "calls": tr.get("calls")}
+    for p in ("p10", "p50", "p90"):
+        if f"{p}_ns" in tr:
+            out[f"{p}_us"] = round(tr[f"{p}_ns"] / 1e3, 3)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -466,8 +688,11 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=0,
                     help="buffer sets rotated (0: enough to exceed 512 MB touched)")
     ap.add_argument("--no-graph", action="store_true", help="launch from Python each step")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle time per CPU baseline run (one thread, then all threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the per-step percentiles, launch floor and copy ceiling")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size 5 times "
                          "(counter calibration under rocprofv3)")
@@ -487,8 +712,10 @@ def main(argv=None):
               "(the path shards by sequence with no exchange; no multi-GPU run exists)",
               file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
-    import numpy as np
     import torch
 
     import gen
@@ -504,41 +731,64 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    if args.no_graph:
-        def replay():
-            with torch.cuda.stream(stream):
-                for s in sets:
-                    launch(case, s)
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for s in sets:              # one eager pass first (library loaded, args checked)
-                launch(case, s)
-        stream.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for s in sets:
-                launch(case, s)
+    # one eager launch per buffer set: loads the library and checks every
+    # argument set once (setup, neither warm-up nor timed)
+    with torch.cuda.stream(stream):
+        for s in sets:
+            launch(case, s)
+    stream.synchronize()
 
-        def replay():
-            with torch.cuda.stream(stream):
-                g.replay()
+    def launch_fn(i):
+        s = sets[i % R]
+        return lambda: launch(case, s)
 
-    warm_replays = max(1, -(-args.warmup // R))
-    timed_replays = max(1, -(-args.steps // R))
-    for _ in range(warm_replays):
-        replay()
-    torch.cuda.synchronize()
+    W, K = args.warmup, args.steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(timed_replays):
-        replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    steps = timed_replays * R
-    ms = e0.elapsed_time(e1) / steps
+    if args.no_graph:
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                launch(case, sets[i % R])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            for i in range(W, W + K):
+                launch(case, sets[i % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        # warm-up: W launches in one graph; timed: exactly K launches in one
+        # graph, continuing the rotation, behind a spin kernel so that the
+        # whole graph is submitted before its first launch starts
+        if W:
+            gw = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gw, stream=stream):
+                for i in range(W):
+                    launch(case, sets[i % R])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(W, W + K):
+                launch(case, sets[i % R])
+        torch.cuda.synchronize()
+        if W:
+            with torch.cuda.stream(stream):
+                gw.replay()
+        _gate(stream)
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
     secs = ms / 1e3
     kernel_us = ms * 1e3
+
+    context = None
+    if not args.no_context and not args.no_graph:
+        n_iso = min(K, 200)
+        context = {"isolated_launch_us": isolated_launch_times(
+            [launch_fn(i) for i in range(W, W + n_iso)], stream)}
+        context.update(context_measurements(case, bytes_per_launch, K, stream, dev))
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -565,13 +815,19 @@ def main(argv=None):
                     "traffic": read_traffic(args.workload),
                     "algorithmic_bytes_per_launch": bytes_per_launch,
                     "kernel_us": round(kernel_us, 3)}
+    prof = read_profile_times(args.workload)
+    roofline["rocprof_kernel_us"] = prof
+    if prof:
+        ach = (flops / 1e12 if flops else bytes_per_launch / 1e9) / (prof["avg_us"] * 1e-6)
+        roofline["rocprof_frac"] = round(ach / (MFMA_BF16_PEAK_TFLOPS if flops
+                                                 else HBM_PEAK_GBPS), 4)
     line = {
         "metric": METRIC,
         "value": round(tokens / secs, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warm_replays * R,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -580,9 +836,12 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                    "tokens_per_step": tokens, "io_dtype": "bf16",
-                   "buffer_sets_rotated": R, "graph": not args.no_graph},
+                   "buffer_sets_rotated": R, "graph": not args.no_graph,
+                   "setup_launches": R},
         "roofline": roofline,
     }
+    if context is not None:
+        line["context"] = context
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -58,6 +58,28 @@ int32_t kvrc_selftest_recip(const float *b, float *recip, int64_t n, hipStream_t
  */
 int32_t kvrc_selftest_e4m3(const float *x, uint8_t *code, int64_t n, hipStream_t stream);
 
+/*
+ * Measurement probes (not part of the method): they give a timing harness
+ * the two reference points against which the kernels are read.
+ *
+ * kvrc_selftest_empty - launches a kernel that does nothing, with
+ * `workgroups` workgroups of `threads` threads (1 <= threads <= 1024,
+ * 1 <= workgroups <= 2^31 - 1): its duration is the launch and dispatch
+ * floor of a grid of that shape. Returns KVRC_OK, KVRC_ERR_SHAPE or
+ * KVRC_ERR_HIP. Asynchronous on `stream`.
+ *
+ * kvrc_selftest_copy - copies `bytes` bytes from src to dst with 16-byte
+ * loads and stores (each thread moves four 16-byte pieces, all loads issued
+ * before the stores; loads non-temporal, as the kernels' streaming inputs):
+ * a plain device copy, the bandwidth ceiling of a kernel that moves the same
+ * bytes. src and dst are device memory, 16-byte aligned and not
+ * overlapping; bytes is a multiple of 16 and at most 2^40. Returns KVRC_OK
+ * (also for bytes == 0: nothing launched), KVRC_ERR_NULL, KVRC_ERR_SHAPE,
+ * KVRC_ERR_ALIGN, KVRC_ERR_ALIAS or KVRC_ERR_HIP. Asynchronous on `stream`.
+ */
+int32_t kvrc_selftest_empty(int64_t workgroups, int32_t threads, hipStream_t stream);
+int32_t kvrc_selftest_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
            "kvrc_norm_rope_cache", "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
            "kvrc_mla_kv_head_paged_blk",
            "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_recip",
-           "kvrc_selftest_e4m3",
+           "kvrc_selftest_e4m3", "kvrc_selftest_empty", "kvrc_selftest_copy",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -46,7 +46,8 @@ EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
                     "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
                     "kvrc_mla_kv_head_paged_blk", "qsa_prepare", "qsa_select_topk",
-                    "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3")
+                    "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3",
+                    "kvrc_selftest_empty", "kvrc_selftest_copy")
 
 _lib = None
 
@@ -98,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.kvrc_selftest_recip.restype = I32
     L.kvrc_selftest_e4m3.argtypes = [P, P, I64, P]
     L.kvrc_selftest_e4m3.restype = I32
+    L.kvrc_selftest_empty.argtypes = [I64, I32, P]
+    L.kvrc_selftest_empty.restype = I32
+    L.kvrc_selftest_copy.argtypes = [P, P, I64, P]
+    L.kvrc_selftest_copy.restype = I32
     _lib = L
     return L
 
@@ -376,6 +381,27 @@ def kvrc_selftest_e4m3(x, code, *, stream=None):
         raise ValueError("x and code must have the same length")
     _check(lib().kvrc_selftest_e4m3(_ptr(x), _ptr(code), x.numel(), _stream(stream)),
            "kvrc_selftest_e4m3")
+
+
+def kvrc_selftest_empty(workgroups, threads=256, *, stream=None):
+    """Measurement probe: an empty kernel of `workgroups` x `threads`."""
+    _check(lib().kvrc_selftest_empty(int(workgroups), int(threads), _stream(stream)),
+           "kvrc_selftest_empty")
+
+
+def kvrc_selftest_copy(src, dst, *, stream=None):
+    """Measurement probe: a plain 16-byte-vector device copy of src into dst
+    (contiguous GPU tensors of the same byte size, a multiple of 16)."""
+    for name, t in (("src", src), ("dst", dst)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(lib().kvrc_selftest_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "kvrc_selftest_copy")
 
 
 def qsa_prepare(raw_index_keys, block_keys, key_length, rope_cos, rope_sin, k_norm_weight,

@@ -52,6 +52,30 @@ __global__ __launch_bounds__(256) void e4m3_kernel(const float4 *__restrict__ x,
     }
 }
 
+__global__ void empty_kernel() {}
+
+// Four 16-byte pieces per thread: piece k of workgroup g, thread t is
+// g * 1024 + k * 256 + t, so each load and store instruction of a wavefront
+// covers 1 KiB of consecutive bytes.
+__global__ __launch_bounds__(256) void copy_kernel(const kvrc::u32x4 *__restrict__ src,
+                                                   kvrc::u32x4 *__restrict__ dst, int64_t n16)
+{
+    const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    kvrc::u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t i = base + 256 * k;
+        if (i < n16)
+            v[k] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t i = base + 256 * k;
+        if (i < n16)
+            dst[i] = v[k];
+    }
+}
+
 bool overlaps(const void *p, const void *q, int64_t bytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
@@ -126,5 +150,36 @@ extern "C" int32_t kvrc_selftest_e4m3(const float *x, uint8_t *code, int64_t n, 
     (void)hipGetLastError();
     hipLaunchKernelGGL(e4m3_kernel, dim3(grid), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(x), reinterpret_cast<uint32_t *>(code), n4);
+    return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
+}
+
+extern "C" int32_t kvrc_selftest_empty(int64_t workgroups, int32_t threads, hipStream_t stream)
+{
+    if (workgroups < 1 || workgroups > (int64_t)INT32_MAX || threads < 1 || threads > 1024)
+        return KVRC_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(empty_kernel, dim3((unsigned)workgroups), dim3((unsigned)threads), 0,
+                       stream);
+    return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
+}
+
+extern "C" int32_t kvrc_selftest_copy(const void *src, void *dst, int64_t bytes,
+                                      hipStream_t stream)
+{
+    if (bytes < 0 || bytes % 16 || bytes > ((int64_t)1 << 40))
+        return KVRC_ERR_SHAPE;
+    if (bytes == 0)
+        return KVRC_OK;
+    if (!src || !dst)
+        return KVRC_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+        return KVRC_ERR_ALIGN;
+    if (overlaps(src, dst, bytes))
+        return KVRC_ERR_ALIAS;
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = (n16 + 1023) / 1024;          // <= 2^26
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const kvrc::u32x4 *>(src), static_cast<kvrc::u32x4 *>(dst), n16);
     return hipGetLastError() == hipSuccess ? KVRC_OK : KVRC_ERR_HIP;
 }

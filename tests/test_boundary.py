@@ -99,6 +99,31 @@ def test_paged_validation(over, want):
     assert paged(**over) == want
 
 
+@pytest.mark.parametrize("over", [
+    # row widths above the library's bound of 2^20 elements
+    dict(Dv=(1 << 20) + 8), dict(Dk=(1 << 20) + 8), dict(Dv=1 << 32),
+    # 2^31 - 1 tokens of 2^20 + 2^20 elements with one cache row: every size
+    # passes alone, but kv spans 2^31 * 2^21 * 2 bytes (beyond int64's range
+    # before the cap, 2^53 with it); here the cache product overflows instead
+    dict(B=(1 << 31) - 1, S=1, Dv=1 << 20, Dk=1 << 20, NB=1 << 45, BS=1 << 10),
+    # the cache byte span rows * Dv * 2 passes 2^63
+    dict(NB=1 << 40, BS=1 << 10, Dv=1 << 20),
+    dict(NB=1 << 62, BS=1, Dk=64),
+])
+def test_paged_validation_at_the_caps(over):
+    """Sizes at and past the bounds: every byte span is formed with checked
+    products, so extreme sizes give a shape error, never an overflow (run
+    under the host sanitizer build as well)."""
+    assert paged(**over) == SHAPE
+
+
+def test_norm_and_blk_validation_at_the_caps():
+    assert norm(Dv=(1 << 20) + 8) == SHAPE
+    assert norm(Bc=1 << 40, Sc=1 << 20, Dv=1 << 20) == SHAPE
+    assert paged_blk(Dk=(1 << 20) + 8) == SHAPE
+    assert paged_blk(B=1 << 30, S=2, BS=1, NB=1 << 62) == SHAPE
+
+
 def paged_blk(**over):
     a = dict(kv=A["kv"], gamma=A["gamma"], cos=A["cos"], sin=A["sin"], idx=A["idx"], kc=A["kc"],
              ckv=A["ckv"], scale=None, B=2, S=300, Dv=512, Dk=64, NB=64, BS=128, dt=0, eps=1e-6,
@@ -211,6 +236,15 @@ def test_mla_validation(over, want):
     assert mla(**over) == want
 
 
+@pytest.mark.parametrize("over", [
+    dict(He=(1 << 20) + 32), dict(He=1 << 62), dict(NB=1 << 62, BS=2),
+    dict(NB=1 << 55, BS=1 << 8),                   # rows * 512 * 2 passes 2^63
+])
+def test_mla_validation_at_the_caps(over):
+    assert mla(**over) == SHAPE
+    assert mla(dt=1, sc=M["sc"], **over) == SHAPE
+
+
 SL = {name: (i + 60) << 32 for i, name in enumerate(["q", "k", "kl", "sc", "ix", "err"])}
 
 
@@ -270,6 +304,16 @@ def test_qsa_validation(over, want):
     assert qsa(**over) == want
 
 
+@pytest.mark.parametrize("over", [
+    dict(L=1 << 31), dict(kbs=1 << 31), dict(kbs=(1 << 62) + 1),
+    # N * Bcap * Di * 2 passes 2^63
+    dict(N=3, klc=3, Bcap=1 << 62), dict(N=1, klc=1, L=(1 << 31) - 1, Bcap=1 << 50, Di=4096),
+])
+def test_qsa_validation_at_the_caps(over):
+    assert qsa(**over) == SHAPE
+
+
+
 @pytest.mark.parametrize("x,code,n,want", [
     (A["kv"], A["ckv"], 3, SHAPE), (A["kv"], A["ckv"], -4, SHAPE), (None, A["ckv"], 4, NULL),
     (A["kv"], None, 4, NULL), (A["kv"] + 4, A["ckv"], 4, ALIGN), (A["kv"], A["ckv"] + 2, 4, ALIGN),
@@ -278,6 +322,24 @@ def test_qsa_validation(over, want):
 ])
 def test_selftest_e4m3_validation(x, code, n, want):
     assert k.lib().kvrc_selftest_e4m3(x, code, n, None) == want
+
+
+@pytest.mark.parametrize("wg,threads,want", [
+    (0, 256, SHAPE), (-1, 64, SHAPE), (1 << 31, 64, SHAPE), (1, 0, SHAPE), (1, 1025, SHAPE),
+])
+def test_selftest_empty_validation(wg, threads, want):
+    assert k.lib().kvrc_selftest_empty(wg, threads, None) == want
+
+
+@pytest.mark.parametrize("src,dst,n,want", [
+    (A["kv"], A["ckv"], 8, SHAPE), (A["kv"], A["ckv"], -16, SHAPE),
+    (A["kv"], A["ckv"], (1 << 40) + 16, SHAPE), (None, A["ckv"], 16, NULL),
+    (A["kv"], None, 16, NULL), (A["kv"] + 8, A["ckv"], 16, ALIGN), (A["kv"], A["ckv"] + 4, 16, ALIGN),
+    (A["kv"], A["kv"] + 16, 32, ALIAS), (A["kv"] + 16, A["kv"], 32, ALIAS),
+    (A["kv"], A["ckv"], 0, OK), (None, None, 0, OK),
+])
+def test_selftest_copy_validation(src, dst, n, want):
+    assert k.lib().kvrc_selftest_copy(src, dst, n, None) == want
 
 
 def test_binding_refuses_cpu_tensors():
