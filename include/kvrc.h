@@ -8,8 +8,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every data pointer is caller-owned DEVICE memory of the current HIP
- *   device. The library allocates nothing, keeps no state between calls and
- *   needs no workspace; it is safe to call from several host threads.
+ *   device. The library allocates nothing and keeps no state between calls.
+ *   The MLA head entry points (kvrc_mla_kv_head_paged and _paged_blk) take
+ *   a caller-owned workspace, with the rules stated at their declaration;
+ *   every other entry point needs no workspace and is safe to call from
+ *   several host threads at once.
  * - Work is enqueued asynchronously on `stream` (NULL = the null stream).
  *   Buffers must stay valid until that work has completed. Caches are
  *   updated in place.
@@ -105,8 +108,10 @@ int32_t kvrc_version(void);
  *   ckv_cache     bf16, int8 or E4M3FN (uint8 codes) [num_blocks, block_size, 1, Dv]
  *   ckv_scale     float32 [num_blocks, block_size, 1]; must be NULL for BF16
  *                 and non-NULL for INT8 and FP8_E4M3
- *   Dv, Dk        multiples of 8, >= 8 (Dk even is the source's rule; 8 is
- *                 this library's vector width)
+ *   Dv, Dk        multiples of 8, 8 <= Dv, Dk <= 2^20 (Dk even is the
+ *                 source's rule; 8 is this library's vector width, 2^20 its
+ *                 bound on a row); B*S <= 2^31 - 1; every byte size the
+ *                 shapes imply must stay below 2^63 (else KVRC_ERR_SHAPE)
  *   eps           added to the mean square
  *   err_count     optional device int32, see above
  * Returns KVRC_OK (also when B*S == 0: nothing is launched and the caches are
@@ -227,7 +232,7 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *   ckv_scale     float32 [num_blocks, block_size, 1]; NULL for BF16,
  *                 non-NULL for INT8 and FP8_E4M3 (else KVRC_ERR_DTYPE)
  *   ckv_dtype     a kvrc_cache_dtype
- *   He            a multiple of 32, >= 32; T <= 2^31 - 1
+ *   He            a multiple of 32, 32 <= He <= 2^20; T <= 2^31 - 1
  *   workspace     device memory of at least
  *                 kvrc_mla_kv_head_workspace_bytes(T) bytes (workspace_bytes
  *                 gives its size), 16-byte aligned, owned by the caller. It
@@ -322,7 +327,9 @@ int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const vo
  *   past_incomplete_rope      float32 [N, 2*Dr] (cos || sin); NULL iff rope off
  *   next_incomplete_raw_keys  bf16 [N, kbs-1, Di] out; must not overlap any input
  *   next_incomplete_rope      float32 [N, 2*Dr] out; NULL iff rope off
- *   Di multiple of 8; Dr even, 2 <= Dr <= Di when rope is on; kbs >= 2.
+ *   Di multiple of 8, <= 4096; Dr even, 2 <= Dr <= Di when rope is on;
+ *   2 <= kbs <= 2^31 - 1; L <= 2^31 - 1; every byte size the shapes imply
+ *   must stay below 2^63 (else KVRC_ERR_SHAPE).
  * Returns KVRC_OK (also when N*L == 0: nothing is written, including the next
  * state), or an error status with nothing written. On the device a sequence
  * with K < L, or whose blocks reach past Bcap, is skipped (err_count).

@@ -28,7 +28,7 @@ bool overlap(Range a, Range b)
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// a*b with overflow / negative guard (sizes here fit easily in int64).
+// a*b with overflow / negative guard.
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
     if (a < 0 || b < 0)
@@ -38,6 +38,20 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out)
     *out = a * b;
     return true;
 }
+
+// *out = a*b*c*d, false if a factor is negative or the product passes
+// INT64_MAX (every byte span below is formed this way, never with a bare
+// multiplication).
+bool prod_ok(int64_t *out, int64_t a, int64_t b, int64_t c = 1, int64_t d = 1)
+{
+    int64_t ab, abc;
+    return mul_ok(a, b, &ab) && mul_ok(ab, c, &abc) && mul_ok(abc, d, out);
+}
+
+// Largest Dv and Dk of a norm-rope-cache row (elements), and largest He of
+// the MLA head: bounds of this library, far above any model's row width,
+// that keep every per-row quantity far from overflow.
+constexpr int64_t kMaxRowElems = (int64_t)1 << 20;
 
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? KVRC_OK : KVRC_ERR_HIP; }
 
@@ -56,9 +70,10 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
         return KVRC_ERR_DTYPE;
     if (B < 0 || S < 0 || rows < 0 || limit < 0)
         return KVRC_ERR_SHAPE;
-    if (Dv < 8 || Dk < 8 || Dv % 8 || Dk % 8)
+    if (Dv < 8 || Dk < 8 || Dv % 8 || Dk % 8 || Dv > kMaxRowElems || Dk > kMaxRowElems)
         return KVRC_ERR_SHAPE;
-    int64_t T, D = Dv + Dk;
+    int64_t T;
+    const int64_t D = Dv + Dk;                // <= 2^21
     if (!mul_ok(B, S, &T) || T > (int64_t)INT32_MAX)
         return KVRC_ERR_SHAPE;
     if (T == 0)
@@ -77,13 +92,14 @@ int32_t norm_rope_cache_common(const void *kv, const void *gamma, const void *co
     // ceil(S / block_size) without forming S + block_size (block_size may be
     // near 2^63 when num_blocks is 0)
     const int64_t chunks = block_size > 0 ? S / block_size + (S % block_size != 0) : 0;
-    const int64_t index_count = block_size > 0 ? B * chunks : T;
-    int64_t kbytes, cbytes, sbytes = 0;
-    if (!mul_ok(rows, Dk * 2, &kbytes) || !mul_ok(rows, Dv * (quant ? 1 : 2), &cbytes) ||
-        (quant && !mul_ok(rows, 4, &sbytes)))
+    int64_t index_count = T, kbytes, cbytes, sbytes = 0, kvbytes, csbytes, ibytes;
+    if ((block_size > 0 && !prod_ok(&index_count, B, chunks)) ||
+        !prod_ok(&kbytes, rows, Dk, 2) || !prod_ok(&cbytes, rows, Dv, quant ? 1 : 2) ||
+        (quant && !prod_ok(&sbytes, rows, 4)) || !prod_ok(&kvbytes, T, D, 2) ||
+        !prod_ok(&csbytes, T, Dk, 2) || !prod_ok(&ibytes, index_count, 8))
         return KVRC_ERR_SHAPE;
-    const Range in[] = {span(kv, T * D * 2), span(gamma, Dv * 2), span(cos, T * Dk * 2),
-                        span(sin, T * Dk * 2), span(index, index_count * 8)};
+    const Range in[] = {span(kv, kvbytes), span(gamma, Dv * 2), span(cos, csbytes),
+                        span(sin, csbytes), span(index, ibytes)};
     const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
                          span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
@@ -215,15 +231,16 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     const bool quant = ckv_dtype != KVRC_CACHE_BF16;   // one byte per element + scale
     int64_t rows;
     if (T < 0 || T > (int64_t)INT32_MAX || He < kvrc::kMlaHeadK || He % kvrc::kMlaHeadK ||
-        num_blocks < 0 || block_size < 1 || !mul_ok(num_blocks, block_size, &rows))
+        He > kMaxRowElems || num_blocks < 0 || block_size < 1 ||
+        !mul_ok(num_blocks, block_size, &rows))
         return KVRC_ERR_SHAPE;
-    int64_t xbytes, wbytes, kbytes, cbytes;
-    if (!mul_ok(T, He * 2, &xbytes) || !mul_ok(576, He * 2, &wbytes) ||
-        !mul_ok(rows, 64 * 2, &kbytes) || !mul_ok(rows, 512 * (quant ? 1 : 2), &cbytes))
-        return KVRC_ERR_SHAPE;
-    const int64_t sbytes = quant ? rows * 4 : 0;
     const int64_t chunks = blk && S > 0 ? S / block_size + (S % block_size != 0) : 0;
-    const int64_t index_count = blk ? B * chunks : T;
+    int64_t xbytes, wbytes, kbytes, cbytes, sbytes = 0, csbytes, ibytes, index_count = T;
+    if (!prod_ok(&xbytes, T, He, 2) || !prod_ok(&wbytes, 576, He, 2) ||
+        !prod_ok(&kbytes, rows, 64, 2) || !prod_ok(&cbytes, rows, 512, quant ? 1 : 2) ||
+        (quant && !prod_ok(&sbytes, rows, 4)) || (blk && !prod_ok(&index_count, B, chunks)) ||
+        !prod_ok(&ibytes, index_count, 8) || !prod_ok(&csbytes, T, 64, 2))
+        return KVRC_ERR_SHAPE;
     if (T == 0)
         return KVRC_OK;                       // empty input: caches untouched
     const int64_t wsbytes = kvrc::mla_kv_head_workspace_bytes(T);
@@ -240,7 +257,7 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
         !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
     const Range in[] = {span(x, xbytes), span(w_dkv_kr, wbytes), span(gamma, 1024),
-                        span(cos, T * 128), span(sin, T * 128), span(index, index_count * 8)};
+                        span(cos, csbytes), span(sin, csbytes), span(index, ibytes)};
     const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
                          span(workspace, wsbytes), span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
@@ -331,9 +348,10 @@ int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t
     const int64_t chunk = want < fit ? want : fit;
     if (chunk < 16)
         return KVRC_ERR_SHAPE;
-    int64_t qbytes, kbytes, sbytes, ibytes;
-    if (!mul_ok(N, H * Di * 2, &qbytes) || !mul_ok(N, Bcap * Di * 2, &kbytes) ||
-        !mul_ok(N, jcap * 4, &sbytes) || !mul_ok(N, topk * 4, &ibytes))
+    int64_t qbytes, kbytes, sbytes, ibytes, klbytes;
+    if (!prod_ok(&qbytes, N, H, Di, 2) || !prod_ok(&kbytes, N, Bcap, Di, 2) ||
+        !prod_ok(&sbytes, N, jcap, 4) || !prod_ok(&ibytes, N, topk, 4) ||
+        !prod_ok(&klbytes, key_length_count, 8))
         return KVRC_ERR_SHAPE;
     if (N == 0)
         return KVRC_OK;
@@ -343,7 +361,7 @@ int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t
         !aligned(scores, 4) || !aligned(indices, 4) || !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
     const Range in[] = {span(query, qbytes), span(block_keys, kbytes),
-                        span(key_length, key_length_count * 8)};
+                        span(key_length, klbytes)};
     const Range out[] = {span(scores, sbytes), span(indices, ibytes),
                          span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
@@ -386,7 +404,8 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
                     hipStream_t stream)
 {
     const int64_t kbs = key_block_size;
-    if (N < 0 || L < 0 || Bcap < 0 || kbs < 2)
+    if (N < 0 || L < 0 || L > (int64_t)INT32_MAX || Bcap < 0 || kbs < 2 ||
+        kbs > (int64_t)INT32_MAX)
         return KVRC_ERR_SHAPE;
     if (Di < 8 || Di % 8 || Di > kvrc::kQsaMaxDi)
         return KVRC_ERR_SHAPE;
@@ -398,10 +417,14 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
         return KVRC_ERR_SHAPE;
     if (N > 0 && key_length_count != 1 && key_length_count != N)
         return KVRC_ERR_SHAPE;
-    int64_t NL, rowsN, capN;
-    if (!mul_ok(N, L, &NL) || !mul_ok(N, kbs - 1, &rowsN) || !mul_ok(N, Bcap, &capN))
+    const int64_t Drr = rope ? Dr : 0;
+    int64_t NL, rowsN, capN, rawb, ropeb, pastb, stateb, capb, klbytes;
+    if (!mul_ok(N, L, &NL) || !mul_ok(N, kbs - 1, &rowsN) || !mul_ok(N, Bcap, &capN) ||
+        !prod_ok(&rawb, NL, Di, 2) || !prod_ok(&ropeb, NL, Drr, 4) ||
+        !prod_ok(&pastb, rowsN, Di, 2) || !prod_ok(&stateb, N, 2 * Drr, 4) ||
+        !prod_ok(&capb, capN, Di, 2) || !prod_ok(&klbytes, key_length_count, 8))
         return KVRC_ERR_SHAPE;
-    const int64_t nb_max = (kbs - 1 + L) / kbs;
+    const int64_t nb_max = (kbs - 1 + L) / kbs;       // both < 2^31
     int64_t grid;
     if (!mul_ok(N, nb_max + 1, &grid) || grid > (int64_t)INT32_MAX)
         return KVRC_ERR_SHAPE;
@@ -418,17 +441,16 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
         !aligned(next_incomplete_rope, 4) || !aligned(err_count, 4))
         return KVRC_ERR_ALIGN;
 
-    const int64_t Drr = rope ? Dr : 0;
-    const Range in[] = {span(raw_index_keys, NL * Di * 2),
-                        span(key_length, key_length_count * 8),
-                        span(rope_cos, NL * Drr * 4),
-                        span(rope_sin, NL * Drr * 4),
+    const Range in[] = {span(raw_index_keys, rawb),
+                        span(key_length, klbytes),
+                        span(rope_cos, ropeb),
+                        span(rope_sin, ropeb),
                         span(k_norm_weight, k_norm_weight ? Di * 2 : 0),
-                        span(past_incomplete_raw_keys, rowsN * Di * 2),
-                        span(past_incomplete_rope, N * 2 * Drr * 4)};
-    const Range out[] = {span(block_keys, capN * Di * 2),
-                         span(next_incomplete_raw_keys, rowsN * Di * 2),
-                         span(next_incomplete_rope, N * 2 * Drr * 4),
+                        span(past_incomplete_raw_keys, pastb),
+                        span(past_incomplete_rope, stateb)};
+    const Range out[] = {span(block_keys, capb),
+                         span(next_incomplete_raw_keys, pastb),
+                         span(next_incomplete_rope, stateb),
                          span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
         for (const Range &i : in)

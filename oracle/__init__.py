@@ -31,15 +31,25 @@ class OracleError(RuntimeError):
     pass
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the oracle with gcc (float32, no contraction, OpenMP over rows)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+# Host sanitizers for a checking build of the oracle: address errors and
+# undefined behaviour abort the process (no recovery).
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the oracle with gcc (float32, no contraction, OpenMP over rows).
+    sanitize=True builds a checking copy with SANITIZE_FLAGS at `out` (it must
+    be loaded into a process that preloads the sanitizer runtimes)."""
+    path = out or _LIB_PATH
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-fopenmp", "-o", path + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(path + ".tmp", path)
+    return path
 
 
 def _load():
