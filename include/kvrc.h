@@ -177,7 +177,7 @@ int32_t kvrc_norm_rope_cache(const void *kv, const void *gamma, const void *cos,
 /*
  * kvrc_mla_kv_head_workspace_bytes - bytes of device workspace that
  * kvrc_mla_kv_head_paged needs for T tokens (the first phase of the pages'
- * "workspace size, then execute" convention; 4104 bytes per 256 tokens, for
+ * "workspace size, then execute" convention; 4112 bytes per 256 tokens, for
  * every ckv cache type).
  * Returns -1 for T < 0 or T > 2^31 - 1, 0 for T == 0.
  */
@@ -236,26 +236,29 @@ int64_t kvrc_mla_kv_head_workspace_bytes(int64_t T);
  *   workspace     device memory of at least
  *                 kvrc_mla_kv_head_workspace_bytes(T) bytes (workspace_bytes
  *                 gives its size), 16-byte aligned, owned by the caller. It
- *                 must be all zero when first used; every call that runs to
- *                 its end leaves it all zero again, so one workspace serves
- *                 any number of calls in order on a stream (HIP graph
- *                 replays included).
- * Concurrency: the two workgroups of a pair wait for each other, which
- * needs the partner to be placed on a compute unit while the first one
- * waits. Alongside kernels that never wait this holds (their workgroups
- * finish and free their units). Two MLA head calls running at the same time
- * on one device (different streams) can fill every unit with workgroups
- * waiting for partners that cannot be placed: do not overlap MLA head calls
- * on a device (order them on one stream, or with events), and give calls
- * on different streams separate workspaces.
+ *                 must be all zero when first used; every call leaves it all
+ *                 zero again, so one workspace serves any number of calls in
+ *                 order on a stream (HIP graph replays included). Calls that
+ *                 may run at the same time need separate workspaces.
+ * Concurrency: the two workgroups that share 256 token rows exchange
+ * per-row partial sums through the workspace. Neither ever waits for a
+ * partner that has not started: a workgroup that finds no partials and no
+ * claim from its partner after a short wait (20 us) takes the partner's
+ * half over and computes both halves itself (the partner, when it starts,
+ * finds its half taken and leaves); only a partner that has started - and
+ * is therefore running - is waited for. MLA head calls may therefore run at
+ * the same time as any other work, other MLA head calls included (on other
+ * streams, each with its own workspace); the outputs are the same bits
+ * whichever workgroup computes them.
  * Returns KVRC_OK (also when T == 0: nothing is launched), or an error
  * status with nothing written: KVRC_ERR_WORKSPACE when workspace_bytes is
  * too small; outputs (the workspace included) must not overlap inputs or
  * each other. err_count counts slots outside [-1, num_blocks*block_size),
- * and also a workgroup whose partner did not publish its partial sums
- * within about a second (its rows are then not valid; the workspace was
- * not zero, another call used it at the same time, or MLA head calls
- * overlapped on the device).
+ * and a workspace found not zero (a flag or claim left by another call:
+ * each call marks its own with a fresh tag, so such words are ignored and
+ * the outputs stay valid; zero the workspace again). It would also count a
+ * started partner that published nothing for about ten seconds, which the
+ * GPU's forward progress rules out (those rows would be left unwritten).
  */
 int32_t kvrc_mla_kv_head_paged(const void *x, const void *w_dkv_kr, const void *gamma,
                                float alpha_kv, const void *cos, const void *sin,

@@ -80,6 +80,26 @@ int32_t kvrc_selftest_e4m3(const float *x, uint8_t *code, int64_t n, hipStream_t
 int32_t kvrc_selftest_empty(int64_t workgroups, int32_t threads, hipStream_t stream);
 int32_t kvrc_selftest_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+/*
+ * kvrc_selftest_mla_kv_head_stalled - kvrc_mla_kv_head_paged (same
+ * arguments, status codes and results) with the second workgroup of every
+ * pair held back for stall_us microseconds (0 .. 10^7) before it claims its
+ * half, so that the takeover path runs: the first workgroup, finding no
+ * partials and no claim from its partner, computes both halves of the pair
+ * itself. When steals is not NULL (a device int32 the caller clears, 4-byte
+ * aligned), the number of halves taken over is added to it. Not part of the
+ * method: it lets a test check that the takeover gives the same outputs and
+ * leaves the workspace zero.
+ */
+int32_t kvrc_selftest_mla_kv_head_stalled(const void *x, const void *w_dkv_kr, const void *gamma,
+                                          float alpha_kv, const void *cos, const void *sin,
+                                          const int64_t *slot_mapping, void *k_cache,
+                                          void *ckv_cache, float *ckv_scale, int64_t T,
+                                          int64_t He, int64_t num_blocks, int64_t block_size,
+                                          int32_t ckv_dtype, float eps, void *workspace,
+                                          int64_t workspace_bytes, int32_t *err_count,
+                                          int64_t stall_us, int32_t *steals, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

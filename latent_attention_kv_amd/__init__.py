@@ -35,6 +35,7 @@ __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
            "kvrc_mla_kv_head_paged_blk",
            "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_recip",
            "kvrc_selftest_e4m3", "kvrc_selftest_empty", "kvrc_selftest_copy",
+           "kvrc_selftest_mla_kv_head_stalled",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -47,7 +48,8 @@ EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_
                     "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
                     "kvrc_mla_kv_head_paged_blk", "qsa_prepare", "qsa_select_topk",
                     "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3",
-                    "kvrc_selftest_empty", "kvrc_selftest_copy")
+                    "kvrc_selftest_empty", "kvrc_selftest_copy",
+                    "kvrc_selftest_mla_kv_head_stalled")
 
 _lib = None
 
@@ -103,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_selftest_empty.restype = I32
     L.kvrc_selftest_copy.argtypes = [P, P, I64, P]
     L.kvrc_selftest_copy.restype = I32
+    L.kvrc_selftest_mla_kv_head_stalled.argtypes = [P, P, P, F, P, P, P, P, P, P, I64, I64, I64,
+                                                    I64, I32, F, P, I64, P, I64, P, P]
+    L.kvrc_selftest_mla_kv_head_stalled.restype = I32
     _lib = L
     return L
 
@@ -277,14 +282,16 @@ def _mla_caches(k_cache, ckv_cache, ckv_scale):
 
 def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, ckv_cache,
                            ckv_scale=None, *, workspace, alpha_kv=1.0, eps=1e-6, err_count=None,
-                           stream=None):
+                           stream=None, _stall_us=None, _steals=None):
     """MLA kv-path head into paged caches: x [T, He], w_dkv_kr [576, He],
     gamma [512], cos / sin [T, 64], slot_mapping [T]; k_cache
     [NB, BS, 1, 64] (bf16) and ckv_cache [NB, BS, 1, 512] (bf16, or int8 /
     E4M3FN codes with ckv_scale [NB, BS, 1] float32) are updated in place.
     workspace: a contiguous device tensor of at least
     kvrc_mla_kv_head_workspace_bytes(T) bytes, all zero before its first use
-    (each completed call leaves it zero)."""
+    (each call leaves it zero); calls that may overlap need separate ones.
+    _stall_us / _steals (tests only): call kvrc_selftest_mla_kv_head_stalled,
+    which holds back the second workgroup of every pair (include/kvrc_selftest.h)."""
     _need(x, "x", _BF16, 2)
     _need(w_dkv_kr, "w_dkv_kr", _BF16, 2)
     _need(gamma, "gamma", _BF16, 1)
@@ -305,6 +312,16 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
             not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if _stall_us is not None:
+        if _steals is not None:
+            _need(_steals, "_steals", (torch.int32,), 1)
+        st = lib().kvrc_selftest_mla_kv_head_stalled(
+            _ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv), _ptr(cos), _ptr(sin),
+            _ptr(slot_mapping), _ptr(k_cache), _ptr(ckv_cache), _ptr(ckv_scale), T, He, NB, BS,
+            dt, float(eps), _ptr(workspace), ws_bytes, _err_ptr(err_count), int(_stall_us),
+            _ptr(_steals), _stream(stream))
+        _check(st, "kvrc_selftest_mla_kv_head_stalled")
+        return
     st = lib().kvrc_mla_kv_head_paged(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma), float(alpha_kv),
                                       _ptr(cos), _ptr(sin), _ptr(slot_mapping), _ptr(k_cache),
                                       _ptr(ckv_cache), _ptr(ckv_scale), T, He, NB, BS, dt,

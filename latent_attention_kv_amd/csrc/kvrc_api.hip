@@ -7,7 +7,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kvrc_launch.hpp"
+#include "kvrc_selftest.h"
 
 namespace {
 
@@ -218,12 +221,26 @@ namespace {
 // Shared body of the two MLA head entry points: index = the slot mapping
 // [T] (index_count = T, B = S = 0) or the block index
 // [B * ceil(S / block_size)] (index_count entries, T = B * S).
+// Tag of an MLA head call, in [1, 2^30): the kernel marks the pair flags and
+// claim words of the workspace with it, so that words left by another call
+// never match this one's.
+uint32_t next_mla_tag()
+{
+    static std::atomic<uint32_t> counter{0};
+    return counter.fetch_add(1, std::memory_order_relaxed) % ((1u << 30) - 1) + 1;
+}
+
+// Microseconds a half waits for its partner's partials before it tries to
+// take the partner's half over: far beyond the spread of start times of the
+// two halves of a pair when both are placed, and short next to the kernel.
+constexpr uint32_t kStealMicros = 20;
+
 int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float alpha_kv,
                    const void *cos, const void *sin, const int64_t *index, bool blk, int64_t B,
                    int64_t S, void *k_cache, void *ckv_cache, float *ckv_scale, int64_t T,
                    int64_t He, int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
                    float eps, void *workspace, int64_t workspace_bytes, int32_t *err_count,
-                   hipStream_t stream)
+                   hipStream_t stream, uint32_t stall_us = 0, int32_t *steals = nullptr)
 {
     if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8 &&
         ckv_dtype != KVRC_CACHE_FP8_E4M3)
@@ -290,6 +307,10 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     a.eps = eps;
     a.workspace = workspace;
     a.err = err_count;
+    a.tag = next_mla_tag();
+    a.steal_us = kStealMicros;
+    a.stall_us = stall_us;
+    a.steals = steals;
     (void)hipGetLastError();
     return launch_status(kvrc::launch_mla_kv_head(a, stream));
 }
@@ -322,6 +343,25 @@ int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const vo
     return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, block_index, true, B, S, k_cache,
                       ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
                       workspace, workspace_bytes, err_count, stream);
+}
+
+int32_t kvrc_selftest_mla_kv_head_stalled(const void *x, const void *w_dkv_kr, const void *gamma,
+                                          float alpha_kv, const void *cos, const void *sin,
+                                          const int64_t *slot_mapping, void *k_cache,
+                                          void *ckv_cache, float *ckv_scale, int64_t T,
+                                          int64_t He, int64_t num_blocks, int64_t block_size,
+                                          int32_t ckv_dtype, float eps, void *workspace,
+                                          int64_t workspace_bytes, int32_t *err_count,
+                                          int64_t stall_us, int32_t *steals, hipStream_t stream)
+{
+    if (stall_us < 0 || stall_us > 10000000)
+        return KVRC_ERR_SHAPE;
+    if (steals && reinterpret_cast<uintptr_t>(steals) % 4)
+        return KVRC_ERR_ALIGN;
+    return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, slot_mapping, false, 0, 0, k_cache,
+                      ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
+                      workspace, workspace_bytes, err_count, stream,
+                      (uint32_t)stall_us, steals);
 }
 
 int32_t qsa_select_topk(const void *query, const void *block_keys, const int64_t *key_length,

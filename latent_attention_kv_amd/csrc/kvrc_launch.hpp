@@ -100,6 +100,12 @@ struct MlaKvHeadArgs {
     float alpha, eps;
     void *workspace;          // mla_kv_head_workspace_bytes(T) bytes, zero between calls
     int32_t *err;             // nullable
+    uint32_t tag;             // call tag in [1, 2^30): marks this call's flags and claims
+    uint32_t steal_us;        // microseconds a half waits for its partner before trying
+                              // to take over the partner's half
+    uint32_t stall_us;        // test only (0 otherwise): half 1 of every pair waits this
+                              // long before claiming its half
+    int32_t *steals;          // test only (nullable): halves taken over by their partner
 };
 
 hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream);
@@ -109,8 +115,8 @@ constexpr int64_t kMlaHeadK = 32;
 // Token rows per workgroup pair of the MLA head kernel.
 constexpr int64_t kMlaPairRows = 256;
 // Workspace of one MLA head call: per pair of workgroups, their per-row
-// partial square sums, per-row partial maxima (quantised ckv) and two
-// ready flags.
+// partial square sums, per-row partial maxima (quantised ckv), two ready
+// flags and two claim words.
 int64_t mla_kv_head_workspace_bytes(int64_t T);
 
 // One block-selection launch (see qsa_select_topk in kvrc.h).

@@ -52,7 +52,7 @@
 //     their per-row partial sums through the caller's workspace (a ready
 //     flag per half, set after the sums; the partner reads the sums, zeroes
 //     them and clears the flag, so the workspace is all zero again when the
-//     call ends);
+//     call ends; see the claim protocol below);
 //     rows are normalised and rotated in registers, staged as bf16 in LDS
 //     and scattered with 16-byte stores per cache row piece;
 //   * a quantised ckv cache needs the maximum of each row over both halves:
@@ -62,11 +62,20 @@
 //     registers until the scale is known, then the codes are staged (one
 //     byte each) and scattered like the bf16 rows, half 0 also writing the
 //     row scale.
-// The wait for the partner is bounded: past the limit the workgroup counts
-// an error and goes on (its rows are then wrong), so the kernel always ends.
-// A partner is dispatched at most 8 workgroups later on the same XCD, and
-// workgroups retire as soon as their pair has swapped, so both halves of a
-// pair are resident together whenever one of them waits.
+// No wait depends on the two halves of a pair being resident together (HIP
+// promises nothing about dispatch order or co-residency): each half claims
+// its half of the pair in the workspace when it starts (a claim word per
+// half, marked with a tag fresh for every call). A half that reaches the
+// exchange and finds neither its partner's partials nor its partner's claim
+// after a short wait claims the partner's half itself ("takeover") and
+// computes both halves, one after the other with the same code, so the
+// outputs are the same bits; the partner, when it is placed, finds its half
+// taken and leaves without writing. A partner that has claimed is resident
+// and running, so waiting for its partials always ends (a bound of seconds
+// only keeps the kernel finite). Two calls may run at the same time on one
+// device, each with its own workspace.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "kvrc_launch.hpp"
 
@@ -113,9 +122,17 @@ constexpr int kSumOff = kRedOff + 2 * kRows * 4;
 constexpr int kRedMaxOff = kSumOff + kRows * 4;
 constexpr int kMaxOff = kRedMaxOff + 2 * kRows * 4;
 constexpr int kEpiBytes = kMaxOff + kRows * 4;
-constexpr int kLdsBytes = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
-// bounded wait for the partner's sums (polls with a short sleep in between)
-constexpr int kSpinLimit = 1 << 20;
+// two control words (the claim result, the exchange outcome), after both
+constexpr int kCtlOff = kPipeBytes > kEpiBytes ? kPipeBytes : kEpiBytes;
+constexpr int kLdsBytes = kCtlOff + 16;
+// Claim words of the workspace: the call tag times 4 plus a state.
+constexpr uint32_t kClaimed = 1, kStolen = 2;
+// Outcomes of a pass's exchange step.
+constexpr int kGot = 0, kStole = 1, kLost = 2, kExit = 3;
+// Wall-clock (100 MHz) bound of a wait for a partner that has claimed its
+// half: such a partner is resident and running, so its partials come; the
+// bound (10 s) only keeps the kernel finite.
+constexpr uint64_t kSafetyTicks = 1000000000ull;
 // cache-policy operand of a buffer store: sc1 (device scope, write-through)
 constexpr int kStoreSc1 = 16;
 
@@ -127,19 +144,89 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // c ^ ((r >> 2) & 3).
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
+// Claim of a half, in two steps by wavefront 0, lane 0. At the start,
+// claim_begin reads this half's flag and tries the claim word from 0 to this
+// call's "claimed" (the results are read only after the K loop, so the
+// atomics' latency hides behind it). After the K loop, claim_settle tells
+// whether the partner took the half over: then both words of this half are
+// reset to zero (nobody else touches them again in this call). A word that
+// was neither zero nor this call's (left by another call: a workspace that
+// was not zero) is counted in err, and the claim is retried from it.
+struct ClaimStart {
+    uint32_t old_claim, old_flag;
+};
+
+__device__ __forceinline__ ClaimStart claim_begin(uint32_t *my_claim, const uint32_t *my_flag,
+                                                  uint32_t tag)
+{
+    ClaimStart c;
+    c.old_flag = __hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t expected = 0u;
+    __hip_atomic_compare_exchange_strong(my_claim, &expected, (tag << 2) | kClaimed,
+                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    c.old_claim = expected;                 // 0 when the claim succeeded
+    return c;
+}
+
+__device__ bool claim_settle(ClaimStart c, uint32_t *my_claim, uint32_t *my_flag, uint32_t tag,
+                             int32_t *err)
+{
+    const uint32_t claimed = (tag << 2) | kClaimed, stolen = (tag << 2) | kStolen;
+    // the raw values are first looked at here (the compiler may not move a
+    // comparison of them, and with it the wait for the atomics, before the
+    // K loop)
+    asm volatile("" : "+v"(c.old_flag), "+v"(c.old_claim));
+    bool dirty = c.old_flag != 0u;
+    bool taken = c.old_claim == stolen;
+    if (c.old_claim != 0u && !taken) {
+        dirty = true;
+        uint32_t old = c.old_claim;
+        for (;;) {             // a failed exchange means the partner just took it
+            if (old == stolen) {
+                taken = true;
+                break;
+            }
+            uint32_t expected = old;
+            if (__hip_atomic_compare_exchange_strong(my_claim, &expected, claimed,
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+            old = expected;
+        }
+    }
+    if (taken) {               // this half's words are no one else's any more
+        __hip_atomic_store(my_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(my_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (dirty && err)
+        atomicAdd(err, 1);
+    return taken;
+}
+
 // The exchange of per-row partial values between the two workgroups of a
 // pair, run by wavefront 0 (lane l: rows 4 l .. 4 l + 3): publish p (and p2,
-// with kTwo) in this half's areas of the workspace (then the flag, with
-// release order), wait for the partner's flag (bounded), read its values
-// into q (q2), zero them and clear its flag, so the areas are all zero again
-// afterwards. Returns false when the wait timed out (q, q2 are then not the
-// partner's).
+// with kTwo) in this half's areas of the workspace, then the flag (this
+// call's tag, with release order); wait for the partner's flag. Outcomes:
+//   kGot   - the partner's values are in q (q2); their areas are zeroed, its
+//            flag cleared and its claim word reset (the partner touches
+//            neither again in this call);
+//   kStole - the partner did not publish within steal_ticks and had not
+//            claimed its half: this workgroup claimed it instead ("stolen")
+//            and computes both halves; the partner, when it starts, sees the
+//            word and leaves;
+//   kLost  - the partner claimed its half but published nothing within the
+//            safety bound (not expected while the GPU makes progress).
+// A partner that has claimed its half is resident and running, so waiting
+// for it always ends; a partner that has not is never waited for beyond
+// steal_ticks. No wait depends on the dispatch order or on co-residency.
 template <bool kTwo>
-__device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, float *mine2,
-                                              float *theirs2, uint32_t *my_flag,
-                                              uint32_t *their_flag, const float (&p)[4],
-                                              const float (&p2)[4], float (&q)[4],
-                                              float (&q2)[4], int lane)
+__device__ __forceinline__ int pair_exchange(float *mine, float *theirs, float *mine2,
+                                             float *theirs2, uint32_t *my_flag,
+                                             uint32_t *their_flag, uint32_t *their_claim,
+                                             uint32_t tag, uint32_t steal_ticks,
+                                             const float (&p)[4], const float (&p2)[4],
+                                             float (&q)[4], float (&q2)[4], int lane)
 {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -150,16 +237,43 @@ __device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, float 
     }
     // release: the wavefront's values above are visible before the flag
     if (lane == 0)
-        __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
+        __hip_atomic_store(my_flag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int outcome = kGot;
     if (lane == 0) {
-        while (__hip_atomic_load(their_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-               spins < kSpinLimit) {
+        const uint32_t claimed = (tag << 2) | kClaimed, stolen = (tag << 2) | kStolen;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        bool tried = false;
+        for (;;) {
+            if (__hip_atomic_load(their_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag)
+                break;
+            const uint64_t waited = __builtin_amdgcn_s_memrealtime() - t0;
+            if (!tried && waited >= steal_ticks) {
+                tried = true;
+                uint32_t c = __hip_atomic_load(their_claim, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                while (c != claimed) {
+                    uint32_t expected = c;
+                    if (__hip_atomic_compare_exchange_strong(their_claim, &expected, stolen,
+                                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)) {
+                        outcome = kStole;
+                        break;
+                    }
+                    c = expected;
+                }
+                if (outcome == kStole)
+                    break;
+            }
+            if (waited >= kSafetyTicks) {
+                outcome = kLost;
+                break;
+            }
             __builtin_amdgcn_s_sleep(2);
-            ++spins;
         }
     }
-    const bool timed_out = __builtin_amdgcn_readfirstlane(spins) >= kSpinLimit;
+    outcome = __builtin_amdgcn_readfirstlane(outcome);
+    if (outcome != kGot)
+        return outcome;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -172,17 +286,21 @@ __device__ __forceinline__ bool pair_exchange(float *mine, float *theirs, float 
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // the partner's values are read and zeroed: clear its flag (the next use
-    // of this area is a later kernel on the stream)
-    if (!timed_out && lane == 0)
+    // the partner's values are read and zeroed, and it has published its
+    // last word for this call: clear its flag and its claim
+    if (lane == 0) {
         __hip_atomic_store(their_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return !timed_out;
+        __hip_atomic_store(their_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return kGot;
 }
 
 // Q: the ckv cache type (kvrc_cache_dtype: 0 bf16, 1 int8, 2 E4M3FN).
+// steal_ticks, stall_ticks: a.steal_us, a.stall_us in ticks of the device's
+// wall clock (s_memrealtime).
 template <int Q>
 __global__ __launch_bounds__(kThreads)
-void mla_kv_head_kernel(MlaKvHeadArgs a)
+void mla_kv_head_kernel(MlaKvHeadArgs a, uint32_t steal_ticks, uint32_t stall_ticks)
 {
     constexpr int kEsz = Q == 0 ? 2 : 1;        // bytes per ckv element
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -201,29 +319,41 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     if (pair >= npairs)
         return;                               // padding of the grid: both halves leave
     const int64_t row0 = pair * kRows;
-    const bool rope_wave = half == 1 && wn == 1;         // columns 432..575 of the output
-    const int ntn = rope_wave ? kNt - kRopeTiles : kNt;  // tiles holding kv (not rope) columns
 
-    // ---- direct global -> LDS loads ---------------------------------------
-    // A 1 KiB block holds 16 rows of 64 bytes (one K step); lane l writes
-    // byte 16 l: row 16 b + l / 4, slot l % 4, i.e. piece (l % 4) ^ swz(row)
-    // of that row. x block b = token rows 16 b .. +16 (rows past T read row
-    // T - 1: valid memory, results dropped); W block b = rows 16 b .. +16 of
-    // this half of W.
-    const uint16_t *xsrc[kXBlocks];
-#pragma unroll
-    for (int i = 0; i < kXBlocks; ++i) {
-        const int r = 16 * (kXBlocks * wave + i) + (lane >> 2);
-        int64_t t = row0 + r;
-        t = t < T ? t : T - 1;
-        xsrc[i] = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
+    // ---- workspace: float sums[npairs][2][256], float maxima[npairs][2][256]
+    // (quantised ckv only), uint32 flags[npairs][2], uint32 claims[npairs][2]
+    float *const part = reinterpret_cast<float *>(a.workspace);
+    uint32_t *const flags = reinterpret_cast<uint32_t *>(part + npairs * 4 * kRows);
+    uint32_t *const claims = flags + npairs * 2;
+    auto area = [&](int k, int h) { return part + ((k * npairs + pair) * 2 + h) * kRows; };
+    uint32_t *const ctl = reinterpret_cast<uint32_t *>(smem + kCtlOff);
+
+    // ---- claim this half for the call (settled after the first K loop) ----
+    // (left unset outside wavefront 0, lane 0, the only lane that reads it:
+    // no merge of values at the end of the branch, which would wait for the
+    // atomics here)
+    ClaimStart claim;
+    if (wave == 0 && lane == 0) {
+        if (half == 1 && stall_ticks) {                 // test only
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__builtin_amdgcn_s_memrealtime() - t0 < stall_ticks)
+                __builtin_amdgcn_s_sleep(8);
+        }
+        claim = claim_begin(claims + pair * 2 + half, flags + pair * 2 + half, a.tag);
     }
-    const uint16_t *wsrc[kMaxWBlocks];
-#pragma unroll
-    for (int i = 0; i < kMaxWBlocks; ++i) {
-        const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
-        wsrc[i] = a.w + (int64_t)(kHalfCols * half + r) * He + ((lane & 3) ^ swz(r)) * 8;
-    }
+
+    // Passes: 0 = this half, its partials exchanged with the partner; after a
+    // takeover (kStole) 1 = the partner's half, then 2 = this half again
+    // (the accumulators hold one half at a time). Every pass runs the same
+    // code on the same operands, so a half's outputs are the same bits
+    // whichever workgroup computes them.
+    auto run_pass = [&](const int hh, const int pass) __attribute__((always_inline)) -> int {
+    // Each copy of the pass forms its per-lane values from its own reading
+    // of the lane index, so that the copy after a takeover neither shares
+    // nor prolongs the registers of the first.
+    int lane_v = tid & 63;
+    asm volatile("" : "+v"(lane_v));
+    const int lane = lane_v;
     // The cache slots of the rows this wavefront scatters (rows wave + 8 i,
     // i < 32) are fetched now, lane i holding row i's: their latency hides
     // behind the K loop instead of preceding each row's stores. With the
@@ -247,6 +377,29 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
     unsigned char *const xdst = smem + kXRing + wave * kXBlocks * 1024;  // + stage * kStageA
     unsigned char *const wdst = smem + wb0 * 1024;               // + stage * kStageB + i KiB
+
+    const bool rope_wave = hh == 1 && wn == 1;           // columns 432..575 of the output
+    const int ntn = rope_wave ? kNt - kRopeTiles : kNt;  // tiles holding kv (not rope) columns
+    // ---- direct global -> LDS loads ---------------------------------------
+    // A 1 KiB block holds 16 rows of 64 bytes (one K step); lane l writes
+    // byte 16 l: row 16 b + l / 4, slot l % 4, i.e. piece (l % 4) ^ swz(row)
+    // of that row. x block b = token rows 16 b .. +16 (rows past T read row
+    // T - 1: valid memory, results dropped); W block b = rows 16 b .. +16 of
+    // the pass's half of W.
+    const uint16_t *xsrc[kXBlocks];
+#pragma unroll
+    for (int i = 0; i < kXBlocks; ++i) {
+        const int r = 16 * (kXBlocks * wave + i) + (lane >> 2);
+        int64_t t = row0 + r;
+        t = t < T ? t : T - 1;
+        xsrc[i] = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
+    }
+    const uint16_t *wsrc[kMaxWBlocks];
+#pragma unroll
+    for (int i = 0; i < kMaxWBlocks; ++i) {
+        const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
+        wsrc[i] = a.w + (int64_t)(kHalfCols * hh + r) * He + ((lane & 3) ^ swz(r)) * 8;
+    }
 
     f32x4 acc[kMt][kNt];
 #pragma unroll
@@ -374,7 +527,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     float g[kNt][4];
 #pragma unroll
     for (int n = 0; n < kNt; ++n) {
-        const int col = kHalfCols * half + kWaveCols * wn + 16 * n + cq;
+        const int col = kHalfCols * hh + kWaveCols * wn + 16 * n + cq;
         const uint2 gw = *reinterpret_cast<const uint2 *>(a.gamma + (col < kNorm ? col : 0));
         g[n][0] = alpha * bf16_lo(gw.x); g[n][1] = alpha * bf16_hi(gw.x);
         g[n][2] = alpha * bf16_lo(gw.y); g[n][3] = alpha * bf16_hi(gw.y);
@@ -418,12 +571,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     }
     __syncthreads();
 
-    // ---- swap the per-row partials with the other half of the pair --------
-    // workspace: float sums[npairs][2][256], float maxima[npairs][2][256]
-    // (quantised ckv only), then uint32 flags[npairs][2].
-    float *const part = reinterpret_cast<float *>(a.workspace);
-    uint32_t *const flags = reinterpret_cast<uint32_t *>(part + npairs * 4 * kRows);
-    auto area = [&](int k, int h) { return part + ((k * npairs + pair) * 2 + h) * kRows; };
+    // ---- the per-row partials of both halves ------------------------------
     if (wave == 0) {
         float p[4], q[4], p2[4], q2[4];
 #pragma unroll
@@ -431,20 +579,62 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             p[j] = red[4 * lane + j] + red[kRows + 4 * lane + j];
             p2[j] = Q != 0 ? fmaxf(red_max[4 * lane + j], red_max[kRows + 4 * lane + j]) : 0.0f;
         }
-        const bool ok = pair_exchange<Q != 0>(area(0, half), area(0, 1 - half), area(1, half),
-                                              area(1, 1 - half), flags + pair * 2 + half,
-                                              flags + pair * 2 + (1 - half), p, p2, q, q2, lane);
-        // the same order in both halves: the sum of columns 0..287 first
+        int st = kGot;
+        if (pass == 0) {
+            bool taken = false;
+            if (lane == 0)
+                taken = claim_settle(claim, claims + pair * 2 + half, flags + pair * 2 + half,
+                                     a.tag, a.err);
+            if (__builtin_amdgcn_readfirstlane((int)taken)) {
+                st = kExit;            // the partner took this half over
+            } else {
+                st = pair_exchange<Q != 0>(area(0, hh), area(0, 1 - hh), area(1, hh),
+                                           area(1, 1 - hh), flags + pair * 2 + hh,
+                                           flags + pair * 2 + (1 - hh),
+                                           claims + pair * 2 + (1 - hh), a.tag, steal_ticks,
+                                           p, p2, q, q2, lane);
+                if (st == kStole && lane == 0 && a.steals)
+                    atomicAdd(a.steals, 1);
+                if (st == kLost && lane == 0 && a.err)
+                    atomicAdd(a.err, 1);
+            }
+        } else {
+            // after a takeover both areas of the pair are this workgroup's:
+            // pass 1 keeps the partner's partials in the partner's areas,
+            // next to this half's, published in pass 0 (each lane rereads
+            // only the rows it wrote)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sums[4 * lane + j] = half == 0 ? p[j] + q[j] : q[j] + p[j];
-            if constexpr (Q != 0)
-                maxs[4 * lane + j] = fmaxf(p2[j], q2[j]);
+            for (int j = 0; j < 4; ++j) {
+                if (pass == 1) {
+                    __hip_atomic_store(area(0, hh) + 4 * lane + j, p[j], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    if constexpr (Q != 0)
+                        __hip_atomic_store(area(1, hh) + 4 * lane + j, p2[j], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                q[j] = __hip_atomic_load(area(0, 1 - hh) + 4 * lane + j, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+                q2[j] = Q != 0 ? __hip_atomic_load(area(1, 1 - hh) + 4 * lane + j,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.0f;
+            }
         }
-        if (!ok && lane == 0 && a.err)
-            atomicAdd(a.err, 1);
+        if (st == kGot) {
+            // the same order in both halves: the sum of columns 0..287 first
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sums[4 * lane + j] = hh == 0 ? p[j] + q[j] : q[j] + p[j];
+                if constexpr (Q != 0)
+                    maxs[4 * lane + j] = fmaxf(p2[j], q2[j]);
+            }
+        }
+        if (lane == 0)
+            ctl[1] = (uint32_t)st;
     }
     __syncthreads();
+    const int outcome = (int)ctl[1];
+    if (outcome != kGot)
+        return outcome;                       // nothing written by this pass
 
     unsigned char *stage = smem;
     // 1 / rms of row r (the same expression wherever it is needed) and, for a
@@ -542,8 +732,8 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
     constexpr int kCkvPieces0 = kHalfCols * kEsz / 16;           // 36 (18)
     constexpr int kCkvPieces1 = (kNorm - kHalfCols) * kEsz / 16;  // 28 (14)
     constexpr int kKPieces = kRope * 2 / 16;                      // 8
-    const int nckv = half == 0 ? kCkvPieces0 : kCkvPieces1;
-    const int npieces = half == 0 ? kCkvPieces0 : kCkvPieces1 + kKPieces;
+    const int nckv = hh == 0 ? kCkvPieces0 : kCkvPieces1;
+    const int npieces = hh == 0 ? kCkvPieces0 : kCkvPieces1 + kKPieces;
     const int64_t ckv_row = kNorm * kEsz;
     const bool buf = a.cache_rows * ckv_row <= (int64_t)UINT32_MAX;
     const __amdgpu_buffer_rsrc_t ckv_rsrc =
@@ -562,12 +752,12 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
                                          (int)(my_slot >> 32), i) << 32) |
                                     (uint32_t)__builtin_amdgcn_readlane((int)my_slot, i));
         if (v < 0 || v >= a.cache_rows) {
-            if (half == 0 && v != -1 && lane == 0 && a.err)
+            if (hh == 0 && v != -1 && lane == 0 && a.err)
                 atomicAdd(a.err, 1);
             continue;
         }
         if constexpr (Q != 0) {
-            if (half == 0 && lane == 63)
+            if (hh == 0 && lane == 63)
                 a.ckv_scale[v] = row_scale_of(r);
         }
         if (lane < npieces) {
@@ -575,7 +765,7 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             const u32x4 w = {cv.x, cv.y, cv.z, cv.w};
             // lanes below nckv write the ckv row piece, the others the k row
             // (two stores, each with one descriptor for the whole wavefront)
-            const int64_t ckv_off = v * ckv_row + kHalfCols * kEsz * half + lane * 16;
+            const int64_t ckv_off = v * ckv_row + kHalfCols * kEsz * hh + lane * 16;
             const int64_t k_off = v * kRope * 2 + (lane - nckv) * 16;
             if (lane < nckv) {
                 if (buf)
@@ -594,6 +784,37 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
             }
         }
     }
+    __syncthreads();                          // the staged rows are read: LDS reused
+    return kGot;
+    };   // run_pass
+
+    if (run_pass(half, 0) != kStole)
+        return;
+    // The partner's half, then this half again. (A loop, so that the rarely
+    // used second copy of the pass is the only one besides the first.)
+#pragma nounroll
+    for (int pass = 1; pass <= 2; ++pass)
+        run_pass(pass == 1 ? 1 - half : half, pass);
+
+    // ---- after a takeover the pair's areas, this half's flag and its claim
+    // are this workgroup's to clear (the partner resets its own claim word
+    // when it starts and finds it taken) -----------------------------------
+    if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    __hip_atomic_store(area(k, h) + 4 * lane + j, 0.0f, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            __hip_atomic_store(flags + pair * 2 + half, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(claims + pair * 2 + half, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 }  // namespace
@@ -601,12 +822,34 @@ void mla_kv_head_kernel(MlaKvHeadArgs a)
 int64_t mla_kv_head_workspace_bytes(int64_t T)
 {
     const int64_t npairs = T > 0 ? (T + kRows - 1) / kRows : 0;
-    return npairs * (4 * kRows * 4 + 2 * 4);
+    return npairs * (4 * kRows * 4 + 4 * 4);
+}
+
+// Ticks per microsecond of the current device's wall clock (the counter the
+// kernel's waits read), queried once per device.
+uint32_t wall_ticks_per_us()
+{
+    static std::atomic<uint32_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 100;
+    uint32_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz < 1000)
+            khz = 100000;                     // the 100 MHz of gfx9 parts
+        v = (uint32_t)(khz / 1000);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)
 {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    const uint32_t tpu = wall_ticks_per_us();
+    const uint32_t steal_ticks = a.steal_us * tpu, stall_ticks = a.stall_us * tpu;
     const int64_t npairs = (a.T + kRows - 1) / kRows;
     const int64_t grid = 16 * ((npairs + 7) / 8);   // pairs in groups of 8: b and b + 8
     const void *fn = a.ckv == 1 ? reinterpret_cast<const void *>(mla_kv_head_kernel<1>)
@@ -617,13 +860,13 @@ hipError_t launch_mla_kv_head(const MlaKvHeadArgs &a, hipStream_t stream)
         return e;
     if (a.ckv == 1)
         hipLaunchKernelGGL(mla_kv_head_kernel<1>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
-                           stream, a);
+                           stream, a, steal_ticks, stall_ticks);
     else if (a.ckv == 2)
         hipLaunchKernelGGL(mla_kv_head_kernel<2>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
-                           stream, a);
+                           stream, a, steal_ticks, stall_ticks);
     else
         hipLaunchKernelGGL(mla_kv_head_kernel<0>, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes,
-                           stream, a);
+                           stream, a, steal_ticks, stall_ticks);
     return hipGetLastError();
 }
 

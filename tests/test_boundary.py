@@ -157,7 +157,7 @@ def test_norm_validation(over, want):
 
 M = {name: (i + 40) << 32 for i, name in enumerate(
     ["x", "w", "gamma", "cos", "sin", "slot", "kc", "ckv", "err", "ws", "sc"])}
-WS_300 = 2 * (4 * 256 * 4 + 2 * 4)      # 300 tokens: two pairs of workgroups
+WS_300 = 2 * (4 * 256 * 4 + 4 * 4)      # 300 tokens: two pairs of workgroups
 
 
 def mla(**over):
@@ -201,12 +201,12 @@ def test_mla_blk_validation(over, want):
 
 def test_mla_workspace_bytes():
     """One pair of workgroups per 256 tokens: 256 partial sums and 256
-    partial maxima per half, and two flags."""
+    partial maxima per half, two flags and two claim words."""
     f = k.lib().kvrc_mla_kv_head_workspace_bytes
     assert f(0) == 0
-    assert f(1) == f(256) == 4104
-    assert f(257) == 2 * 4104
-    assert f(32768) == 128 * 4104
+    assert f(1) == f(256) == 4112
+    assert f(257) == 2 * 4112
+    assert f(32768) == 128 * 4112
     assert f(-1) == -1 and f(1 << 31) == -1
     assert f(300) == WS_300
 
@@ -322,6 +322,30 @@ def test_qsa_validation_at_the_caps(over):
 ])
 def test_selftest_e4m3_validation(x, code, n, want):
     assert k.lib().kvrc_selftest_e4m3(x, code, n, None) == want
+
+
+def test_selftest_mla_stalled_validation():
+    """The stalled selftest takes the MLA head's checks, plus its own."""
+    L = k.lib()
+
+    def call(**over):
+        a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
+                 slot=M["slot"], kc=M["kc"], ckv=M["ckv"], sc=None, T=300, He=7168, NB=64,
+                 BS=128, dt=0, eps=1e-6, ws=M["ws"], wsb=WS_300, err=None, stall=100,
+                 steals=None, stream=None)
+        a.update(over)
+        return L.kvrc_selftest_mla_kv_head_stalled(
+            a["x"], a["w"], a["gamma"], a["alpha"], a["cos"], a["sin"], a["slot"], a["kc"],
+            a["ckv"], a["sc"], a["T"], a["He"], a["NB"], a["BS"], a["dt"], a["eps"], a["ws"],
+            a["wsb"], a["err"], a["stall"], a["steals"], a["stream"])
+
+    assert call(stall=-1) == SHAPE
+    assert call(stall=10 ** 7 + 1) == SHAPE
+    assert call(steals=M["err"] + 2) == ALIGN
+    assert call(He=16) == SHAPE
+    assert call(wsb=WS_300 - 1) == WORKSPACE
+    assert call(ws=M["x"]) == ALIAS
+    assert call(T=0) == OK
 
 
 @pytest.mark.parametrize("wg,threads,want", [

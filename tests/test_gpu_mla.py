@@ -641,3 +641,102 @@ def test_mla_all_tokens_skipped(kind):
     assert int(err.item()) == 0
     for name, spec in case["caches"].items():
         np.testing.assert_array_equal(got[name], spec.numpy(), err_msg=name)
+
+
+# ---------------------------------------------------------------------------
+# The pair exchange without any co-residency assumption
+# ---------------------------------------------------------------------------
+
+def _mla_device_inputs(case):
+    return (dbf(case["x"]), dbf(case["w"]), dbf(case["gamma"]), dbf(case["cos"]),
+            dbf(case["sin"]), torch.from_numpy(case["slot_mapping"]).to(DEV))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_mla_takeover_gives_the_same_bits(kind):
+    """The second workgroup of every pair is held back (3 ms) before it
+    claims its half: the first one finds neither partials nor a claim, takes
+    the partner's half over and computes both halves itself; the outputs are
+    bit-identical to the paired computation, every pair was taken over, the
+    partner left without writing, and the workspace ends zero."""
+    say(f"[mla] takeover {kind}")
+    case = gen.mla_kv_head_case(560, B=1, S=2305, He=256, num_blocks=160, block_size=16,
+                                slot_kind="random", skip_frac=0.05, ckv_dtype=kind)
+    want = run_mla_gpu(case)
+    T = case["x"].shape[0]
+    caches = {n: dev_cache(spec.numpy()) for n, spec in case["caches"].items()}
+    ws = new_workspace(T)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    steals = torch.zeros(1, dtype=torch.int32, device=DEV)
+    k.kvrc_mla_kv_head_paged(*_mla_device_inputs(case), caches["k_cache"], caches["ckv_cache"],
+                             caches.get("ckv_scale"), workspace=ws, alpha_kv=case["alpha"],
+                             eps=case["eps"], err_count=err, _stall_us=3000, _steals=steals)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+    assert int(err.item()) == 0
+    assert int(steals.item()) == -(-T // 256), "every pair's second half was taken over"
+    got = {n: host_cache(t) for n, t in caches.items()}
+    for n in want:
+        np.testing.assert_array_equal(got[n], want[n], err_msg=n)
+    compare_mla(case, got)
+
+
+def test_mla_overlapping_calls_on_two_streams():
+    """Two MLA head calls in flight at once on two streams, each with its own
+    workspace and with more workgroups than the chip holds (1280 each): pairs
+    may be split by the other call's workgroups. Both end with err_count 0,
+    workspaces zero, and outputs bit-identical to the same calls made one
+    after the other (which meet the oracle bound)."""
+    say("[mla] two overlapping calls, 1280 workgroups each")
+    cases = [gen.mla_kv_head_case(541, B=4, S=40960, He=64, num_blocks=1400, block_size=128,
+                                  slot_kind="random", skip_frac=0.01),
+             gen.mla_kv_head_case(542, B=4, S=40960, He=64, num_blocks=1400, block_size=128,
+                                  slot_kind="random", skip_frac=0.01, ckv_dtype="int8")]
+    want = [run_mla_gpu(c) for c in cases]
+    compare_mla(cases[0], want[0])
+    ins = [_mla_device_inputs(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        caches = [{n: dev_cache(spec.numpy()) for n, spec in c["caches"].items()} for c in cases]
+        ws = [new_workspace(c["x"].shape[0]) for c in cases]
+        errs = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in cases]
+        torch.cuda.synchronize()
+        for c, i, ca, w, e, s in zip(cases, ins, caches, ws, errs, streams):
+            k.kvrc_mla_kv_head_paged(*i, ca["k_cache"], ca["ckv_cache"], ca.get("ckv_scale"),
+                                     workspace=w, alpha_kv=c["alpha"], eps=c["eps"],
+                                     err_count=e, stream=s)
+        torch.cuda.synchronize()
+        for c, ca, w, e, wt in zip(cases, caches, ws, errs, want):
+            assert int(e.item()) == 0
+            assert int(torch.count_nonzero(w)) == 0, "workspace not left zero"
+            for n, t in ca.items():
+                np.testing.assert_array_equal(host_cache(t), wt[n], err_msg=f"rep {rep} {n}")
+        say(f"[mla] overlap rep {rep}: both calls equal the sequential ones")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+def test_mla_workspace_left_dirty_is_counted_and_ignored(kind):
+    """Flags and claim words left in the workspace by another call (written
+    here from the host: each call marks its own with a fresh tag, so these
+    can never match) are counted in err_count, and the outputs are still the
+    clean call's."""
+    case = gen.mla_kv_head_case(543, B=1, S=700, He=128, num_blocks=64, block_size=16,
+                                slot_kind="random", ckv_dtype=kind)
+    want = run_mla_gpu(case)
+    T = case["x"].shape[0]
+    npairs = -(-T // 256)
+    ws = new_workspace(T)
+    words = ws.view(torch.int32)
+    flags0 = npairs * 4 * 256                       # after the sums and maxima areas
+    words[:flags0] = 0x7F7F7F7F                     # stale partials
+    words[flags0:flags0 + 2 * npairs] = 0x7FFFFFFF   # flags of no call (tags are below 2^30)
+    words[flags0 + 2 * npairs:flags0 + 4 * npairs] = -1   # claim words of no call
+    caches = {n: dev_cache(spec.numpy()) for n, spec in case["caches"].items()}
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    k.kvrc_mla_kv_head_paged(*_mla_device_inputs(case), caches["k_cache"], caches["ckv_cache"],
+                             caches.get("ckv_scale"), workspace=ws, alpha_kv=case["alpha"],
+                             eps=case["eps"], err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) > 0, "a workspace that was not zero must be reported"
+    for n, t in caches.items():
+        np.testing.assert_array_equal(host_cache(t), want[n], err_msg=n)
