@@ -13,9 +13,10 @@ Measurement:
   * one eager launch per buffer set first (setup: loads the library and
     checks every argument set); then exactly W warm-up launches in one HIP
     graph and exactly K timed launches in another, continuing the rotation;
-  * the timed graph is enqueued behind a spin kernel, so that the whole
-    graph is submitted before its first launch starts; HIP events on the
-    launch stream bracket its replay: ms_per_step = elapsed / K,
+  * a spin kernel, the warm-up graph and the timed graph are enqueued back
+    to back, so that both graphs are submitted before the first launch starts
+    and the warm-up launches lead straight into the timed ones; HIP events on
+    the launch stream bracket the timed replay: ms_per_step = elapsed / K,
     value = tokens / step time, and the kernel's average launch duration is
     the same elapsed / K (one launch per step, back to back);
   * roofline: algorithmic bytes (or flops) per launch / average launch
@@ -770,10 +771,13 @@ def main(argv=None):
             for i in range(W, W + K):
                 launch(case, sets[i % R])
         torch.cuda.synchronize()
+        # spin kernel, then the warm-up graph right before the timed one: the
+        # warm-up launches run back to back into the timed region (the GPU is
+        # at its working clock when the first timed launch starts)
+        _gate(stream)
         if W:
             with torch.cuda.stream(stream):
                 gw.replay()
-        _gate(stream)
         e0.record(stream)
         with torch.cuda.stream(stream):
             g.replay()

@@ -298,14 +298,27 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t nb_max)
+// Work items are laid out XCD by XCD: workgroup g runs item
+// (g mod 8) * per_xcd + g / 8 (round-robin dispatch puts workgroup g on XCD
+// g mod 8), so each XCD takes a contiguous run of (sequence, block) items
+// and touches one contiguous stretch of the raw keys (an eighth of the
+// sequences) instead of a slice of every sequence: fewer pages per XCD's
+// address translation cache and its L2 (measured 7.24 -> 7.11 us per call
+// on the 32 x 2048-token workload).
+constexpr uint32_t kXcds = 8;
+
+__global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t nb_max,
+                                                              uint32_t per_xcd, uint32_t items)
 {
     constexpr int64_t Di = kWaveDi;
     constexpr int kPairs = kWaveDi / 2;              // = 64 lanes
     const int lane = threadIdx.x;
+    const uint32_t item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (item >= items)
+        return;
     const uint32_t per = (uint32_t)(nb_max + 1);
-    const int64_t n = blockIdx.x / per;
-    const int64_t j = blockIdx.x % per;
+    const int64_t n = item / per;
+    const int64_t j = item % per;
     const int64_t K = a.key_length[a.klc == 1 ? 0 : n];
     const int64_t kbs = a.kbs, L = a.L;
     if (K < L || K / kbs > a.Bcap) {
@@ -460,9 +473,10 @@ __global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t
 hipError_t launch_wave(const QsaArgs &a, hipStream_t stream)
 {
     const int64_t nb_max = (a.kbs - 1 + a.L) / a.kbs;
-    const int64_t grid = a.N * (nb_max + 1);
-    hipLaunchKernelGGL(qsa_prepare_wave_kernel, dim3((uint32_t)grid), dim3(64), 0, stream, a,
-                       nb_max);
+    const int64_t items = a.N * (nb_max + 1);           // < 2^31 (checked by the caller)
+    const int64_t per_xcd = (items + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(qsa_prepare_wave_kernel, dim3((uint32_t)(per_xcd * kXcds)), dim3(64), 0,
+                       stream, a, nb_max, (uint32_t)per_xcd, (uint32_t)items);
     return hipGetLastError();
 }
 
