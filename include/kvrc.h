@@ -297,6 +297,29 @@ int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const vo
                                    int32_t *err_count, hipStream_t stream);
 
 /*
+ * kvrc_mla_kv_head_paged_noalloc - kvrc_mla_kv_head_paged for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, arguments,
+ * results and status codes, without the workspace arguments. The workspace
+ * is a static device array of the library, one per device (2 MiB, held until
+ * the process ends), so T may be at most 2^17 = 131072 tokens
+ * (KVRC_ERR_WORKSPACE beyond). The call allocates nothing: the array's
+ * address is looked up once per device, on the first call with that device
+ * current (KVRC_ERR_HIP if that fails), and each call first clears its part
+ * of the array with a small kernel on `stream`. Every call on a device
+ * shares that device's array: calls that overlap on one device (different
+ * streams, or host threads without ordering) race and their outputs are
+ * undefined; order them on one stream, or use kvrc_mla_kv_head_paged with
+ * separate workspaces.
+ */
+int32_t kvrc_mla_kv_head_paged_noalloc(const void *x, const void *w_dkv_kr, const void *gamma,
+                                       float alpha_kv, const void *cos, const void *sin,
+                                       const int64_t *slot_mapping, void *k_cache,
+                                       void *ckv_cache, float *ckv_scale, int64_t T, int64_t He,
+                                       int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                                       float eps, int32_t *err_count, hipStream_t stream);
+
+/*
  * qsa_prepare - one index key per complete key block, for sparse attention.
  *
  * Source: openvino.opset17.qsa_prepare (description and Parameters list).

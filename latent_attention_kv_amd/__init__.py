@@ -35,7 +35,8 @@ __all__ = ["kvrc_paged_norm_rope_cache", "kvrc_paged_blk_norm_rope_cache",
            "kvrc_mla_kv_head_paged_blk",
            "qsa_prepare", "qsa_select_topk", "kvrc_selftest_arith", "kvrc_selftest_recip",
            "kvrc_selftest_e4m3", "kvrc_selftest_empty", "kvrc_selftest_copy",
-           "kvrc_selftest_mla_kv_head_stalled",
+           "kvrc_selftest_mla_kv_head_stalled", "kvrc_mla_kv_head_paged_noalloc",
+           "MLA_NOALLOC_MAX_TOKENS",
            "select_blocks_capacity", "KvrcError", "lib", "LIB_PATH", "CACHE_BF16", "CACHE_INT8", "CACHE_FP8_E4M3",
            "EXPORTED_SYMBOLS"]
 
@@ -43,13 +44,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvrc.so"
 CACHE_BF16 = 0
 CACHE_INT8 = 1
 CACHE_FP8_E4M3 = 2
+# largest T of kvrc_mla_kv_head_paged_noalloc (its static workspace)
+MLA_NOALLOC_MAX_TOKENS = 1 << 17
 EXPORTED_SYMBOLS = ("kvrc_status_string", "kvrc_version", "kvrc_paged_norm_rope_cache",
                     "kvrc_paged_blk_norm_rope_cache", "kvrc_norm_rope_cache",
                     "kvrc_mla_kv_head_workspace_bytes", "kvrc_mla_kv_head_paged",
                     "kvrc_mla_kv_head_paged_blk", "qsa_prepare", "qsa_select_topk",
                     "kvrc_selftest_arith", "kvrc_selftest_recip", "kvrc_selftest_e4m3",
                     "kvrc_selftest_empty", "kvrc_selftest_copy",
-                    "kvrc_selftest_mla_kv_head_stalled")
+                    "kvrc_selftest_mla_kv_head_stalled", "kvrc_mla_kv_head_paged_noalloc")
 
 _lib = None
 
@@ -108,6 +111,9 @@ def lib() -> ctypes.CDLL:
     L.kvrc_selftest_mla_kv_head_stalled.argtypes = [P, P, P, F, P, P, P, P, P, P, I64, I64, I64,
                                                     I64, I32, F, P, I64, P, I64, P, P]
     L.kvrc_selftest_mla_kv_head_stalled.restype = I32
+    L.kvrc_mla_kv_head_paged_noalloc.argtypes = [P, P, P, F, P, P, P, P, P, P, I64, I64, I64,
+                                                 I64, I32, F, P, P]
+    L.kvrc_mla_kv_head_paged_noalloc.restype = I32
     _lib = L
     return L
 
@@ -329,6 +335,36 @@ def kvrc_mla_kv_head_paged(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache, 
                                       _ptr(workspace), ws_bytes, _err_ptr(err_count),
                                       _stream(stream))
     _check(st, "kvrc_mla_kv_head_paged")
+
+
+def kvrc_mla_kv_head_paged_noalloc(x, w_dkv_kr, gamma, cos, sin, slot_mapping, k_cache,
+                                   ckv_cache, ckv_scale=None, *, alpha_kv=1.0, eps=1e-6,
+                                   err_count=None, stream=None):
+    """kvrc_mla_kv_head_paged without a workspace argument: the library's
+    static device workspace serves (T <= MLA_NOALLOC_MAX_TOKENS); the call
+    allocates nothing. Calls that overlap on one device race."""
+    _need(x, "x", _BF16, 2)
+    _need(w_dkv_kr, "w_dkv_kr", _BF16, 2)
+    _need(gamma, "gamma", _BF16, 1)
+    _need(cos, "cos", _BF16, 2)
+    _need(sin, "sin", _BF16, 2)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    NB, BS, dt = _mla_caches(k_cache, ckv_cache, ckv_scale)
+    T, He = x.shape
+    if tuple(w_dkv_kr.shape) != (576, He):
+        raise ValueError("w_dkv_kr must be [576, He]")
+    if tuple(gamma.shape) != (512,):
+        raise ValueError("gamma must be [512]")
+    if tuple(cos.shape) != (T, 64) or tuple(sin.shape) != (T, 64):
+        raise ValueError("cos / sin must be [T, 64]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have T entries")
+    st = lib().kvrc_mla_kv_head_paged_noalloc(_ptr(x), _ptr(w_dkv_kr), _ptr(gamma),
+                                              float(alpha_kv), _ptr(cos), _ptr(sin),
+                                              _ptr(slot_mapping), _ptr(k_cache), _ptr(ckv_cache),
+                                              _ptr(ckv_scale), T, He, NB, BS, dt, float(eps),
+                                              _err_ptr(err_count), _stream(stream))
+    _check(st, "kvrc_mla_kv_head_paged_noalloc")
 
 
 def kvrc_mla_kv_head_paged_blk(x, w_dkv_kr, gamma, cos, sin, block_index, k_cache, ckv_cache,

@@ -221,6 +221,53 @@ namespace {
 // Shared body of the two MLA head entry points: index = the slot mapping
 // [T] (index_count = T, B = S = 0) or the block index
 // [B * ceil(S / block_size)] (index_count entries, T = B * S).
+// Zero `bytes` bytes (a multiple of 16) at p, 16 bytes per thread: a kernel
+// rather than hipMemsetAsync, so that the clear also replays correctly in a
+// captured HIP graph.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4 *p, int64_t n16)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_fill(void *p, int64_t bytes, hipStream_t stream)
+{
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((uint32_t)((n16 + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<uint4 *>(p), n16);
+    return hipGetLastError();
+}
+
+// Static device scratch of the allocation-free MLA head entry point: the
+// workspace of up to kNoAllocMaxTokens tokens (2^17 tokens: 512 pairs of
+// workgroups, 4112 bytes each, 2 MiB), one copy per device, held until the
+// process ends. In host code `scratch` is only a stand-in for the symbol:
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kNoAllocMaxTokens = (int64_t)1 << 17;
+constexpr int64_t kNoAllocScratchBytes = (kNoAllocMaxTokens / 256) * (4 * 256 * 4 + 4 * 4);
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch` (nullptr if HIP
+// reports an error). The first call on a device looks it up, with that
+// device current; two threads racing on the first call store the same value.
+void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 // Tag of an MLA head call, in [1, 2^30): the kernel marks the pair flags and
 // claim words of the workspace with it, so that words left by another call
 // never match this one's.
@@ -240,7 +287,8 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
                    int64_t S, void *k_cache, void *ckv_cache, float *ckv_scale, int64_t T,
                    int64_t He, int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
                    float eps, void *workspace, int64_t workspace_bytes, int32_t *err_count,
-                   hipStream_t stream, uint32_t stall_us = 0, int32_t *steals = nullptr)
+                   hipStream_t stream, uint32_t stall_us = 0, int32_t *steals = nullptr,
+                   bool static_scratch = false)
 {
     if (ckv_dtype != KVRC_CACHE_BF16 && ckv_dtype != KVRC_CACHE_INT8 &&
         ckv_dtype != KVRC_CACHE_FP8_E4M3)
@@ -261,10 +309,10 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     if (T == 0)
         return KVRC_OK;                       // empty input: caches untouched
     const int64_t wsbytes = kvrc::mla_kv_head_workspace_bytes(T);
-    if (workspace_bytes < wsbytes)
+    if (static_scratch ? wsbytes > kNoAllocScratchBytes : workspace_bytes < wsbytes)
         return KVRC_ERR_WORKSPACE;
     if (!x || !w_dkv_kr || !gamma || !cos || !sin || !index || !k_cache || !ckv_cache ||
-        !workspace)
+        (!static_scratch && !workspace))
         return KVRC_ERR_NULL;
     if (quant != (ckv_scale != nullptr))
         return KVRC_ERR_DTYPE;
@@ -276,13 +324,28 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     const Range in[] = {span(x, xbytes), span(w_dkv_kr, wbytes), span(gamma, 1024),
                         span(cos, csbytes), span(sin, csbytes), span(index, ibytes)};
     const Range out[] = {span(k_cache, kbytes), span(ckv_cache, cbytes), span(ckv_scale, sbytes),
-                         span(workspace, wsbytes), span(err_count, err_count ? 4 : 0)};
+                         span(workspace, static_scratch ? 0 : wsbytes),
+                         span(err_count, err_count ? 4 : 0)};
     for (const Range &o : out) {
         for (const Range &i : in)
             if (overlap(o, i))
                 return KVRC_ERR_ALIAS;
         for (const Range &o2 : out)
             if (&o2 != &o && overlap(o, o2))
+                return KVRC_ERR_ALIAS;
+    }
+    if (static_scratch) {
+        // the library's own array (looked up once per device; no
+        // allocation): a caller's buffer overlaps it only by pointing into it
+        workspace = scratch_address();
+        if (!workspace)
+            return KVRC_ERR_HIP;
+        const Range ws = span(workspace, wsbytes);
+        for (const Range &r : in)
+            if (overlap(ws, r))
+                return KVRC_ERR_ALIAS;
+        for (const Range &r : out)
+            if (overlap(ws, r))
                 return KVRC_ERR_ALIAS;
     }
     kvrc::MlaKvHeadArgs a;
@@ -312,6 +375,12 @@ int32_t mla_common(const void *x, const void *w_dkv_kr, const void *gamma, float
     a.stall_us = stall_us;
     a.steals = steals;
     (void)hipGetLastError();
+    if (static_scratch) {
+        // the array keeps the last call's contents: clear this call's part
+        const hipError_t e = launch_zero_fill(workspace, wsbytes, stream);
+        if (e != hipSuccess)
+            return KVRC_ERR_HIP;
+    }
     return launch_status(kvrc::launch_mla_kv_head(a, stream));
 }
 
@@ -343,6 +412,18 @@ int32_t kvrc_mla_kv_head_paged_blk(const void *x, const void *w_dkv_kr, const vo
     return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, block_index, true, B, S, k_cache,
                       ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
                       workspace, workspace_bytes, err_count, stream);
+}
+
+int32_t kvrc_mla_kv_head_paged_noalloc(const void *x, const void *w_dkv_kr, const void *gamma,
+                                       float alpha_kv, const void *cos, const void *sin,
+                                       const int64_t *slot_mapping, void *k_cache,
+                                       void *ckv_cache, float *ckv_scale, int64_t T, int64_t He,
+                                       int64_t num_blocks, int64_t block_size, int32_t ckv_dtype,
+                                       float eps, int32_t *err_count, hipStream_t stream)
+{
+    return mla_common(x, w_dkv_kr, gamma, alpha_kv, cos, sin, slot_mapping, false, 0, 0, k_cache,
+                      ckv_cache, ckv_scale, T, He, num_blocks, block_size, ckv_dtype, eps,
+                      nullptr, 0, err_count, stream, 0, nullptr, true);
 }
 
 int32_t kvrc_selftest_mla_kv_head_stalled(const void *x, const void *w_dkv_kr, const void *gamma,

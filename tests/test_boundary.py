@@ -324,6 +324,32 @@ def test_selftest_e4m3_validation(x, code, n, want):
     assert k.lib().kvrc_selftest_e4m3(x, code, n, None) == want
 
 
+def test_mla_noalloc_validation():
+    """The allocation-free MLA head: the MLA head's checks, T up to 2^17 (its
+    static workspace), and no workspace arguments."""
+    L = k.lib()
+
+    def call(**over):
+        a = dict(x=M["x"], w=M["w"], gamma=M["gamma"], alpha=1.0, cos=M["cos"], sin=M["sin"],
+                 slot=M["slot"], kc=M["kc"], ckv=M["ckv"], sc=None, T=300, He=7168, NB=64,
+                 BS=128, dt=0, eps=1e-6, err=None, stream=None)
+        a.update(over)
+        return L.kvrc_mla_kv_head_paged_noalloc(
+            a["x"], a["w"], a["gamma"], a["alpha"], a["cos"], a["sin"], a["slot"], a["kc"],
+            a["ckv"], a["sc"], a["T"], a["He"], a["NB"], a["BS"], a["dt"], a["eps"], a["err"],
+            a["stream"])
+
+    assert k.MLA_NOALLOC_MAX_TOKENS == 1 << 17
+    assert call(T=(1 << 17) + 1, He=64) == WORKSPACE
+    assert call(T=-1) == SHAPE
+    assert call(He=16) == SHAPE
+    assert call(x=None) == NULL
+    assert call(slot=M["slot"] + 4) == ALIGN
+    assert call(dt=1) == DTYPE
+    assert call(kc=M["x"] + 4096) == ALIAS
+    assert call(T=0) == OK and call(T=0, x=None) == OK
+
+
 def test_selftest_mla_stalled_validation():
     """The stalled selftest takes the MLA head's checks, plus its own."""
     L = k.lib()
