@@ -10,15 +10,16 @@ Measurement:
   * R independent buffer sets (inputs and caches) are rotated so that the
     touched bytes of R consecutive steps exceed the 256 MB Infinity Cache;
     every step therefore reads its inputs from HBM;
-  * one eager launch per buffer set first (setup: loads the library and
-    checks every argument set); then exactly W warm-up launches in one HIP
-    graph and exactly K timed launches in another, continuing the rotation;
-  * a spin kernel, the warm-up graph and the timed graph are enqueued back
-    to back, so that both graphs are submitted before the first launch starts
-    and the warm-up launches lead straight into the timed ones; HIP events on
-    the launch stream bracket the timed replay: ms_per_step = elapsed / K,
-    value = tokens / step time, and the kernel's average launch duration is
-    the same elapsed / K (one launch per step, back to back);
+  * one eager launch per buffer set first (setup: loads the library, checks
+    every argument set and measures the host's cost of a launch call); then
+    exactly W warm-up and exactly K timed launches, continuing the rotation;
+  * the launches are enqueued behind a spin kernel that lasts at least twice
+    their total host cost, so they are all submitted before the first one
+    starts and run back to back; HIP events on the launch stream bracket the
+    K timed launches: ms_per_step = elapsed / K, value = tokens / step time,
+    and the kernel's average launch duration is the same elapsed / K (one
+    launch per step); the line says whether the host did finish enqueuing
+    first (--timing graph replays two HIP graphs instead);
   * roofline: algorithmic bytes (or flops) per launch / average launch
     duration, against the MI355X HBM3E peak of 8 TB/s (or the bf16 dense
     matrix peak); rocprof_kernel_us repeats the per-dispatch duration
@@ -472,6 +473,22 @@ def ingest_profile(args) -> int:
         out[counter] = {"kib_per_dispatch": round(kib, 3), "dispatches": len(mine),
                         "copy_kib": round(cal, 3), "scale": round(factor, 5),
                         "bytes_per_dispatch": round(kib * 1024 * factor)}
+        # the bench's reference kernels in the same run: the empty kernel per
+        # grid shape (the fixed traffic of a launch) and the same-bytes copy
+        ref = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            if "empty_kernel" in r["Kernel_Name"]:
+                key = f"empty_kernel grid {r['Grid_Size']} x wg {r['Workgroup_Size']}"
+            elif "copy_kernel" in r["Kernel_Name"]:
+                key = f"copy_kernel grid {r['Grid_Size']}"
+            else:
+                continue
+            ref.setdefault(key, []).append(float(r["Counter_Value"]))
+        for key, v in ref.items():
+            out.setdefault("reference_kernel_traffic", {}).setdefault(key, {})[counter] = \
+                round(sum(v) / len(v) * 1024 * factor)
     out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_dispatch"] + \
         out["WRITE_SIZE"]["bytes_per_dispatch"]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -520,7 +537,14 @@ def ingest_profile(args) -> int:
                   f"{c['bytes_per_dispatch']} |")
     md += ["", f"Measured traffic per launch: {out['bytes_per_launch']} bytes "
                f"({out['bytes_per_launch'] / alg * 100:.1f} % of the algorithmic bytes); "
-               f"{out['bytes_per_launch'] / avg_s / 1e9:.1f} GB/s at the average duration.",
+               f"{out['bytes_per_launch'] / avg_s / 1e9:.1f} GB/s at the average duration."]
+    if out.get("reference_kernel_traffic"):
+        md += ["", "The same counters on the bench's reference kernels (bytes per dispatch, "
+                   "scaled alike):", "", "| kernel | FETCH_SIZE bytes | WRITE_SIZE bytes |",
+               "|---|---|---|"]
+        md += [f"| {key} | {v.get('FETCH_SIZE')} | {v.get('WRITE_SIZE')} |"
+               for key, v in sorted(out["reference_kernel_traffic"].items())]
+    md += [
            "", f"Kernel sources hash: {out['source_hash']}."]
     if bench_line:
         md += ["", "## bench.py line of the same run", "", "    " + bench_line]
@@ -688,7 +712,10 @@ def main(argv=None):
     ap.add_argument("--workload", default="prefill_paged", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--sets", type=int, default=0,
                     help="buffer sets rotated (0: enough to exceed 512 MB touched)")
-    ap.add_argument("--no-graph", action="store_true", help="launch from Python each step")
+    ap.add_argument("--timing", choices=["queued", "graph"], default="queued",
+                    help="queued: the launches are enqueued behind a spin kernel long enough to "
+                         "cover their submission, then run back to back; graph: a warm-up and "
+                         "a timed HIP graph, replayed back to back")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time per CPU baseline run (one thread, then all threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -733,10 +760,14 @@ def main(argv=None):
 
     stream = torch.cuda.Stream()
     # one eager launch per buffer set: loads the library and checks every
-    # argument set once (setup, neither warm-up nor timed)
+    # argument set once (setup, neither warm-up nor timed); it also gives the
+    # host's cost of one launch call
     with torch.cuda.stream(stream):
+        launch(case, sets[0])
+        h0 = time.perf_counter()
         for s in sets:
             launch(case, s)
+        host_us = (time.perf_counter() - h0) / R * 1e6
     stream.synchronize()
 
     def launch_fn(i):
@@ -746,21 +777,30 @@ def main(argv=None):
     W, K = args.warmup, args.steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
+    host_ahead = None
+    if args.timing == "queued":
+        # A spin kernel long enough for the host to enqueue every launch
+        # (twice the measured host cost, at least 5 ms), then W warm-up and K
+        # timed launches: the GPU runs them back to back, with nothing
+        # between two launches but the dispatch of the next. The event after
+        # the spin kernel tells whether the host finished enqueuing first.
+        gate_ms = max(5.0, 2e-3 * (W + K) * host_us)
+        _gate(stream, gate_ms)
+        eg = torch.cuda.Event()
+        eg.record(stream)
         with torch.cuda.stream(stream):
             for i in range(W):
                 launch(case, sets[i % R])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        with torch.cuda.stream(stream):
+            e0.record(stream)
             for i in range(W, W + K):
                 launch(case, sets[i % R])
-        e1.record(stream)
+            e1.record(stream)
+        host_ahead = not eg.query()
         torch.cuda.synchronize()
     else:
         # warm-up: W launches in one graph; timed: exactly K launches in one
-        # graph, continuing the rotation, behind a spin kernel so that the
-        # whole graph is submitted before its first launch starts
+        # graph, continuing the rotation; a spin kernel, then both graphs back
+        # to back (the gap between the two graphs falls in the timed region)
         if W:
             gw = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gw, stream=stream):
@@ -771,9 +811,6 @@ def main(argv=None):
             for i in range(W, W + K):
                 launch(case, sets[i % R])
         torch.cuda.synchronize()
-        # spin kernel, then the warm-up graph right before the timed one: the
-        # warm-up launches run back to back into the timed region (the GPU is
-        # at its working clock when the first timed launch starts)
         _gate(stream)
         if W:
             with torch.cuda.stream(stream):
@@ -788,7 +825,7 @@ def main(argv=None):
     kernel_us = ms * 1e3
 
     context = None
-    if not args.no_context and not args.no_graph:
+    if not args.no_context:
         n_iso = min(K, 200)
         context = {"isolated_launch_us": isolated_launch_times(
             [launch_fn(i) for i in range(W, W + n_iso)], stream)}
@@ -840,8 +877,9 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                    "tokens_per_step": tokens, "io_dtype": "bf16",
-                   "buffer_sets_rotated": R, "graph": not args.no_graph,
-                   "setup_launches": R},
+                   "buffer_sets_rotated": R, "timing": args.timing,
+                   "host_enqueued_ahead": host_ahead, "host_us_per_launch": round(host_us, 1),
+                   "setup_launches": R + 1},
         "roofline": roofline,
     }
     if context is not None:
