@@ -450,9 +450,10 @@ def ingest_profile(args) -> int:
     for r in trace:
         name = r["Kernel_Name"]
         if "empty_kernel" in name:
-            key = f"empty_kernel grid {r['Grid_Size_X']} x wg {r['Workgroup_Size_X']}"
+            key = (f"empty_kernel, {r['Grid_Size_X']} threads in workgroups of "
+                   f"{r['Workgroup_Size_X']}")
         elif "copy_kernel" in name:
-            key = f"copy_kernel grid {r['Grid_Size_X']}"
+            key = f"copy_kernel, {r['Grid_Size_X']} threads"
         else:
             continue
         ctx.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
@@ -480,9 +481,10 @@ def ingest_profile(args) -> int:
             if r["Counter_Name"] != counter:
                 continue
             if "empty_kernel" in r["Kernel_Name"]:
-                key = f"empty_kernel grid {r['Grid_Size']} x wg {r['Workgroup_Size']}"
+                key = (f"empty_kernel, {r['Grid_Size']} threads in workgroups of "
+                       f"{r['Workgroup_Size']}")
             elif "copy_kernel" in r["Kernel_Name"]:
-                key = f"copy_kernel grid {r['Grid_Size']}"
+                key = f"copy_kernel, {r['Grid_Size']} threads"
             else:
                 continue
             ref.setdefault(key, []).append(float(r["Counter_Value"]))
