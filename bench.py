@@ -405,11 +405,13 @@ def _csv_rows(path):
 
 
 def _find_csv(d, suffix):
-    for root, _, files in os.walk(d):
-        for f in files:
-            if f.endswith(suffix):
-                return os.path.join(root, f)
-    raise FileNotFoundError(f"no *{suffix} under {d}")
+    """The newest *suffix file under d (a directory reused by several runs
+    keeps the older files)."""
+    found = [os.path.join(root, f) for root, _, files in os.walk(d) for f in files
+             if f.endswith(suffix)]
+    if not found:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return max(found, key=os.path.getmtime)
 
 
 def ingest_profile(args) -> int:
