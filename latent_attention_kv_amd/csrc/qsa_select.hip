@@ -15,17 +15,18 @@
 //   * the scores are a dense contraction (H x nb x Di), so they run on the
 //     matrix cores (v_mfma_f32_16x16x32_bf16); wavefront w takes the
 //     16-block column tiles w, w + 8, ... and every head tile of each;
-//   * a tile's accumulator holds 4 heads x 16 blocks per 16-lane row, so a
-//     head's maximum or sum over a tile's blocks is four DPP steps inside the
-//     row; partial results are combined per head in a fixed order;
 //   * scores in log2 units (scale * log2 e * q . k): the softmax is a
 //     maximum, exp2 and a sum per head, and Q takes one reciprocal per head;
 //   * qsa_select_fast_kernel (Di / 32, H / 16 and the column tiles per
-//     wavefront known at compile time): each wavefront loads the key
-//     fragments of its own tiles straight into registers, q passes through
-//     LDS once (loaded while the key length is read: it does not depend on
-//     it), and all scores stay in registers from the MFMA to Q;
-//   * qsa_select_kernel (every other shape): keys staged in LDS chunks; a
+//     wavefront known at compile time): keys as the A operand, so each lane
+//     holds one head of 4 blocks per tile and a head's statistics stay in
+//     the lane; key fragments go straight into registers, requested with q
+//     and the key length when the workgroup starts; the per-lane softmax
+//     partials meet once in LDS (maximum, sum and a factor per partial);
+//   * qsa_select_kernel (every other shape): q as the A operand, a tile's
+//     accumulator holds 4 heads x 16 blocks per 16-lane row, so a head's
+//     maximum or sum over a tile is four DPP steps inside the row, partial
+//     results combined per head in a fixed order; keys staged in LDS chunks; a
 //     sequence that fits one chunk with few enough tiles per wavefront keeps
 //     its scores in registers, a longer one takes three sweeps over its
 //     chunks (maxima, sums, Q), each recomputing its tiles;
@@ -42,11 +43,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRankMax = 2048;
 constexpr int kMaxTiles = 16;            // score tiles a wavefront holds in registers
+constexpr int kPartStride = 4 * kWaves + 1; // fast kernel: lane partials per head (+1: banks)
 
 // rows_a rows of a, then rows of b (row-major bf16, row length Di, 16-byte
 // pieces) into consecutive LDS rows of rowb bytes. Each thread issues kBatch
@@ -107,6 +110,18 @@ constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRor8 = 0x128;         // row_ror:8 (in a 16-lane row: lane xor 8)
+
+// Workgroup barrier that orders LDS only: its fences wait for this thread's
+// LDS operations, not for its global loads and stores (__syncthreads waits for
+// both). For barriers between LDS producers and consumers where no thread
+// reads global memory another thread of the workgroup wrote.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // The maximum steps are single v_max_f32_dpp instructions. The values are
 // results of arithmetic (never signalling NaNs), so the IEEE-mode v_max_f32
@@ -213,8 +228,40 @@ __device__ __forceinline__ void pool_and_select(const QsaSelectArgs &a, const fl
             R[j] = 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
+    if (J <= kThreads / 4) {
+        // ---- top-k by rank, up to 128 blocks: the position of block j is
+        // the number of keys above its own (ranks 0 .. J-1, each once),
+        // counted by the four lanes 4 j .. 4 j + 3, lane r over the key pairs
+        // 4 t + r (the four lanes of a quad read 64 consecutive bytes), and
+        // added over the quad in two DPP steps
+        // (every read is issued before the first compare: pairs past the
+        // keys reread the last pair and count nothing)
+        const int j = tid >> 2, r = tid & 3;
+        const uint64_t key = j < J ? K[j] : 0ull;
+        int cnt = 0;
+        if (j < J) {
+            constexpr int kPairs = kThreads / 4 / 2 / 4;  // pairs per lane at 128 keys
+            ulonglong2 kk[kPairs];
+#pragma unroll
+            for (int t = 0; t < kPairs; ++t)
+                kk[t] = *reinterpret_cast<const ulonglong2 *>(K + 2 * min(r + 4 * t, J4 / 2 - 1));
+#pragma unroll
+            for (int t = 0; t < kPairs; ++t) {
+                const bool in = 2 * (r + 4 * t) < J4;
+                cnt += in && kk[t].x > key;
+                cnt += in && kk[t].y > key;
+            }
+        }
+        cnt += __builtin_amdgcn_update_dpp(0, cnt, kDppXor1, 0xF, 0xF, false);
+        cnt += __builtin_amdgcn_update_dpp(0, cnt, kDppXor2, 0xF, 0xF, false);
+        if (j < J && r == 0 && cnt < a.topk)
+            out_idx[cnt] = (key >> 32) != 0 ? j : -1;        // a NaN score leaves -1
+        for (int p = J + tid; p < a.topk; p += kThreads)
+            out_idx[p] = -1;
+        return;
+    }
     if (by_rank) {
         // ---- top-k by rank: the position of block j is the number of keys
         // above its own (ranks 0 .. J-1, each once). The count for each block
@@ -236,7 +283,7 @@ __device__ __forceinline__ void pool_and_select(const QsaSelectArgs &a, const fl
             }
             atomicAdd(R + j, cnt);
         }
-        __syncthreads();
+        lds_barrier();
         for (int j = tid; j < J; j += kThreads) {
             const int rank = R[j];
             if (rank < a.topk)
@@ -515,11 +562,25 @@ __global__ __launch_bounds__(kThreads) void qsa_select_kernel(QsaSelectArgs a)
 
 // Fast path for the common shapes, all sizes known at compile time: Di = 32 DK,
 // H = 16 HT, and at most JWM column tiles per wavefront (Bcap <= 128 JWM).
-// Each wavefront loads the key fragments of its column tiles straight from
-// memory into registers (no other wavefront needs them), q passes through
-// LDS once, and every score of the sequence stays in registers from the
-// matrix cores to the head sum; per-wavefront head maxima and sums are
-// combined per head in wavefront order.
+//
+// The keys are the A operand (rows = blocks) and q the B operand (columns =
+// heads), so lane (g, fr) of a tile holds head 16 ht + fr for blocks 4 g .. 4 g
+// + 3 of it: a head's maximum and sum over the lane's blocks stay in the lane.
+// Wavefront w takes column tiles w + 8 jl; each lane loads the key fragments
+// of its tile rows straight into registers: those of the first tile when the
+// workgroup starts, together with q and the key length (rows clamped to the
+// capacity; a fragment past the sequence is loaded and never used), the
+// others once the key length shows that their tile holds blocks of the
+// sequence. q passes through LDS once; tiles past the sequence are skipped.
+//
+// Softmax per head over its 32 lane partials (8 wavefronts x 4 lane groups),
+// in log2 units s = scale log2(e) q . k: lane partial p holds m_p = max s
+// over its blocks and z_p = sum exp2(s - m_p); with M = max_p m_p and
+// Z = sum_p z_p exp2(m_p - M), each score's softmax term is
+// exp2(s - m_p) c_p with c_p = exp2(m_p - M) / Z, the factorisation of
+// exp2(s - M) / Z over the partials (one pass over the scores, one exchange
+// of partials through LDS). Q's head sum takes each lane's products over its
+// head tiles, then the 16 head lanes of a tile row in four DPP steps.
 template <int DK, int HT, int JWM>
 __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs a)
 {
@@ -527,40 +588,54 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int Di = 32 * DK, H = 16 * HT, rowb = 2 * Di + 16, pieces = Di / 8;
     constexpr int QP = H * pieces, QPT = (QP + kThreads - 1) / kThreads;
+    // head tiles whose q fragments are held at once (at most 16 fragments =
+    // 64 registers); with all of them held, q is read from LDS once
+    constexpr int QF = 16 / DK < HT ? 16 / DK : HT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, g = lane >> 4;             // fragment row / column, lane group
     const int64_t n = blockIdx.x;
 
-    // LDS: q [H][Di] (rows padded by 16 bytes), per-wavefront head maxima and
-    // sums [H][kWaves] x 2, the combined head maxima and reciprocal sums
-    // [H] x 2, Q [Bcap], P [Jcap] (both rounded up to 4), the rank keys and
-    // ranks [min(Jcap rounded up to 4, kRankMax)] (8 + 4 bytes)
+    // LDS: q [H][Di] (rows padded by 16 bytes); per head its lane partials
+    // m_p (then c_p) and z_p [H][kPartStride] x 2; Q [Bcap rounded up to 16];
+    // P [Jcap], the rank keys and ranks as in pool_and_select
+    const int rows16 = (int)(a.Bcap + 15) / 16 * 16;
     unsigned char *q_lds = smem;
-    float *wmax = reinterpret_cast<float *>(smem + H * rowb);
-    float *wsum = wmax + H * kWaves;
-    float *hmax = wsum + H * kWaves;
-    float *hrz = hmax + H;
-    float *Q = hrz + H;
-    float *P = Q + (a.Bcap + 3) / 4 * 4;
+    float *pm = reinterpret_cast<float *>(smem + H * rowb);
+    float *pz = pm + H * kPartStride;
+    float *Q = pz + H * kPartStride;
+    float *P = Q + rows16;
     uint64_t *K = reinterpret_cast<uint64_t *>(P + (a.Jcap + 3) / 4 * 4);
     int *R = reinterpret_cast<int *>(K + min((int)(a.Jcap + 3) / 4 * 4, kRankMax));
 
     float *scores = a.scores + n * a.Jcap;
     int32_t *out_idx = a.indices + n * a.topk;
-    // the key length first (a uniform load), then the q rows, which do not
-    // depend on it, so that both latencies overlap
+    const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
+    const int last = (int)a.Bcap - 1;
+    auto load_keys = [&](bf16x8 *f, int jl) __attribute__((always_inline)) {
+        const int row = min(16 * (wave + kWaves * jl) + fr, last);
+#pragma unroll
+        for (int u = 0; u < DK; ++u)
+            f[u] = *reinterpret_cast<const bf16x8 *>(kn + (int64_t)row * Di + 32 * u + 8 * g);
+    };
+    // the key length, the q rows and the first tile's key fragments are all
+    // requested before any of them is waited for
     const int64_t Klen = __builtin_nontemporal_load(a.key_length + (a.klc == 1 ? 0 : n));
+    bf16x8 kf[JWM][DK];
     {
         const uint16_t *qn = a.query + n * (int64_t)H * Di;
-        uint4 qs[QPT];
+        // (a vector type, not uint4: the struct copies of uint4 kept the
+        // array in scratch memory here)
+        u32x4 qs[QPT];
 #pragma unroll
         for (int b = 0; b < QPT; ++b) {
             const int c = min(tid + b * kThreads, QP - 1);
-            qs[b] = *reinterpret_cast<const uint4 *>(qn + (c / pieces) * Di + (c % pieces) * 8);
+            qs[b] = *reinterpret_cast<const u32x4 *>(qn + (c / pieces) * Di + (c % pieces) * 8);
         }
+        load_keys(kf[0], 0);
 #pragma unroll
         for (int b = 0; b < QPT; ++b) {
             const int c = min(tid + b * kThreads, QP - 1);
-            *reinterpret_cast<uint4 *>(q_lds + (c / pieces) * rowb + (c % pieces) * 16) = qs[b];
+            *reinterpret_cast<u32x4 *>(q_lds + (c / pieces) * rowb + (c % pieces) * 16) = qs[b];
         }
     }
     const int nb = sequence_blocks_of(a, Klen, scores, out_idx, tid);
@@ -570,165 +645,201 @@ __global__ __launch_bounds__(kThreads) void qsa_select_fast_kernel(QsaSelectArgs
     const int J = nb == 0 ? 0 : (nb + sel + cmpr - 3) / sel + 1;
 
     if (nb > 0) {
-        const uint16_t *kn = a.keys + n * a.Bcap * (int64_t)Di;
-        const int fr = lane & 15, g = lane >> 4;         // fragment row / column, lane group
+#pragma unroll
+        for (int jl = 1; jl < JWM; ++jl)
+            if (16 * (wave + kWaves * jl) < nb)
+                load_keys(kf[jl], jl);
         const float scale2 = a.scale * 1.44269504088896341f;
+        lds_barrier();                                   // q in LDS (the keys may still arrive)
 
-        // the key fragments of column tiles wave + 8 jl (rows past the
-        // sequence clamped to its last block: they are computed, never
-        // used); q is in LDS already
-        bf16x8 kf[JWM][DK];
-#pragma unroll
-        for (int jl = 0; jl < JWM; ++jl) {
-            const int row = min(16 * (wave + kWaves * jl) + fr, nb - 1);
-#pragma unroll
-            for (int u = 0; u < DK; ++u)
-                kf[jl][u] = *reinterpret_cast<const bf16x8 *>(kn + (int64_t)row * Di + 32 * u + 8 * g);
-        }
-        __syncthreads();
-
-        // scores (log2 units): e[jl][ht] = the tile of head tile ht and column
-        // tile wave + 8 jl
-        // (the q fragments of QF head tiles, at most 8 fragments = 32
-        // registers, are read before their MFMAs, so the LDS reads overlap
-        // instead of one wait each)
-        constexpr int QF = 8 / DK < HT ? (8 / DK > 0 ? 8 / DK : 1) : HT;   // head tiles per batch
+        // scores (log2 units): e[jl][ht] = tile of column tile wave + 8 jl and
+        // head tile ht, for the tiles that hold blocks of the sequence (each
+        // MFMA result is read by the multiply in the same branch)
         f32x4 e[JWM][HT];
         bf16x8 qf[QF][DK];
+        auto load_q = [&](int ht0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            if (ht % QF == 0) {
-#pragma unroll
-                for (int hq = 0; hq < QF; ++hq)
-#pragma unroll
-                    for (int u = 0; u < DK; ++u)
-                        qf[hq][u] = *reinterpret_cast<const bf16x8 *>(
-                            q_lds + (16 * (ht + hq) + fr) * rowb + (32 * u + 8 * g) * 2);
-                // every fragment is needed here: the reads are all issued
-                // before the first MFMA (the scheduler would otherwise trade
-                // them against registers, one wait per read)
-#pragma unroll
-                for (int hq = 0; hq < QF; ++hq)
-#pragma unroll
-                    for (int u = 0; u < DK; ++u)
-                        asm volatile("" ::"v"(qf[hq][u]));
-            }
-#pragma unroll
-            for (int jl = 0; jl < JWM; ++jl) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int hq = 0; hq < QF; ++hq)
 #pragma unroll
                 for (int u = 0; u < DK; ++u)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht % QF][u], kf[jl][u], acc, 0, 0, 0);
+                    qf[hq][u] = *reinterpret_cast<const bf16x8 *>(
+                        q_lds + (16 * (ht0 + hq) + fr) * rowb + (32 * u + 8 * g) * 2);
+            // every fragment is read before the first MFMA that needs one
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    e[jl][ht][q] = scale2 * acc[q];
-            }
-        }
-        bool ok[JWM];                                   // this lane's column exists
+            for (int hq = 0; hq < QF; ++hq)
 #pragma unroll
-        for (int jl = 0; jl < JWM; ++jl)
-            ok[jl] = 16 * (wave + kWaves * jl) + fr < nb;
-
-        // head maxima: over this wavefront's columns, then over the wavefronts
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float m = -INFINITY;
-#pragma unroll
-                for (int jl = 0; jl < JWM; ++jl)
-                    m = ok[jl] ? fmaxf(m, e[jl][ht][q]) : m;
-                m = row_max16(m);
-                if (fr == 0)
-                    wmax[(16 * ht + 4 * g + q) * kWaves + wave] = m;
-            }
-        __syncthreads();
-        for (int h = tid; h < H; h += kThreads) {
-            const f32x4 lo = *reinterpret_cast<const f32x4 *>(wmax + h * kWaves);
-            const f32x4 hi = *reinterpret_cast<const f32x4 *>(wmax + h * kWaves + 4);
-            hmax[h] = fmaxf(fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])),
-                            fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])));
-        }
-        __syncthreads();
-
-        // exp2(s - max) in place. exp2f only adjusts arguments below -126
-        // (subnormal results); at or above it, it equals the bare v_exp_f32.
-        // So a lane whose smallest argument is >= -126 (every lane unless
-        // scores spread over 126 in log2 units) takes v_exp_f32 alone.
-        float xmin = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float lo = INFINITY;
-#pragma unroll
-                for (int jl = 0; jl < JWM; ++jl)
-                    lo = ok[jl] ? fminf(lo, e[jl][ht][q]) : lo;
-                xmin = fminf(xmin, lo - m[q]);
-            }
-        }
-        if (xmin < -126.0f) {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int jl = 0; jl < JWM; ++jl)
-                        e[jl][ht][q] = ok[jl] ? exp2f(e[jl][ht][q] - m[q]) : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const f32x4 m = *reinterpret_cast<const f32x4 *>(hmax + 16 * ht + 4 * g);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int jl = 0; jl < JWM; ++jl)
-                        e[jl][ht][q] = ok[jl] ? __builtin_amdgcn_exp2f(e[jl][ht][q] - m[q]) : 0.0f;
-            }
-        }
-        // head sums: over this wavefront's columns, then over the wavefronts
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float z = 0.0f;
-#pragma unroll
-                for (int jl = 0; jl < JWM; ++jl)
-                    z += e[jl][ht][q];
-                z = row_sum16(z);
-                if (fr == 0)
-                    wsum[(16 * ht + 4 * g + q) * kWaves + wave] = z;
-            }
-        __syncthreads();
-        for (int h = tid; h < H; h += kThreads) {
-            const f32x4 lo = *reinterpret_cast<const f32x4 *>(wsum + h * kWaves);
-            const f32x4 hi = *reinterpret_cast<const f32x4 *>(wsum + h * kWaves + 4);
-            hrz[h] = 1.0f / (lo[0] + lo[1] + lo[2] + lo[3] + hi[0] + hi[1] + hi[2] + hi[3]);
-        }
-        __syncthreads();
-
-        // Q[block] = sum over heads of exp2(s - max) / sum
+                for (int u = 0; u < DK; ++u)
+                    asm volatile("" ::"v"(qf[hq][u]));
+        };
+        if constexpr (QF == HT)
+            load_q(0);
 #pragma unroll
         for (int jl = 0; jl < JWM; ++jl) {
-            float qv = 0.0f;
+            if (16 * (wave + kWaves * jl) < nb) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const f32x4 rz = *reinterpret_cast<const f32x4 *>(hrz + 16 * ht + 4 * g);
+                for (int ht = 0; ht < HT; ++ht) {
+                    if constexpr (QF < HT)
+                        if (ht % QF == 0)
+                            load_q(ht);
+                    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    qv += e[jl][ht][q] * rz[q];
+                    for (int u = 0; u < DK; ++u)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[jl][u], qf[ht % QF][u], acc,
+                                                                      0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        e[jl][ht][q] = scale2 * acc[q];
+                }
             }
-            // the 4 lane groups hold the same block for different heads
-            qv += __shfl_xor(qv, 16, 64);
-            qv += __shfl_xor(qv, 32, 64);
-            if (g == 0 && ok[jl])
-                Q[16 * (wave + kWaves * jl) + fr] = qv;
+        }
+
+        // this lane's maximum and minimum per head over its blocks of the
+        // sequence (the tile the sequence ends in is masked)
+        float hi[HT], lo[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            hi[ht] = -INFINITY;
+            lo[ht] = INFINITY;
+        }
+#pragma unroll
+        for (int jl = 0; jl < JWM; ++jl) {
+            const int t0 = 16 * (wave + kWaves * jl);
+            if (t0 + 16 <= nb) {
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) {
+                    const f32x4 v = e[jl][ht];
+                    hi[ht] = fmaxf(fmaxf(fmaxf(fmaxf(hi[ht], v[0]), v[1]), v[2]), v[3]);
+                    lo[ht] = fminf(fminf(fminf(fminf(lo[ht], v[0]), v[1]), v[2]), v[3]);
+                }
+            } else if (t0 < nb) {
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool ok = t0 + 4 * g + q < nb;
+                        hi[ht] = ok ? fmaxf(hi[ht], e[jl][ht][q]) : hi[ht];
+                        lo[ht] = ok ? fminf(lo[ht], e[jl][ht][q]) : lo[ht];
+                    }
+            }
+        }
+
+        // exp2(s - m_p) in place and z_p. exp2f only adjusts arguments below
+        // -126 (subnormal results); at or above it, it equals the bare
+        // v_exp_f32, which a lane takes unless its scores spread over more
+        // than 126 (log2 units).
+        bool wide = false;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+            wide = wide || lo[ht] - hi[ht] < -126.0f;
+        float z[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+            z[ht] = 0.0f;
+        auto exp_pass = [&](auto ex) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jl = 0; jl < JWM; ++jl) {
+                const int t0 = 16 * (wave + kWaves * jl);
+                if (t0 + 16 <= nb) {
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            e[jl][ht][q] = ex(e[jl][ht][q] - hi[ht]);
+                            z[ht] += e[jl][ht][q];
+                        }
+                } else if (t0 < nb) {
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const bool ok = t0 + 4 * g + q < nb;
+                            e[jl][ht][q] = ok ? ex(e[jl][ht][q] - hi[ht]) : 0.0f;
+                            z[ht] += e[jl][ht][q];
+                        }
+                }
+            }
+        };
+        if (wide)
+            exp_pass([](float x) __attribute__((always_inline)) { return exp2f(x); });
+        else
+            exp_pass([](float x) __attribute__((always_inline)) { return __builtin_amdgcn_exp2f(x); });
+
+        // lane partial p = 4 wave + g of head 16 ht + fr (m_p = -inf for a
+        // lane without blocks: its factor comes out 0)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int at = (16 * ht + fr) * kPartStride + 4 * wave + g;
+            pm[at] = hi[ht];
+            pz[at] = z[ht];
+        }
+        lds_barrier();
+
+        // per head: M, Z and the factors c_p, eight lanes per head with four
+        // partials each (the three DPP steps leave the same result in all
+        // eight lanes); c_p replaces m_p
+        for (int it = tid; it < H * 8; it += kThreads) {
+            float *m4 = pm + (it >> 3) * kPartStride + 4 * (it & 7);
+            const float *z4 = pz + (it >> 3) * kPartStride + 4 * (it & 7);
+            const float m0 = m4[0], m1 = m4[1], m2 = m4[2], m3 = m4[3];
+            float M = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+            M = fmaxf(M, dpp<kDppXor1>(M));
+            M = fmaxf(M, dpp<kDppXor2>(M));
+            M = fmaxf(M, dpp<kDppHalfMirror>(M));
+            const float w0 = exp2f(m0 - M), w1 = exp2f(m1 - M), w2 = exp2f(m2 - M),
+                        w3 = exp2f(m3 - M);
+            float Z = z4[0] * w0 + z4[1] * w1 + z4[2] * w2 + z4[3] * w3;
+            Z += dpp<kDppXor1>(Z);
+            Z += dpp<kDppXor2>(Z);
+            Z += dpp<kDppHalfMirror>(Z);
+            // Z >= 1 (the largest partial has w = 1 and z >= 1): the hardware
+            // reciprocal (1 ulp) serves
+            const float rz = __builtin_amdgcn_rcpf(Z);
+            m4[0] = w0 * rz;
+            m4[1] = w1 * rz;
+            m4[2] = w2 * rz;
+            m4[3] = w3 * rz;
+        }
+        lds_barrier();
+
+        // Q: per block of this lane, the sum over its head tiles of
+        // exp2(s - m_p) c_p, then over the 16 head lanes of the tile row by a
+        // transposing reduction: each step pairs lane fr with a partner that
+        // differs in one more bit (xor 8, then the mirror inside 8 lanes,
+        // which flips bit 2, then xor 2 and xor 1), keeps half of its values
+        // and adds the partner's copy of them, so lane fr ends with block
+        // 4 g + (fr >> 2) of the tile (fr = 4 k + r, r < 4: the same sum).
+        float cf[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+            cf[ht] = pm[(16 * ht + fr) * kPartStride + 4 * wave + g];
+        const bool b3 = fr & 8, b2 = fr & 4;
+#pragma unroll
+        for (int jl = 0; jl < JWM; ++jl) {
+            const int t0 = 16 * (wave + kWaves * jl);
+            if (t0 < nb) {
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[q] = e[jl][0][q] * cf[0];
+#pragma unroll
+                    for (int ht = 1; ht < HT; ++ht)
+                        v[q] = __builtin_fmaf(e[jl][ht][q], cf[ht], v[q]);
+                }
+                // bit 3: keep blocks {0, 1} or {2, 3}
+                const float k0 = b3 ? v[2] : v[0], s0 = b3 ? v[0] : v[2];
+                const float k1 = b3 ? v[3] : v[1], s1 = b3 ? v[1] : v[3];
+                const float x0 = k0 + dpp<kDppRor8>(s0), x1 = k1 + dpp<kDppRor8>(s1);
+                // bit 2: keep one of the two
+                const float k = b2 ? x1 : x0, s = b2 ? x0 : x1;
+                float y = k + dpp<kDppHalfMirror>(s);
+                y += dpp<kDppXor2>(y);
+                y += dpp<kDppXor1>(y);
+                if ((fr & 3) == 0)
+                    Q[t0 + 4 * g + (fr >> 2)] = y;
+            }
         }
     }
-    __syncthreads();
+    lds_barrier();
     pool_and_select(a, Q, P, K, R, nb, J, scores, out_idx, tid, lane, wave);
 }
 
@@ -755,7 +866,7 @@ typedef void (*SelectKernel)(QsaSelectArgs);
 
 SelectKernel fast_select_kernel(int64_t Di, int64_t H, int64_t Bcap)
 {
-    if (Di % 32 || H % 16)
+    if (Di % 32 || H % 16 || Bcap < 1)
         return nullptr;
     const int64_t dk = Di / 32, ht = H / 16;
     const int64_t per_wave = ((Bcap + 15) / 16 + kWaves - 1) / kWaves;
@@ -782,7 +893,7 @@ hipError_t launch_qsa_select(const QsaSelectArgs &a, hipStream_t stream)
     int64_t lds;
     if (k) {
         const int64_t jcap4 = (a.Jcap + 3) / 4 * 4;
-        lds = a.H * (a.Di * 2 + 16) + 4 * ((2 * kWaves + 2) * a.H + (a.Bcap + 3) / 4 * 4 + jcap4) +
+        lds = a.H * (a.Di * 2 + 16) + 4 * (2 * kPartStride * a.H + (a.Bcap + 15) / 16 * 16 + jcap4) +
               12 * (jcap4 < kRankMax ? jcap4 : kRankMax);
     } else {
         k = qsa_select_kernel;
