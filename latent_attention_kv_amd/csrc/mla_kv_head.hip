@@ -43,8 +43,9 @@
 //     used, then one barrier publishes them;
 //   * the two workgroups of a pair are blockIdx b and b + 8, which the
 //     dispatcher places on the same XCD: their x rows meet in that XCD's L2;
-//   * staged rows are 64 bytes with their four 16-byte pieces permuted by
-//     (row / 4) mod 4, so the 16 lanes of a fragment read cover all 64 banks;
+//   * staged rows are 64 bytes with their four 16-byte pieces permuted
+//     (swz below) so that every eight lanes of a fragment read, which the
+//     LDS serves together, hit eight different 16-byte bank groups;
 //   * epilogue: the MFMAs take W as their first operand, so each lane's
 //     accumulators are 4 consecutive output columns of one token row (no
 //     transpose); squares are reduced per row across lanes (permlane swaps)
@@ -140,9 +141,18 @@ constexpr int kStoreSc1 = 16;
 // 6:4, lgkmcnt 11:8; the unused counters at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// Piece permutation of a staged row: piece c of row r sits in slot
-// c ^ ((r >> 2) & 3).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Piece permutation of a staged row: piece c of row r sits in slot c ^ swz(r),
+// swz(r) = 2 (b2 ^ b3) + (b1 ^ b3) with bk bit k of r. The LDS serves a
+// 16-byte read eight lanes (128 bytes) at a time: the eight rows of a group
+// share bit 3, so for each parity of r (its 64-byte half of the 128) the four
+// rows take four different slots; over all 16 rows, rows equal mod 4 (the
+// same 64-byte quarter of 256 bytes) also take four different slots.
+// (The counters showed (r >> 2) & 3, right for 16 lanes at a time, leaving
+// one conflict cycle per access.)
+__device__ __forceinline__ int swz(int r)
+{
+    return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+}
 
 // Claim of a half, in two steps by wavefront 0, lane 0. At the start,
 // claim_begin reads this half's flag and tries the claim word from 0 to this
