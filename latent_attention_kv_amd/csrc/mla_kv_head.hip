@@ -28,19 +28,20 @@
 // operands reach a compute unit through its texture path, whose rate bounds
 // this kernel, so the tile is chosen for bytes per flop: a PAIR of
 // workgroups owns 256 token rows, one workgroup per half of the 576 output
-// columns (columns 0..287, and 288..575 with the 64 rope columns). Per K
-// step of 32 a workgroup then streams 16 KiB of x and 18 KiB of W (34 KiB)
+// columns (columns 0..287, and 288..575 with the 64 rope columns). Per 32
+// of K a workgroup then streams 16 KiB of x and 18 KiB of W (34 KiB)
 // instead of 8 + 36 KiB for a 128 x 576 tile, for the same matrix work.
 //   * 8 wavefronts = 4 (rows) x 2 (columns); wavefront (wm, wn) accumulates
 //     rows 64 wm .. +64 and columns 144 wn .. +144 of its half as 4 x 9 tiles
 //     of 16 x 16 (144 accumulator registers, two wavefronts per SIMD);
-//   * K advances 32 at a time; the slices pass through two LDS rings filled
-//     by direct global -> LDS loads (global_load_lds_dwordx4: no staging
-//     registers, no LDS store instructions): W (288 x 32, 18 KiB) in 3
-//     stages two steps ahead of the MFMAs, x (256 x 32, 16 KiB) in 4 stages
-//     three steps ahead, as x streams from HBM while W is shared through L2;
-//     each wavefront waits only for its own loads of the step about to be
-//     used, then one barrier publishes them;
+//   * K advances 64 at a time (two MFMA steps of 32): a staged row is then
+//     one whole 128-byte line of x or W, which halves the line requests per
+//     byte against 64-byte rows (measured: ~5 % of the call); the slices pass
+//     through two LDS rings filled by direct global -> LDS loads
+//     (global_load_lds_dwordx4: no staging registers, no LDS store
+//     instructions), W (288 x 64, 36 KiB) and x (256 x 64, 32 KiB), two
+//     stages each, loaded one step ahead of the MFMAs; each wavefront waits
+//     only for its own loads, then one barrier publishes them;
 //   * the two workgroups of a pair are blockIdx b and b + 8, which the
 //     dispatcher places on the same XCD: their x rows meet in that XCD's L2;
 //   * staged rows are 64 bytes with their four 16-byte pieces permuted
@@ -93,24 +94,24 @@ constexpr int kNorm = 512;
 constexpr int kRope = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKt = (int)kMlaHeadK;        // K per stage (one MFMA K)
-constexpr int kRowBytes = kKt * 2;         // 64
-constexpr int kStageA = kRows * kRowBytes; // 16384
-constexpr int kStageB = kHalfCols * kRowBytes; // 18432
-// Two LDS rings: W slices (3 stages, loaded 2 steps ahead) and x slices (4
-// stages, loaded 3 steps ahead: x streams from HBM while W is mostly served
-// by L2).
-constexpr int kWStages = 3, kWLead = kWStages - 1;
-constexpr int kXStages = 4, kXLead = kXStages - 1;
+constexpr int kKt = (int)kMlaHeadK;        // K of one MFMA (32)
+constexpr int kKs = 2 * kKt;               // K per ring stage (64): a staged row is
+                                           // one 128-byte line of x or W
+constexpr int kRowBytes = kKs * 2;         // 128
+constexpr int kStageA = kRows * kRowBytes; // 32768
+constexpr int kStageB = kHalfCols * kRowBytes; // 36864
+// Two LDS rings of two stages each, W slices and x slices, each stage loaded
+// one step (K 64) ahead of its MFMAs.
+constexpr int kWStages = 2, kXStages = 2;
 constexpr int kXRing = kWStages * kStageB;              // offset of the x ring
-constexpr int kPipeBytes = kXRing + kXStages * kStageA; // 120832
-// the 16 x blocks and 18 W blocks (1 KiB each, one load instruction) of a
-// step: wavefront w loads x blocks 2w, 2w + 1, then W blocks (3 each for
-// w < 2, 2 for the others)
-constexpr int kXBlocks = 2;
-static_assert(kStageA / 1024 == kXBlocks * kWaves && 2 * 3 + 6 * 2 == kStageB / 1024,
+constexpr int kPipeBytes = kXRing + kXStages * kStageA; // 139264
+// the 32 x blocks and 36 W blocks (1 KiB = 8 rows each, one load
+// instruction) of a stage: wavefront w loads x blocks 4w .. 4w + 3, then W
+// blocks (5 each for w < 4, 4 for the others)
+constexpr int kXBlocks = 4;
+static_assert(kStageA / 1024 == kXBlocks * kWaves && 4 * 5 + 4 * 4 == kStageB / 1024,
               "block split");
-constexpr int kMaxWBlocks = 3;
+constexpr int kMaxWBlocks = 5;
 constexpr int kMt = 4, kNt = 9;            // 16 x 16 tiles per wavefront
 constexpr int kWaveCols = kNt * 16;        // 144
 constexpr int kRopeTiles = 4;              // tiles 5..8 of the rope wavefront
@@ -141,18 +142,12 @@ constexpr int kStoreSc1 = 16;
 // 6:4, lgkmcnt 11:8; the unused counters at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// Piece permutation of a staged row: piece c of row r sits in slot c ^ swz(r),
-// swz(r) = 2 (b2 ^ b3) + (b1 ^ b3) with bk bit k of r. The LDS serves a
-// 16-byte read eight lanes (128 bytes) at a time: the eight rows of a group
-// share bit 3, so for each parity of r (its 64-byte half of the 128) the four
-// rows take four different slots; over all 16 rows, rows equal mod 4 (the
-// same 64-byte quarter of 256 bytes) also take four different slots.
-// (The counters showed (r >> 2) & 3, right for 16 lanes at a time, leaving
-// one conflict cycle per access.)
-__device__ __forceinline__ int swz(int r)
-{
-    return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
-}
+// Piece permutation of a staged row (128 bytes, eight 16-byte pieces): piece
+// c of row r sits in slot c ^ (r % 8). The LDS serves a 16-byte read eight
+// lanes (128 bytes) at a time; the eight lanes of a fragment read take rows
+// r .. r + 7 (r a multiple of 8) at one piece, so they hit eight different
+// slots, i.e. eight different 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // Claim of a half, in two steps by wavefront 0, lane 0. At the start,
 // claim_begin reads this half's flag and tries the claim word from 0 to this
@@ -318,8 +313,8 @@ void mla_kv_head_kernel(MlaKvHeadArgs a, uint32_t steal_ticks, uint32_t stall_ti
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int wm = wave & 3, wn = wave >> 2;
-    const int nw = wave < 2 ? 3 : 2;                     // W blocks of this wavefront
-    const int wb0 = wave < 2 ? 3 * wave : 6 + 2 * (wave - 2);
+    const int nw = wave < 4 ? 5 : 4;                     // W blocks of this wavefront
+    const int wb0 = wave < 4 ? 5 * wave : 20 + 4 * (wave - 4);
     // blockIdx b and b + 8 form a pair (same XCD under round-robin dispatch)
     const int bx = blockIdx.x;
     const int half = (bx >> 3) & 1;
@@ -391,25 +386,31 @@ void mla_kv_head_kernel(MlaKvHeadArgs a, uint32_t steal_ticks, uint32_t stall_ti
     const bool rope_wave = hh == 1 && wn == 1;           // columns 432..575 of the output
     const int ntn = rope_wave ? kNt - kRopeTiles : kNt;  // tiles holding kv (not rope) columns
     // ---- direct global -> LDS loads ---------------------------------------
-    // A 1 KiB block holds 16 rows of 64 bytes (one K step); lane l writes
-    // byte 16 l: row 16 b + l / 4, slot l % 4, i.e. piece (l % 4) ^ swz(row)
-    // of that row. x block b = token rows 16 b .. +16 (rows past T read row
-    // T - 1: valid memory, results dropped); W block b = rows 16 b .. +16 of
-    // the pass's half of W.
+    // A 1 KiB block holds 8 rows of 128 bytes (one stage); lane l writes
+    // byte 16 l: row 8 b + l / 8, slot l % 8, i.e. piece (l % 8) ^ (l / 8) of
+    // that row. x block b = token rows 8 b .. +8 (rows past T read row T - 1:
+    // valid memory, results dropped); W block b = rows 8 b .. +8 of the
+    // pass's half of W. When He = 64 q + 32, the last stage holds K 0..31
+    // only: its lanes of pieces 4..7 reread their row's pieces 0..3 (within
+    // the row), and its second MFMA step is skipped.
+    const int piece = (lane & 7) ^ (lane >> 3);
     const uint16_t *xsrc[kXBlocks];
 #pragma unroll
     for (int i = 0; i < kXBlocks; ++i) {
-        const int r = 16 * (kXBlocks * wave + i) + (lane >> 2);
+        const int r = 8 * (kXBlocks * wave + i) + (lane >> 3);
         int64_t t = row0 + r;
         t = t < T ? t : T - 1;
-        xsrc[i] = a.x + t * He + ((lane & 3) ^ swz(r)) * 8;
+        xsrc[i] = a.x + t * He + piece * 8;
     }
     const uint16_t *wsrc[kMaxWBlocks];
 #pragma unroll
     for (int i = 0; i < kMaxWBlocks; ++i) {
-        const int r = (wb0 + (i < nw ? i : 0)) * 16 + (lane >> 2);
-        wsrc[i] = a.w + (int64_t)(kHalfCols * hh + r) * He + ((lane & 3) ^ swz(r)) * 8;
+        const int r = (wb0 + (i < nw ? i : 0)) * 8 + (lane >> 3);
+        wsrc[i] = a.w + (int64_t)(kHalfCols * hh + r) * He + piece * 8;
     }
+    const int nks = (int)((He + kKs - 1) / kKs);
+    const bool tail = He % kKs != 0;                     // He % 64 == 32
+    const int tail_back = tail && piece >= 4 ? kKt : 0;
 
     f32x4 acc[kMt][kNt];
 #pragma unroll
@@ -418,83 +419,84 @@ void mla_kv_head_kernel(MlaKvHeadArgs a, uint32_t steal_ticks, uint32_t stall_ti
         for (int n = 0; n < kNt; ++n)
             acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // fragment reads: lane l takes row (l % 16) of a tile, K piece l / 16
-    // (tile row offsets are multiples of 16, so swz of the row is swz(l % 16))
+    // fragment reads: lane l takes row (l % 16) of a tile, K piece l / 16 of
+    // the MFMA step's 32 (piece 4 s + l / 16 of the staged row in step s);
+    // tile row offsets are multiples of 16, so swz of the row is swz(l % 16)
     const int fr = lane & 15, fc = lane >> 4;
-    const int a_off = (64 * wm + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
-    const int b_off = (kWaveCols * wn + fr) * kRowBytes + ((fc ^ swz(fr)) << 4);
+    int a_off[2], b_off[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        a_off[sb] = (64 * wm + fr) * kRowBytes + (((4 * sb + fc) ^ swz(fr)) << 4);
+        b_off[sb] = (kWaveCols * wn + fr) * kRowBytes + (((4 * sb + fc) ^ swz(fr)) << 4);
+    }
 
-    // prologue: x of steps 0 .. kXLead - 1, then W of steps 0 .. kWLead - 1
-    // (this order matters to the waits below)
-    const int nk = (int)(He / kKt);
-    for (int st = 0; st < kXLead && st < nk; ++st)
+    // prologue: stage 0, x then W
+    {
+        const int back = nks == 1 ? tail_back : 0;
 #pragma unroll
         for (int i = 0; i < kXBlocks; ++i)
-            __builtin_amdgcn_global_load_lds(xsrc[i] + st * kKt,
-                                             (lds_void *)(xdst + st * kStageA + i * 1024), 16, 0, 0);
-    for (int st = 0; st < kWLead && st < nk; ++st) {
+            __builtin_amdgcn_global_load_lds(xsrc[i] - back, (lds_void *)(xdst + i * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < kMaxWBlocks; ++i)
             if (i < nw)
-                __builtin_amdgcn_global_load_lds(wsrc[i] + st * kKt,
-                                                 (lds_void *)(wdst + st * kStageB + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(wsrc[i] - back, (lds_void *)(wdst + i * 1024), 16, 0,
+                                                 0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        // This wavefront's loads complete in issue order. Its W blocks of
-        // step kt are its last loads issued before those of step kt - 1
-        // (x of step kt went out kXLead - kWLead steps earlier, before
-        // them), so allowing exactly the loads of step kt - 1 to stay in
-        // flight leaves both x and W of step kt in LDS; the barrier
+    for (int ks = 0; ks < nks; ++ks) {
+        // Every load of this wavefront still in flight is for stage ks
+        // (issued during step ks - 1, or the prologue); the barrier then
         // publishes every wavefront's and tells that all are past step
-        // kt - 1, whose stages are refilled next.
+        // ks - 1, whose buffers are refilled during this step.
         asm volatile("" ::: "memory");
-        const int pending = kt == 0 ? (nk > 1 ? nw : 0)
-                                    : (kt + kXLead - 1 < nk ? kXBlocks : 0) +
-                                          (kt + kWLead - 1 < nk ? nw : 0);
-        switch (pending) {
-        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(5)); break;
-        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2)); break;
-        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
-        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // raised wave priority while this step's MFMAs issue (measured
-        // ~1 % faster: the arbiter favours the wavefront feeding the matrix
-        // pipe over the one still waiting on its loads)
+        // raised wave priority while this step's MFMAs issue (the arbiter
+        // favours the wavefront feeding the matrix pipe)
         __builtin_amdgcn_s_setprio(1);
-        const int sx = kt + kXLead, sw = kt + kWLead;    // steps loaded during this one
-        const bool more_x = sx < nk, more_w = sw < nk;
-        unsigned char *const xd = xdst + (sx % kXStages) * kStageA;
-        unsigned char *const wd = wdst + (sw % kWStages) * kStageB;
-        const unsigned char *xbase = smem + kXRing + (kt % kXStages) * kStageA;
-        const unsigned char *wbase = smem + (kt % kWStages) * kStageB;
-        bf16x8 af[kMt], bf[2];
+        const int sn = ks + 1;                           // the stage loaded during this step
+        const bool more = sn < nks;
+        const int64_t koff = (int64_t)sn * kKs - (sn == nks - 1 ? tail_back : 0);
+        unsigned char *const xd = xdst + (sn & 1) * kStageA;
+        unsigned char *const wd = wdst + (sn & 1) * kStageB;
+        const unsigned char *xbase = smem + kXRing + (ks & 1) * kStageA;
+        const unsigned char *wbase = smem + (ks & 1) * kStageB;
+        const int nsub = tail && ks == nks - 1 ? 1 : 2;
 #pragma unroll
-        for (int m = 0; m < kMt; ++m)
-            af[m] = *reinterpret_cast<const bf16x8 *>(xbase + a_off + m * 16 * kRowBytes);
-        bf[0] = *reinterpret_cast<const bf16x8 *>(wbase + b_off);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = 0; n < kNt; ++n) {
-            if (n + 1 < kNt)
-                bf[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(wbase + b_off + (n + 1) * 16 * kRowBytes);
-            // one load between MFMA groups: the x blocks first, then W
-            if (n < kXBlocks) {
-                if (more_x)
-                    __builtin_amdgcn_global_load_lds(xsrc[n] + sx * kKt, (lds_void *)(xd + n * 1024),
-                                                     16, 0, 0);
-            } else if (n - kXBlocks < kMaxWBlocks) {
-                if (more_w && n - kXBlocks < nw)
-                    __builtin_amdgcn_global_load_lds(wsrc[n - kXBlocks] + sw * kKt,
-                                                     (lds_void *)(wd + (n - kXBlocks) * 1024), 16, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int sb = 0; sb < 2; ++sb) {
+            if (sb == 1 && nsub == 1)
+                break;
+            bf16x8 af[kMt], bf[2];
 #pragma unroll
             for (int m = 0; m < kMt; ++m)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[n & 1], af[m], acc[m][n], 0, 0, 0);
+                af[m] = *reinterpret_cast<const bf16x8 *>(xbase + a_off[sb] + m * 16 * kRowBytes);
+            bf[0] = *reinterpret_cast<const bf16x8 *>(wbase + b_off[sb]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < kNt; ++n) {
+                if (n + 1 < kNt)
+                    bf[(n + 1) & 1] =
+                        *reinterpret_cast<const bf16x8 *>(wbase + b_off[sb] + (n + 1) * 16 * kRowBytes);
+                // during the first MFMA step, one load between MFMA groups:
+                // the x blocks first, then W
+                if (sb == 0 && more) {
+                    if (n < kXBlocks) {
+                        __builtin_amdgcn_global_load_lds(xsrc[n] + koff, (lds_void *)(xd + n * 1024),
+                                                         16, 0, 0);
+                    } else if (n - kXBlocks < kMaxWBlocks) {
+                        if (n - kXBlocks < nw)
+                            __builtin_amdgcn_global_load_lds(wsrc[n - kXBlocks] + koff,
+                                                             (lds_void *)(wd + (n - kXBlocks) * 1024),
+                                                             16, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < kMt; ++m)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[n & 1], af[m], acc[m][n], 0,
+                                                                        0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
     }
