@@ -169,6 +169,30 @@ def test_select_edge_lengths_and_broadcast():
     compare_select(one, *run_select_gpu(one))
 
 
+@pytest.mark.parametrize("H,Di", [(64, 128), (48, 96)])
+def test_select_rank_paths_around_128_candidates(H, Di):
+    """Up to 128 selection blocks the top-k counts each block's rank on four
+    lanes with a quad sum; from 129 on, in segments added with LDS atomics.
+    J = nb / 2 + 1 = 127, 128, 129, 130 (sel 2, cmp 1) on both kernels (the
+    compile-time kernel at H 64 / Di 128, the general one at H 48 / Di 96);
+    the rows past each sequence's blocks are NaN, and the compile-time kernel
+    loads the fragments of its first tile before the key length is known."""
+    say(f"[select] rank paths around 128 candidates, H={H} Di={Di}")
+    case = gen.qsa_select_case(718 + H, N=4, H=H, Di=Di, Bcap=260, kbs=16, sel_ratio=2, cmp_ratio=1,
+                               topk=20)
+    kl = np.array([252 * 16 + 3, 254 * 16, 256 * 16 + 15, 258 * 16], dtype=np.int64)
+    keys = case["block_keys"].copy()
+    fresh = gen.bf16_bits(gen.rng_for(719 + H).standard_normal(keys.shape, dtype=np.float32))
+    for n in range(4):
+        nb = int(kl[n]) // 16
+        keys[n, :nb] = fresh[n, :nb]
+        keys[n, nb:] = gen.BF16_NAN
+    case = dict(case, block_keys=keys, key_length=kl)
+    got = run_select_gpu(case)
+    compare_select(case, *got)
+    assert [S.num_selection_blocks(int(x) // 16, 2, 1) for x in kl] == [127, 128, 129, 130]
+
+
 def test_select_invalid_lengths_counted():
     case = gen.qsa_select_case(712, N=3, H=16, Di=32, Bcap=8, kbs=16, sel_ratio=1, cmp_ratio=1,
                                topk=4)
