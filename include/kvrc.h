@@ -397,7 +397,10 @@ int32_t qsa_prepare(const void *raw_index_keys, void *block_keys, const int64_t 
  * Arguments:
  *   query         bf16 [N, H, Di]        H a multiple of 16 (<= 1024)
  *   block_keys    bf16 [N, Bcap, Di]     Di a multiple of 32 (<= 4096); rows
- *                                        >= nb are not read
+ *                                        >= nb do not affect the results
+ *                                        (they may be read, so the whole
+ *                                        array must be readable; any values,
+ *                                        NaN included)
  *   key_length    int64 [key_length_count], count 1 or N; read on the device
  *   scale         the score scale (e.g. 1 / sqrt(Di))
  *   sel_ratio     l'/d >= 1 (selection block / key block), cmp_ratio l/d >= 1
