@@ -280,17 +280,58 @@ __global__ __launch_bounds__(kThreads) void qsa_prepare_kernel(QsaArgs a, int64_
 
 // ---------------------------------------------------------------------------
 // Di = 128 and blocks of at most 64 rows: one wavefront per (sequence, new
-// block), lane l owning the dimension pair (2 l, 2 l + 1). Every row of the
-// block is one 256-byte load instruction of the wavefront, all issued before
-// the first is added, and each lane adds its pair down the rows in token
-// order as the rows arrive: no LDS and no barrier. The norm's chunk c (dims
-// 8 c .. 8 c + 7) lies on lanes 4 c .. 4 c + 3; its square sum is taken in
-// element order, then the 16 chunk partials are folded in halves (c + 8,
-// + 4, + 2, + 1): the same operations in the same order as the general
-// kernel, so the keys are bit-identical.
+// block), lane l owning the dimension pair (2 l, 2 l + 1) of the key. The
+// block's rows go straight from memory into LDS, four rows per 1 KiB load
+// (16 loads, all issued before the first is used: no staging registers, no
+// LDS stores); as each load lands, the lanes read their pair from its four
+// rows and add them to their running sums in token order. The norm's chunk c
+// (dims 8 c .. 8 c + 7) lies on lanes 4 c .. 4 c + 3; its square sum is
+// taken in element order, then the 16 chunk partials are folded in halves
+// (c + 8, + 4, + 2, + 1): the same operations in the same order as the
+// general kernel, so the keys are bit-identical.
 // ---------------------------------------------------------------------------
 constexpr int kWaveDi = 128;
 constexpr int kWaveMaxRows = 64;
+constexpr int kRowLoads = kWaveMaxRows / 4;     // 1 KiB loads: four 256-byte rows each
+constexpr int kCpolNt = 2;                      // cache policy of the row loads: non-temporal
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits until at most n vector memory loads of the
+// wavefront are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; the
+// other counters at their maxima, i.e. not waited for)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Adds rows 4 K .. 4 K + 3 of the staged block (row i at stage[64 i], one
+// dimension pair per lane) to the running sums once the K-th of the NK row
+// loads has landed, then recurses to the next four rows. Loads complete in
+// issue order and no load is issued after the row loads, so the K-th has
+// landed when at most NK - 1 - K loads are outstanding. Full: all 4 NK rows
+// belong to the block; otherwise rows i >= kbs add +0 (they hold a repeat of
+// the last row).
+template <int K, int NK, bool Full>
+struct RowGroupSum {
+    static __device__ __forceinline__ void run(const uint32_t *stage, int lane, int64_t kbs,
+                                               float &sum0, float &sum1)
+    {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NK - 1 - K));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = 4 * K + t;
+            const uint32_t raw = stage[i * 64 + lane];
+            const uint32_t v = Full || i < kbs ? raw : 0u;
+            sum0 = sum0 + bf16_lo(v);
+            sum1 = sum1 + bf16_hi(v);
+        }
+        RowGroupSum<K + 1, NK, Full>::run(stage, lane, kbs, sum0, sum1);
+    }
+};
+template <int NK, bool Full>
+struct RowGroupSum<NK, NK, Full> {
+    static __device__ __forceinline__ void run(const uint32_t *, int, int64_t, float &, float &) {}
+};
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float v)
@@ -376,20 +417,10 @@ __global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t
         return;
     const int64_t tau0 = b * kbs;                       // first token of the block
     const int64_t np = tau0 < P ? P - tau0 : 0;         // rows taken from the carried state
-    const uint32_t *past = reinterpret_cast<const uint32_t *>(a.past_raw + n * (kbs - 1) * Di) + lane;
-    const uint32_t *rawn = reinterpret_cast<const uint32_t *>(a.raw + n * L * Di) + lane;
-
-    // ---- every row of the block in flight at once (rows past kbs repeat the
-    // last row: the loads stay unconditional and are added as +0 below) ----
-    uint32_t w[kWaveMaxRows];
-#pragma unroll
-    for (int i = 0; i < kWaveMaxRows; ++i) {
-        const int64_t ii = i < kbs ? i : kbs - 1;
-        const uint32_t *src = ii < np ? past + ii * kPairs : rawn + (tau0 + ii - P) * kPairs;
-        w[i] = stream_load<uint32_t>(src);
-    }
     // this lane's outputs: dims d0 = 2 lane, d1 = d0 + 1; the RoPE covers
-    // dims [base, 128), output o = d - base
+    // dims [base, 128), output o = d - base. Its cos/sin and weight values are
+    // requested before the rows: no load may follow the row loads, whose
+    // completion is tracked by count below.
     const int64_t base = Di - Dr;
     const int d0 = 2 * lane;
     const bool rot = Dr && d0 >= base;
@@ -409,16 +440,31 @@ __global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t
     }
     const uint32_t gw = a.weight ? *reinterpret_cast<const uint32_t *>(a.weight + d0) : 0u;
 
-    // ---- block mean: float32 sum down the rows in token order -------------
-    // (a sum that starts at +0 is never -0, so the +0 terms past kbs leave it
-    // unchanged)
-    float sum0 = 0.0f, sum1 = 0.0f;
+    // ---- the block's rows straight into LDS: load k brings rows 4 k .. 4 k + 3
+    // (lane l: row 4 k + l / 16, 16-byte piece l % 16; the load writes lane l's
+    // 16 bytes at byte 16 l of its 1 KiB, so row i lands at stage[64 i]).
+    // Rows past kbs repeat the last row, so all 16 loads are always issued ---
+    __shared__ __align__(16) uint32_t stage[kWaveMaxRows * kPairs];
+    const int piece = lane & 15, sub = lane >> 4;
+    const uint16_t *pastb = a.past_raw + n * (kbs - 1) * Di + 8 * piece;
+    const uint16_t *rawb = a.raw + n * L * Di + 8 * piece;     // + (token - P) rows
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < kWaveMaxRows; ++i) {
-        const uint32_t v = i < kbs ? w[i] : 0u;
-        sum0 = sum0 + bf16_lo(v);
-        sum1 = sum1 + bf16_hi(v);
+    for (int k = 0; k < kRowLoads; ++k) {
+        const int64_t i = 4 * k + sub;
+        const int64_t ii = i < kbs ? i : kbs - 1;
+        const uint16_t *src = ii < np ? pastb + ii * Di : rawb + (tau0 + ii - P) * Di;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(stage + 256 * k), 16, 0, kCpolNt);
     }
+
+    // ---- block mean: float32 sum down the rows in token order, four rows
+    // at a time as their load lands (a sum that starts at +0 is never -0, so
+    // the +0 terms past kbs leave it unchanged) ------------------------------
+    float sum0 = 0.0f, sum1 = 0.0f;
+    if (kbs == kWaveMaxRows)
+        RowGroupSum<0, kRowLoads, true>::run(stage, lane, kbs, sum0, sum1);
+    else
+        RowGroupSum<0, kRowLoads, false>::run(stage, lane, kbs, sum0, sum1);
     const float fk = (float)kbs;
     const float m0 = sum0 / fk, m1 = sum1 / fk;
 

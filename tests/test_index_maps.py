@@ -8,6 +8,10 @@ Nothing here runs on the GPU.
   of 1 KiB writes byte 16 l from lane l (row l / 8 of the block, slot l % 8)
   and fetches piece (l % 8) ^ (l / 8); a fragment read (MFMA step s) takes
   row fr = l % 16 of a 16-row tile and piece 4 s + l / 16.
+* QSAPrepare rows (qsa_prepare.hip, Di = 128): load k of a block brings
+  rows 4 k .. 4 k + 3, lane l fetching 16-byte piece l % 16 of row
+  4 k + l / 16 and writing it at LDS byte 1024 k + 16 l; lane p then reads
+  the 4-byte word 64 i + p for the dimension pair (2 p, 2 p + 1) of row i.
 * Block selection (qsa_select.hip): the DPP lane permutations used by the
   reductions (quad permutes, row_ror:8, half-row and row mirrors), and the
   transposing reduction of the Q head sum and the eight-lane partial combine.
@@ -78,6 +82,24 @@ def test_mla_former_permutation_conflicted_for_eight_lanes():
     offs = [off(lane) for lane in range(64)]
     assert any(len({(o % 128) // 16 for o in offs[8 * g:8 * g + 8]}) < 8 for g in range(8))
     assert all(len({(o % 256) // 16 for o in offs[16 * g:16 * g + 16]}) == 16 for g in range(4))
+
+# ---------------------------------------------------------------------------
+# QSAPrepare direct row loads
+
+def test_qsa_row_loads_land_where_the_column_reads_look():
+    dims_at_byte = {}
+    for k in range(16):
+        for lane in range(64):
+            row, piece = 4 * k + lane // 16, lane % 16
+            byte = 1024 * k + 16 * lane
+            for e in range(8):                   # the piece's eight bf16 dims
+                dims_at_byte[byte + 2 * e] = (row, 8 * piece + e)
+    assert len(dims_at_byte) == 64 * 128         # every (row, dim) staged once
+    for i in range(64):
+        for p in range(64):
+            word = 64 * i + p
+            assert dims_at_byte[4 * word] == (i, 2 * p)          # low half
+            assert dims_at_byte[4 * word + 2] == (i, 2 * p + 1)  # high half
 
 # ---------------------------------------------------------------------------
 # DPP lane permutations inside a 16-lane row (the source lane of each lane)
