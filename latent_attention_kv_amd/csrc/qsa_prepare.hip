@@ -373,40 +373,56 @@ __global__ __launch_bounds__(64) void qsa_prepare_wave_kernel(QsaArgs a, int64_t
 
     if (j == nb_max) {
         // ---- carry state: tokens [t1, K) of the incomplete block ----------
-        // 16 pieces of 16 bytes per row; 8 per lane in flight; indices past
-        // the end repeat the last piece (load and store), so every load and
-        // store is unconditional
+        // At most kbs - 1 <= 63 rows of 16 pieces of 16 bytes: lane l takes
+        // pieces l + 64 k (k < 16), indices past the end repeating the last
+        // piece, and the rope row's values d = l, l + 64 (Dr <= 128). Every
+        // load is issued before the first store: one memory round trip.
         const int64_t r2 = K % kbs, t1 = K - r2;
+        if (r2 == 0)
+            return;
         const int total = (int)r2 * 16;
-        for (int e0 = lane; e0 < total; e0 += 64 * 8) {
-            u32x4 v[8];
+        u32x4 v[16];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int e = min(e0 + 64 * k, total - 1);
-                const int64_t tau = t1 + e / 16;
-                const uint16_t *src = tau < P
-                    ? a.past_raw + (n * (kbs - 1) + (tau - (P - r))) * Di
-                    : a.raw + (n * L + (tau - P)) * Di;
-                v[k] = *reinterpret_cast<const u32x4 *>(src + 8 * (e % 16));
+        for (int k = 0; k < 16; ++k) {
+            const int e = min(lane + 64 * k, total - 1);
+            const int64_t tau = t1 + e / 16;
+            const uint16_t *src = tau < P
+                ? a.past_raw + (n * (kbs - 1) + (tau - (P - r))) * Di
+                : a.raw + (n * L + (tau - P)) * Di;
+            v[k] = *reinterpret_cast<const u32x4 *>(src + 8 * (e % 16));
+        }
+        float cv[2] = {0.0f, 0.0f}, sv[2] = {0.0f, 0.0f};
+        if (Dr) {
+            const float *cr, *sr;
+            if (t1 < P) {
+                cr = a.past_rope + n * 2 * Dr;
+                sr = cr + Dr;
+            } else {
+                cr = a.rope_cos + (n * L + (t1 - P)) * Dr;
+                sr = a.rope_sin + (n * L + (t1 - P)) * Dr;
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int e = min(e0 + 64 * k, total - 1);
-                *reinterpret_cast<u32x4 *>(a.next_raw + (n * (kbs - 1) + e / 16) * Di + 8 * (e % 16)) = v[k];
+            for (int k = 0; k < 2; ++k) {
+                const int d = lane + 64 * k;
+                if (d < Dr) {
+                    cv[k] = cr[d];
+                    sv[k] = sr[d];
+                }
             }
         }
-        if (Dr && r2 > 0) {
-            for (int64_t d = lane; d < Dr; d += 64) {
-                float c, sn;
-                if (t1 < P) {
-                    c = a.past_rope[n * 2 * Dr + d];
-                    sn = a.past_rope[n * 2 * Dr + Dr + d];
-                } else {
-                    c = a.rope_cos[(n * L + (t1 - P)) * Dr + d];
-                    sn = a.rope_sin[(n * L + (t1 - P)) * Dr + d];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = min(lane + 64 * k, total - 1);
+            *reinterpret_cast<u32x4 *>(a.next_raw + (n * (kbs - 1) + e / 16) * Di + 8 * (e % 16)) = v[k];
+        }
+        if (Dr) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int d = lane + 64 * k;
+                if (d < Dr) {
+                    a.next_rope[n * 2 * Dr + d] = cv[k];
+                    a.next_rope[n * 2 * Dr + Dr + d] = sv[k];
                 }
-                a.next_rope[n * 2 * Dr + d] = c;
-                a.next_rope[n * 2 * Dr + Dr + d] = sn;
             }
         }
         return;
