@@ -353,6 +353,9 @@ def test_qsa_named_workload_bit_exact():
     (6, 65, 8, 2, 3), (1, 2048, 256, 256, 64), (3, 50, 136, 40, 2),
     (3, 130, 128, 128, 64), (2, 70, 128, 2, 33), (2, 90, 128, 64, 65),
     (1, 70, 4096, 64, 32),                                     # the largest Di accepted
+    # one-wavefront kernel: the smallest block (one carried row at most),
+    # blocks whose last load group is partial, the largest partial block
+    (3, 150, 128, 64, 2), (2, 77, 128, 64, 5), (2, 200, 128, 32, 63),
 ])
 @pytest.mark.parametrize("variant", ["full", "no_norm", "no_rope", "plain", "broadcast"])
 def test_qsa_shapes_and_features(N, L, Di, Dr, kbs, variant):
@@ -405,13 +408,13 @@ def test_qsa_invalid_lengths_counted_one_wavefront_kernel():
     np.testing.assert_array_equal(got, want_bk)
 
 
-@pytest.mark.parametrize("seed", [700, 701])
-def test_qsa_chained_calls_match_whole_history(seed):
+@pytest.mark.parametrize("seed,kbs", [(700, 16), (701, 16), (702, 64), (703, 5)])
+def test_qsa_chained_calls_match_whole_history(seed, kbs):
     """Random chunking of each sequence's token stream across calls, with the
     state carried by the library itself, equals (bit for bit) the oracle's
     single call over the whole stream."""
     rng = gen.rng_for(seed)
-    N, T, Di, Dr, kbs = 3, 400, 128, 64, 16
+    N, T, Di, Dr = 3, 400, 128, 64
     Bcap = T // kbs + 1
     raw = gen.bf16_bits(rng.standard_normal((N, T, Di)).astype(np.float32))
     pos = np.broadcast_to(np.arange(T), (N, T))
