@@ -12,6 +12,9 @@ Nothing here runs on the GPU.
   rows 4 k .. 4 k + 3, lane l fetching 16-byte piece l % 16 of row
   4 k + l / 16 and writing it at LDS byte 1024 k + 16 l; lane p then reads
   the 4-byte word 64 i + p for the dimension pair (2 p, 2 p + 1) of row i.
+  At most W row loads are in flight: W issued first, load K + W issued after
+  group K is added; the wait before group K allows min(NK - K, W) - 1
+  outstanding loads.
 * Block selection (qsa_select.hip): the DPP lane permutations used by the
   reductions (quad permutes, row_ror:8, half-row and row mirrors), and the
   transposing reduction of the Q head sum and the eight-lane partial combine.
@@ -100,6 +103,55 @@ def test_qsa_row_loads_land_where_the_column_reads_look():
             word = 64 * i + p
             assert dims_at_byte[4 * word] == (i, 2 * p)          # low half
             assert dims_at_byte[4 * word + 2] == (i, 2 * p + 1)  # high half
+
+def window_schedule(nk, w, extra_older=0):
+    """The wave's vector-memory program: ('load', k) and ('wait', n) in issue
+    order, extra_older loads (the cos/sin and weight values) first."""
+    prog = [("load", -1 - i) for i in range(extra_older)]
+    prog += [("load", k) for k in range(min(w, nk))]
+    for k in range(nk):
+        prog.append(("wait", min(nk - k, w) - 1))
+        prog.append(("use", k))
+        if k + w < nk:
+            prog.append(("load", k + w))
+    return prog
+
+def loads_done_at_each_use(prog):
+    """With in-order completion, a wait for at most n outstanding guarantees
+    every load but the n youngest issued so far: the set guaranteed at each use."""
+    issued, guaranteed, out = [], set(), {}
+    for op, v in prog:
+        if op == "load":
+            issued.append(v)
+        elif op == "wait":
+            guaranteed |= set(issued[:len(issued) - v] if v else issued)
+        else:
+            out[v] = set(guaranteed)
+    return out
+
+@pytest.mark.parametrize("w", range(1, 17))
+@pytest.mark.parametrize("extra", [0, 3])
+def test_qsa_row_window_waits_cover_each_group(w, extra):
+    prog = window_schedule(16, w, extra)
+    assert sorted(v for op, v in prog if op == "load" and v >= 0) == list(range(16))
+    done = loads_done_at_each_use(prog)
+    for k in range(16):
+        assert k in done[k]                       # the group's load has landed
+    # never more than w row loads in flight
+    inflight = 0
+    for op, v in prog:
+        if op == "load" and v >= 0:
+            inflight += 1
+            assert inflight <= w
+        elif op == "use":
+            inflight -= 1
+
+def test_qsa_row_window_pin_fails_with_a_wait_one_too_weak():
+    # waiting for min(NK - K, W) outstanding instead of that minus one lets a
+    # group be read before its load lands: the check above must catch it
+    prog = [(op, v + 1) if op == "wait" else (op, v) for op, v in window_schedule(16, 10)]
+    done = loads_done_at_each_use(prog)
+    assert any(k not in done[k] for k in range(16))
 
 # ---------------------------------------------------------------------------
 # DPP lane permutations inside a 16-lane row (the source lane of each lane)
