@@ -369,6 +369,15 @@ def test_qsa_shapes_and_features(N, L, Di, Dr, kbs, variant):
     compare_qsa(run_qsa_gpu(case), oracle.run_qsa_case(case), exact=True)
 
 
+def test_qsa_more_blocks_than_the_chip_holds_at_once():
+    """100 sequences x 2048 tokens on the one-wavefront kernel: 3300
+    workgroups, more than are resident at once (16 KiB of LDS each, ten per
+    compute unit), so compute units run several in turn on the same LDS."""
+    say("[parity] qsa N=100 L=2048 Di=128 Dr=64 kbs=64")
+    case = gen.qsa_case(620, N=100, L=2048, Di=128, Dr=64, kbs=64, past_max=8192)
+    compare_qsa(run_qsa_gpu(case), oracle.run_qsa_case(case), exact=True)
+
+
 def test_qsa_invalid_lengths_counted():
     case = gen.qsa_case(600, N=4, L=40, Di=64, Dr=16, kbs=8, past_max=30)
     kl = case["key_length"].copy()

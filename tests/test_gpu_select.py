@@ -149,6 +149,16 @@ def test_select_shapes(N, H, Di, Bcap, kbs, sel, cmp, topk):
     compare_select(case, *run_select_gpu(case))
 
 
+def test_select_more_sequences_than_the_chip_holds_at_once():
+    """600 sequences on the compile-time kernel: more workgroups than are
+    resident at once (LDS and registers hold two per compute unit), so
+    compute units run several in turn on the same LDS."""
+    say("[select] N=600 H=64 Di=128 Bcap=256")
+    case = gen.qsa_select_case(719, N=600, H=64, Di=128, Bcap=256, kbs=64, sel_ratio=2, cmp_ratio=1,
+                               topk=16, kl_lo=64)
+    compare_select(case, *run_select_gpu(case))
+
+
 def test_select_edge_lengths_and_broadcast():
     """key_length below one block (no block), exactly the capacity, a
     broadcast key_length, and topk beyond the block count (padding)."""
