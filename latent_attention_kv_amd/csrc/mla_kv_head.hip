@@ -44,7 +44,7 @@
 //     only for its own loads, then one barrier publishes them;
 //   * the two workgroups of a pair are blockIdx b and b + 8, which the
 //     dispatcher places on the same XCD: their x rows meet in that XCD's L2;
-//   * staged rows are 64 bytes with their four 16-byte pieces permuted
+//   * staged rows are 128 bytes with their eight 16-byte pieces permuted
 //     (swz below) so that every eight lanes of a fragment read, which the
 //     LDS serves together, hit eight different 16-byte bank groups;
 //   * epilogue: the MFMAs take W as their first operand, so each lane's
