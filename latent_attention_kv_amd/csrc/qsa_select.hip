@@ -31,9 +31,10 @@
 //     its scores in registers, a longer one takes three sweeps over its
 //     chunks (maxima, sums, Q), each recomputing its tiles;
 //   * pooling on LDS; top-k by rank: every block gets a 64-bit key (score
-//     above, index below) and lands at the number of larger keys, counted in
-//     segments spread over the workgroup; above kRankMax candidates,
-//     repeated arg-max on one wavefront.
+//     above, index below) and lands at the number of larger keys, counted by
+//     four lanes per candidate (up to 128 candidates) or in segments spread
+//     over the workgroup; above kRankMax candidates, repeated arg-max on one
+//     wavefront.
 // Float32 throughout (exp2f of the device library); deterministic: every
 // floating-point reduction has a fixed order.
 #include "kvrc_launch.hpp"
