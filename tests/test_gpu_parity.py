@@ -453,6 +453,40 @@ def test_qsa_chained_calls_match_whole_history(seed, kbs):
     assert torch.equal(bk.view(torch.int16), dbf(want_bk).view(torch.int16))
 
 
+def test_qsa_graph_replays_match_the_oracle():
+    """QSAPrepare captured in a HIP graph: every replay, with the outputs reset
+    eagerly in between, writes the block keys and the next carry state the
+    oracle gives, bit for bit."""
+    case = gen.qsa_case(630, N=6, L=300, Di=128, Dr=64, kbs=64, past_max=500)
+    want = oracle.run_qsa_case(case)
+    N, Di, kbs, Dr = case["N"], case["Di"], case["kbs"], case["Dr"]
+    ins = (dbf(case["raw_index_keys"]), None, dt(case["key_length"]), dt(case["rope_cos"]),
+           dt(case["rope_sin"]), dbf(case["k_norm_weight"]), dbf(case["past_incomplete_raw_keys"]),
+           dt(case["past_incomplete_rope"]))
+    bk = dbf(case["caches"]["block_keys"].numpy())
+    nraw = dbf(np.full((N, kbs - 1, Di), 0x7FC0, dtype=np.uint16))
+    nrope = torch.full((N, 2 * Dr), float("nan"), device=DEV)
+
+    def call():
+        k.qsa_prepare(ins[0], bk, *ins[2:], nraw, nrope, key_block_size=kbs, eps=case["eps"])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(4):
+        bk.view(torch.int16).fill_(gen.BF16_SENTINEL)       # eager reset between replays
+        nraw.view(torch.int16).fill_(0x7FC0)
+        nrope.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare_qsa((bk, nraw, nrope), want, exact=True)
+
+
 def test_graph_replays_match_eager():
     """The bench replays captured launches: every replay, with eager work and
     synchronisation in between, must give the eager (oracle-equal) result."""

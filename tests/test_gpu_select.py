@@ -159,6 +159,42 @@ def test_select_more_sequences_than_the_chip_holds_at_once():
     compare_select(case, *run_select_gpu(case))
 
 
+def test_select_graph_replays_match_eager():
+    """Block selection captured in a HIP graph: every replay, with the outputs
+    reset eagerly in between, gives the eager call's scores and indices bit
+    for bit (the kernel is deterministic), and those meet the oracle's bar."""
+    case = gen.qsa_select_case(720, N=20, H=64, Di=128, Bcap=256, kbs=64, sel_ratio=2, cmp_ratio=1,
+                               topk=16, kl_lo=64)
+    want_scores, want_idx = run_select_gpu(case)
+    compare_select(case, want_scores, want_idx)
+    N = case["N"]
+    q, keys = dbf(case["query"]), dbf(case["block_keys"])
+    kl = torch.from_numpy(case["key_length"]).to(DEV)
+    scores = torch.full((N, case["Jcap"]), -7.0, dtype=torch.float32, device=DEV)
+    idx = torch.full((N, case["topk"]), -7, dtype=torch.int32, device=DEV)
+
+    def call():
+        k.qsa_select_topk(q, keys, kl, scores, idx, key_block_size=case["kbs"],
+                          sel_ratio=case["sel_ratio"], cmp_ratio=case["cmp_ratio"],
+                          scale=case["scale"])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(4):
+        scores.fill_(-7.0)                                   # eager reset between replays
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(scores.cpu().numpy().view(np.uint32), want_scores.view(np.uint32)), rep
+        assert np.array_equal(idx.cpu().numpy(), want_idx), rep
+
+
 def test_select_edge_lengths_and_broadcast():
     """key_length below one block (no block), exactly the capacity, a
     broadcast key_length, and topk beyond the block count (padding)."""
